@@ -1,0 +1,76 @@
+// Internal layout helpers shared by the host pack code and the device kernels
+// of libsvdq (not part of the public ABI). Everything here is plain integer
+// arithmetic on sizes and offsets.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "svdq.h"
+
+namespace svdq {
+
+constexpr int kGroupInt4 = 64;    // INT4 scale group along K
+constexpr int kBlockMx = 32;      // MXFP4 scale block along K
+constexpr int kStepK = 128;       // K per stage-1 step (two INT4 groups)
+constexpr int kMaxRank = 128;
+
+inline int rank32(int r) { return (r + 31) / 32 * 32; }
+inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+inline svdq_status check_desc(const svdq_layer_desc* d) {
+  if (!d) return SVDQ_ERR_NULL;
+  if (d->format != SVDQ_FMT_INT4_G64 && d->format != SVDQ_FMT_MXFP4_G32) return SVDQ_ERR_FORMAT;
+  if (d->K <= 0 || d->N <= 0 || d->K % 256 != 0 || d->N % 32 != 0) return SVDQ_ERR_SHAPE;
+  if (d->K > 65536 || d->N > 65536) return SVDQ_ERR_SHAPE;
+  if (d->rank < 0 || d->rank > kMaxRank || d->rank % 16 != 0) return SVDQ_ERR_SHAPE;
+  if (d->rank > d->K || d->rank > d->N) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+
+inline size_t scale_bytes(const svdq_layer_desc* d, int64_t rows) {
+  return d->format == SVDQ_FMT_INT4_G64 ? (size_t)rows * (d->K / kGroupInt4) * 4
+                                        : (size_t)rows * (d->K / kBlockMx);
+}
+// Row stride of the INT4 activation scales [K/64][act_rows(M)] in the workspace.
+inline int64_t act_rows(int64_t M) { return (M + 15) / 16 * 16; }
+
+inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
+  svdq_packed_sizes s;
+  s.mu = (size_t)d->K * 4;
+  s.l1 = (size_t)d->K * rank32(d->rank) * 2;
+  s.l2 = (size_t)d->N * rank32(d->rank) * 2;
+  s.qw = (size_t)d->N * d->K / 2;
+  s.sw = scale_bytes(d, d->N);
+  s.bias = (size_t)d->N * 2;
+  return s;
+}
+
+// Workspace: [qX: M x K/2][sX][Z: M x rank32 bf16], each 256-byte aligned.
+struct WsLayout {
+  size_t qx, sx, z, total;
+};
+inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
+  WsLayout w;
+  w.qx = 0;
+  w.sx = align256((size_t)M * d->K / 2);
+  w.z = w.sx + align256(scale_bytes(d, d->format == SVDQ_FMT_INT4_G64 ? act_rows(M) : M));
+  w.total = w.z + align256((size_t)M * rank32(d->rank) * 2);
+  return w;
+}
+
+// L1 device layout: [K/128][rank32/32][t=8][lane=64][8] bf16 where lane = 32h + c
+// holds L1[128 s + 64 h + 8 t + j][32 cb + c], j = 0..7.
+inline size_t l1_index(int K, int r32, int k, int col) {
+  (void)K;
+  int s = k / 128, kk = k % 128, h = kk / 64, t = (kk % 64) / 8, j = kk % 8;
+  int cb = col / 32, c = col % 32;
+  return ((((size_t)s * (r32 / 32) + cb) * 8 + t) * 64 + (32 * h + c)) * 8 + j;
+}
+
+// MXFP4 scale layout [rows][K/256][h=2][s=4]: block kb = 8c + 2s + h.
+inline size_t mx_scale_index(int K, int64_t row, int kb) {
+  int c = kb / 8, s = (kb % 8) / 2, h = kb % 2;
+  return (((size_t)row * (K / 256) + c) * 2 + h) * 4 + s;
+}
+
+}  // namespace svdq

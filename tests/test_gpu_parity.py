@@ -1,0 +1,208 @@
+"""GPU parity of libsvdq's HIP path against the CPU oracle (MI355X only).
+
+Bars (stated here, applied below):
+  - activation codes, scales and INT4 int32 group sums: bit-exact;
+  - Z = x_hat L1 (bf16 on the device): relative Frobenius <= 1e-2, max abs <= 2e-2 max|Z|;
+  - Y: relative Frobenius <= 1e-2 and max abs <= 2e-2 max|Y|.
+Every input is seeded and synthetic (bit_svdquant_diffusion_amd.synth).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import bit_svdquant_diffusion_amd as S
+from bit_svdquant_diffusion_amd import synth
+from oracle import svdq_oracle as O
+from tests import gpu_cases as C
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    S.lib()
+    yield
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _spec(name, M, K, N, r, fmt, seed, **kw):
+    return synth.LayerSpec(name, M, K, N, r, fmt, seed, **kw)
+
+
+SMALL = [
+    _spec("c0", 256, 512, 512, 16, "int4", 0),
+    _spec("c0_fp4", 256, 512, 512, 16, "mxfp4", 0),
+    _spec("ragged_m300", 300, 768, 544, 32, "int4", 11),
+    _spec("ragged_m300_fp4", 300, 768, 544, 32, "mxfp4", 11),
+    _spec("m1", 1, 512, 256, 16, "int4", 12),
+    _spec("m1_fp4", 1, 512, 256, 16, "mxfp4", 12),
+    _spec("m17_r0", 17, 256, 96, 0, "int4", 13),
+    _spec("m17_r0_fp4", 17, 256, 96, 0, "mxfp4", 13),
+    _spec("r128", 200, 256, 160, 128, "int4", 14),
+    _spec("r128_fp4", 200, 256, 160, 128, "mxfp4", 14),
+    _spec("wide_k", 96, 2048, 64, 48, "int4", 15),
+]
+
+
+def _run_stage1(spec):
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    ws = torch.full((S.workspace_bytes(layer, spec.M),), 0xFF, dtype=torch.uint8, device="cuda")
+    S.stage1(layer, dev, x, ws)
+    torch.cuda.synchronize()
+    return layer, dev, x, ws
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_stage1_codes_scales_z(spec):
+    _say(f"[stage1] {spec}")
+    layer, dev, x, ws = _run_stage1(spec)
+    got = S.unpack_workspace(layer, spec.M, ws.cpu().numpy())
+    ref = C.oracle_pack(spec)
+    lay = C.layer_data(spec)
+    y, parts = O.forward(ref, lay.x, return_parts=True)
+    assert np.array_equal(got["codes"], parts["qx"].astype(np.int8)), "activation codes"
+    assert np.array_equal(got["scales"], parts["sx"]), "activation scales"
+    if spec.rank:
+        zr = parts["z"]
+        d = got["z"] - zr
+        assert np.linalg.norm(d) <= 1e-2 * np.linalg.norm(zr)
+        assert np.abs(d).max() <= 2e-2 * np.abs(zr).max()
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_forward_matches_oracle(spec):
+    _say(f"[forward] {spec}")
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    ws = torch.full((S.workspace_bytes(layer, spec.M),), 0xFF, dtype=torch.uint8, device="cuda")
+    y = torch.full((spec.M, spec.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    S.linear_forward(layer, dev, x, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    yg = C.bf16_tensor_to_f32(y)
+    ref = C.oracle_pack(spec)
+    yr = O.forward(ref, C.layer_data(spec).x)
+    fro, mx = C.check_y(yg, yr, spec.name)
+    _say(f"  rel_fro={fro:.2e} max_rel={mx:.2e}")
+
+
+@pytest.mark.parametrize("spec", [s for s in SMALL if s.fmt == "int4"], ids=lambda s: s.name)
+def test_int4_group_sums_bit_exact(spec):
+    _say(f"[group sums] {spec}")
+    layer, dev, x, ws = _run_stage1(spec)
+    p = S.debug_int4_group_sums(layer, dev, ws, spec.M, 0, spec.M, 0, spec.N)
+    torch.cuda.synchronize()
+    ref = C.oracle_pack(spec)
+    xh = O.smooth_activations(C.layer_data(spec).x, ref["mu"])
+    qx, _ = O.quant_int4_rows(xh)
+    want = O.int4_group_sums(qx, ref["qw"])
+    assert np.array_equal(p.cpu().numpy(), want)
+
+
+def test_group_sums_window():
+    spec = SMALL[2]
+    layer, dev, x, ws = _run_stage1(spec)
+    p = S.debug_int4_group_sums(layer, dev, ws, spec.M, 131, 150, 67, 200)
+    torch.cuda.synchronize()
+    ref = C.oracle_pack(spec)
+    qx, _ = O.quant_int4_rows(O.smooth_activations(C.layer_data(spec).x, ref["mu"]))
+    want = O.int4_group_sums(qx[131:281], ref["qw"][67:267])
+    assert np.array_equal(p.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_deterministic_and_m0(fmt):
+    spec = _spec("det", 300, 768, 544, 32, fmt, 11)
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    y1 = S.linear_forward(layer, dev, x)
+    y2 = S.linear_forward(layer, dev, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # M == 0: no-op
+    y0 = S.linear_forward(layer, dev, x[:0])
+    assert y0.shape == (0, spec.N)
+
+
+def test_rows_are_independent():
+    """A row's output does not depend on the other rows in the batch (ragged tiles)."""
+    spec = _spec("indep", 300, 768, 544, 32, "int4", 11)
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    full = S.linear_forward(layer, dev, x)
+    part = S.linear_forward(layer, dev, x[257:300].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(full[257:300].view(torch.int16), part.view(torch.int16))
+
+
+def test_library_pack_end_to_end():
+    """svdq_pack_weights (randomized SVD) + forward stays within the Y bar of the oracle."""
+    spec = SMALL[0]
+    lay = C.layer_data(spec)
+    ax = np.abs(lay.x).max(axis=0)
+    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+    lin = S.SVDQLinear(layer, S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=3))
+    y = lin(C.x_device(spec))
+    torch.cuda.synchronize()
+    ref = C.oracle_pack(spec)
+    C.check_y(C.bf16_tensor_to_f32(y), O.forward(ref, lay.x), "library pack")
+
+
+def test_bad_device_args_rejected():
+    spec = SMALL[0]
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(S.SvdqError) as e:
+        S.linear_forward(layer, dev, x, workspace=ws)
+    assert e.value.status == 4
+    xm = torch.empty(spec.M * spec.K + 1, dtype=torch.bfloat16, device="cuda")[1:].view(spec.M, spec.K)
+    with pytest.raises(S.SvdqError) as e:
+        S.linear_forward(layer, dev, xm)
+    assert e.value.status == 2
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads (the configurations the benchmark times), sampled rows
+# ----------------------------------------------------------------------------
+FULL = [synth.config_layers(i)[0] for i in (1, 2, 3)] + synth.config_layers(4)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("spec", FULL, ids=lambda s: s.name)
+def test_full_size_sampled(spec):
+    _say(f"[full] {spec}")
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    ws = torch.full((S.workspace_bytes(layer, spec.M),), 0xFF, dtype=torch.uint8, device="cuda")
+    y = torch.full((spec.M, spec.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    S.linear_forward(layer, dev, x, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    lay = C.layer_data(spec)
+    ref = C.oracle_pack(spec)
+    # codes and scales of every row, bit-exact
+    got = S.unpack_workspace(layer, spec.M, ws.cpu().numpy())
+    xh = O.smooth_activations(lay.x, ref["mu"])
+    qx, sx = O.quantize_activations(xh, spec.fmt)
+    assert np.array_equal(got["codes"], qx.astype(np.int8))
+    assert np.array_equal(got["scales"], sx)
+    # Y on sampled rows (rows are independent in every step)
+    rows = C.sample_rows(spec.M)
+    yr = O.forward(ref, lay.x[rows])
+    yg = C.bf16_tensor_to_f32(y)[rows]
+    fro, mx = C.check_y(yg, yr, spec.name)
+    _say(f"  rows={len(rows)} rel_fro={fro:.2e} max_rel={mx:.2e}")
+    if spec.fmt == "int4":
+        m0 = int(rows[len(rows) // 2])
+        mc = min(64, spec.M - m0)
+        p = S.debug_int4_group_sums(layer, dev, ws, spec.M, m0, mc, spec.N - 96, 96)
+        torch.cuda.synchronize()
+        want = O.int4_group_sums(qx[m0:m0 + mc], ref["qw"][spec.N - 96:])
+        assert np.array_equal(p.cpu().numpy(), want)

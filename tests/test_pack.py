@@ -1,0 +1,112 @@
+"""Host pack of libsvdq (C++, no GPU) against the CPU oracle.
+
+mu is bit-exact; given the oracle's smoothing and bf16 factors the library's
+residual codes and scales are bit-exact; the library's own randomized SVD
+lands within the Eckart-Young bound of the oracle's exact truncated SVD."""
+import numpy as np
+import pytest
+
+import bit_svdquant_diffusion_amd as S
+from bit_svdquant_diffusion_amd import synth
+from oracle import svdq_oracle as O
+
+
+def _layer(spec_idx=0, fmt=None, K=None, N=None, r=None, M=None, seed=None):
+    spec = synth.config_layers(spec_idx)[0]
+    if any(v is not None for v in (fmt, K, N, r, M, seed)):
+        spec = synth.LayerSpec("t", M or spec.M, K or spec.K, N or spec.N,
+                               spec.rank if r is None else r, fmt or spec.fmt,
+                               spec.seed if seed is None else seed)
+    return spec, synth.make_layer(spec)
+
+
+CASES = [
+    dict(),                                  # config 0: 256x512->512 r16 INT4
+    dict(fmt="mxfp4"),                       # same shapes, MXFP4
+    dict(K=256, N=96, r=0, M=40, seed=3),    # no low-rank branch
+    dict(K=256, N=128, r=128, M=40, seed=4), # rank == min(K, N) limit of the ABI
+    dict(K=768, N=224, r=48, M=64, seed=5, fmt="mxfp4"),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_quantize_residual_bit_exact(case):
+    spec, lay = _layer(**case)
+    ax = np.abs(lay.x).max(axis=0)
+    ref = O.pack(lay.w_lin, lay.bias, ax, spec.rank, spec.fmt)
+    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+    host = S.quantize_residual(layer, lay.w_lin, lay.bias, ref["mu"],
+                               O.bf16_to_bits(ref["l1"]), O.bf16_to_bits(ref["l2"]))
+    u = S.unpack_weights(layer, host)
+    assert np.array_equal(u["mu"], ref["mu"])
+    want_codes = ref["qw"].astype(np.int8)
+    assert np.array_equal(u["codes"], want_codes)
+    assert np.array_equal(u["scales"], ref["sw"])
+    assert np.array_equal(u["l1"], O.bf16_to_bits(ref["l1"]))
+    assert np.array_equal(u["l2"], O.bf16_to_bits(ref["l2"]))
+    assert np.array_equal(u["bias"], O.bf16_to_bits(lay.bias))
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_pack_weights_smoothing_and_svd(case):
+    spec, lay = _layer(**case)
+    ax = np.abs(lay.x).max(axis=0)
+    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+    host = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=7)
+    u = S.unpack_weights(layer, host)
+    _, mu = O.smoothing_factors(ax, lay.w_lin)
+    assert np.array_equal(u["mu"], mu)                                   # bit-exact
+    wh = O.smoothed_weight(lay.w_lin, mu)
+    l1 = O.bf16_from_bits(u["l1"]).astype(np.float64)
+    l2 = O.bf16_from_bits(u["l2"]).astype(np.float64)
+    err_lib = np.sum((wh - l1 @ l2) ** 2)
+    ol1, ol2 = O.low_rank_factors(wh, spec.rank, round_bf16=True)
+    err_or = np.sum((wh - ol1.astype(np.float64) @ ol2.astype(np.float64)) ** 2)
+    sv = np.linalg.svd(wh, compute_uv=False)
+    tail = np.sum(sv[spec.rank:] ** 2)
+    # randomized SVD within 1e-3 of the exact truncated SVD (both bf16-rounded)
+    assert err_lib <= err_or * (1 + 1e-3) + 1e-12 * np.sum(sv ** 2)
+    assert err_lib >= tail * (1 - 1e-9)
+    # the codes are the oracle's quantization of the residual against these factors
+    ref = O.pack(lay.w_lin, lay.bias, ax, spec.rank, spec.fmt,
+                 factors=(u["mu"], O.bf16_from_bits(u["l1"]), O.bf16_from_bits(u["l2"])))
+    assert np.array_equal(u["codes"], ref["qw"].astype(np.int8))
+    assert np.array_equal(u["scales"], ref["sw"])
+
+
+def test_pack_deterministic_and_seeded():
+    spec, lay = _layer()
+    ax = np.abs(lay.x).max(axis=0)
+    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+    a = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=1)
+    b = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=1)
+    for n in S.PACKED_FIELDS:
+        assert np.array_equal(a[n], b[n])
+
+
+def test_pack_null_bias_is_zero():
+    spec, lay = _layer(K=256, N=64, r=16, M=8, seed=9)
+    ax = np.abs(lay.x).max(axis=0)
+    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+    u = S.unpack_weights(layer, S.pack_weights(layer, lay.w_lin, None, ax))
+    assert np.all(u["bias"] == 0)
+
+
+def test_device_layout_of_l1_matches_stage1_order():
+    """L1 is stored so that lane 32h+c of MFMA t in step s holds L1[128s+64h+8t+j][32cb+c]."""
+    K, N, r = 256, 64, 48
+    layer = S.Layer(K, N, r, "int4")
+    rng = np.random.default_rng(2)
+    l1 = O.bf16_to_bits(O.to_bf16(rng.standard_normal((K, r))))
+    l2 = O.bf16_to_bits(O.to_bf16(rng.standard_normal((r, N))))
+    host = S.quantize_residual(layer, rng.standard_normal((N, K)).astype(np.float32), None,
+                               np.ones(K, np.float32), l1, l2)
+    dev_l1 = host["l1"].view(np.uint16).reshape(K // 128, 2, 8, 64, 8)   # r32 = 64
+    for (k, c) in [(0, 0), (5, 47), (200, 33), (255, 16)]:
+        s, kk = divmod(k, 128)
+        h, rem = divmod(kk, 64)
+        t, j = divmod(rem, 8)
+        assert dev_l1[s, c // 32, t, 32 * h + c % 32, j] == l1[k, c]
+    assert np.all(dev_l1[:, 1, :, :, :][:, :, np.arange(64) % 32 >= 16, :] == 0)  # padded cols
+    dev_l2 = host["l2"].view(np.uint16).reshape(N, 64)
+    assert np.array_equal(dev_l2[:, :r], l2.T) and np.all(dev_l2[:, r:] == 0)
