@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the SVDQuant W4A4 linear on one MI355X.
+
+A step is one svdq_linear_forward (kernel 1: smoothing + 4-bit activation
+quantization + X_hat L1; kernel 2: 4-bit GEMM + low-rank up-projection + bias)
+over one batch of synthetic input already resident in HBM. The workload is
+the FLUX-style MLP up-projection M=4608 tokens, K=3072 -> N=12288, rank 32,
+MXFP4 (E2M1 + E8M0 per 32) -- the 4608x3072x12288 layer. `value` is effective
+TOPS = 2*M*N*K / time per step (the low-rank flops are not counted).
+
+Also measured in the same run: the GEMM kernel's average duration with HIP
+events on the library's stream (roofline against the MXFP4 dense MFMA peak),
+kernel 1's achieved HBM bandwidth, INT4 layers of the same family as a
+secondary line, and the CPU oracle on a bounded sample of rows (baseline only).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SVDQuant W4A4 linear effective TOPS at 4608×3072×12288; % of MFMA peak"
+PEAK_TFLOPS = {"mxfp4": 10100.0, "int4": 5000.0}   # MI355X dense MFMA: FP4 10.1 PF, INT8 5.0 POPS
+PEAK_HBM_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm_mxfp4_mlp_up_4608x3072x12288_counters.md")
+GEMM_SOURCE = os.path.join(ROOT, "bit_svdquant_diffusion_amd", "csrc", "svdq_gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_workload(spec, rotate, torch, S, synth, seed=0):
+    """Pack the layer with the library (randomized SVD) and replicate inputs,
+    outputs, workspaces and packed weights `rotate` times in HBM."""
+    import numpy as np
+    t0 = time.time()
+    lay = synth.make_layer(spec)
+    ax = np.abs(lay.x).max(axis=0)
+    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+    host = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=seed)
+    log(f"  packed {spec.name} in {time.time() - t0:.1f}s")
+    x0 = torch.from_numpy(lay.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    sets = []
+    wsb = S.workspace_bytes(layer, spec.M)
+    for _ in range(rotate):
+        dev = S.to_device(layer, host)
+        sets.append(dict(
+            dev=dev, x=x0.clone(),
+            ws=torch.empty(wsb, dtype=torch.uint8, device="cuda"),
+            y=torch.empty((spec.M, spec.N), dtype=torch.bfloat16, device="cuda")))
+    return layer, host, lay, sets
+
+
+def time_forward(layer, sets, steps, warmup, torch, S):
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        s = sets[i % len(sets)]
+        S.linear_forward(layer, s["dev"], s["x"], y=s["y"], workspace=s["ws"], stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        S.linear_forward(layer, s["dev"], s["x"], y=s["y"], workspace=s["ws"], stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def time_split(layer, sets, steps, warmup, torch, S):
+    """Same steps as stage1 + gemm with events around each kernel (same stream)."""
+    stream = torch.cuda.current_stream()
+    M = sets[0]["x"].shape[0]
+    for i in range(warmup):
+        s = sets[i % len(sets)]
+        S.stage1(layer, s["dev"], s["x"], s["ws"], stream=stream)
+        S.gemm(layer, s["dev"], s["ws"], M, s["y"], stream=stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        ev[i][0].record(stream)
+        S.stage1(layer, s["dev"], s["x"], s["ws"], stream=stream)
+        ev[i][1].record(stream)
+        S.gemm(layer, s["dev"], s["ws"], M, s["y"], stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    t2 = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return t1, t2
+
+
+def stage1_bytes(spec):
+    """Algorithmic HBM bytes of kernel 1: read X (bf16) and mu, L1; write codes, scales, Z."""
+    r32 = (spec.rank + 31) // 32 * 32
+    scale = spec.M * spec.K // 64 * 4 if spec.fmt == "int4" else spec.M * spec.K // 32
+    return (spec.M * spec.K * 2 + spec.K * 4 + spec.K * r32 * 2 + spec.M * spec.K // 2 + scale
+            + spec.M * r32 * 2)
+
+
+def gemm_bytes(spec):
+    """Algorithmic HBM bytes of kernel 2: read codes + scales of X and W, Z, L2, bias; write Y."""
+    r32 = (spec.rank + 31) // 32 * 32
+    g = 64 if spec.fmt == "int4" else 32
+    sbytes = 4 if spec.fmt == "int4" else 1
+    return ((spec.M + spec.N) * spec.K // 2 + (spec.M + spec.N) * spec.K // g * sbytes
+            + (spec.M + spec.N) * r32 * 2 + spec.N * 2 + spec.M * spec.N * 2)
+
+
+def traffic_from_profile():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken on the current GEMM source (sha256 recorded in the summary)."""
+    try:
+        txt = open(PROFILE_COUNTERS).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_sha and m_b) or m_sha.group(1) != src:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(layer, host, lay, spec, budget_s):
+    """The oracle's forward on a bounded sample of the same workload's rows,
+    with the same packed weights (logical values), on the host's cores."""
+    import numpy as np
+    from oracle import svdq_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    import bit_svdquant_diffusion_amd as S
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    u = S.unpack_weights(layer, host)
+    packed = dict(fmt=spec.fmt, mu=u["mu"], l1=O.bf16_from_bits(u["l1"]),
+                  l2=O.bf16_from_bits(u["l2"]), bias=O.bf16_from_bits(u["bias"]),
+                  qw=u["codes"] if spec.fmt == "int4" else u["codes"].astype(np.uint8),
+                  sw=u["scales"])
+    import contextlib
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        rows = 64
+        while True:
+            t0 = time.perf_counter()
+            O.forward(packed, lay.x[:rows])
+            t = time.perf_counter() - t0
+            if t >= 0.5 * budget_s or rows >= spec.M:
+                break
+            rows = int(min(spec.M, max(2 * rows, rows * 0.8 * budget_s / max(t, 1e-3)) // 64 * 64))
+    tops = 2.0 * rows * spec.N * spec.K / t / 1e12
+    return dict(value=round(tops, 6), unit="TOPS", cores=cores, kind="oracle",
+                sample=f"{rows} of {spec.M} token rows of the same layer ({spec.M}x{spec.K}->{spec.N}, "
+                       f"r{spec.rank}, {spec.fmt}); oracle forward (NumPy float64) took {t:.1f}s; "
+                       f"pack excluded")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="distinct buffer sets cycled (defeats the 256 MB MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the layer shards over tokens with no exchange, see the "
+              f"design notes. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_svdquant_diffusion_amd as S
+    from bit_svdquant_diffusion_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    S.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    spec = synth.config_layers(2)[0]          # 4608 x 3072 -> 12288, r32, MXFP4
+    layer, host, lay, sets = make_workload(spec, args.rotate, torch, S, synth)
+    flops = 2.0 * spec.M * spec.N * spec.K
+
+    ms, wall_ms = time_forward(layer, sets, args.steps, args.warmup, torch, S)
+    tops = flops / (ms * 1e-3) / 1e12
+    log(f"forward: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us), {tops:.1f} effective TOPS")
+    t1, t2 = time_split(layer, sets, args.steps, args.warmup, torch, S)
+    gemm_tflops = flops / (t2 * 1e-3) / 1e12
+    s1_gbs = stage1_bytes(spec) / (t1 * 1e-3) / 1e9
+    log(f"stage1 {t1 * 1e3:.1f} us ({s1_gbs:.0f} GB/s), gemm {t2 * 1e3:.1f} us ({gemm_tflops:.1f} TFLOP/s)")
+
+    traffic = traffic_from_profile()
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "FLUX-style MLP up-projection, MXFP4 SVDQuant W4A4 linear",
+                   "M": spec.M, "K": spec.K, "N": spec.N, "rank": spec.rank, "format": spec.fmt,
+                   "group": 32, "io": "bf16", "parallelism": "single GPU"},
+        "pct_of_mfma_peak": round(100.0 * tops / PEAK_TFLOPS["mxfp4"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_TFLOPS["mxfp4"],
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_TFLOPS["mxfp4"], 4),
+                     "traffic": traffic, "kernel": "gemm_mxfp4_kernel<256,256>",
+                     "kernel_avg_us": round(t2 * 1e3, 2), "algorithmic_bytes": gemm_bytes(spec)},
+        "stage1": {"kernel": "stage1_kernel<MXFP4>", "avg_us": round(t1 * 1e3, 2), "bound": "hbm",
+                   "achieved": round(s1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(s1_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": stage1_bytes(spec)},
+    }
+    if not args.no_secondary:
+        sec = []
+        for idx in (3, 1):
+            sp = synth.config_layers(idx)[0]
+            del sets
+            torch.cuda.empty_cache()
+            l2, _, _, sets = make_workload(sp, args.rotate, torch, S, synth)
+            ms2, _ = time_forward(l2, sets, max(10, args.steps // 2), args.warmup, torch, S)
+            a1, a2 = time_split(l2, sets, max(10, args.steps // 2), args.warmup, torch, S)
+            fl = 2.0 * sp.M * sp.N * sp.K
+            t = fl / (ms2 * 1e-3) / 1e12
+            sec.append({"workload": sp.name, "M": sp.M, "K": sp.K, "N": sp.N, "rank": sp.rank,
+                        "format": sp.fmt, "ms_per_step": round(ms2, 6), "effective_tops": round(t, 2),
+                        "pct_of_int8_peak": round(100 * t / PEAK_TFLOPS["int4"], 2),
+                        "stage1_us": round(a1 * 1e3, 2), "gemm_us": round(a2 * 1e3, 2)})
+            log(f"{sp.name}: {ms2 * 1e3:.1f} us/step, {t:.1f} TOPS (stage1 {a1*1e3:.1f} us, gemm {a2*1e3:.1f} us)")
+        out["secondary"] = sec
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(layer, host, lay, spec, args.cpu_budget)
+        log(f"  {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,7 @@ import numpy as np
 __all__ = [
     "SvdqError", "FMT_INT4", "FMT_MXFP4", "LayerDesc", "lib", "lib_path", "status_string",
     "packed_bytes", "pack_weights", "quantize_residual", "unpack_weights", "workspace_bytes",
-    "to_device", "linear_forward", "stage1", "unpack_workspace", "debug_int4_group_sums",
+    "to_device", "linear_forward", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer",
 ]
 
@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = [
     "svdq_status_string", "svdq_version", "svdq_packed_bytes", "svdq_pack_weights",
     "svdq_quantize_residual", "svdq_unpack_weights", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_stage1", "svdq_unpack_workspace",
-    "svdq_debug_int4_group_sums",
+    "svdq_debug_int4_group_sums", "svdq_gemm",
 ]
 
 
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "svdq_workspace_bytes": [D, i64, P(sz)],
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
         "svdq_stage1": [D, P(Packed), vp, i64, vp, sz, vp],
+        "svdq_gemm": [D, P(Packed), vp, sz, i64, vp, vp],
         "svdq_unpack_workspace": [D, i64, vp, sz, vp, vp, vp],
         "svdq_debug_int4_group_sums": [D, P(Packed), vp, sz, i64, i64, i64, i64, i64, vp, vp],
     }
@@ -252,6 +253,15 @@ def stage1(layer: Layer, dev: dict, x, workspace=None, stream=None):
     _check(lib().svdq_stage1(ctypes.byref(d), ctypes.byref(p), _ptr(x), M, _ptr(workspace),
                              workspace.numel(), _stream(stream)), "svdq_stage1")
     return workspace
+
+
+def gemm(layer: Layer, dev: dict, workspace, M: int, y, stream=None):
+    """Kernel (2) alone on a workspace filled by stage1() for the same M."""
+    p = _packed_struct(layer, dev)
+    d = layer.desc
+    _check(lib().svdq_gemm(ctypes.byref(d), ctypes.byref(p), _ptr(workspace), workspace.numel(),
+                           int(M), _ptr(y), _stream(stream)), "svdq_gemm")
+    return y
 
 
 def unpack_workspace(layer: Layer, M: int, ws_host: np.ndarray) -> dict:

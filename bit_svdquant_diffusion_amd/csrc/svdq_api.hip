@@ -103,12 +103,11 @@ GemmArgs gemm_args(const svdq_layer_desc* d, const svdq_packed* dev, int64_t M, 
 }
 
 bool sync_debug() {
-  static int v = -1;
-  if (v < 0) {
+  static const bool v = [] {
     const char* e = std::getenv("SVDQ_SYNC_DEBUG");
-    v = (e && *e == '1') ? 1 : 0;
-  }
-  return v == 1;
+    return e && *e == '1';
+  }();
+  return v;
 }
 
 svdq_status after_launch(hipError_t e, hipStream_t s) {
@@ -146,6 +145,18 @@ svdq_status svdq_linear_forward(const svdq_layer_desc* d, const svdq_packed* dev
   hipStream_t s = (hipStream_t)stream;
   st = after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), s), s);
   if (st != SVDQ_OK) return st;
+  return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), s), s);
+}
+
+svdq_status svdq_gemm(const svdq_layer_desc* d, const svdq_packed* dev, const void* ws,
+                      size_t ws_bytes, int64_t M, uint16_t* y, void* stream) {
+  svdq_status st = common_checks(d, dev, ws, M, ws, ws_bytes);
+  if (st != SVDQ_OK || M == 0) return st;
+  if (!y) return SVDQ_ERR_NULL;
+  if (!aligned16(y)) return SVDQ_ERR_SHAPE;
+  st = check_device();
+  if (st != SVDQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
   return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), s), s);
 }
 

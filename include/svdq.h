@@ -196,6 +196,16 @@ SVDQ_API svdq_status svdq_stage1(const svdq_layer_desc* desc, const svdq_packed*
                         int64_t M, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Kernel (2) of svdq_linear_forward alone: the 4-bit GEMM with its epilogue,
+ * reading the activation codes, scales and X_hat L1 that svdq_stage1 left in
+ * `workspace` for the same M. svdq_stage1 followed by svdq_gemm on one stream
+ * equals svdq_linear_forward. Errors: as svdq_linear_forward.
+ */
+SVDQ_API svdq_status svdq_gemm(const svdq_layer_desc* desc, const svdq_packed* dev,
+                               const void* workspace, size_t workspace_bytes, int64_t M,
+                               uint16_t* y, void* hip_stream);
+
+/*
  * Logical view of a workspace written by svdq_stage1/svdq_linear_forward and
  * copied to host memory. Any output may be NULL.
  *   codes int8 [M][K] (INT4 values or E2M1 code bits); scales INT4 fp32
