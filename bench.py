@@ -33,7 +33,7 @@ METRIC = "SVDQuant W4A4 linear effective TOPS at 4608×3072×12288; % of MFMA pe
 PEAK_TFLOPS = {"mxfp4": 10100.0, "int4": 5000.0}   # MI355X dense MFMA: FP4 10.1 PF, INT8 5.0 POPS
 PEAK_HBM_GBS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm_mxfp4_mlp_up_4608x3072x12288_counters.md")
-GEMM_SOURCE = os.path.join(ROOT, "bit_svdquant_diffusion_amd", "csrc", "svdq_gemm.hip")
+GEMM_SOURCE = os.path.join(ROOT, "bit_svdquant_diffusion_amd", "csrc", "svdq_gemm_mxfp4.hip")
 
 
 def log(*a):
@@ -227,7 +227,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * tops / PEAK_TFLOPS["mxfp4"], 2),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_TFLOPS["mxfp4"],
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_TFLOPS["mxfp4"], 4),
-                     "traffic": traffic, "kernel": "gemm_mxfp4_kernel<256,256>",
+                     "traffic": traffic, "kernel": "gemm_mxfp4_kernel<256,256,2,4>",
                      "kernel_avg_us": round(t2 * 1e3, 2), "algorithmic_bytes": gemm_bytes(spec)},
         "stage1": {"kernel": "stage1_kernel<MXFP4>", "avg_us": round(t1 * 1e3, 2), "bound": "hbm",
                    "achieved": round(s1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -11,7 +11,6 @@
 #include "svdq_layout.h"
 
 namespace svdq {
-hipError_t prepare_kernels();   // svdq_gemm.hip: one-time per-device kernel attributes
 
 namespace {
 
@@ -30,7 +29,7 @@ svdq_status check_device() {
   if (s == 0) {
     hipDeviceProp_t p;
     bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
-              std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_kernels() == hipSuccess;
+              std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess;
     s = ok ? 1 : 2;
     g_dev_state[dev].store(s, std::memory_order_release);
   }

@@ -32,6 +32,13 @@ struct GemmArgs {
   int32_t* p;
   int m0, mc, n0, nc;
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st);
+hipError_t prepare_gemm_mxfp4();   // one-time per device: kernel LDS attribute
+
+inline hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  return a.fmt == SVDQ_FMT_MXFP4_G32 ? launch_gemm_mxfp4(a, st) : launch_gemm_int4(a, st);
+}
 
 }  // namespace svdq

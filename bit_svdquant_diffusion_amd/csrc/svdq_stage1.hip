@@ -56,23 +56,23 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
 
   for (int s = wave; s < nsteps; s += WAVES) {
     // 1. coalesced load of the 32 x 128 slab, 4 rows per instruction
-    uint4 raw[8];
+    u32x4 raw[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int row = min(m0 + 4 * j + lr, M - 1);
-      raw[j] = *reinterpret_cast<const uint4*>(x + (size_t)row * K + s * 128 + lc * 8);
+      raw[j] = *reinterpret_cast<const u32x4*>(x + (size_t)row * K + s * 128 + lc * 8);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint4*>(slab + (4 * j + lr) * S1_PITCH + lc * 16) = raw[j];
+      *reinterpret_cast<u32x4*>(slab + (4 * j + lr) * S1_PITCH + lc * 16) = raw[j];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // 2. group layout: lane (r, h) takes row r, channels 64h .. 64h+63 of the step
-    uint4 xv[8];
+    u32x4 xv[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      xv[t] = *reinterpret_cast<const uint4*>(slab + r * S1_PITCH + h * 128 + t * 16);
+      xv[t] = *reinterpret_cast<const u32x4*>(slab + r * S1_PITCH + h * 128 + t * 16);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -81,9 +81,9 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
     float xh[64];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      float4 mv = *reinterpret_cast<const float4*>(mu + k0 + 4 * t);
-      uint32_t w0 = (t & 1) ? xv[t / 2].z : xv[t / 2].x;
-      uint32_t w1 = (t & 1) ? xv[t / 2].w : xv[t / 2].y;
+      const f32x4 mv = *reinterpret_cast<const f32x4*>(mu + k0 + 4 * t);
+      const uint32_t w0 = xv[t / 2][(t & 1) * 2 + 0];
+      const uint32_t w1 = xv[t / 2][(t & 1) * 2 + 1];
       xh[4 * t + 0] = bf16lo(w0) * mv.x;
       xh[4 * t + 1] = bf16hi(w0) * mv.y;
       xh[4 * t + 2] = bf16lo(w1) * mv.z;
@@ -134,9 +134,9 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
       }
     }
     if (row_ok) {
-      uint4* dst = reinterpret_cast<uint4*>(qx + (size_t)m * (K / 2) + k0 / 2);
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      u32x4* dst = reinterpret_cast<u32x4*>(qx + (size_t)m * (K / 2) + k0 / 2);
+      dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
     }
 
     // 4. Z += bf16(x_hat) L1 on 32x32x16 bf16 MFMA (8 per 32 columns)
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
         if (c < ncb) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            uint4 bv = *reinterpret_cast<const uint4*>(
+            u32x4 bv = *reinterpret_cast<const u32x4*>(
                 l1s + ((((size_t)s * ncb + c) * 8 + t) * 64 + lane) * 8);
-            uint4 av = make_uint4(ab[4 * t], ab[4 * t + 1], ab[4 * t + 2], ab[4 * t + 3]);
+            u32x4 av = u32x4{ab[4 * t], ab[4 * t + 1], ab[4 * t + 2], ab[4 * t + 3]};
             zacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 *reinterpret_cast<bf16x8*>(&av), *reinterpret_cast<bf16x8*>(&bv), zacc[c], 0, 0, 0);
           }
@@ -164,9 +164,12 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
   // reduce the WAVES partial Z tiles in wave order and store bf16
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
-  for (int c = 0; c < ncb; ++c)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[((wave * ncb + c) * 16 + i) * 64 + lane] = zacc[c][i];
+  for (int c = 0; c < 4; ++c)
+    if (c < ncb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[((wave * ncb + c) * 16 + i) * 64 + lane] = zacc[c][i];
+    }
   __syncthreads();
   const int total = ncb * 16 * 64;
   for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
