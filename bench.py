@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -207,6 +209,13 @@ def main():
     s1_gbs = stage1_bytes(spec) / (t1 * 1e-3) / 1e9
     log(f"stage1 {t1 * 1e3:.1f} us ({s1_gbs:.0f} GB/s), gemm {t2 * 1e3:.1f} us ({gemm_tflops:.1f} TFLOP/s)")
 
+    if args.copy_calib_mb:
+        src = torch.empty(args.copy_calib_mb << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     traffic = traffic_from_profile()
     out = {
         "metric": METRIC,

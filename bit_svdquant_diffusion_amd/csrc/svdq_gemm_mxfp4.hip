@@ -7,236 +7,228 @@
 // E2M1 operands and their E8M0 block scales go straight into
 // v_mfma_scale_f32_32x32x64_f8f6f4: the hardware applies 2^(e_w + e_x) per
 // 32-channel block and accumulates in fp32, so no dequantization runs on the
-// vector ALUs. The MFMA is issued with the weight fragment as operand A and
-// the activation fragment as operand B, so a lane's 16 results are 4 runs of
-// 4 consecutive output channels of one token: Y is written 8 bytes at a time.
+// vector ALUs. The weight fragment is operand A and the activation fragment
+// operand B, so a lane's 16 results are 4 runs of 4 consecutive output
+// channels of one token.
 //
-// Tiling: a BM x BN output tile per workgroup of WGM x WGN waves (two waves
-// per SIMD for the default 256 x 256 / 8-wave shape, so one wave's barrier
-// and LDS traffic hide behind the other's MFMAs). K advances in stages of 128
-// channels (64 bytes per row), double buffered in LDS; global loads for stage
-// s+2 are in flight while stage s computes.
+// Data path: codes and scale bytes of both operands are stored in fragment
+// order (one 1 KiB block = one wave's MFMA operand), so every global->LDS
+// transfer is a direct `global_load_lds_dwordx4` of a contiguous 1 KiB with
+// no register staging, and every LDS fragment read is a contiguous,
+// bank-conflict-free 1 KiB. A ring of NSTAGE K-stages (128 channels each)
+// keeps NSTAGE-1 stages of loads in flight to cover L2-miss latency.
+// The output tile is staged through the (then idle) ring so each wave writes
+// Y in full 128-byte rows.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
 
 namespace svdq {
 
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mxfp4_kernel(GemmArgs a, int tiles_m,
-                                                                  int tiles_n) {
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int LA = BM * 4 / NT, LB = BN * 4 / NT;   // 16-byte chunks per thread per stage
-  static_assert(LA * NT == BM * 4 && LB * NT == BN * 4, "tile / thread mismatch");
-  constexpr int STAGE = (BM + BN) * G_PITCH;
+namespace {
+constexpr int kBM = 256, kBN = 256, kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
+constexpr int kWM = kBM / kWGM, kWN = kBN / kWGN, kTM = kWM / 32, kTN = kWN / 32;
+constexpr int kNStage = 4;
+// one ring slot: A codes (8 blocks x 2 steps x 1 KiB), B codes, A scales, B scales
+constexpr int kCodeA = 0, kCodeB = 16384, kScA = 32768, kScB = 33792, kSlot = 34816;
+constexpr int kOutPitch = 136;                       // bytes per staged output row (128 + 8)
+constexpr size_t kLds = (size_t)kNStage * kSlot;
+static_assert(kLds >= (size_t)kNW * kWM * kOutPitch, "output staging must fit in the ring");
+static_assert(kWM * 4 == kBM * 2 && kTM == 4 && kTN == 2, "layout below assumes 2x4 waves");
+
+// Stage barrier of the ring: wait until at most `n` of this wave's global->LDS
+// transfers are outstanding (they complete in issue order) and all its LDS reads
+// have returned, then s_barrier. No memory fence: a fence would also wait for
+// the later stages' transfers that are meant to stay in flight. The scheduling
+// barriers keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier(int n) {
+  __builtin_amdgcn_sched_barrier(0);
+  // s_waitcnt: vmcnt = n (bits 3:0), expcnt = 7 (no wait), lgkmcnt = 0
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0070 | 0); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0070 | 5); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0070 | 10); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0070 | 0); break;
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
+}  // namespace
+
+__global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   extern __shared__ __align__(16) uint8_t smem[];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wave / kWGN, wn = wave % kWGN;
   const TileMap tmap = map_tile(blockIdx.x, tiles_m, tiles_n, 8);
-  const int m0 = tmap.tm * BM, n0 = tmap.tn * BN;
+  const int m0 = tmap.tm * kBM, n0 = tmap.tn * kBN;
   const int M = a.M, N = a.N, K = a.K;
-  const int KB = K / 2;        // bytes per row
-  const int nst = K / 128;     // K-stages (even: K % 256 == 0)
-  const int nch = K / 256;     // scale words per row and half
+  const int MB = (M + 31) / 32, NB = N / 32;      // 32-row blocks of X (padded) and W
+  const int KS = K / 64;                          // 64-channel steps
+  const int nst = K / 128;                        // K-stages
+  const int mb0 = m0 / 32, nb0 = n0 / 32;
 
-  // global -> LDS staging: chunk c = tid + NT i covers row c/4, bytes 16 (c%4)
-  const uint8_t* ga[LA];
-  const uint8_t* gb[LB];
-  int la[LA], lb[LB];
+  // ---- this wave's share of every stage's transfers: 4 code blocks + 1 scale dword ----
+  const uint8_t* gsrc[4];
+  int ldst[4];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int c = tid + NT * i, row = c >> 2, chk = c & 3;
-    ga[i] = a.qx + (size_t)min(m0 + row, M - 1) * KB + chk * 16;
-    la[i] = row * G_PITCH + chk * 16;
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave * 4 + i;   // 0..15 A blocks, 16..31 B blocks; block (bl, step) = (q/2, q%2)
+    if (q < 16) {
+      const int b = min(mb0 + (q >> 1), MB - 1);
+      gsrc[i] = a.qx + ((size_t)b * KS + (q & 1)) * 1024 + lane * 16;
+      ldst[i] = kCodeA + q * 1024;
+    } else {
+      const int b = min(nb0 + ((q - 16) >> 1), NB - 1);
+      gsrc[i] = a.qw + ((size_t)b * KS + (q & 1)) * 1024 + lane * 16;
+      ldst[i] = kCodeB + (q - 16) * 1024;
+    }
   }
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int c = tid + NT * i, row = c >> 2, chk = c & 3;
-    gb[i] = a.qw + (size_t)min(n0 + row, N - 1) * KB + chk * 16;
-    lb[i] = (BM + row) * G_PITCH + chk * 16;
+  const uint8_t* ssrc;
+  size_t sstride;
+  int sdst;
+  if (wave < 4) {   // A scale blocks mb0 + 2w, mb0 + 2w + 1
+    const int b = min(mb0 + 2 * wave + (lane >> 5), MB - 1);
+    ssrc = reinterpret_cast<const uint8_t*>(a.sx) + (size_t)b * 128 + (lane & 31) * 4;
+    sstride = (size_t)MB * 128;
+    sdst = kScA + wave * 256;
+  } else {
+    const int b = min(nb0 + 2 * (wave - 4) + (lane >> 5), NB - 1);
+    ssrc = reinterpret_cast<const uint8_t*>(a.sw) + (size_t)b * 128 + (lane & 31) * 4;
+    sstride = (size_t)NB * 128;
+    sdst = kScB + (wave - 4) * 256;
   }
 
-  // MFMA lane roles: lane (lr = l%32, h = l/32) holds row lr of a 32-row block
-  // and channels [32h, 32h+32) of each 64-channel step.
+#define SVDQ_ISSUE(ST)                                                                             \
+  {                                                                                                \
+    uint8_t* slot = smem + ((ST) % kNStage) * kSlot;                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
+        __builtin_amdgcn_global_load_lds(gsrc[i] + (size_t)(ST) * 2048, lds_ptr(slot + ldst[i]), 16, 0, 0); \
+    __builtin_amdgcn_global_load_lds(ssrc + (size_t)(ST) * sstride, lds_ptr(slot + sdst), 4, 0, 0); \
+  }
+
+  f32x16 acc[kTN][kTM];
+#pragma unroll
+  for (int j = 0; j < kTN; ++j)
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
+
+  // prologue: stages 0 .. NSTAGE-2 in flight
+#pragma unroll
+  for (int s = 0; s < kNStage - 1; ++s)
+    if (s < nst) SVDQ_ISSUE(s)
+
+  for (int st = 0; st < nst; ++st) {
+    // this wave's transfers for stage st are done once at most min(NSTAGE-2, nst-1-st)
+    // later stages (5 transfers each) are still outstanding
+    const int later = min(kNStage - 2, nst - 1 - st);
+    ring_barrier(5 * later);   // everyone's stage st landed; everyone finished stage st-1
+    if (st + kNStage - 1 < nst) SVDQ_ISSUE(st + kNStage - 1)
+
+    const uint8_t* slot = smem + (st % kNStage) * kSlot;
+    uint32_t sa[kTM], sb[kTN];
+#pragma unroll
+    for (int t = 0; t < kTM; ++t)
+      sa[t] = *reinterpret_cast<const uint16_t*>(slot + kScA + (wm * kTM + t) * 128 + lane * 2);
+#pragma unroll
+    for (int t = 0; t < kTN; ++t)
+      sb[t] = *reinterpret_cast<const uint16_t*>(slot + kScB + (wn * kTN + t) * 128 + lane * 2);
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      i32x8 fa[kTM], fb[kTN];
+#pragma unroll
+      for (int t = 0; t < kTM; ++t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + step) * 1024 + lane * 16);
+        fa[t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int t = 0; t < kTN; ++t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + step) * 1024 + lane * 16);
+        fb[t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+          if (step == 0)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[j], fa[i], acc[j][i], 4, 4, 0, (int)sb[j], 0, (int)sa[i]);
+          else
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[j], fa[i], acc[j][i], 4, 4, 1, (int)sb[j], 1, (int)sa[i]);
+        }
+    }
+  }
+#undef SVDQ_ISSUE
+
+  // ---- epilogue: + (X_hat L1) L2 on bf16 MFMA (L2^T fragment as A, Z fragment as B) ----
   const int h = lane >> 5, lr = lane & 31;
-  const int fa_off = (wm * WM + lr) * G_PITCH + h * 16;        // + t*32*G_PITCH + step*32
-  const int fb_off = (BM + wn * WN + lr) * G_PITCH + h * 16;
-  // scale words (4 E8M0 bytes = 4 consecutive 64-channel steps) per row and half
-  const uint32_t* sxp[TM];
-  const uint32_t* swp[TN];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    const int row = min(m0 + wm * WM + t * 32 + lr, M - 1);
-    sxp[t] = reinterpret_cast<const uint32_t*>(a.sx) + (size_t)row * nch * 2 + h;
-  }
-#pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    const int col = min(n0 + wn * WN + t * 32 + lr, N - 1);
-    swp[t] = reinterpret_cast<const uint32_t*>(a.sw) + (size_t)col * nch * 2 + h;
-  }
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) acc[j][i] = f32x16{};
-
-  u32x4 ra[LA], rb[LB];
-  uint32_t sx[TM], sw[TN], sxn[TM], swn[TN];
-
-  // prologue: stage 0 into LDS buffer 0, stage 1 in registers, scale words of chunks 0, 1
-#pragma unroll
-  for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i]);
-#pragma unroll
-  for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i]);
-#pragma unroll
-  for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(smem + la[i]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(smem + lb[i]) = rb[i];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + 64);
-#pragma unroll
-  for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + 64);
-#pragma unroll
-  for (int t = 0; t < TM; ++t) sx[t] = sxp[t][0];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) sw[t] = swp[t][0];
-  const int c1 = nch > 1 ? 1 : 0;
-#pragma unroll
-  for (int t = 0; t < TM; ++t) sxn[t] = sxp[t][2 * c1];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) swn[t] = swp[t][2 * c1];
-  __syncthreads();
-
-#define SVDQ_MX_COMPUTE(BUF, O0)                                                                 \
-  {                                                                                              \
-    const uint8_t* base = smem + (BUF) * STAGE;                                                  \
-    _Pragma("unroll") for (int step = 0; step < 2; ++step) {                                     \
-      i32x8 fa[TM], fb[TN];                                                                      \
-      _Pragma("unroll") for (int t = 0; t < TM; ++t) {                                           \
-        const u32x4 v = *reinterpret_cast<const u32x4*>(base + fa_off + t * 32 * G_PITCH + step * 32); \
-        fa[t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};                       \
-      }                                                                                          \
-      _Pragma("unroll") for (int t = 0; t < TN; ++t) {                                           \
-        const u32x4 v = *reinterpret_cast<const u32x4*>(base + fb_off + t * 32 * G_PITCH + step * 32); \
-        fb[t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};                       \
-      }                                                                                          \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) _Pragma("unroll") for (int i = 0; i < TM; ++i) { \
-        if (step == 0)                                                                           \
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                           \
-              fb[j], fa[i], acc[j][i], 4, 4, (O0), (int)sw[j], (O0), (int)sx[i]);                \
-        else                                                                                     \
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                           \
-              fb[j], fa[i], acc[j][i], 4, 4, (O0) + 1, (int)sw[j], (O0) + 1, (int)sx[i]);        \
-      }                                                                                          \
-    }                                                                                            \
-  }
-
-  for (int st = 0; st < nst; st += 2) {
-    // even stage st (LDS buffer 0, scale bytes 0 and 1 of chunk st/2);
-    // registers hold stage st+1: park it in buffer 1, fetch stage st+2
-#pragma unroll
-    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(smem + STAGE + la[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(smem + STAGE + lb[i]) = rb[i];
-    if (st + 2 < nst) {
-#pragma unroll
-      for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + (st + 2) * 64);
-#pragma unroll
-      for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + (st + 2) * 64);
-    }
-    SVDQ_MX_COMPUTE(0, 0)
-    __syncthreads();
-    // odd stage st+1 (buffer 1, scale bytes 2 and 3)
-    if (st + 2 < nst) {
-#pragma unroll
-      for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(smem + la[i]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(smem + lb[i]) = rb[i];
-#pragma unroll
-      for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + (st + 3) * 64);
-#pragma unroll
-      for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + (st + 3) * 64);
-    }
-    SVDQ_MX_COMPUTE(1, 2)
-    // next chunk's scale words become current; fetch the one after
-    const int cn = min(st / 2 + 2, nch - 1);
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      sx[t] = sxn[t];
-      sxn[t] = sxp[t][2 * cn];
-    }
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      sw[t] = swn[t];
-      swn[t] = swp[t][2 * cn];
-    }
-    __syncthreads();
-  }
-#undef SVDQ_MX_COMPUTE
-
-  // epilogue: + (X_hat L1) L2 on bf16 MFMA (L2^T fragment as A, Z fragment as B)
   if (a.r32 > 0) {
     for (int c = 0; c < a.r32 / 16; ++c) {
-      bf16x8 zf[TM], lf[TN];
+      bf16x8 zf[kTM], lf[kTN];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const int row = min(m0 + wm * WM + t * 32 + lr, M - 1);
-        uint4 v = *reinterpret_cast<const uint4*>(a.z + (size_t)row * a.r32 + 16 * c + 8 * h);
+      for (int t = 0; t < kTM; ++t) {
+        const int row = min(m0 + wm * kWM + t * 32 + lr, M - 1);
+        u32x4 v = *reinterpret_cast<const u32x4*>(a.z + (size_t)row * a.r32 + 16 * c + 8 * h);
         zf[t] = *reinterpret_cast<bf16x8*>(&v);
       }
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int col = min(n0 + wn * WN + t * 32 + lr, N - 1);
-        uint4 v = *reinterpret_cast<const uint4*>(a.l2t + (size_t)col * a.r32 + 16 * c + 8 * h);
+      for (int t = 0; t < kTN; ++t) {
+        const int col = min(n0 + wn * kWN + t * 32 + lr, N - 1);
+        u32x4 v = *reinterpret_cast<const u32x4*>(a.l2t + (size_t)col * a.r32 + 16 * c + 8 * h);
         lf[t] = *reinterpret_cast<bf16x8*>(&v);
       }
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < kTN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < kTM; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[j], zf[i], acc[j][i], 0, 0, 0);
     }
   }
-  // + bias, bf16, 8-byte stores: lane holds token m = .. + lr and channels
-  // n = .. + 8q + 4h + (0..3) for q = 0..3
+
+  // ---- + bias, bf16; stage the wave's 128 x 64 tile in LDS, store full rows ----
+  ring_barrier(0);   // the ring is free
+  uint8_t* ot = smem + wave * (kWM * kOutPitch);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
+  for (int j = 0; j < kTN; ++j) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * h;
-      if (n >= N) continue;
-      const uint2 bw = *reinterpret_cast<const uint2*>(a.bias + n);
+      const int nl = j * 32 + 8 * q + 4 * h;             // channel within the wave tile
+      const int n = min(n0 + wn * kWN + nl, N - 4);
+      const u32x2 bw = *reinterpret_cast<const u32x2*>(a.bias + n);
       const float b0 = bf16lo(bw.x), b1 = bf16hi(bw.x), b2 = bf16lo(bw.y), b3 = bf16hi(bw.y);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WM + i * 32 + lr;
-        if (m >= M) continue;
-        uint2 o;
+      for (int i = 0; i < kTM; ++i) {
+        u32x2 o;
         o.x = pack_bf16x2(acc[j][i][4 * q + 0] + b0, acc[j][i][4 * q + 1] + b1);
         o.y = pack_bf16x2(acc[j][i][4 * q + 2] + b2, acc[j][i][4 * q + 3] + b3);
-        *reinterpret_cast<uint2*>(a.y + (size_t)m * N + n) = o;
+        *reinterpret_cast<u32x2*>(ot + (i * 32 + lr) * kOutPitch + nl * 2) = o;
       }
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rsub = lane >> 3, chunk = lane & 7;
+  const int ncol = n0 + wn * kWN + chunk * 8;
+#pragma unroll 4
+  for (int it = 0; it < kWM / 8; ++it) {
+    const int rl = it * 8 + rsub;
+    const int m = m0 + wm * kWM + rl;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ot + rl * kOutPitch + chunk * 16);
+    if (m < M && ncol < N) *reinterpret_cast<u32x4*>(a.y + (size_t)m * N + ncol) = v;
+  }
 }
 
-namespace {
-constexpr int kBM = 256, kBN = 256, kWGM = 2, kWGN = 4;
-constexpr size_t kLds = 2 * (size_t)(kBM + kBN) * G_PITCH;
-}  // namespace
-
 hipError_t prepare_gemm_mxfp4() {
-  return hipFuncSetAttribute((const void*)gemm_mxfp4_kernel<kBM, kBN, kWGM, kWGN>,
+  return hipFuncSetAttribute((const void*)gemm_mxfp4_kernel,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
 }
 
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
   const int tm = (a.M + kBM - 1) / kBM, tn = (a.N + kBN - 1) / kBN;
-  hipLaunchKernelGGL((gemm_mxfp4_kernel<kBM, kBN, kWGM, kWGN>), dim3(tm * tn),
-                     dim3(64 * kWGM * kWGN), kLds, st, a, tm, tn);
+  hipLaunchKernelGGL(gemm_mxfp4_kernel, dim3(tm * tn), dim3(64 * kNW), kLds, st, a, tm, tn);
   return hipGetLastError();
 }
 

@@ -27,6 +27,8 @@ inline svdq_status check_desc(const svdq_layer_desc* d) {
   return SVDQ_OK;
 }
 
+inline int64_t round32(int64_t v) { return (v + 31) / 32 * 32; }
+
 inline size_t scale_bytes(const svdq_layer_desc* d, int64_t rows) {
   return d->format == SVDQ_FMT_INT4_G64 ? (size_t)rows * (d->K / kGroupInt4) * 4
                                         : (size_t)rows * (d->K / kBlockMx);
@@ -45,17 +47,38 @@ inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
   return s;
 }
 
-// Workspace: [qX: M x K/2][sX][Z: M x rank32 bf16], each 256-byte aligned.
+// Workspace: [qX][sX][Z: M x rank32 bf16], each 256-byte aligned. INT4: qX
+// row-major [M][K/2], sX fp32 [K/64][act_rows(M)]. MXFP4: qX and sX in
+// fragment order over round32(M) rows (see below).
 struct WsLayout {
   size_t qx, sx, z, total;
 };
 inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   WsLayout w;
+  const bool int4 = d->format == SVDQ_FMT_INT4_G64;
+  const int64_t rows = int4 ? M : round32(M);
   w.qx = 0;
-  w.sx = align256((size_t)M * d->K / 2);
-  w.z = w.sx + align256(scale_bytes(d, d->format == SVDQ_FMT_INT4_G64 ? act_rows(M) : M));
+  w.sx = align256((size_t)rows * d->K / 2);
+  w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
   w.total = w.z + align256((size_t)M * rank32(d->rank) * 2);
   return w;
+}
+
+// Fragment order of MXFP4 codes: rows in blocks of 32, K in steps of 64; each
+// (block, step) is 1 KiB = 64 lanes x 16 bytes, lane l = 32h + r holding row
+// 32*block + r, channels 64*step + 32h + [0, 32) (even channel in the low
+// nibble). One (block, step) is exactly one MFMA operand of one wave.
+inline size_t f_code_byte(int K, int64_t row, int k) {
+  const int64_t b = row / 32;
+  const int r = (int)(row % 32), S = k / 64, h = (k % 64) / 32, j = k % 32;
+  return (((size_t)b * (K / 64) + S) * 64 + (32 * h + r)) * 16 + j / 2;
+}
+// Fragment order of MXFP4 scale bytes: [K/128 stage][rows32/32 block][64 lanes][2];
+// lane l = 32h + r of block b at stage st holds the bytes of the 32-channel
+// blocks kb = 4 st + 2 step + h (step = 0, 1) of row 32 b + r.
+inline size_t f_scale_index(int64_t rows32, int64_t row, int kb) {
+  const int st = kb / 4, step = (kb % 4) / 2, h = kb % 2;
+  return (((size_t)st * (rows32 / 32) + row / 32) * 64 + (32 * h + row % 32)) * 2 + step;
 }
 
 // L1 device layout: [K/128][rank32/32][t=8][lane=64][8] bf16 where lane = 32h + c
@@ -67,10 +90,5 @@ inline size_t l1_index(int K, int r32, int k, int col) {
   return ((((size_t)s * (r32 / 32) + cb) * 8 + t) * 64 + (32 * h + c)) * 8 + j;
 }
 
-// MXFP4 scale layout [rows][K/256][h=2][s=4]: block kb = 8c + 2s + h.
-inline size_t mx_scale_index(int K, int64_t row, int kb) {
-  int c = kb / 8, s = (kb % 8) / 2, h = kb % 2;
-  return (((size_t)row * (K / 256) + c) * 2 + h) * 4 + s;
-}
 
 }  // namespace svdq

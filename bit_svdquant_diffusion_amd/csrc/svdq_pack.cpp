@@ -365,9 +365,9 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
         } else {
           uint8_t sb;
           quant_mx_block(&rrow[(size_t)g * gsz], gsz, cq.data(), &sb);
-          sw_b[mx_scale_index(K, n, g)] = sb;
+          sw_b[f_scale_index(N, n, g)] = sb;
           for (int j = 0; j < gsz; j += 2)
-            qrow[(g * gsz + j) / 2] = (uint8_t)((cq[j] & 15) | ((cq[j + 1] & 15) << 4));
+            out->qw[f_code_byte(K, n, g * gsz + j)] = (uint8_t)((cq[j] & 15) | ((cq[j + 1] & 15) << 4));
         }
       }
     }
@@ -479,7 +479,7 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
     if (!h->qw) return SVDQ_ERR_NULL;
     for (size_t n = 0; n < (size_t)N; ++n)
       for (int k = 0; k < K; ++k) {
-        uint8_t byte = h->qw[n * K / 2 + k / 2];
+        uint8_t byte = int4 ? h->qw[n * K / 2 + k / 2] : h->qw[f_code_byte(K, n, k)];
         int nib = (k & 1) ? (byte >> 4) : (byte & 15);
         codes[n * K + k] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
       }
@@ -495,7 +495,7 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
       const int G = K / kBlockMx;
       for (int n = 0; n < N; ++n)
         for (int g = 0; g < G; ++g)
-          ((uint8_t*)scales)[(size_t)n * G + g] = ((const uint8_t*)h->sw)[mx_scale_index(K, n, g)];
+          ((uint8_t*)scales)[(size_t)n * G + g] = ((const uint8_t*)h->sw)[f_scale_index(N, n, g)];
     }
   }
   if (l1 && r > 0) {
@@ -530,7 +530,7 @@ svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const voi
     const uint8_t* q = base + L.qx;
     for (int64_t m = 0; m < M; ++m)
       for (int k = 0; k < K; ++k) {
-        uint8_t byte = q[(size_t)m * K / 2 + k / 2];
+        uint8_t byte = int4 ? q[(size_t)m * K / 2 + k / 2] : q[f_code_byte(K, m, k)];
         int nib = (k & 1) ? (byte >> 4) : (byte & 15);
         codes[(size_t)m * K + k] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
       }
@@ -547,7 +547,7 @@ svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const voi
       const int G = K / kBlockMx;
       for (int64_t m = 0; m < M; ++m)
         for (int g = 0; g < G; ++g)
-          ((uint8_t*)scales)[(size_t)m * G + g] = s[mx_scale_index(K, m, g)];
+          ((uint8_t*)scales)[(size_t)m * G + g] = s[f_scale_index(round32(M), m, g)];
     }
   }
   if (z && r > 0) {

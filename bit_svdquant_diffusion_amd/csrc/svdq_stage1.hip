@@ -40,6 +40,7 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
   const int m0 = blockIdx.x * S1_ROWS;
   const int nsteps = K / 128;
   const int Mp = (M + 15) / 16 * 16;   // row stride of the INT4 scales
+  const int MB = (M + 31) / 32;        // 32-row blocks (MXFP4 fragment order)
   const int ncb = r32 / 32;
   uint8_t* slab = smem + wave * (S1_ROWS * S1_PITCH);
 
@@ -127,16 +128,23 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
           packed[4 * b + w] = word;
         }
         if (row_ok) {
-          const int kb = 4 * s + 2 * h + b;
-          reinterpret_cast<uint8_t*>(sx)[(((size_t)m * (K / 256) + kb / 8) * 2 + (kb % 2)) * 4 +
-                                         (kb % 8) / 2] = (uint8_t)(e + 127);
+          // fragment-order scale byte: block kb = 4s + 2h + b -> stage s, step h, half b
+          reinterpret_cast<uint8_t*>(sx)[(((size_t)s * MB + m / 32) * 64 + 32 * b + r) * 2 + h] =
+              (uint8_t)(e + 127);
         }
       }
     }
     if (row_ok) {
-      u32x4* dst = reinterpret_cast<u32x4*>(qx + (size_t)m * (K / 2) + k0 / 2);
-      dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-      dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+      if constexpr (FMT == SVDQ_FMT_INT4_G64) {
+        u32x4* dst = reinterpret_cast<u32x4*>(qx + (size_t)m * (K / 2) + k0 / 2);
+        dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+      } else {
+        // fragment order: step S = 2s + h of row block m/32, lanes r and 32 + r
+        uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + 2 * s + h) * 1024;
+        *reinterpret_cast<u32x4*>(blk + r * 16) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        *reinterpret_cast<u32x4*>(blk + (32 + r) * 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+      }
     }
 
     // 4. Z += bf16(x_hat) L1 on 32x32x16 bf16 MFMA (8 per 32 columns)
