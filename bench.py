@@ -236,7 +236,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * tops / PEAK_TFLOPS["mxfp4"], 2),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_TFLOPS["mxfp4"],
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_TFLOPS["mxfp4"], 4),
-                     "traffic": traffic, "kernel": "gemm_mxfp4_kernel<256,256,2,4>",
+                     "traffic": traffic, "kernel": "svdq::gemm_mxfp4_kernel (persistent, 192x384 tiles)",
                      "kernel_avg_us": round(t2 * 1e3, 2), "algorithmic_bytes": gemm_bytes(spec)},
         "stage1": {"kernel": "stage1_kernel<MXFP4>", "avg_us": round(t1 * 1e3, 2), "bound": "hbm",
                    "achieved": round(s1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -16,13 +16,17 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950 ready, 2 unsupported
+std::atomic<int> g_dev_cus[kMaxDevices];     // compute units of each ready device
 std::mutex g_dev_mu;
 
-svdq_status check_device() {
+svdq_status check_device(int* cus = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SVDQ_ERR_DEVICE;
   int s = g_dev_state[dev].load(std::memory_order_acquire);
-  if (s == 1) return SVDQ_OK;
+  if (s == 1) {
+    if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    return SVDQ_OK;
+  }
   if (s == 2) return SVDQ_ERR_DEVICE;
   std::lock_guard<std::mutex> lock(g_dev_mu);
   s = g_dev_state[dev].load(std::memory_order_acquire);
@@ -31,8 +35,10 @@ svdq_status check_device() {
     bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
               std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess;
     s = ok ? 1 : 2;
+    if (ok) g_dev_cus[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
     g_dev_state[dev].store(s, std::memory_order_release);
   }
+  if (s == 1 && cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
   return s == 1 ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
@@ -139,12 +145,13 @@ svdq_status svdq_linear_forward(const svdq_layer_desc* d, const svdq_packed* dev
   if (st != SVDQ_OK || M == 0) return st;
   if (!y) return SVDQ_ERR_NULL;
   if (!aligned16(y)) return SVDQ_ERR_SHAPE;
-  st = check_device();
+  int cus = 0;
+  st = check_device(&cus);
   if (st != SVDQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   st = after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), s), s);
   if (st != SVDQ_OK) return st;
-  return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), s), s);
+  return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), cus, s), s);
 }
 
 svdq_status svdq_gemm(const svdq_layer_desc* d, const svdq_packed* dev, const void* ws,
@@ -153,10 +160,11 @@ svdq_status svdq_gemm(const svdq_layer_desc* d, const svdq_packed* dev, const vo
   if (st != SVDQ_OK || M == 0) return st;
   if (!y) return SVDQ_ERR_NULL;
   if (!aligned16(y)) return SVDQ_ERR_SHAPE;
-  st = check_device();
+  int cus = 0;
+  st = check_device(&cus);
   if (st != SVDQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), s), s);
+  return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), cus, s), s);
 }
 
 svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_packed* dev,
@@ -183,7 +191,7 @@ svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_pack
   a.n0 = (int)n0;
   a.nc = (int)nc;
   hipStream_t s = (hipStream_t)stream;
-  return after_launch(launch_gemm(a, s), s);
+  return after_launch(launch_gemm(a, 0, s), s);
 }
 
 }  // extern "C"

@@ -1,53 +1,67 @@
 // Kernel (2) of the forward for MXFP4 layers: Q4(X_hat) Q4(R)^T on the
-// block-scaled FP4 MFMA, plus the epilogue that adds (X_hat L1) L2 and the
-// bias before the single bf16 write of Y (aiflownews.com, "What SVDQuant
-// actually does": two-branch computation, FP4 data type; "Nunchaku: the
-// inference engine...": the branches share the output write).
+// block-scaled FP4 MFMA, plus the low-rank up-projection (X_hat L1) L2 and the
+// bias, added before the single bf16 write of Y (aiflownews.com, "What
+// SVDQuant actually does": two-branch computation, FP4 data type; "Nunchaku:
+// the inference engine...": the branches share the output write).
 //
 // E2M1 operands and their E8M0 block scales go straight into
-// v_mfma_scale_f32_32x32x64_f8f6f4: the hardware applies 2^(e_w + e_x) per
-// 32-channel block and accumulates in fp32, so no dequantization runs on the
-// vector ALUs. The weight fragment is operand A and the activation fragment
-// operand B, so a lane's 16 results are 4 runs of 4 consecutive output
-// channels of one token.
+// v_mfma_scale_f32_32x32x64_f8f6f4: the hardware applies 2^(e_x + e_w) per
+// 32-channel block and accumulates in fp32; no dequantization runs on the
+// vector ALUs. The low-rank branch is r32/32 more "stages" of the same
+// pipeline on v_mfma_f32_32x32x16_bf16 accumulating into the same registers.
 //
-// Data path: codes and scale bytes of both operands are stored in fragment
-// order (one 1 KiB block = one wave's MFMA operand), so every global->LDS
-// transfer is a direct `global_load_lds_dwordx4` of a contiguous 1 KiB with
-// no register staging, and every LDS fragment read is a contiguous,
-// bank-conflict-free 1 KiB. A ring of NSTAGE K-stages (128 channels each)
-// keeps NSTAGE-1 stages of loads in flight to cover L2-miss latency.
-// The output tile is staged through the (then idle) ring so each wave writes
-// Y in full 128-byte rows.
+// Data path. Every operand (4-bit codes, E8M0 bytes, Z = X_hat L1, L2^T) is
+// stored in MFMA fragment order, one 1 KiB block per wave operand, so each
+// global->LDS transfer is a direct `global_load_lds_dwordx4` of contiguous
+// bytes and each LDS fragment read is a contiguous, conflict-free 1 KiB.
+// Workgroups are persistent (one per CU) and walk their tiles; a ring of four
+// LDS slots runs across tile boundaries with three stages in flight, so the
+// next tile's first stages load while the current tile finishes and stores.
+//
+// Schedule. Eight waves, 2 (M) x 4 (N), each owning a 96 x 96 sub-tile of the
+// 192 x 384 tile (3 x 3 blocks of 32 x 32). One workgroup barrier per stage.
+// The second half (step 1) of each stage's MFMAs is issued right after the
+// next barrier, so every wave enters each stage with matrix work queued while
+// its LDS reads for the new stage are in flight.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
 
 namespace svdq {
 
 namespace {
-constexpr int kBM = 256, kBN = 256, kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
+constexpr int kBM = 192, kBN = 384, kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
 constexpr int kWM = kBM / kWGM, kWN = kBN / kWGN, kTM = kWM / 32, kTN = kWN / 32;
+constexpr int kMB = kBM / 32, kNBt = kBN / 32;     // 32-row blocks per tile: 6 (A), 12 (B)
 constexpr int kNStage = 4;
-// one ring slot: A codes (8 blocks x 2 steps x 1 KiB), B codes, A scales, B scales
-constexpr int kCodeA = 0, kCodeB = 16384, kScA = 32768, kScB = 33792, kSlot = 34816;
-constexpr int kOutPitch = 136;                       // bytes per staged output row (128 + 8)
+constexpr int kOps = 6;                            // transfers per wave per stage
+constexpr int kStores = 2 * 3 * 3;                 // 16-byte Y stores per wave per tile
+// one ring slot: A fragments (6 blocks x 2 steps x 1 KiB), B fragments (12 x 2 x 1 KiB),
+// A scale bytes (6 x 128 B), B scale bytes (12 x 128 B)
+constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 1024;
+constexpr int kScB = kScA + kMB * 128, kSlot = kScB + kNBt * 128;
 constexpr size_t kLds = (size_t)kNStage * kSlot;
-static_assert(kLds >= (size_t)kNW * kWM * kOutPitch, "output staging must fit in the ring");
-static_assert(kWM * 4 == kBM * 2 && kTM == 4 && kTN == 2, "layout below assumes 2x4 waves");
+static_assert(kTM == 3 && kTN == 3, "schedule below assumes 3 x 3 blocks per wave");
+static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
+static_assert(2 * (kMB + kNBt) == (kNW - 2) * kOps, "waves 0-5 move the fragment blocks");
+static_assert(kMB * 128 == 3 * 256 && kNBt * 128 == 6 * 256, "scale bytes move as 256-byte dword transfers");
 
-// Stage barrier of the ring: wait until at most `n` of this wave's global->LDS
-// transfers are outstanding (they complete in issue order) and all its LDS reads
-// have returned, then s_barrier. No memory fence: a fence would also wait for
-// the later stages' transfers that are meant to stay in flight. The scheduling
-// barriers keep the compiler from moving LDS accesses across it.
+// Ring barrier: wait until at most n of this wave's vector-memory operations
+// are outstanding, and its LDS reads have returned, then s_barrier. Vector
+// memory operations retire in issue order (loads and stores alike), so n =
+// the number issued after the transfer being waited for. No memory fence (a
+// fence would also drain the stages meant to stay in flight); scheduling
+// barriers keep LDS accesses on their side.
+#define SVDQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)   /* expcnt 7, lgkmcnt 0 */
 __device__ __forceinline__ void ring_barrier(int n) {
   __builtin_amdgcn_sched_barrier(0);
-  // s_waitcnt: vmcnt = n (bits 3:0), expcnt = 7 (no wait), lgkmcnt = 0
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0070 | 0); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0070 | 5); break;
-    case 10: __builtin_amdgcn_s_waitcnt(0x0070 | 10); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0070 | 0); break;
+    case 0: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(6)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(12)); break;
+    case 18: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(18)); break;
+    case 24: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(24)); break;
+    case 30: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(30)); break;
+    default: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
   }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -55,170 +69,232 @@ __device__ __forceinline__ void ring_barrier(int n) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+  return *reinterpret_cast<uint32_t*>(&v);
+}
+
+struct Geo {
+  int M, N, K, MB, NB, KS, nst, nlr, nstt, tiles_m, tiles_n;
+};
+
+// Ring-step transfers. Every transfer is a full 64-lane direct global->LDS
+// load and every wave issues exactly kOps per stage. Waves 0-5 move six 1 KiB
+// fragment blocks each: code block q (0..35), A blocks first, block q/2 of the
+// tile's 32-row blocks, step q%2 of the stage's two steps (4-bit stage s:
+// 64-channel steps 2s, 2s+1; low-rank stage l: 16-column steps 2l, 2l+1 of Z
+// on the A side and L2^T on the B side). Waves 6-7 move 256-byte dword
+// transfers: in 4-bit stages the A scale bytes (3) and B scale bytes (6); in
+// low-rank stages the tile's 384 bias values (3); the remaining ops repeat
+// the first of their kind (same bytes to the same place).
+__device__ __forceinline__ void issue_block(const GemmArgs& a, const Geo& g, int mb0, int nb0,
+                                            bool lrs, int sl, int q, int lane, uint8_t* slot) {
+  const bool isA = q < 2 * kMB;
+  const int blk = isA ? (q >> 1) : ((q - 2 * kMB) >> 1);
+  const int b = min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);
+  const uint8_t* tensor = lrs ? reinterpret_cast<const uint8_t*>(isA ? a.z : a.l2t) : (isA ? a.qx : a.qw);
+  const int per = lrs ? a.r32 / 16 : g.KS;
+  const size_t off = ((size_t)b * per + 2 * sl + (q & 1)) * 1024 + lane * 16;
+  const int dst = isA ? kCodeA + q * 1024 : kCodeB + (q - 2 * kMB) * 1024;
+  __builtin_amdgcn_global_load_lds(tensor + off, lds_ptr(slot + dst), 16, 0, 0);
+}
+// dword transfer o (0..11) of waves 6-7
+__device__ __forceinline__ void issue_small(const GemmArgs& a, const Geo& g, int mb0, int nb0,
+                                            bool lrs, int sl, int o, int lane, uint8_t* slot) {
+  if (lrs) {   // bias: lane l of op k holds channels 128 k + 2 l, +1 of the tile
+    const int k = o < 3 ? o : 0;
+    const int n = min(nb0 * 32 + 128 * k + 2 * lane, g.N - 2);
+    __builtin_amdgcn_global_load_lds(a.bias + n, lds_ptr(slot + kScA + 256 * k), 4, 0, 0);
+    return;
+  }
+  const bool isA = o < 3 || o >= 9;
+  const int k = o < 3 ? o : (o < 9 ? o - 3 : 0);   // 256-byte piece = 2 blocks of 128
+  const int b = min((isA ? mb0 : nb0) + 2 * k + (lane >> 5), (isA ? g.MB : g.NB) - 1);
+  const int rows = isA ? g.MB : g.NB;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw);
+  const uint8_t* src = base + ((size_t)sl * rows + b) * 128 + (lane & 31) * 4;
+  __builtin_amdgcn_global_load_lds(src, lds_ptr(slot + (isA ? kScA : kScB) + 256 * k), 4, 0, 0);
+}
 }  // namespace
 
-__global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g, int grid) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWGN, wn = wave % kWGN;
-  const TileMap tmap = map_tile(blockIdx.x, tiles_m, tiles_n, 8);
-  const int m0 = tmap.tm * kBM, n0 = tmap.tn * kBN;
-  const int M = a.M, N = a.N, K = a.K;
-  const int MB = (M + 31) / 32, NB = N / 32;      // 32-row blocks of X (padded) and W
-  const int KS = K / 64;                          // 64-channel steps
-  const int nst = K / 128;                        // K-stages
-  const int mb0 = m0 / 32, nb0 = n0 / 32;
+  const int h = lane >> 5, lr = lane & 31;
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / grid + 1 : 0;
+  const int total = my_tiles * g.nstt;   // ring steps of this workgroup
 
-  // ---- this wave's share of every stage's transfers: 4 code blocks + 1 scale dword ----
-  const uint8_t* gsrc[4];
-  int ldst[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave * 4 + i;   // 0..15 A blocks, 16..31 B blocks; block (bl, step) = (q/2, q%2)
-    if (q < 16) {
-      const int b = min(mb0 + (q >> 1), MB - 1);
-      gsrc[i] = a.qx + ((size_t)b * KS + (q & 1)) * 1024 + lane * 16;
-      ldst[i] = kCodeA + q * 1024;
-    } else {
-      const int b = min(nb0 + ((q - 16) >> 1), NB - 1);
-      gsrc[i] = a.qw + ((size_t)b * KS + (q & 1)) * 1024 + lane * 16;
-      ldst[i] = kCodeB + (q - 16) * 1024;
-    }
-  }
-  const uint8_t* ssrc;
-  size_t sstride;
-  int sdst;
-  if (wave < 4) {   // A scale blocks mb0 + 2w, mb0 + 2w + 1
-    const int b = min(mb0 + 2 * wave + (lane >> 5), MB - 1);
-    ssrc = reinterpret_cast<const uint8_t*>(a.sx) + (size_t)b * 128 + (lane & 31) * 4;
-    sstride = (size_t)MB * 128;
-    sdst = kScA + wave * 256;
-  } else {
-    const int b = min(nb0 + 2 * (wave - 4) + (lane >> 5), NB - 1);
-    ssrc = reinterpret_cast<const uint8_t*>(a.sw) + (size_t)b * 128 + (lane & 31) * 4;
-    sstride = (size_t)NB * 128;
-    sdst = kScB + (wave - 4) * 256;
-  }
-
-#define SVDQ_ISSUE(ST)                                                                             \
-  {                                                                                                \
-    uint8_t* slot = smem + ((ST) % kNStage) * kSlot;                                               \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
-        __builtin_amdgcn_global_load_lds(gsrc[i] + (size_t)(ST) * 2048, lds_ptr(slot + ldst[i]), 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds(ssrc + (size_t)(ST) * sstride, lds_ptr(slot + sdst), 4, 0, 0); \
+  // issue side: next ring step to load (tile-local index, stage, block origins of that tile)
+  int is_t = 0, is_s = 0, is_mb0 = 0, is_nb0 = 0;
+#define SVDQ_ISSUE(GS)                                                                              \
+  {                                                                                                 \
+    if (is_s == 0) {                                                                                \
+      const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, 4);         \
+      is_mb0 = tmi.tm * kMB;                                                                        \
+      is_nb0 = tmi.tn * kNBt;                                                                       \
+    }                                                                                               \
+    uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
+    const bool lrs = is_s >= g.nst;                                                                 \
+    const int sl = lrs ? is_s - g.nst : is_s;                                                       \
+    if (wave < kNW - 2) {                                                                           \
+      if (lrs && a.r32 == 0) {                                                                      \
+        _Pragma("unroll") for (int i = 0; i < kOps; ++i) issue_small(a, g, is_mb0, is_nb0, true, sl, 0, lane, slot_w); \
+      } else {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < kOps; ++i)                                            \
+            issue_block(a, g, is_mb0, is_nb0, lrs, sl, wave * kOps + i, lane, slot_w);              \
+      }                                                                                             \
+    } else {                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < kOps; ++i)                                              \
+          issue_small(a, g, is_mb0, is_nb0, lrs, sl, (wave - (kNW - 2)) * kOps + i, lane, slot_w);  \
+    }                                                                                               \
+    if (++is_s == g.nstt) {                                                                         \
+      is_s = 0;                                                                                     \
+      ++is_t;                                                                                       \
+    }                                                                                               \
   }
 
   f32x16 acc[kTN][kTM];
-#pragma unroll
-  for (int j = 0; j < kTN; ++j)
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
+  i32x4 f0a[kTM], f0b[kTN], f1a[kTM], f1b[kTN];
+  uint32_t sa[kTM] = {0, 0, 0}, sb[kTN] = {0, 0, 0}, pa[kTM], pb[kTN];
 
-  // prologue: stages 0 .. NSTAGE-2 in flight
-#pragma unroll
-  for (int s = 0; s < kNStage - 1; ++s)
-    if (s < nst) SVDQ_ISSUE(s)
-
-  for (int st = 0; st < nst; ++st) {
-    // this wave's transfers for stage st are done once at most min(NSTAGE-2, nst-1-st)
-    // later stages (5 transfers each) are still outstanding
-    const int later = min(kNStage - 2, nst - 1 - st);
-    ring_barrier(5 * later);   // everyone's stage st landed; everyone finished stage st-1
-    if (st + kNStage - 1 < nst) SVDQ_ISSUE(st + kNStage - 1)
-
-    const uint8_t* slot = smem + (st % kNStage) * kSlot;
-    uint32_t sa[kTM], sb[kTN];
-#pragma unroll
-    for (int t = 0; t < kTM; ++t)
-      sa[t] = *reinterpret_cast<const uint16_t*>(slot + kScA + (wm * kTM + t) * 128 + lane * 2);
-#pragma unroll
-    for (int t = 0; t < kTN; ++t)
-      sb[t] = *reinterpret_cast<const uint16_t*>(slot + kScB + (wn * kTN + t) * 128 + lane * 2);
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      i32x8 fa[kTM], fb[kTN];
-#pragma unroll
-      for (int t = 0; t < kTM; ++t) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + step) * 1024 + lane * 16);
-        fa[t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int t = 0; t < kTN; ++t) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + step) * 1024 + lane * 16);
-        fb[t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-          if (step == 0)
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[j], fa[i], acc[j][i], 4, 4, 0, (int)sb[j], 0, (int)sa[i]);
-          else
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[j], fa[i], acc[j][i], 4, 4, 1, (int)sb[j], 1, (int)sa[i]);
-        }
-    }
+#define SVDQ_READ(SLOT, STEP, FA, FB)                                                               \
+  {                                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < kTM; ++t)                                                 \
+        FA[t] = *reinterpret_cast<const i32x4*>((SLOT) + kCodeA + ((wm * kTM + t) * 2 + (STEP)) * 1024 + lane * 16); \
+    _Pragma("unroll") for (int t = 0; t < kTN; ++t)                                                 \
+        FB[t] = *reinterpret_cast<const i32x4*>((SLOT) + kCodeB + ((wn * kTN + t) * 2 + (STEP)) * 1024 + lane * 16); \
   }
-#undef SVDQ_ISSUE
-
-  // ---- epilogue: + (X_hat L1) L2 on bf16 MFMA (L2^T fragment as A, Z fragment as B) ----
-  const int h = lane >> 5, lr = lane & 31;
-  if (a.r32 > 0) {
-    for (int c = 0; c < a.r32 / 16; ++c) {
-      bf16x8 zf[kTM], lf[kTN];
-#pragma unroll
-      for (int t = 0; t < kTM; ++t) {
-        const int row = min(m0 + wm * kWM + t * 32 + lr, M - 1);
-        u32x4 v = *reinterpret_cast<const u32x4*>(a.z + (size_t)row * a.r32 + 16 * c + 8 * h);
-        zf[t] = *reinterpret_cast<bf16x8*>(&v);
-      }
-#pragma unroll
-      for (int t = 0; t < kTN; ++t) {
-        const int col = min(n0 + wn * kWN + t * 32 + lr, N - 1);
-        u32x4 v = *reinterpret_cast<const u32x4*>(a.l2t + (size_t)col * a.r32 + 16 * c + 8 * h);
-        lf[t] = *reinterpret_cast<bf16x8*>(&v);
-      }
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[j], zf[i], acc[j][i], 0, 0, 0);
-    }
+  // MFMAs of one step, weight fragment as operand A and activation fragment as
+  // operand B: 4-bit (scaled, opsel = step) or low-rank (bf16)
+#define SVDQ_MFMA(LOWRANK, STEP, FA, FB, XA, XB)                                                    \
+  {                                                                                                 \
+    if constexpr (!(LOWRANK)) {                                                                     \
+      _Pragma("unroll") for (int j = 0; j < kTN; ++j) _Pragma("unroll") for (int i = 0; i < kTM; ++i) \
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                               \
+              i32x8{FB[j][0], FB[j][1], FB[j][2], FB[j][3], 0, 0, 0, 0},                              \
+              i32x8{FA[i][0], FA[i][1], FA[i][2], FA[i][3], 0, 0, 0, 0}, acc[j][i], 4, 4, (STEP),     \
+              (int)XB[j], (STEP), (int)XA[i]);                                                        \
+    } else {                                                                                        \
+      _Pragma("unroll") for (int j = 0; j < kTN; ++j) _Pragma("unroll") for (int i = 0; i < kTM; ++i) \
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, FB[j]),      \
+                                                             __builtin_bit_cast(bf16x8, FA[i]), acc[j][i], 0, 0, 0); \
+    }                                                                                               \
+  }
+  // One ring step. The deferred second half of the previous step's MFMAs goes
+  // first, so the matrix pipe has work while this step's fragments load.
+  // Waves 0-3 issue their transfers for ring step gs + 3 before their LDS
+  // reads, waves 4-7 after their step-0 MFMAs, so each SIMD's two waves do
+  // not stall on transfer issue at the same time. `stores_due` counts the
+  // ring steps whose wait must also let the last tile's Y stores stay in
+  // flight.
+#define SVDQ_STEP(LOWRANK, LAST, DO_MFMA)                                                           \
+  {                                                                                                 \
+    ring_barrier(kOps * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));         \
+    if (stores_due > 0) --stores_due;                                                               \
+    if (pending) {                                                                                  \
+      SVDQ_MFMA(LOWRANK, 1, f1a, f1b, pa, pb)                                                       \
+      pending = false;                                                                              \
+    }                                                                                               \
+    const bool more = gs + kNStage - 1 < total;                                                     \
+    if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)                                              \
+    const uint8_t* slot = smem + (gs % kNStage) * kSlot;                                            \
+    if (DO_MFMA) {                                                                                  \
+      if (!(LOWRANK)) {                                                                             \
+        _Pragma("unroll") for (int t = 0; t < kTM; ++t)                                             \
+            sa[t] = *reinterpret_cast<const uint16_t*>(slot + kScA + (wm * kTM + t) * 128 + lane * 2); \
+        _Pragma("unroll") for (int t = 0; t < kTN; ++t)                                             \
+            sb[t] = *reinterpret_cast<const uint16_t*>(slot + kScB + (wn * kTN + t) * 128 + lane * 2); \
+      }                                                                                             \
+      SVDQ_READ(slot, 0, f0a, f0b)                                                                  \
+      SVDQ_READ(slot, 1, f1a, f1b)                                                                  \
+      SVDQ_MFMA(LOWRANK, 0, f0a, f0b, sa, sb)                                                       \
+      if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)                                           \
+      _Pragma("unroll") for (int t = 0; t < kTM; ++t) pa[t] = sa[t];                                \
+      _Pragma("unroll") for (int t = 0; t < kTN; ++t) pb[t] = sb[t];                                \
+      if (LAST) {                                                                                   \
+        SVDQ_MFMA(LOWRANK, 1, f1a, f1b, pa, pb)                                                     \
+      } else {                                                                                      \
+        pending = true;                                                                             \
+      }                                                                                             \
+    } else if (more && wave >= 4) {                                                                 \
+      SVDQ_ISSUE(gs + kNStage - 1)                                                                  \
+    }                                                                                               \
+    ++gs;                                                                                           \
   }
 
-  // ---- + bias, bf16; stage the wave's 128 x 64 tile in LDS, store full rows ----
-  ring_barrier(0);   // the ring is free
-  uint8_t* ot = smem + wave * (kWM * kOutPitch);
+  bool pending = false;   // deferred step-1 MFMAs of the previous ring step
+  int gs = 0, stores_due = 0;
+  const int nlr = g.nstt - g.nst;
+  // prologue: the first kNStage - 1 ring steps in flight
+  for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
+  for (int ct = 0; ct < my_tiles; ++ct) {
+    const TileMap tmc = map_tile((int)blockIdx.x + ct * grid, g.tiles_m, g.tiles_n, 4);
+    const int n0 = tmc.tn * kBN + wn * kWN;
 #pragma unroll
-  for (int j = 0; j < kTN; ++j) {
+    for (int j = 0; j < kTN; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int nl = j * 32 + 8 * q + 4 * h;             // channel within the wave tile
-      const int n = min(n0 + wn * kWN + nl, N - 4);
-      const u32x2 bw = *reinterpret_cast<const u32x2*>(a.bias + n);
-      const float b0 = bf16lo(bw.x), b1 = bf16hi(bw.x), b2 = bf16lo(bw.y), b3 = bf16hi(bw.y);
+      for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
+    for (int s4 = 0; s4 < g.nst; ++s4) SVDQ_STEP(false, s4 == g.nst - 1, true)
+    for (int l = 0; l < nlr; ++l) SVDQ_STEP(true, l == nlr - 1, a.r32 > 0)
+
+    // + bias (from the last low-rank slot), bf16. The accumulator lane holds
+    // token m0 + 32 i + lr and channels 32 j + 8 q + 4 h + (0..3); swapping the
+    // packed pairs (q = 1, h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <->
+    // (q = 2, h = 1) between the lane halves leaves lane h with channels
+    // 32 j + 8 h + (0..7) and 32 j + 16 + 8 h + (0..7): two 16-byte stores,
+    // 32 contiguous bytes of one row per lane pair.
+    const uint8_t* bslot = smem + ((gs - 1) % kNStage) * kSlot + kScA + wn * kWN * 2;
+    // Y rows of this tile as a buffer resource: stores past its end are dropped
+    const int ynrec = min(g.M - tmc.tm * kBM, kBM) * g.N * 2;
+    const __amdgpu_buffer_rsrc_t yrs =
+        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.N, 0, ynrec, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      float bv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 bw = *reinterpret_cast<const u32x2*>(bslot + (32 * j + 8 * q + 4 * h) * 2);
+        bv[4 * q + 0] = bf16lo(bw.x);
+        bv[4 * q + 1] = bf16hi(bw.x);
+        bv[4 * q + 2] = bf16lo(bw.y);
+        bv[4 * q + 3] = bf16hi(bw.y);
+      }
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
-        u32x2 o;
-        o.x = pack_bf16x2(acc[j][i][4 * q + 0] + b0, acc[j][i][4 * q + 1] + b1);
-        o.y = pack_bf16x2(acc[j][i][4 * q + 2] + b2, acc[j][i][4 * q + 3] + b3);
-        *reinterpret_cast<u32x2*>(ot + (i * 32 + lr) * kOutPitch + nl * 2) = o;
+        uint32_t o[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          o[p] = cvt_bf16x2(acc[j][i][2 * p] + bv[2 * p], acc[j][i][2 * p + 1] + bv[2 * p + 1]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {   // (o[4p], o[4p+1]) is q = 2p, (o[4p+2], o[4p+3]) is q = 2p+1
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
+            o[4 * p + w] = r[0];
+            o[4 * p + 2 + w] = r[1];
+          }
+        }
+        // always issued (the ring waits count them); the resource drops rows
+        // past M and a block past N is sent past the end
+        const int col = n0 + 32 * j + 8 * h;
+        const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
       }
     }
+    stores_due = kNStage - 1;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int rsub = lane >> 3, chunk = lane & 7;
-  const int ncol = n0 + wn * kWN + chunk * 8;
-#pragma unroll 4
-  for (int it = 0; it < kWM / 8; ++it) {
-    const int rl = it * 8 + rsub;
-    const int m = m0 + wm * kWM + rl;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ot + rl * kOutPitch + chunk * 16);
-    if (m < M && ncol < N) *reinterpret_cast<u32x4*>(a.y + (size_t)m * N + ncol) = v;
-  }
+#undef SVDQ_STEP
+#undef SVDQ_READ
+#undef SVDQ_MFMA
+#undef SVDQ_ISSUE
+#undef SVDQ_READ
+#undef SVDQ_MFMA
 }
 
 hipError_t prepare_gemm_mxfp4() {
@@ -226,9 +302,24 @@ hipError_t prepare_gemm_mxfp4() {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
 }
 
-hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
-  const int tm = (a.M + kBM - 1) / kBM, tn = (a.N + kBN - 1) / kBN;
-  hipLaunchKernelGGL(gemm_mxfp4_kernel, dim3(tm * tn), dim3(64 * kNW), kLds, st, a, tm, tn);
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st) {
+  Geo g;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = a.K;
+  g.MB = (a.M + 31) / 32;
+  g.NB = a.N / 32;
+  g.KS = a.K / 64;
+  g.nst = a.K / 128;
+  g.nlr = a.r32 > 0 ? a.r32 / 32 : 1;   // at least one: the bias rides in a low-rank stage
+  g.nstt = g.nst + g.nlr;
+  g.tiles_m = (a.M + kBM - 1) / kBM;
+  g.tiles_n = (a.N + kBN - 1) / kBN;
+  const int ntiles = g.tiles_m * g.tiles_n;
+  // persistent grid: one workgroup per CU, a multiple of 8 so each stays on its XCD's tiles
+  int grid = num_cus > 0 ? num_cus : 256;
+  if (grid > ntiles) grid = ntiles;
+  hipLaunchKernelGGL(gemm_mxfp4_kernel, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
   return hipGetLastError();
 }
 

@@ -12,20 +12,25 @@ struct Stage1Args {
   const uint16_t* x;    // bf16 [M][K]
   const float* mu;      // [K]
   const uint16_t* l1s;  // L1 in stage-1 MFMA order
-  uint8_t* qx;          // [M][K/2]
-  void* sx;             // INT4 fp32 [K/64][M]; MXFP4 u8 [M][K/256][2][4]
-  uint16_t* z;          // bf16 [M][r32]
+  // activation codes, scales and Z = X_hat L1: INT4 qx [M][K/2], sx fp32
+  // [K/64][Mp], z bf16 [M][r32]; MXFP4 in fragment order over round32(M) rows,
+  // the same layouts as the weight's qw, sw and l2
+  uint8_t* qx;
+  void* sx;
+  uint16_t* z;
 };
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t st);
 
 struct GemmArgs {
   int fmt, M, N, K, r32;
+  // operands in the layouts of Stage1Args and the packed layer (z and l2t
+  // unused when r32 == 0)
   const uint8_t* qx;
   const void* sx;
-  const uint16_t* z;     // bf16 [M][r32] (unused when r32 == 0)
-  const uint8_t* qw;     // [N][K/2]
-  const void* sw;        // INT4 fp32 [K/64][N]; MXFP4 u8 [N][K/256][2][4]
-  const uint16_t* l2t;   // bf16 [N][r32]
+  const uint16_t* z;
+  const uint8_t* qw;
+  const void* sw;
+  const uint16_t* l2t;
   const uint16_t* bias;  // bf16 [N]
   uint16_t* y;           // bf16 [M][N]
   // group-sum test hook (INT4): window and output, p == nullptr for the normal epilogue
@@ -33,12 +38,12 @@ struct GemmArgs {
   int m0, mc, n0, nc;
 };
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st);
 hipError_t prepare_gemm_mxfp4();   // one-time per device: kernel LDS attribute
 
-inline hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+inline hipError_t launch_gemm(const GemmArgs& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  return a.fmt == SVDQ_FMT_MXFP4_G32 ? launch_gemm_mxfp4(a, st) : launch_gemm_int4(a, st);
+  return a.fmt == SVDQ_FMT_MXFP4_G32 ? launch_gemm_mxfp4(a, num_cus, st) : launch_gemm_int4(a, st);
 }
 
 }  // namespace svdq

@@ -60,7 +60,7 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   w.qx = 0;
   w.sx = align256((size_t)rows * d->K / 2);
   w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
-  w.total = w.z + align256((size_t)M * rank32(d->rank) * 2);
+  w.total = w.z + align256((size_t)rows * rank32(d->rank) * 2);
   return w;
 }
 
@@ -73,6 +73,16 @@ inline size_t f_code_byte(int K, int64_t row, int k) {
   const int r = (int)(row % 32), S = k / 64, h = (k % 64) / 32, j = k % 32;
   return (((size_t)b * (K / 64) + S) * 64 + (32 * h + r)) * 16 + j / 2;
 }
+// Fragment order of a bf16 operand with rank32 columns (Z = X_hat L1 and L2^T
+// on the MXFP4 path): rows in blocks of 32, columns in steps of 16; each
+// (block, step) is 1 KiB = 64 lanes x 8 bf16, lane l = 32h + r holding row
+// 32*block + r, columns 16*step + 8h + [0, 8). Returns an element index.
+inline size_t frag16_index(int r32, int64_t row, int col) {
+  const int64_t b = row / 32;
+  const int r = (int)(row % 32), c = col / 16, h = (col % 16) / 8, j = col % 8;
+  return (((size_t)b * (r32 / 16) + c) * 64 + (32 * h + r)) * 8 + j;
+}
+
 // Fragment order of MXFP4 scale bytes: [K/128 stage][rows32/32 block][64 lanes][2];
 // lane l = 32h + r of block b at stage st holds the bytes of the 32-channel
 // blocks kb = 4 st + 2 step + h (step = 0, 1) of row 32 b + r.

@@ -326,8 +326,10 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
     std::memset(out->l2, 0, (size_t)N * r32 * 2);
     for (int k = 0; k < K; ++k)
       for (int c = 0; c < r; ++c) out->l1[l1_index(K, r32, k, c)] = l1b[(size_t)k * r + c];
+    const bool mx = d->format == SVDQ_FMT_MXFP4_G32;
     for (int i = 0; i < r; ++i)
-      for (int n = 0; n < N; ++n) out->l2[(size_t)n * r32 + i] = l2b[(size_t)i * N + n];
+      for (int n = 0; n < N; ++n)
+        out->l2[mx ? frag16_index(r32, n, i) : (size_t)n * r32 + i] = l2b[(size_t)i * N + n];
   }
   for (int n = 0; n < N; ++n) {
     float b = bias ? bias[n] : 0.f;
@@ -506,7 +508,8 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
   if (l2 && r > 0) {
     if (!h->l2) return SVDQ_ERR_NULL;
     for (int i = 0; i < r; ++i)
-      for (int n = 0; n < N; ++n) l2[(size_t)i * N + n] = h->l2[(size_t)n * r32 + i];
+      for (int n = 0; n < N; ++n)
+        l2[(size_t)i * N + n] = h->l2[int4 ? (size_t)n * r32 + i : frag16_index(r32, n, i)];
   }
   if (bias) {
     if (!h->bias) return SVDQ_ERR_NULL;
@@ -553,7 +556,9 @@ svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const voi
   if (z && r > 0) {
     const uint16_t* zb = (const uint16_t*)(base + L.z);
     for (int64_t m = 0; m < M; ++m)
-      for (int i = 0; i < r; ++i) z[(size_t)m * r + i] = (float)bf16_to_double(zb[(size_t)m * r32 + i]);
+      for (int i = 0; i < r; ++i)
+        z[(size_t)m * r + i] =
+            (float)bf16_to_double(zb[int4 ? (size_t)m * r32 + i : frag16_index(r32, m, i)]);
   }
   return SVDQ_OK;
 }

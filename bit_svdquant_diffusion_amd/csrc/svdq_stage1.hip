@@ -186,7 +186,14 @@ __global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
     const int l = idx & 63, i = (idx >> 6) & 15, c = idx >> 10;
     const int row = m0 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
     const int col = 32 * c + (l & 31);
-    if (row < M) z[(size_t)row * r32 + col] = (uint16_t)f2bf(acc);
+    if (row < M) {
+      if constexpr (FMT == SVDQ_FMT_INT4_G64) {
+        z[(size_t)row * r32 + col] = (uint16_t)f2bf(acc);
+      } else {   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
+        z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
+          col % 8] = (uint16_t)f2bf(acc);
+      }
+    }
   }
 }
 
