@@ -33,6 +33,10 @@ constexpr int kBM = 192, kBN = 384, kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
 constexpr int kWM = kBM / kWGM, kWN = kBN / kWGN, kTM = kWM / 32, kTN = kWN / 32;
 constexpr int kMB = kBM / 32, kNBt = kBN / 32;     // 32-row blocks per tile: 6 (A), 12 (B)
 constexpr int kNStage = 4;
+// The 32 workgroups resident on one XCD take 8 tile-rows x 4 tile-columns:
+// per K stage they share 8 A blocks of 12 KiB and 4 B blocks of 24 KiB, the
+// split that minimizes the bytes the XCD's L2 must fetch for them.
+constexpr int kGroupM = 8;
 constexpr int kOps = 6;                            // transfers per wave per stage
 constexpr int kStores = 2 * 3 * 3;                 // 16-byte Y stores per wave per tile
 // one ring slot: A fragments (6 blocks x 2 steps x 1 KiB), B fragments (12 x 2 x 1 KiB),
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
 #define SVDQ_ISSUE(GS)                                                                              \
   {                                                                                                 \
     if (is_s == 0) {                                                                                \
-      const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, 4);         \
+      const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, kGroupM);         \
       is_mb0 = tmi.tm * kMB;                                                                        \
       is_nb0 = tmi.tn * kNBt;                                                                       \
     }                                                                                               \
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   // prologue: the first kNStage - 1 ring steps in flight
   for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
   for (int ct = 0; ct < my_tiles; ++ct) {
-    const TileMap tmc = map_tile((int)blockIdx.x + ct * grid, g.tiles_m, g.tiles_n, 4);
+    const TileMap tmc = map_tile((int)blockIdx.x + ct * grid, g.tiles_m, g.tiles_n, kGroupM);
     const int n0 = tmc.tn * kBN + wn * kWN;
 #pragma unroll
     for (int j = 0; j < kTN; ++j)

@@ -84,6 +84,7 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = ""):
     d = y_gpu.astype(np.float64) - y_ref
     fro = np.linalg.norm(d) / max(np.linalg.norm(y_ref), 1e-30)
     mx = np.abs(d).max() / max(np.abs(y_ref).max(), 1e-30)
+    print(f"[parity] {what}: rel_fro={fro:.3e} max_abs_rel={mx:.3e}", flush=True)
     assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
     assert fro <= Y_REL_FRO, f"{what}: relative Frobenius error {fro:.3e} > {Y_REL_FRO}"
     assert mx <= Y_MAX_ABS, f"{what}: max abs error {mx:.3e} max|Y| > {Y_MAX_ABS}"
