@@ -33,12 +33,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);
 }
 
-// INT4 code of x_hat for a group with scale s = fl32(amax/7) > 0 and inv ~ 1/s:
-// round half to even of the exact quotient x_hat/s, clamped to [-7, 7].
-// Fast path: t = x_hat*inv is within 1.4e-6 of the exact quotient, so if t is
-// farther than 1e-5 from a half-integer, rint(t) is the answer. Otherwise the
-// exact answer is counted from the signs of |x_hat| - (k + 1/2) s, each an
-// exactly-signed fused multiply-add (the product (k+1/2) s is exact inside it).
+// Exact INT4 code of x_hat for a group with scale s = fl32(amax/7) > 0: round
+// half to even of the exact quotient x_hat/s, clamped to [-7, 7]. The code is
+// counted from the signs of |x_hat| - (k + 1/2) s, each an exactly-signed
+// fused multiply-add (the product (k + 1/2) s is exact inside it). Used when a
+// rounded quotient lies too close to a half-integer to be trusted.
 __device__ __forceinline__ int q_int4_slow(float xh, float s) {
   float a = fabsf(xh);
   int q = 0;
@@ -54,24 +53,18 @@ __device__ __forceinline__ int q_int4_slow(float xh, float s) {
   }
   return xh < 0.f ? -q : q;
 }
-__device__ __forceinline__ int q_int4(float xh, float s, float inv, bool exact_all) {
-  float t = xh * inv;
-  t = __builtin_fminf(__builtin_fmaxf(t, -7.0f), 7.0f);
-  float q0 = __builtin_rintf(t);
-  float d = t - q0;
-  if (exact_all || __builtin_fabsf(d) > 0.49999f) return q_int4_slow(xh, s);
-  return (int)q0;
-}
 
 // E2M1 code (sign | e1 e0 | m) of an already scaled value v, round to nearest
-// with ties to the even mantissa bit, saturating at 6: the decision points are
-// the midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 between neighbouring values.
+// with ties to the even mantissa bit, saturating at 6. The grid spacing is
+// 1/2 below 2, 1 in [2, 4) and 2 from 4 on: with r = [|v| >= 2] + [|v| >= 4],
+// q = rint(|v| 2^(1-r)) (an exact product, then round half to even) counts
+// grid steps inside range r, and the code is q + 2r, saturated at 7.
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
-  float a = __builtin_fabsf(v);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-               (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+  const float a = __builtin_fabsf(v);
+  const int r = (int)(a >= 2.0f) + (int)(a >= 4.0f);
+  const float step_inv = __uint_as_float((uint32_t)(128 - r) << 23);   // 2^(1-r)
+  const uint32_t c = (uint32_t)__builtin_rintf(a * step_inv) + 2u * (uint32_t)r;
+  return (c < 7u ? c : 7u) | ((__float_as_uint(v) >> 28) & 8u);
 }
 
 // OCP MX shared exponent for E2M1: floor(log2 amax) - 2 clamped to [-127, 127]

@@ -91,13 +91,14 @@ inline size_t f_scale_index(int64_t rows32, int64_t row, int kb) {
   return (((size_t)st * (rows32 / 32) + row / 32) * 64 + (32 * h + row % 32)) * 2 + step;
 }
 
-// L1 device layout: [K/128][rank32/32][t=8][lane=64][8] bf16 where lane = 32h + c
-// holds L1[128 s + 64 h + 8 t + j][32 cb + c], j = 0..7.
+// L1 device layout: [K/256][4 quarters][rank32/16][t=2][lane=64][8] bf16 where
+// lane = 16j + c holds L1[256 s + 64 w + 16 j + 8 t + e][16 cb + c], e = 0..7:
+// the B operand of stage-1 MFMA t of wave w in step s for the 16 columns cb.
 inline size_t l1_index(int K, int r32, int k, int col) {
   (void)K;
-  int s = k / 128, kk = k % 128, h = kk / 64, t = (kk % 64) / 8, j = kk % 8;
-  int cb = col / 32, c = col % 32;
-  return ((((size_t)s * (r32 / 32) + cb) * 8 + t) * 64 + (32 * h + c)) * 8 + j;
+  const int s = k / 256, w = (k % 256) / 64, j = (k % 64) / 16, t = (k % 16) / 8, e = k % 8;
+  const int cb = col / 16, c = col % 16;
+  return (((((size_t)s * 4 + w) * (r32 / 16) + cb) * 2 + t) * 64 + (16 * j + c)) * 8 + e;
 }
 
 

@@ -8,211 +8,316 @@
 //     rounded to bf16 ("the low rank branch held at higher precision such as
 //     16 bit"; the branches "share inputs", same page).
 //
-// Work split: a workgroup owns 32 tokens; its WAVES waves split K in steps of
-// 128 channels (wave w takes steps w, w+WAVES, ...). Per step a wave
-//   1. loads the 32x128 bf16 slab with coalesced 16-byte loads (4 rows per
-//      instruction) and writes it to its own LDS slab (row pitch 272 bytes);
-//   2. reads it back so that lane (r = l%32, h = l/32) holds row r, channels
-//      [64h, 64h+64) of the step: exactly one INT4 group (two MXFP4 blocks),
-//      and exactly the A-operand run of eight 32x32x16 bf16 MFMAs;
-//   3. quantizes its group alone (no cross-lane reduction) and stores 32
-//      bytes of codes plus the scale;
-//   4. accumulates Z on MFMA against L1, which the pack stores in the same
-//      lane order (one contiguous 1 KiB per wave per MFMA).
-// The WAVES partial Z tiles are summed in LDS in wave order (deterministic)
-// and stored as bf16 [M][rank32].
+// Work split: a workgroup owns 16 tokens and walks K in steps of 256
+// channels; its four waves take one 64-channel quarter of every step each, so
+// a wave's quarter holds exactly one INT4 group (two MXFP4 blocks) per token.
+// Lane (r = l%16, j = l/16) holds token r and channels 16j .. 16j+15 of the
+// quarter. Per step a wave
+//   1. finds its quarter of X (16 tokens x 128 bytes) and of mu in LDS, moved
+//      there by direct global->LDS transfers issued D steps ahead into a ring
+//      of D + 1 slots; loads the step's L1 fragments into registers, then
+//      issues the transfers D steps ahead. Vector-memory operations retire in
+//      issue order, so each wait names exactly the operations issued after
+//      what it waits for, and no register carries a load across iterations;
+//   2. reads its 16 values of x, multiplies by mu (x_hat = fl32(x mu));
+//   3. quantizes: the group (block) absolute maximum is combined across the 4
+//      (2) lanes that share it with lane swaps; codes are stored as 8 bytes;
+//   4. accumulates Z on 16x16x32 bf16 MFMAs (two per 16 columns of L1).
+// X lands in LDS through direct global->LDS transfers whose per-lane source
+// addresses lay each token's 128 bytes out with its 16-byte chunks XOR-
+// swizzled by the token index, so the read-back is free of bank conflicts.
+// The four partial Z tiles are summed in LDS in wave order (deterministic)
+// and stored as bf16.
 #include "svdq_device.h"
 #include "svdq_internal.h"
 
 namespace svdq {
 
-constexpr int S1_ROWS = 32;
-constexpr int S1_PITCH = 272;  // bytes per LDS row: 256 data + 16 pad
+constexpr int S1_ROWS = 16;
+constexpr int S1_STEP = 256;                 // channels per step
+constexpr int S1_WAVES = 4;                  // one 64-channel quarter each
+constexpr int S1_XQ = S1_ROWS * 64 * 2;      // bytes of one wave's X quarter (2 KiB)
+constexpr int S1_MU = S1_WAVES * S1_XQ;      // offset of the step's mu in a ring slot
+constexpr int S1_SLOT = S1_MU + S1_STEP * 4; // X of all waves + mu of the step
 
-template <int FMT, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void stage1_kernel(
+typedef __attribute__((address_space(3))) void s1_lds_void;
+// s_waitcnt operand: vmcnt n (n < 64), expcnt and lgkmcnt not waited on
+#define S1_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070 | 0x0f00)
+
+// Vector-memory operations of one step and wave, in issue order: L1
+// fragments (2 per 16 columns), the ring transfers D steps ahead (2 X, 1 mu),
+// the two stores (codes, scale; they always issue, token m0 of every
+// workgroup exists). After step i's transfers are issued, what follows them
+// when step i waits is: in the first D steps, the later prologue transfers
+// and the whole steps before i; afterwards, the rest of step i - D and the
+// D - 1 steps between. The largest count must fit the 63 operations a wave
+// can have outstanding. (The compiler itself waits for all outstanding
+// operations before the MFMAs that read the L1 registers; keeping L1 in the
+// ring instead costs more LDS than the deeper X ring gains.)
+template <int NCB> struct S1Cfg {
+  static constexpr int kX = 3, kSt = 2;
+  static constexpr int kPerStep = 2 * NCB + kX + kSt;
+  static constexpr int kDepth0 = 1 + (61 - kSt) / kPerStep;
+  static constexpr int kDepth = kDepth0 > 7 ? 7 : kDepth0;
+  static constexpr int count(int i) {   // operations issued after step i's transfers
+    return i < kDepth ? kX * (kDepth - 1 - i) + i * kPerStep : kSt + (kDepth - 1) * kPerStep;
+  }
+  static_assert(count(kDepth) <= 62, "wait count out of range");
+};
+
+// max over the lanes l and l ^ 16 (and l ^ 32): each swap returns, between
+// its two results, the lane's own value and its partner's
+__device__ __forceinline__ float s1_max16(float a) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float s1_max32(float a) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+typedef __bf16 s1_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t s1_cvt_bf16x2(float lo, float hi) {
+  s1_bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// E2M1 codes of 8 values scaled by 2^-e, element 2i in the low nibble of byte i
+__device__ __forceinline__ uint32_t s1_e2m1x8(const float* v, int e) {
+  if (e >= -126) {   // normal scale: v_cvt_scalef32_pk_fp4_f32 divides by 2^e exactly, RNE, saturating
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
+  }
+  const float sinv = exp2_neg(e);
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_code(v[i] * sinv) << (4 * i);
+  return w;
+}
+
+template <int FMT, int NCB>
+__global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
-    uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, int M, int K,
-    int r32) {
+    uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, int M, int K) {
+  using Cfg = S1Cfg<NCB>;
+  constexpr int D = Cfg::kDepth;
+  constexpr int r32 = NCB * 16;
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = blockIdx.x * S1_ROWS;
-  const int nsteps = K / 128;
+  const int nsteps = K / S1_STEP;
   const int Mp = (M + 15) / 16 * 16;   // row stride of the INT4 scales
   const int MB = (M + 31) / 32;        // 32-row blocks (MXFP4 fragment order)
-  const int ncb = r32 / 32;
-  uint8_t* slab = smem + wave * (S1_ROWS * S1_PITCH);
 
-  // MFMA-layout coordinates of this lane
-  const int r = lane & 31, h = lane >> 5;
+  const int r = lane & 15, j = lane >> 4;
   const int m = m0 + r;
   const bool row_ok = m < M;
-  // coalesced-load coordinates
-  const int lr = lane >> 4, lc = lane & 15;
 
-  f32x16 zacc[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) zacc[c] = f32x16{};
+  // X transfer d (0, 1) of this lane: 16-byte unit u = 64 d + lane of the
+  // quarter, token u / 8, chunk (u % 8) ^ ((token / 2) % 8)
+  const int tA = lane >> 3, tB = 8 + (lane >> 3);
+  const uint16_t* srcA = x + (size_t)min(m0 + tA, M - 1) * K + wave * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
+  const uint16_t* srcB = x + (size_t)min(m0 + tB, M - 1) * K + wave * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
+  // read-back of chunks 2j, 2j+1 of token r
+  const int rd0 = (r * 8 + ((2 * j) ^ ((r >> 1) & 7))) * 16;
+  const int rd1 = (r * 8 + ((2 * j + 1) ^ ((r >> 1) & 7))) * 16;
 
-  for (int s = wave; s < nsteps; s += WAVES) {
-    // 1. coalesced load of the 32 x 128 slab, 4 rows per instruction
-    u32x4 raw[8];
+  f32x4 zacc[NCB > 0 ? NCB : 1];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int row = min(m0 + 4 * j + lr, M - 1);
-      raw[j] = *reinterpret_cast<const u32x4*>(x + (size_t)row * K + s * 128 + lc * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4*>(slab + (4 * j + lr) * S1_PITCH + lc * 16) = raw[j];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 2. group layout: lane (r, h) takes row r, channels 64h .. 64h+63 of the step
-    u32x4 xv[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      xv[t] = *reinterpret_cast<const u32x4*>(slab + r * S1_PITCH + h * 128 + t * 16);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
 
-    const int k0 = s * 128 + h * 64;
-    float xh[64];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const f32x4 mv = *reinterpret_cast<const f32x4*>(mu + k0 + 4 * t);
-      const uint32_t w0 = xv[t / 2][(t & 1) * 2 + 0];
-      const uint32_t w1 = xv[t / 2][(t & 1) * 2 + 1];
-      xh[4 * t + 0] = bf16lo(w0) * mv.x;
-      xh[4 * t + 1] = bf16hi(w0) * mv.y;
-      xh[4 * t + 2] = bf16lo(w1) * mv.z;
-      xh[4 * t + 3] = bf16hi(w1) * mv.w;
-    }
+  // ring transfers of step I; past the last step they re-read the first
+  // bytes of X and mu into the slot, so every step issues the same number
+#define S1_ISSUE(I)                                                                                \
+  {                                                                                                \
+    const bool real_ = (I) < nsteps;                                                               \
+    const size_t xo_ = real_ ? (size_t)(I) * S1_STEP : 0;                                          \
+    uint8_t* slot_ = smem + ((I) % (D + 1)) * S1_SLOT;                                             \
+    __builtin_amdgcn_global_load_lds(real_ ? srcA + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ), 16, 0, 0);        \
+    __builtin_amdgcn_global_load_lds(real_ ? srcB + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ + 1024), 16, 0, 0); \
+    __builtin_amdgcn_global_load_lds(real_ ? mu + xo_ + wave * 64 + lane : mu,                     \
+                                     (s1_lds_void*)(slot_ + S1_MU + wave * 256), 4, 0, 0);          \
+  }
+#define S1_WAIT_CASE(k)                                                                            \
+  case k: __builtin_amdgcn_s_waitcnt(S1_VMCNT(Cfg::count(k < D ? k : D))); break;
 
-    // 3. quantize the lane's 64 values
-    uint32_t packed[8];
-    if constexpr (FMT == SVDQ_FMT_INT4_G64) {
-      float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[i]));
-      const float sc = amax / 7.0f;            // IEEE-rounded division
-      const bool zero = !(sc > 0.f);
-      const float inv = zero ? 0.f : 1.0f / sc;
-      const bool exact_all = sc < 0x1p-100f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int q = zero ? 0 : q_int4(xh[8 * w + j], sc, inv, exact_all);
-          word |= ((uint32_t)q & 15u) << (4 * j);
+  for (int d = 0; d < D; ++d) S1_ISSUE(d)
+
+  for (int i = 0; i < nsteps; ++i) {
+        // 1. step i's transfers have landed once only the operations issued
+        //    after them are outstanding
+        __builtin_amdgcn_sched_barrier(0);
+        switch (i < D ? i : D) {
+          S1_WAIT_CASE(0) S1_WAIT_CASE(1) S1_WAIT_CASE(2) S1_WAIT_CASE(3)
+          S1_WAIT_CASE(4) S1_WAIT_CASE(5) S1_WAIT_CASE(6) S1_WAIT_CASE(7)
+          default: __builtin_amdgcn_s_waitcnt(S1_VMCNT(0)); break;
         }
-        packed[w] = word;
-      }
-      if (row_ok) reinterpret_cast<float*>(sx)[(size_t)(2 * s + h) * Mp + m] = sc;
-    } else {
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 l1v[NCB > 0 ? 2 * NCB : 1];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float amax = 0.f;
+        for (int f = 0; f < 2 * NCB; ++f)
+          l1v[f] = *reinterpret_cast<const u32x4*>(l1s + ((((size_t)i * S1_WAVES + wave) * NCB * 2 + f) * 64 + lane) * 8);
+        __builtin_amdgcn_sched_barrier(0);
+        S1_ISSUE(i + D)
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* slot = smem + (i % (D + 1)) * S1_SLOT;
+        const u32x4 xa = *reinterpret_cast<const u32x4*>(slot + wave * S1_XQ + rd0);
+        const u32x4 xb = *reinterpret_cast<const u32x4*>(slot + wave * S1_XQ + rd1);
+        const float* mus = reinterpret_cast<const float*>(slot + S1_MU + wave * 256) + 16 * j;
+        float xh[16];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[32 * b + i]));
-        const int e = mx_exponent(amax);
-        const float sinv = exp2_neg(e);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) word |= e2m1_code(xh[32 * b + 8 * w + j] * sinv) << (4 * j);
-          packed[4 * b + w] = word;
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 mv = *reinterpret_cast<const f32x4*>(mus + 4 * t);
+          const u32x4& xw = t < 2 ? xa : xb;
+          const uint32_t w0 = xw[(t & 1) * 2], w1 = xw[(t & 1) * 2 + 1];
+          xh[4 * t + 0] = bf16lo(w0) * mv.x;
+          xh[4 * t + 1] = bf16hi(w0) * mv.y;
+          xh[4 * t + 2] = bf16lo(w1) * mv.z;
+          xh[4 * t + 3] = bf16hi(w1) * mv.w;
         }
-        if (row_ok) {
-          // fragment-order scale byte: block kb = 4s + 2h + b -> stage s, step h, half b
-          reinterpret_cast<uint8_t*>(sx)[(((size_t)s * MB + m / 32) * 64 + 32 * b + r) * 2 + h] =
-              (uint8_t)(e + 127);
-        }
-      }
-    }
-    if (row_ok) {
-      if constexpr (FMT == SVDQ_FMT_INT4_G64) {
-        u32x4* dst = reinterpret_cast<u32x4*>(qx + (size_t)m * (K / 2) + k0 / 2);
-        dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-        dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
-      } else {
-        // fragment order: step S = 2s + h of row block m/32, lanes r and 32 + r
-        uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + 2 * s + h) * 1024;
-        *reinterpret_cast<u32x4*>(blk + r * 16) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-        *reinterpret_cast<u32x4*>(blk + (32 + r) * 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
-      }
-    }
+        const int k0 = i * S1_STEP + wave * 64;   // first channel of the quarter
 
-    // 4. Z += bf16(x_hat) L1 on 32x32x16 bf16 MFMA (8 per 32 columns)
-    if (ncb > 0) {
-      uint32_t ab[32];
+        // 3. Z += bf16(x_hat) L1: MFMA t takes channels 16j + 8t .. +7 of each lane
+        if constexpr (NCB > 0) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) ab[i] = pack_bf16x2(xh[2 * i], xh[2 * i + 1]);
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 av = u32x4{s1_cvt_bf16x2(xh[8 * t + 0], xh[8 * t + 1]), s1_cvt_bf16x2(xh[8 * t + 2], xh[8 * t + 3]),
+                                   s1_cvt_bf16x2(xh[8 * t + 4], xh[8 * t + 5]), s1_cvt_bf16x2(xh[8 * t + 6], xh[8 * t + 7])};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c < ncb) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            u32x4 bv = *reinterpret_cast<const u32x4*>(
-                l1s + ((((size_t)s * ncb + c) * 8 + t) * 64 + lane) * 8);
-            u32x4 av = u32x4{ab[4 * t], ab[4 * t + 1], ab[4 * t + 2], ab[4 * t + 3]};
-            zacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *reinterpret_cast<bf16x8*>(&av), *reinterpret_cast<bf16x8*>(&bv), zacc[c], 0, 0, 0);
+            for (int c = 0; c < NCB; ++c)
+              zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                               __builtin_bit_cast(bf16x8, l1v[2 * c + t]), zacc[c], 0, 0, 0);
           }
         }
-      }
-    }
-  }
 
-  if (ncb == 0) return;
-  // reduce the WAVES partial Z tiles in wave order and store bf16
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
+
+        // 4. quantize
+        float amax = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (c < ncb) {
+        for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[e]));
+        amax = s1_max16(amax);                   // the lane pair 16 channels apart
+        uint32_t c0, c1;
+        if constexpr (FMT == SVDQ_FMT_INT4_G64) {
+          amax = s1_max32(amax);                 // the 4 lanes of the 64-channel group
+          const float sc = amax / 7.0f;          // IEEE-rounded division
+          // t = x_hat * rcp(s) is within 1.3e-6 of the exact quotient (|q| <= 7,
+          // rcp within 1 ulp), so rint(t) is the answer unless t lies within
+          // 1e-5 of a half-integer; then the lane redoes its values exactly.
+          // Zero and tiny scales always take the exact path.
+          const float inv = __builtin_amdgcn_rcpf(sc);
+          bool near = !(sc >= 0x1p-100f);
+          c0 = 0;
+          c1 = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[((wave * ncb + c) * 16 + i) * 64 + lane] = zacc[c][i];
+          for (int e = 0; e < 8; ++e) {
+            const float t0 = xh[e] * inv, t1 = xh[8 + e] * inv;
+            const float r0 = __builtin_rintf(t0), r1 = __builtin_rintf(t1);
+            near |= __builtin_fabsf(t0 - r0) > 0.49999f;
+            near |= __builtin_fabsf(t1 - r1) > 0.49999f;
+            c0 |= ((uint32_t)(int)r0 & 15u) << (4 * e);
+            c1 |= ((uint32_t)(int)r1 & 15u) << (4 * e);
+          }
+          if (near) {
+            c0 = 0;
+            c1 = 0;
+            if (sc > 0.f) {
+#pragma unroll 1
+              for (int e = 0; e < 8; ++e) {
+                c0 |= ((uint32_t)q_int4_slow(xh[e], sc) & 15u) << (4 * e);
+                c1 |= ((uint32_t)q_int4_slow(xh[8 + e], sc) & 15u) << (4 * e);
+              }
+            }
+          }
+          if (row_ok && j == 0) reinterpret_cast<float*>(sx)[(size_t)(k0 / 64) * Mp + m] = sc;
+          if (row_ok) *reinterpret_cast<u32x2*>(qx + (size_t)m * (K / 2) + k0 / 2 + 8 * j) = u32x2{c0, c1};
+        } else {
+          const int e = mx_exponent(amax);       // block b = j / 2 of the quarter
+          c0 = s1_e2m1x8(xh, e);
+          c1 = s1_e2m1x8(xh + 8, e);
+          if (row_ok && (j & 1) == 0) {
+            // fragment-order scale byte of 32-channel block kb = k0/32 + j/2:
+            // stage kb/4, step (kb%4)/2, half kb%2
+            const int kb = k0 / 32 + (j >> 1);
+            reinterpret_cast<uint8_t*>(sx)[(((size_t)(kb >> 2) * MB + m / 32) * 64 + 32 * (kb & 1) + m % 32) * 2 +
+                                           ((kb >> 1) & 1)] = (uint8_t)(e + 127);
+          }
+          if (row_ok) {
+            // fragment order: 64-channel step k0/64 of row block m/32; channels
+            // 32h .. 32h+31 at lane 32h + m%32, 16 channels = 8 bytes
+            uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + k0 / 64) * 1024;
+            *reinterpret_cast<u32x2*>(blk + (32 * (j >> 1) + m % 32) * 16 + (j & 1) * 8) = u32x2{c0, c1};
+          }
+        }
+
+  }
+#undef S1_ISSUE
+#undef S1_WAIT_CASE
+  // the transfers issued past the last step still write the ring
+  __builtin_amdgcn_s_waitcnt(S1_VMCNT(0));
+
+  if constexpr (NCB > 0) {
+    // reduce the four partial Z tiles in wave order and store bf16
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[((wave * NCB + c) * 4 + e) * 64 + lane] = zacc[c][e];
     }
-  __syncthreads();
-  const int total = ncb * 16 * 64;
-  for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
-    float acc = 0.f;
-    for (int w = 0; w < WAVES; ++w) acc += red[w * total + idx];
-    const int l = idx & 63, i = (idx >> 6) & 15, c = idx >> 10;
-    const int row = m0 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
-    const int col = 32 * c + (l & 31);
-    if (row < M) {
-      if constexpr (FMT == SVDQ_FMT_INT4_G64) {
-        z[(size_t)row * r32 + col] = (uint16_t)f2bf(acc);
-      } else {   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
-        z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
-          col % 8] = (uint16_t)f2bf(acc);
+    __syncthreads();
+    constexpr int total = NCB * 4 * 64;
+    for (int idx = threadIdx.x; idx < total; idx += 64 * S1_WAVES) {
+      float acc = 0.f;
+      for (int w = 0; w < S1_WAVES; ++w) acc += red[w * total + idx];
+      // 16x16 result layout: lane l, reg e -> row 4(l/16) + e, column l%16
+      const int l = idx & 63, e = (idx >> 6) & 3, c = idx >> 8;
+      const int row = m0 + 4 * (l >> 4) + e;
+      const int col = 16 * c + (l & 15);
+      if (row < M) {
+        if constexpr (FMT == SVDQ_FMT_INT4_G64) {
+          z[(size_t)row * r32 + col] = (uint16_t)f2bf(acc);
+        } else {   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
+          z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
+            col % 8] = (uint16_t)f2bf(acc);
+        }
       }
     }
   }
 }
 
-template <int FMT, int WAVES>
+template <int FMT, int NCB>
 static hipError_t launch_t(const Stage1Args& a, hipStream_t st) {
-  const int r32 = a.r32;
-  size_t slab = (size_t)WAVES * S1_ROWS * S1_PITCH;
-  size_t red = (size_t)WAVES * (r32 / 32) * 16 * 64 * 4;
-  size_t lds = slab > red ? slab : red;
+  constexpr int D = S1Cfg<NCB>::kDepth;
+  const size_t ring = (size_t)(D + 1) * S1_SLOT;
+  const size_t red = (size_t)S1_WAVES * NCB * 4 * 64 * 4;
+  const size_t lds = ring > red ? ring : red;
   dim3 grid((a.M + S1_ROWS - 1) / S1_ROWS);
-  hipLaunchKernelGGL((stage1_kernel<FMT, WAVES>), grid, dim3(64 * WAVES), lds, st, a.x, a.mu,
-                     a.l1s, a.qx, a.sx, a.z, a.M, a.K, r32);
+  hipLaunchKernelGGL((stage1_kernel<FMT, NCB>), grid, dim3(64 * S1_WAVES), lds, st, a.x, a.mu, a.l1s,
+                     a.qx, a.sx, a.z, a.M, a.K);
   return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const Stage1Args& a, hipStream_t st) {
+  switch (a.r32) {
+    case 0: return launch_t<FMT, 0>(a, st);
+    case 32: return launch_t<FMT, 2>(a, st);
+    case 64: return launch_t<FMT, 4>(a, st);
+    case 96: return launch_t<FMT, 6>(a, st);
+    case 128: return launch_t<FMT, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (a.fmt == SVDQ_FMT_INT4_G64) return launch_t<SVDQ_FMT_INT4_G64, 4>(a, st);
-  return launch_t<SVDQ_FMT_MXFP4_G32, 4>(a, st);
+  if (a.fmt == SVDQ_FMT_INT4_G64) return launch_fmt<SVDQ_FMT_INT4_G64>(a, st);
+  return launch_fmt<SVDQ_FMT_MXFP4_G32>(a, st);
 }
 
 }  // namespace svdq

@@ -206,3 +206,57 @@ def test_full_size_sampled(spec):
         torch.cuda.synchronize()
         want = O.int4_group_sums(qx[m0:m0 + mc], ref["qw"][spec.N - 96:])
         assert np.array_equal(p.cpu().numpy(), want)
+
+
+def _tie_rows(fmt: str, K: int, M: int) -> np.ndarray:
+    """bf16-representable rows that put the quantizer's decision points in front
+    of the device code with mu = 1: every E2M1 tie (0.25 0.75 1.25 1.75 2.5 3.5
+    5, block max 6 so the MX exponent is 0) or every INT4 half-integer (group
+    max 7 so s = 1), their bf16 neighbours, zeros of both signs, values past
+    saturation, and an all-zero group; each row scaled by its own power of two
+    (the codes are scale invariant, the scales are not)."""
+    rng = np.random.default_rng(123)
+    if fmt == "mxfp4":
+        ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        top, blk = 6.0, 32
+    else:
+        ties = np.arange(7) + 0.5
+        top, blk = 7.0, 64
+    up = ties * (1 + 2.0 ** -7)          # next bf16 above each tie (one ulp at 8 mantissa bits)
+    dn = ties * (1 - 2.0 ** -8)          # next bf16 below
+    base = np.concatenate([ties, up, dn, [0.0, 0.1, top * 0.999]])
+    rows = np.zeros((M, K))
+    for m in range(M):
+        for g in range(K // blk):
+            vals = np.resize(rng.permutation(np.concatenate([base, -base])), blk)
+            vals[g % blk] = top if (m + g) % 2 else -top
+            if (m * 7 + g) % 11 == 0:
+                vals[:] = 0.0                            # all-zero group
+            if (m + 3 * g) % 13 == 0:
+                vals[(g + 1) % blk] = -0.0
+            rows[m, g * blk:(g + 1) * blk] = vals
+        rows[m] *= 2.0 ** ((m % 21) - 10)
+    return O.to_bf16(rows.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_stage1_quantizer_tie_points(fmt):
+    """Codes and scales bit-exact with the oracle on every rounding decision point."""
+    _say(f"[stage1 ties] {fmt}")
+    K, N, r, M = 512, 64, 16, 48
+    layer = S.Layer(K, N, r, fmt)
+    rng = np.random.default_rng(7)
+    l1 = O.bf16_to_bits(O.to_bf16(rng.standard_normal((K, r)).astype(np.float32)))
+    l2 = O.bf16_to_bits(O.to_bf16(rng.standard_normal((r, N)).astype(np.float32)))
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    host = S.quantize_residual(layer, w, None, np.ones(K, np.float32), l1, l2)
+    dev = S.to_device(layer, host, "cuda")
+    xr = _tie_rows(fmt, K, M)
+    x = torch.from_numpy(O.bf16_to_bits(xr).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.full((S.workspace_bytes(layer, M),), 0xFF, dtype=torch.uint8, device="cuda")
+    S.stage1(layer, dev, x, ws)
+    torch.cuda.synchronize()
+    got = S.unpack_workspace(layer, M, ws.cpu().numpy())
+    qx, sx = O.quantize_activations(xr.astype(np.float32), fmt)
+    assert np.array_equal(got["codes"], qx.astype(np.int8)), "activation codes at tie points"
+    assert np.array_equal(got["scales"], sx), "activation scales at tie points"

@@ -93,20 +93,22 @@ def test_pack_null_bias_is_zero():
 
 
 def test_device_layout_of_l1_matches_stage1_order():
-    """L1 is stored so that lane 32h+c of MFMA t in step s holds L1[128s+64h+8t+j][32cb+c]."""
-    K, N, r = 256, 64, 48
+    """L1 is stored so that lane 16j+c of MFMA t of wave w in step s holds
+    L1[256s+64w+16j+8t+e][16cb+c]."""
+    K, N, r = 512, 64, 48
     layer = S.Layer(K, N, r, "int4")
     rng = np.random.default_rng(2)
     l1 = O.bf16_to_bits(O.to_bf16(rng.standard_normal((K, r))))
     l2 = O.bf16_to_bits(O.to_bf16(rng.standard_normal((r, N))))
     host = S.quantize_residual(layer, rng.standard_normal((N, K)).astype(np.float32), None,
                                np.ones(K, np.float32), l1, l2)
-    dev_l1 = host["l1"].view(np.uint16).reshape(K // 128, 2, 8, 64, 8)   # r32 = 64
-    for (k, c) in [(0, 0), (5, 47), (200, 33), (255, 16)]:
-        s, kk = divmod(k, 128)
-        h, rem = divmod(kk, 64)
-        t, j = divmod(rem, 8)
-        assert dev_l1[s, c // 32, t, 32 * h + c % 32, j] == l1[k, c]
-    assert np.all(dev_l1[:, 1, :, :, :][:, :, np.arange(64) % 32 >= 16, :] == 0)  # padded cols
+    dev_l1 = host["l1"].view(np.uint16).reshape(K // 256, 4, 4, 2, 64, 8)   # r32 = 64: 4 blocks of 16
+    for (k, c) in [(0, 0), (5, 47), (200, 33), (255, 16), (300, 1), (511, 40), (77, 20)]:
+        s, kk = divmod(k, 256)
+        w, kk = divmod(kk, 64)
+        j, kk = divmod(kk, 16)
+        t, e = divmod(kk, 8)
+        assert dev_l1[s, w, c // 16, t, 16 * j + c % 16, e] == l1[k, c]
+    assert np.all(dev_l1[:, :, 3] == 0)   # columns 48..63 are padding
     dev_l2 = host["l2"].view(np.uint16).reshape(N, 64)
     assert np.array_equal(dev_l2[:, :r], l2.T) and np.all(dev_l2[:, r:] == 0)
