@@ -86,40 +86,20 @@ struct Geo {
 
 // Ring-step transfers. Every transfer is a full 64-lane direct global->LDS
 // load and every wave issues exactly kOps per stage. Waves 0-5 move six 1 KiB
-// fragment blocks each: code block q (0..35), A blocks first, block q/2 of the
-// tile's 32-row blocks, step q%2 of the stage's two steps (4-bit stage s:
-// 64-channel steps 2s, 2s+1; low-rank stage l: 16-column steps 2l, 2l+1 of Z
-// on the A side and L2^T on the B side). Waves 6-7 move 256-byte dword
-// transfers: in 4-bit stages the A scale bytes (3) and B scale bytes (6); in
-// low-rank stages the tile's 384 bias values (3); the remaining ops repeat
-// the first of their kind (same bytes to the same place).
-__device__ __forceinline__ void issue_block(const GemmArgs& a, const Geo& g, int mb0, int nb0,
-                                            bool lrs, int sl, int q, int lane, uint8_t* slot) {
-  const bool isA = q < 2 * kMB;
-  const int blk = isA ? (q >> 1) : ((q - 2 * kMB) >> 1);
-  const int b = min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);
-  const uint8_t* tensor = lrs ? reinterpret_cast<const uint8_t*>(isA ? a.z : a.l2t) : (isA ? a.qx : a.qw);
-  const int per = lrs ? a.r32 / 16 : g.KS;
-  const size_t off = ((size_t)b * per + 2 * sl + (q & 1)) * 1024 + lane * 16;
-  const int dst = isA ? kCodeA + q * 1024 : kCodeB + (q - 2 * kMB) * 1024;
-  __builtin_amdgcn_global_load_lds(tensor + off, lds_ptr(slot + dst), 16, 0, 0);
-}
-// dword transfer o (0..11) of waves 6-7
-__device__ __forceinline__ void issue_small(const GemmArgs& a, const Geo& g, int mb0, int nb0,
-                                            bool lrs, int sl, int o, int lane, uint8_t* slot) {
-  if (lrs) {   // bias: lane l of op k holds channels 128 k + 2 l, +1 of the tile
-    const int k = o < 3 ? o : 0;
-    const int n = min(nb0 * 32 + 128 * k + 2 * lane, g.N - 2);
-    __builtin_amdgcn_global_load_lds(a.bias + n, lds_ptr(slot + kScA + 256 * k), 4, 0, 0);
-    return;
-  }
-  const bool isA = o < 3 || o >= 9;
-  const int k = o < 3 ? o : (o < 9 ? o - 3 : 0);   // 256-byte piece = 2 blocks of 128
-  const int b = min((isA ? mb0 : nb0) + 2 * k + (lane >> 5), (isA ? g.MB : g.NB) - 1);
-  const int rows = isA ? g.MB : g.NB;
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw);
-  const uint8_t* src = base + ((size_t)sl * rows + b) * 128 + (lane & 31) * 4;
-  __builtin_amdgcn_global_load_lds(src, lds_ptr(slot + (isA ? kScA : kScB) + 256 * k), 4, 0, 0);
+// fragment blocks each: waves 0-1 the A side, waves 2-5 the B side, three
+// 32-row blocks per wave, both 64-channel steps of a 4-bit stage (or both
+// 16-column steps of Z and L2^T in a low-rank stage). Waves 6-7 move 256-byte
+// dword transfers: in 4-bit stages the A scale bytes (3) and B scale bytes
+// (6); in low-rank stages the tile's 384 bias values (3); the remaining ops
+// repeat the first of their kind (same bytes to the same place). The source
+// of every transfer is fixed per tile up to a per-stage offset, so each tile
+// sets six source pointers per wave once.
+//
+// bias transfer k (0..2): lane l holds channels 128 k + 2 l, +1 of the tile
+__device__ __forceinline__ void issue_bias(const GemmArgs& a, const Geo& g, int nb0, int k, int lane,
+                                           uint8_t* slot) {
+  const int n = min(nb0 * 32 + 128 * k + 2 * lane, g.N - 2);
+  __builtin_amdgcn_global_load_lds(a.bias + n, lds_ptr(slot + kScA + 256 * k), 4, 0, 0);
 }
 }  // namespace
 
@@ -133,28 +113,67 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / grid + 1 : 0;
   const int total = my_tiles * g.nstt;   // ring steps of this workgroup
 
-  // issue side: next ring step to load (tile-local index, stage, block origins of that tile)
-  int is_t = 0, is_s = 0, is_mb0 = 0, is_nb0 = 0;
+  // issue side: next ring step to load (tile-local index, stage, tile origin)
+  // and this wave's per-tile transfer sources: waves 0-5 keep the 4-bit
+  // source of their three blocks in src[0..2] and the low-rank source in
+  // src[3..5]; waves 6-7 keep one scale source per transfer
+  int is_t = 0, is_s = 0, is_nb0 = 0;
+  const uint8_t* src[kOps];
+  int srow[kOps];   // waves 6-7: bytes between stages of transfer i
+  const bool blockw = wave < kNW - 2, sidea = wave < 2;
+  const int per_l = a.r32 / 16;
 #define SVDQ_ISSUE(GS)                                                                              \
   {                                                                                                 \
     if (is_s == 0) {                                                                                \
-      const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, kGroupM);         \
-      is_mb0 = tmi.tm * kMB;                                                                        \
+      const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, kGroupM);   \
+      const int mb0 = tmi.tm * kMB;                                                                 \
       is_nb0 = tmi.tn * kNBt;                                                                       \
+      if (blockw) {                                                                                 \
+        const int b0 = sidea ? mb0 + 3 * wave : is_nb0 + 3 * (wave - 2);                            \
+        const int lim = (sidea ? g.MB : g.NB) - 1;                                                  \
+        const uint8_t* t4 = sidea ? a.qx : a.qw;                                                    \
+        const uint8_t* tl = reinterpret_cast<const uint8_t*>(sidea ? a.z : a.l2t);                  \
+        _Pragma("unroll") for (int j = 0; j < 3; ++j) {                                             \
+          const size_t bj = (size_t)min(b0 + j, lim);                                               \
+          src[j] = t4 + bj * g.KS * 1024 + lane * 16;                                               \
+          src[3 + j] = tl + bj * per_l * 1024 + lane * 16;                                          \
+        }                                                                                           \
+      } else {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < kOps; ++i) {                                          \
+          const int o = (wave - (kNW - 2)) * kOps + i;                                              \
+          const bool isA = o < 3 || o >= 9;                                                         \
+          const int k = o < 3 ? o : (o < 9 ? o - 3 : 0);   /* 256-byte piece = 2 blocks of 128 */  \
+          const int b = min((isA ? mb0 : is_nb0) + 2 * k + (lane >> 5), (isA ? g.MB : g.NB) - 1);   \
+          src[i] = reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw) + (size_t)b * 128 + (lane & 31) * 4; \
+          srow[i] = (isA ? g.MB : g.NB) * 128;                                                      \
+        }                                                                                           \
+      }                                                                                             \
     }                                                                                               \
     uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
     const bool lrs = is_s >= g.nst;                                                                 \
     const int sl = lrs ? is_s - g.nst : is_s;                                                       \
-    if (wave < kNW - 2) {                                                                           \
+    if (blockw) {                                                                                   \
       if (lrs && a.r32 == 0) {                                                                      \
-        _Pragma("unroll") for (int i = 0; i < kOps; ++i) issue_small(a, g, is_mb0, is_nb0, true, sl, 0, lane, slot_w); \
+        _Pragma("unroll") for (int i = 0; i < kOps; ++i) issue_bias(a, g, is_nb0, 0, lane, slot_w); \
       } else {                                                                                      \
+        uint8_t* dst = slot_w + (sidea ? kCodeA + 6 * wave * 1024 : kCodeB + 6 * (wave - 2) * 1024); \
         _Pragma("unroll") for (int i = 0; i < kOps; ++i)                                            \
-            issue_block(a, g, is_mb0, is_nb0, lrs, sl, wave * kOps + i, lane, slot_w);              \
+          __builtin_amdgcn_global_load_lds(src[(lrs ? 3 : 0) + i / 2] + (size_t)(2 * sl + (i & 1)) * 1024, \
+                                           lds_ptr(dst + i * 1024), 16, 0, 0);                      \
+      }                                                                                             \
+    } else if (lrs) {                                                                               \
+      _Pragma("unroll") for (int i = 0; i < kOps; ++i) {                                            \
+        const int o = (wave - (kNW - 2)) * kOps + i;                                                \
+        issue_bias(a, g, is_nb0, o < 3 ? o : 0, lane, slot_w);                                      \
       }                                                                                             \
     } else {                                                                                        \
-      _Pragma("unroll") for (int i = 0; i < kOps; ++i)                                              \
-          issue_small(a, g, is_mb0, is_nb0, lrs, sl, (wave - (kNW - 2)) * kOps + i, lane, slot_w);  \
+      _Pragma("unroll") for (int i = 0; i < kOps; ++i) {                                            \
+        const int o = (wave - (kNW - 2)) * kOps + i;                                                \
+        const int k = o < 3 ? o : (o < 9 ? o - 3 : 0);                                              \
+        const bool isA = o < 3 || o >= 9;                                                           \
+        __builtin_amdgcn_global_load_lds(src[i] + (size_t)sl * srow[i],                             \
+                                         lds_ptr(slot_w + (isA ? kScA : kScB) + 256 * k), 4, 0, 0); \
+      }                                                                                             \
     }                                                                                               \
     if (++is_s == g.nstt) {                                                                         \
       is_s = 0;                                                                                     \
