@@ -172,8 +172,9 @@ def cpu_baseline(layer, host, lay, spec, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: clocks and caches take tens of milliseconds to settle")
     ap.add_argument("--rotate", type=int, default=4, help="distinct buffer sets cycled (defeats the 256 MB MALL)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

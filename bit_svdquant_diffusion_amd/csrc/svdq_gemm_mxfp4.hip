@@ -209,7 +209,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
     }                                                                                               \
   }
   // One ring step. The deferred second half of the previous step's MFMAs goes
-  // first, so the matrix pipe has work while this step's fragments load.
+  // first, so the matrix pipe has work while this step's step-0 fragments
+  // load; the step-1 fragments are read behind the step-0 MFMAs.
   // Waves 0-3 issue their transfers for ring step gs + 3 before their LDS
   // reads, waves 4-7 after their step-0 MFMAs, so each SIMD's two waves do
   // not stall on transfer issue at the same time. `stores_due` counts the
@@ -234,8 +235,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
             sb[t] = *reinterpret_cast<const uint16_t*>(slot + kScB + (wn * kTN + t) * 128 + lane * 2); \
       }                                                                                             \
       SVDQ_READ(slot, 0, f0a, f0b)                                                                  \
-      SVDQ_READ(slot, 1, f1a, f1b)                                                                  \
       SVDQ_MFMA(LOWRANK, 0, f0a, f0b, sa, sb)                                                       \
+      SVDQ_READ(slot, 1, f1a, f1b)   /* used by the deferred MFMAs: loads behind step 0 */         \
       if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)                                           \
       _Pragma("unroll") for (int t = 0; t < kTM; ++t) pa[t] = sa[t];                                \
       _Pragma("unroll") for (int t = 0; t < kTN; ++t) pb[t] = sb[t];                                \
