@@ -37,8 +37,17 @@ constexpr int kNStage = 4;
 // per K stage they share 8 A blocks of 12 KiB and 4 B blocks of 24 KiB, the
 // split that minimizes the bytes the XCD's L2 must fetch for them.
 constexpr int kGroupM = 8;
-constexpr int kOps = 6;                            // transfers per wave per stage
 constexpr int kStores = 2 * 3 * 3;                 // 16-byte Y stores per wave per tile
+// Transfers per stage: 36 fragment blocks of 1 KiB and 3 scale (or bias)
+// transfers of up to 1 KiB, spread so that each SIMD (waves w and w + 4)
+// issues 9 or 10 of them: wave w moves kFrag(w) fragment blocks starting at
+// kFrag0(w), and waves 2, 3 and 6 one scale transfer each.
+__host__ __device__ constexpr int kFrag(int w) { return (w & 2) ? 4 : 5; }
+__host__ __device__ constexpr int kFrag0(int w) {
+  return w == 0 ? 0 : w == 1 ? 5 : w == 2 ? 10 : w == 3 ? 14 : w == 4 ? 18 : w == 5 ? 23 : w == 6 ? 28 : 32;
+}
+__host__ __device__ constexpr int kScaleOp(int w) { return w == 2 ? 0 : (w == 3 ? 1 : (w == 6 ? 2 : -1)); }
+__host__ __device__ constexpr int kOpsOf(int w) { return kFrag(w) + (kScaleOp(w) >= 0 ? 1 : 0); }
 // one ring slot: A fragments (6 blocks x 2 steps x 1 KiB), B fragments (12 x 2 x 1 KiB),
 // A scale bytes (6 x 128 B), B scale bytes (12 x 128 B)
 constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 1024;
@@ -46,8 +55,10 @@ constexpr int kScB = kScA + kMB * 128, kSlot = kScB + kNBt * 128;
 constexpr size_t kLds = (size_t)kNStage * kSlot;
 static_assert(kTM == 3 && kTN == 3, "schedule below assumes 3 x 3 blocks per wave");
 static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
-static_assert(2 * (kMB + kNBt) == (kNW - 2) * kOps, "waves 0-5 move the fragment blocks");
-static_assert(kMB * 128 == 3 * 256 && kNBt * 128 == 6 * 256, "scale bytes move as 256-byte dword transfers");
+static_assert(kFrag0(0) == 0 && kFrag0(1) == 5 && kFrag0(2) == 10 && kFrag0(3) == 14 && kFrag0(4) == 18 &&
+              kFrag0(5) == 23 && kFrag0(6) == 28 && kFrag0(7) == 32 && kFrag0(7) + kFrag(7) == 2 * (kMB + kNBt),
+              "fragment blocks partition");
+static_assert(kMB * 128 == 768 && kNBt * 128 == 1536 && kBN * 2 == 768, "scale and bias transfer sizes");
 
 // Ring barrier: wait until at most n of this wave's vector-memory operations
 // are outstanding, and its LDS reads have returned, then s_barrier. Vector
@@ -59,12 +70,15 @@ static_assert(kMB * 128 == 3 * 256 && kNBt * 128 == 6 * 256, "scale bytes move a
 __device__ __forceinline__ void ring_barrier(int n) {
   __builtin_amdgcn_sched_barrier(0);
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(6)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(12)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(5)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(10)); break;
     case 18: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(18)); break;
-    case 24: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(24)); break;
-    case 30: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(30)); break;
+    case 22: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(22)); break;
+    case 23: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(23)); break;
+    case 26: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(26)); break;
+    case 28: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(28)); break;
     default: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
   }
   __builtin_amdgcn_s_barrier();
@@ -84,23 +98,16 @@ struct Geo {
   int M, N, K, MB, NB, KS, nst, nlr, nstt, tiles_m, tiles_n;
 };
 
-// Ring-step transfers. Every transfer is a full 64-lane direct global->LDS
-// load and every wave issues exactly kOps per stage. Waves 0-5 move six 1 KiB
-// fragment blocks each: waves 0-1 the A side, waves 2-5 the B side, three
-// 32-row blocks per wave, both 64-channel steps of a 4-bit stage (or both
-// 16-column steps of Z and L2^T in a low-rank stage). Waves 6-7 move 256-byte
-// dword transfers: in 4-bit stages the A scale bytes (3) and B scale bytes
-// (6); in low-rank stages the tile's 384 bias values (3); the remaining ops
-// repeat the first of their kind (same bytes to the same place). The source
-// of every transfer is fixed per tile up to a per-stage offset, so each tile
-// sets six source pointers per wave once.
-//
-// bias transfer k (0..2): lane l holds channels 128 k + 2 l, +1 of the tile
-__device__ __forceinline__ void issue_bias(const GemmArgs& a, const Geo& g, int nb0, int k, int lane,
-                                           uint8_t* slot) {
-  const int n = min(nb0 * 32 + 128 * k + 2 * lane, g.N - 2);
-  __builtin_amdgcn_global_load_lds(a.bias + n, lds_ptr(slot + kScA + 256 * k), 4, 0, 0);
-}
+// Ring-step transfers: direct global->LDS loads of 16 bytes per lane. A
+// fragment block is 1 KiB (both 64-channel steps of a 4-bit stage, or both
+// 16-column steps of Z and L2^T in a low-rank stage). The tile's scale bytes
+// of a stage are contiguous in the stage-major scale layout: 768 A bytes (48
+// lanes) and 1536 B bytes (64 + 32 lanes). In low-rank stages the three
+// scale transfers move the tile's 384 bias values instead (48 lanes; the
+// other two repeat it: same bytes to the same place). The number of
+// transfers of a wave is the same in every stage. The source of every
+// transfer is fixed per tile up to a per-stage offset, so each tile sets the
+// sources once.
 }  // namespace
 
 __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g, int grid) {
@@ -114,65 +121,61 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   const int total = my_tiles * g.nstt;   // ring steps of this workgroup
 
   // issue side: next ring step to load (tile-local index, stage, tile origin)
-  // and this wave's per-tile transfer sources: waves 0-5 keep the 4-bit
-  // source of their three blocks in src[0..2] and the low-rank source in
-  // src[3..5]; waves 6-7 keep one scale source per transfer
-  int is_t = 0, is_s = 0, is_nb0 = 0;
-  const uint8_t* src[kOps];
-  int srow[kOps];   // waves 6-7: bytes between stages of transfer i
-  const bool blockw = wave < kNW - 2, sidea = wave < 2;
+  // and this wave's per-tile transfer sources: fragment block k of the wave
+  // from src[k] (4-bit) and src[5 + k] (low-rank); the scale transfer from
+  // ssrc (4-bit) and bsrc (bias)
+  const int nfrag = kFrag(wave), frag0 = kFrag0(wave), sop = kScaleOp(wave);
+  const int nops = kOpsOf(wave);
+  const int slanes = sop == 0 ? 48 : (sop == 1 ? 64 : 32);   // active lanes of the scale transfer
+  int is_t = 0, is_s = 0;
+  const uint8_t* src[10];
+  const uint8_t* ssrc = nullptr;
+  const uint8_t* bsrc = nullptr;
+  int sstride = 0;   // bytes between stages of the scale transfer
   const int per_l = a.r32 / 16;
 #define SVDQ_ISSUE(GS)                                                                              \
   {                                                                                                 \
     if (is_s == 0) {                                                                                \
       const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, kGroupM);   \
-      const int mb0 = tmi.tm * kMB;                                                                 \
-      is_nb0 = tmi.tn * kNBt;                                                                       \
-      if (blockw) {                                                                                 \
-        const int b0 = sidea ? mb0 + 3 * wave : is_nb0 + 3 * (wave - 2);                            \
-        const int lim = (sidea ? g.MB : g.NB) - 1;                                                  \
-        const uint8_t* t4 = sidea ? a.qx : a.qw;                                                    \
-        const uint8_t* tl = reinterpret_cast<const uint8_t*>(sidea ? a.z : a.l2t);                  \
-        _Pragma("unroll") for (int j = 0; j < 3; ++j) {                                             \
-          const size_t bj = (size_t)min(b0 + j, lim);                                               \
-          src[j] = t4 + bj * g.KS * 1024 + lane * 16;                                               \
-          src[3 + j] = tl + bj * per_l * 1024 + lane * 16;                                          \
-        }                                                                                           \
-      } else {                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < kOps; ++i) {                                          \
-          const int o = (wave - (kNW - 2)) * kOps + i;                                              \
-          const bool isA = o < 3 || o >= 9;                                                         \
-          const int k = o < 3 ? o : (o < 9 ? o - 3 : 0);   /* 256-byte piece = 2 blocks of 128 */  \
-          const int b = min((isA ? mb0 : is_nb0) + 2 * k + (lane >> 5), (isA ? g.MB : g.NB) - 1);   \
-          src[i] = reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw) + (size_t)b * 128 + (lane & 31) * 4; \
-          srow[i] = (isA ? g.MB : g.NB) * 128;                                                      \
-        }                                                                                           \
+      const int mb0 = tmi.tm * kMB, nb0 = tmi.tn * kNBt;                                            \
+      _Pragma("unroll") for (int k = 0; k < 5; ++k) {                                               \
+        const int it = frag0 + k;                          /* fragment item 0..35 */               \
+        const bool isA = it < 2 * kMB;                                                              \
+        const int blk = isA ? (it >> 1) : ((it - 2 * kMB) >> 1);                                     \
+        const size_t b = (size_t)min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);             \
+        src[k] = (isA ? a.qx : a.qw) + (b * g.KS + (it & 1)) * 1024 + lane * 16;                    \
+        src[5 + k] = reinterpret_cast<const uint8_t*>(isA ? a.z : a.l2t) + (b * per_l + (it & 1)) * 1024 + lane * 16; \
+      }                                                                                             \
+      {                                                                                             \
+        const bool isA = sop == 0;                                                                  \
+        const int blk = (sop == 2 ? 8 : 0) + (lane >> 3);                                           \
+        const int b = min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);                        \
+        ssrc = reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw) + (size_t)b * 128 + (lane & 7) * 16; \
+        sstride = (isA ? g.MB : g.NB) * 128;                                                        \
+        bsrc = reinterpret_cast<const uint8_t*>(a.bias + min(nb0 * 32 + 8 * lane, g.N - 8));        \
       }                                                                                             \
     }                                                                                               \
     uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
     const bool lrs = is_s >= g.nst;                                                                 \
     const int sl = lrs ? is_s - g.nst : is_s;                                                       \
-    if (blockw) {                                                                                   \
-      if (lrs && a.r32 == 0) {                                                                      \
-        _Pragma("unroll") for (int i = 0; i < kOps; ++i) issue_bias(a, g, is_nb0, 0, lane, slot_w); \
-      } else {                                                                                      \
-        uint8_t* dst = slot_w + (sidea ? kCodeA + 6 * wave * 1024 : kCodeB + 6 * (wave - 2) * 1024); \
-        _Pragma("unroll") for (int i = 0; i < kOps; ++i)                                            \
-          __builtin_amdgcn_global_load_lds(src[(lrs ? 3 : 0) + i / 2] + (size_t)(2 * sl + (i & 1)) * 1024, \
-                                           lds_ptr(dst + i * 1024), 16, 0, 0);                      \
-      }                                                                                             \
-    } else if (lrs) {                                                                               \
-      _Pragma("unroll") for (int i = 0; i < kOps; ++i) {                                            \
-        const int o = (wave - (kNW - 2)) * kOps + i;                                                \
-        issue_bias(a, g, is_nb0, o < 3 ? o : 0, lane, slot_w);                                      \
-      }                                                                                             \
+    if (lrs && a.r32 == 0) {                                                                        \
+      /* no low-rank fragments: every transfer of the stage moves the bias */                      \
+      _Pragma("unroll") for (int k = 0; k < 6; ++k)                                                 \
+        if (k < nops && lane < 48) __builtin_amdgcn_global_load_lds(bsrc, lds_ptr(slot_w + kScA), 16, 0, 0); \
     } else {                                                                                        \
-      _Pragma("unroll") for (int i = 0; i < kOps; ++i) {                                            \
-        const int o = (wave - (kNW - 2)) * kOps + i;                                                \
-        const int k = o < 3 ? o : (o < 9 ? o - 3 : 0);                                              \
-        const bool isA = o < 3 || o >= 9;                                                           \
-        __builtin_amdgcn_global_load_lds(src[i] + (size_t)sl * srow[i],                             \
-                                         lds_ptr(slot_w + (isA ? kScA : kScB) + 256 * k), 4, 0, 0); \
+      _Pragma("unroll") for (int k = 0; k < 5; ++k) {                                               \
+        if (k < nfrag) {                                                                            \
+          const int it = frag0 + k;                                                                 \
+          const int dst = it < 2 * kMB ? kCodeA + it * 1024 : kCodeB + (it - 2 * kMB) * 1024;       \
+          __builtin_amdgcn_global_load_lds(src[(lrs ? 5 : 0) + k] + (size_t)sl * 2048, lds_ptr(slot_w + dst), 16, 0, 0); \
+        }                                                                                           \
+      }                                                                                             \
+      if (sop >= 0 && lane < (lrs ? 48 : slanes)) {                                                 \
+        if (lrs)                                                                                    \
+          __builtin_amdgcn_global_load_lds(bsrc, lds_ptr(slot_w + kScA), 16, 0, 0);                 \
+        else                                                                                        \
+          __builtin_amdgcn_global_load_lds(ssrc + (size_t)sl * sstride,                             \
+                                           lds_ptr(slot_w + (sop == 0 ? kScA : kScB + (sop == 2 ? 1024 : 0))), 16, 0, 0); \
       }                                                                                             \
     }                                                                                               \
     if (++is_s == g.nstt) {                                                                         \
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   // flight.
 #define SVDQ_STEP(LOWRANK, LAST, DO_MFMA)                                                           \
   {                                                                                                 \
-    ring_barrier(kOps * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));         \
+    ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));         \
     if (stores_due > 0) --stores_due;                                                               \
     if (pending) {                                                                                  \
       SVDQ_MFMA(LOWRANK, 1, f1a, f1b, pa, pb)                                                       \
