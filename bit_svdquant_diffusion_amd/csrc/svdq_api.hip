@@ -33,7 +33,8 @@ svdq_status check_device(int* cus = nullptr) {
   if (s == 0) {
     hipDeviceProp_t p;
     bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
-              std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess;
+              std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess &&
+              prepare_gemm_int4() == hipSuccess;
     s = ok ? 1 : 2;
     if (ok) g_dev_cus[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
     g_dev_state[dev].store(s, std::memory_order_release);
@@ -182,7 +183,8 @@ svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_pack
   if (ws_bytes < ws_layout(d, M).total) return SVDQ_ERR_WORKSPACE;
   if (m0 < 0 || mc <= 0 || m0 + mc > M || n0 < 0 || nc <= 0 || n0 + nc > d->N)
     return SVDQ_ERR_SHAPE;
-  st = check_device();
+  int cus = 0;
+  st = check_device(&cus);
   if (st != SVDQ_OK) return st;
   GemmArgs a = gemm_args(d, dev, M, ws, nullptr);
   a.p = p;
@@ -191,7 +193,7 @@ svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_pack
   a.n0 = (int)n0;
   a.nc = (int)nc;
   hipStream_t s = (hipStream_t)stream;
-  return after_launch(launch_gemm(a, 0, s), s);
+  return after_launch(launch_gemm(a, cus, s), s);
 }
 
 }  // extern "C"

@@ -1,189 +1,381 @@
 // Kernel (2) of the forward for INT4 layers: Q4(X_hat) Q4(R)^T with per-group
-// dequantization, plus the epilogue that adds (X_hat L1) L2 and the bias
-// before the single bf16 write of Y (aiflownews.com, "What SVDQuant actually
-// does": the two-branch computation; "Nunchaku: the inference engine...": the
-// branches share the output write).
+// dequantization, plus the low-rank up-projection (X_hat L1) L2 and the bias,
+// added before the single bf16 write of Y (aiflownews.com, "What SVDQuant
+// actually does": the two-branch computation; "Nunchaku: the inference
+// engine...": the branches share the output write).
 //
-// Nibbles are widened in registers to int8 holding 16*q ((w<<4)&0xF0F0F0F0 for
-// even channels, w&0xF0F0F0F0 for odd ones); one v_mfma_i32_16x16x64_i8 per
-// 64-channel group gives 256*P exactly in int32; the group is dequantized as
-// acc += float(256 P) * (s_x s_w / 256). Operands are staged through LDS in
-// K-stages of 128 channels (two groups), double buffered.
+// Integer part. Codes are stored in the same fragment order as the MXFP4
+// path: one 1 KiB block per 32 rows and 64-channel group, lane 32h + r holding
+// the 32 channels 32h + [0, 32) of row r. Widened in registers to int8 as
+// 16*q ((w << 4) & 0xF0F0F0F0 for the even channels, w & 0xF0F0F0F0 for the
+// odd ones), one group of a 32 x 32 block is two v_mfma_i32_32x32x32_i8 (even
+// channels, then odd channels into the same accumulator), giving 256 * P
+// exactly in int32.
+//
+// Dequantization. The per-output scale s_w[n] * s_x[m] / 256 of the group is
+// an outer product, so it comes from the matrix unit as well: one
+// v_mfma_f32_32x32x2_f32 with the block's 32 weight scales and 32 activation
+// scales in the first K slot and zeros in the second. That leaves two vector
+// instructions per output and group, acc += float(256 P) * s, in fp32.
+//
+// Data path and schedule follow the MXFP4 kernel: persistent workgroups (one
+// per CU) walk 128 x 256 tiles; direct global->LDS transfers of 16 bytes per
+// lane fill a ring of LDS slots across tile boundaries; eight waves, 2 (M) x
+// 4 (N), each own 64 x 64 (2 x 2 blocks of 32 x 32); one workgroup barrier
+// per 128-channel stage (two groups). The low-rank branch is r32/32 more
+// stages on v_mfma_f32_32x32x16_bf16 into the same accumulators.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
 
 namespace svdq {
 
-// ------------------------------------------------------------------------------------
-// INT4: 128 x 128 tile, 4 waves of 64 x 64, one 16x16x64 i8 MFMA per block and group.
-// ------------------------------------------------------------------------------------
-template <bool DEBUG_P>
-__global__ __launch_bounds__(256) void gemm_int4_kernel(GemmArgs a, int tiles_m, int tiles_n,
-                                                        int tm_off, int tn_off) {
-  constexpr int BM = 128, BN = 128, WM = 64, WN = 64, TM = 4, TN = 4, LA = 2, LB = 2;
-  constexpr int STAGE = (BM + BN) * G_PITCH;
-  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+namespace {
+constexpr int kBM = 128, kBN = 256, kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
+constexpr int kWM = kBM / kWGM, kWN = kBN / kWGN, kTM = kWM / 32, kTN = kWN / 32;
+constexpr int kMB = kBM / 32, kNBt = kBN / 32;     // 32-row blocks per tile: 4 (A), 8 (B)
+constexpr int kNStage = 4;
+constexpr int kGroupM = 8;
+constexpr int kStores = 2 * kTN * kTM;             // 16-byte Y stores per wave per tile
+// Transfers per stage: 24 fragment blocks of 1 KiB (3 per wave, from 3 w)
+// and 3 scale transfers of 1 KiB (A, then two of B) on waves 1, 2 and 3, or,
+// in low-rank stages, copies of the bias transfer. Each SIMD (waves w and
+// w + 4) issues 6 or 7 transfers per stage.
+constexpr int kFragPerWave = 3;
+__host__ __device__ constexpr int kScaleOp(int w) { return (w >= 1 && w <= 3) ? w - 1 : -1; }
+__host__ __device__ constexpr int kOpsOf(int w) { return kFragPerWave + (kScaleOp(w) >= 0 ? 1 : 0); }
+// one ring slot: A codes (4 blocks x 2 groups x 1 KiB), B codes (8 x 2 x 1 KiB),
+// A scales fp32 [2 groups][128], B scales fp32 [2 groups][256]
+constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 1024;
+constexpr int kScB = kScA + 2 * kBM * 4, kSlot = kScB + 2 * kBN * 4;
+constexpr size_t kLds = (size_t)kNStage * kSlot;
+static_assert(kTM == 2 && kTN == 2, "schedule below assumes 2 x 2 blocks per wave");
+static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
+static_assert(kNW * kFragPerWave == 2 * (kMB + kNBt), "fragment blocks partition");
+static_assert(2 * kBM * 4 == 1024 && 2 * kBN * 4 == 2048 && kBN * 2 <= 1024,
+              "one A and two B scale transfers of 64 lanes; the bias fits the A scale area");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  TileMap tmap;
-  if (DEBUG_P) {
-    tmap.tm = tm_off + blockIdx.x % tiles_m;
-    tmap.tn = tn_off + blockIdx.x / tiles_m;
-  } else {
-    tmap = map_tile(blockIdx.x, tiles_m, tiles_n, 8);
+// Ring barrier: wait until at most n of this wave's vector-memory operations
+// are outstanding and its LDS reads have returned, then s_barrier (the same
+// rule as the MXFP4 kernel: operations retire in issue order, so n = the
+// number issued after the transfer being waited for).
+#define SVDQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)   /* expcnt 7, lgkmcnt 0 */
+__device__ __forceinline__ void ring_barrier(int n) {
+  __builtin_amdgcn_sched_barrier(0);
+  switch (n) {
+    case 3: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(4)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(6)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(8)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(12)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(14)); break;
+    case 16: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(16)); break;
+    default: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
   }
-  const int m0 = tmap.tm * BM, n0 = tmap.tn * BN;
-  const int M = a.M, N = a.N, K = a.K;
-  const int KB = K / 2, nst = K / 128, G = K / 64;
-  const int Mp = (M + 15) / 16 * 16;
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
-  const int lrow = tid >> 2, lchk = tid & 3;
-  const uint8_t* ga[LA];
-  const uint8_t* gb[LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) ga[i] = a.qx + (size_t)min(m0 + lrow + 64 * i, M - 1) * KB + lchk * 16;
-#pragma unroll
-  for (int i = 0; i < LB; ++i) gb[i] = a.qw + (size_t)min(n0 + lrow + 64 * i, N - 1) * KB + lchk * 16;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
 
-  const int q = lane >> 4, c16 = lane & 15;   // 16x16 layout: rows 4q+i, col c16
-  const float* sxp[TM];
-  const float* swp[TN];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    int row4 = min(m0 + wm * WM + t * 16 + 4 * q, Mp - 4);
-    sxp[t] = reinterpret_cast<const float*>(a.sx) + row4;
-  }
-#pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    int col = min(n0 + wn * WN + t * 16 + c16, N - 1);
-    swp[t] = reinterpret_cast<const float*>(a.sw) + col;
-  }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+  return *reinterpret_cast<uint32_t*>(&v);
+}
 
-  f32x4 acc[TM][TN];
+// int8 operands of one 32-channel half of a group: 16*q of the even channels
+// (lo) and of the odd channels (hi) of a 16-byte fragment
+__device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{};
-
-  u32x4 ra[LA], rb[LB];
-  auto gload = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + st * 64);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + st * 64);
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* base = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      *reinterpret_cast<u32x4*>(base + (lrow + 64 * i) * G_PITCH + lchk * 16) = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      *reinterpret_cast<u32x4*>(base + (BM + lrow + 64 * i) * G_PITCH + lchk * 16) = rb[i];
-  };
-  auto widen = [](u32x2 w) {
-    return i32x4{(int)((w.x << 4) & 0xF0F0F0F0u), (int)(w.x & 0xF0F0F0F0u),
-                 (int)((w.y << 4) & 0xF0F0F0F0u), (int)(w.y & 0xF0F0F0F0u)};
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) gload(st + 1);
-    const uint8_t* base = smem + buf * STAGE;
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int g = 2 * st + gg;
-      i32x4 fa[TM], fb[TN];
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-        fa[t] = widen(*reinterpret_cast<const u32x2*>(base + (wm * WM + t * 16 + c16) * G_PITCH + gg * 32 + q * 8));
-#pragma unroll
-      for (int t = 0; t < TN; ++t)
-        fb[t] = widen(*reinterpret_cast<const u32x2*>(base + (BM + wn * WN + t * 16 + c16) * G_PITCH + gg * 32 + q * 8));
-      f32x4 sxv[TM];
-      float swv[TN];
-      if (!DEBUG_P) {
-#pragma unroll
-        for (int t = 0; t < TM; ++t) sxv[t] = *reinterpret_cast<const f32x4*>(sxp[t] + (size_t)g * Mp);
-#pragma unroll
-        for (int t = 0; t < TN; ++t) swv[t] = swp[t][(size_t)g * N] * (1.0f / 256.0f);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          i32x4 p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], i32x4{}, 0, 0, 0);
-          if (DEBUG_P) {
-            const int col = n0 + wn * WN + j * 16 + c16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = m0 + wm * WM + i * 16 + 4 * q + e;
-              if (row >= a.m0 && row < a.m0 + a.mc && col >= a.n0 && col < a.n0 + a.nc && row < M)
-                a.p[((size_t)(row - a.m0) * a.nc + (col - a.n0)) * G + g] = p[e] / 256;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] += (float)p[e] * (sxv[i][e] * swv[j]);
-          }
-        }
-    }
-    if (st + 1 < nst) lstore(buf ^ 1);
-    __syncthreads();
-  }
-  if (DEBUG_P) return;
-
-  if (a.r32 > 0) {
-    for (int c = 0; c < a.r32 / 32; ++c) {
-      bf16x8 za[TM], lb[TN];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        int row = min(m0 + wm * WM + t * 16 + c16, M - 1);
-        uint4 v = *reinterpret_cast<const uint4*>(a.z + (size_t)row * a.r32 + 32 * c + 8 * q);
-        za[t] = *reinterpret_cast<bf16x8*>(&v);
-      }
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        int col = min(n0 + wn * WN + t * 16 + c16, N - 1);
-        uint4 v = *reinterpret_cast<const uint4*>(a.l2t + (size_t)col * a.r32 + 32 * c + 8 * q);
-        lb[t] = *reinterpret_cast<bf16x8*>(&v);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za[i], lb[j], acc[i][j], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WN + j * 16 + c16;
-    if (col >= N) continue;
-    const float bv = __uint_as_float((uint32_t)a.bias[col] << 16);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * WM + i * 16 + 4 * q + e;
-        if (row < M) a.y[(size_t)row * N + col] = (uint16_t)f2bf(acc[i][j][e] + bv);
-      }
+  for (int d = 0; d < 4; ++d) {
+    lo[d] = (int)(((uint32_t)w[d] << 4) & 0xF0F0F0F0u);
+    hi[d] = (int)((uint32_t)w[d] & 0xF0F0F0F0u);
   }
 }
 
-hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
+struct Geo {
+  int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;
+  int tm_off, tn_off;   // group-sum hook: the window's first tile
+};
+}  // namespace
+
+// DEBUG_P: instead of dequantizing, write every group sum P (exact int32) of
+// the outputs inside the window [m0, m0 + mc) x [n0, n0 + nc) to p, over the
+// window's tiles only, with the same transfers, widening and MFMAs.
+template <bool DEBUG_P>
+__global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, int grid) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWGN, wn = wave % kWGN;
+  const int h = lane >> 5, lr = lane & 31;
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / grid + 1 : 0;
+  const int total = my_tiles * g.nstt;   // ring steps of this workgroup
+  auto tile_of = [&](int t) -> TileMap {
+    if (DEBUG_P) return TileMap{g.tm_off + t % g.tiles_m, g.tn_off + t / g.tiles_m};
+    return map_tile(t, g.tiles_m, g.tiles_n, kGroupM);
+  };
+
+  // issue side: next ring step to load (tile-local index is_s of tile is_t)
+  // and this wave's per-tile transfer sources as byte offsets from uniform
+  // bases: fragment item 3 w + k from src[k] (4-bit) and src[3 + k]
+  // (low-rank); the scale transfer from ssrc plus the stage times sstride;
+  // the bias from bsrc
+  const int frag0 = kFragPerWave * wave, sop = kScaleOp(wave);
+  const int nops = kOpsOf(wave);
+  int is_t = 0, is_s = 0;
+  uint32_t src[2 * kFragPerWave], ssrc = 0, bsrc = 0, sstride = 0;
+  const int per_l = a.r32 / 16;
+  const uint8_t* const sx_b = reinterpret_cast<const uint8_t*>(a.sx);
+  const uint8_t* const sw_b = reinterpret_cast<const uint8_t*>(a.sw);
+  const uint8_t* const z_b = reinterpret_cast<const uint8_t*>(a.z);
+  const uint8_t* const l2_b = reinterpret_cast<const uint8_t*>(a.l2t);
+  const uint8_t* const bias_b = reinterpret_cast<const uint8_t*>(a.bias);
+#define SVDQ_ISSUE(GS)                                                                              \
+  {                                                                                                 \
+    if (is_s == 0) {                                                                                \
+      const TileMap tmi = tile_of((int)blockIdx.x + is_t * grid);                                   \
+      const int mb0 = tmi.tm * kMB, nb0 = tmi.tn * kNBt;                                            \
+      _Pragma("unroll") for (int k = 0; k < kFragPerWave; ++k) {                                    \
+        const int it = frag0 + k;                          /* fragment item 0..23 */               \
+        const bool isA = it < 2 * kMB;                                                              \
+        const int blk = isA ? (it >> 1) : ((it - 2 * kMB) >> 1);                                     \
+        const uint32_t b = (uint32_t)min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);         \
+        src[k] = (b * g.KS + (it & 1)) * 1024 + lane * 16;                                          \
+        src[kFragPerWave + k] = (b * per_l + (it & 1)) * 1024 + lane * 16;                          \
+      }                                                                                             \
+      if (sop >= 0) {                                                                               \
+        /* entry e = 4 lane (+ 256 for the second B transfer) of [2 groups][T] */                  \
+        const bool isA = sop == 0;                                                                  \
+        const int T = isA ? kBM : kBN;                                                              \
+        const int e = (sop == 2 ? 256 : 0) + 4 * lane;                                              \
+        const int gg = e >= T ? 1 : 0, idx = e - gg * T;                                            \
+        const int lim = isA ? g.act_rows : g.N;                                                     \
+        const int row = min((isA ? mb0 : nb0) * 32 + idx, lim - 4);                                 \
+        ssrc = (uint32_t)(gg * lim + row) * 4;                                                      \
+        sstride = (uint32_t)(2 * lim * 4);                                                          \
+      }                                                                                             \
+      bsrc = (uint32_t)min(nb0 * 32 + 8 * lane, g.N - 8) * 2;                                       \
+    }                                                                                               \
+    uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
+    const bool lrs = is_s >= g.nst;                                                                 \
+    const int sl = lrs ? is_s - g.nst : is_s;                                                       \
+    if (lrs && a.r32 == 0) {                                                                        \
+      /* no low-rank fragments: every transfer of the stage moves the bias */                      \
+      _Pragma("unroll") for (int k = 0; k < kFragPerWave + 1; ++k)                                  \
+        if (k < nops && lane < 32) __builtin_amdgcn_global_load_lds(bias_b + bsrc, lds_ptr(slot_w + kScA), 16, 0, 0); \
+    } else {                                                                                        \
+      _Pragma("unroll") for (int k = 0; k < kFragPerWave; ++k) {                                    \
+        const int it = frag0 + k;                                                                   \
+        const bool isA = it < 2 * kMB;                                                              \
+        const int dst = isA ? kCodeA + it * 1024 : kCodeB + (it - 2 * kMB) * 1024;                  \
+        const uint8_t* base = lrs ? (isA ? z_b : l2_b) : (isA ? a.qx : a.qw);                       \
+        __builtin_amdgcn_global_load_lds(base + (src[(lrs ? kFragPerWave : 0) + k] + (uint32_t)sl * 2048), \
+                                         lds_ptr(slot_w + dst), 16, 0, 0);                          \
+      }                                                                                             \
+      if (sop >= 0) {                                                                               \
+        if (lrs) {                                                                                  \
+          if (lane < 32) __builtin_amdgcn_global_load_lds(bias_b + bsrc, lds_ptr(slot_w + kScA), 16, 0, 0); \
+        } else {                                                                                    \
+          __builtin_amdgcn_global_load_lds((sop == 0 ? sx_b : sw_b) + (ssrc + (uint32_t)sl * sstride), \
+                                           lds_ptr(slot_w + (sop == 0 ? kScA : kScB + 1024 * (sop - 1))), 16, 0, 0); \
+        }                                                                                           \
+      }                                                                                             \
+    }                                                                                               \
+    if (++is_s == g.nstt) {                                                                         \
+      is_s = 0;                                                                                     \
+      ++is_t;                                                                                       \
+    }                                                                                               \
+  }
+
+  f32x16 acc[kTN][kTM];
+
+  // one 64-channel group gg of the stage in `slot`: per block, two i8 MFMAs
+  // for 256 P, one fp32 MFMA for the scale outer product, then the fp32
+  // dequant (or, DEBUG_P, the group-sum writes)
+  auto group = [&](const uint8_t* slot, int gg, int gidx, int m0t, int n0t) {
+    i32x4 alo[kTM], ahi[kTM], blo[kTN], bhi[kTN];
+    float sxv[kTM], swv[kTN];
+#pragma unroll
+    for (int t = 0; t < kTM; ++t) {
+      widen(*reinterpret_cast<const i32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + gg) * 1024 + lane * 16),
+            alo[t], ahi[t]);
+      // K slot 0 (lanes 0-31): token 32 t + lr's scale / 256; K slot 1: zero
+      const float v = *reinterpret_cast<const float*>(slot + kScA + gg * (kBM * 4) + (wm * kWM + 32 * t + lr) * 4);
+      sxv[t] = h ? 0.0f : v * (1.0f / 256.0f);
+    }
+#pragma unroll
+    for (int t = 0; t < kTN; ++t) {
+      widen(*reinterpret_cast<const i32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + gg) * 1024 + lane * 16),
+            blo[t], bhi[t]);
+      const float v = *reinterpret_cast<const float*>(slot + kScB + gg * (kBN * 4) + (wn * kWN + 32 * t + lr) * 4);
+      swv[t] = h ? 0.0f : v;
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo[j], alo[i], i32x16{}, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi[j], ahi[i], p, 0, 0, 0);
+        if constexpr (DEBUG_P) {
+          const int tok = m0t + wm * kWM + 32 * i + lr;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int ch = n0t + wn * kWN + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (tok >= a.m0 && tok < a.m0 + a.mc && ch >= a.n0 && ch < a.n0 + a.nc)
+              a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (g.K / 64) + gidx] = p[e] / 256;
+          }
+        } else {
+          const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x2f32(swv[j], sxv[i], f32x16{}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][i][e] = __builtin_fmaf((float)p[e], sc[e], acc[j][i][e]);
+        }
+      }
+    }
+  };
+
+  int gs = 0, stores_due = 0;
+  const int nlr = g.nstt - g.nst;
+  // prologue: the first kNStage - 1 ring steps in flight
+  for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
+  for (int ct = 0; ct < my_tiles; ++ct) {
+    const TileMap tmc = tile_of((int)blockIdx.x + ct * grid);
+    const int m0t = tmc.tm * kBM, n0t = tmc.tn * kBN;
+    const int n0 = n0t + wn * kWN;
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
+    for (int st = 0; st < g.nst; ++st) {
+      ring_barrier(DEBUG_P ? 0 : nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
+      if (stores_due > 0) --stores_due;
+      const bool more = gs + kNStage - 1 < total;
+      if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)
+      const uint8_t* slot = smem + (gs % kNStage) * kSlot;
+      group(slot, 0, 2 * st, m0t, n0t);
+      if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)
+      group(slot, 1, 2 * st + 1, m0t, n0t);
+      ++gs;
+    }
+    if constexpr (DEBUG_P) continue;
+    for (int l = 0; l < nlr; ++l) {
+      ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
+      if (stores_due > 0) --stores_due;
+      const bool more = gs + kNStage - 1 < total;
+      if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)
+      const uint8_t* slot = smem + (gs % kNStage) * kSlot;
+      if (a.r32 > 0) {
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+          i32x4 fa[kTM], fb[kTN];
+#pragma unroll
+          for (int t = 0; t < kTM; ++t)
+            fa[t] = *reinterpret_cast<const i32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + step) * 1024 + lane * 16);
+#pragma unroll
+          for (int t = 0; t < kTN; ++t)
+            fb[t] = *reinterpret_cast<const i32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + step) * 1024 + lane * 16);
+#pragma unroll
+          for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[j]),
+                                                                  __builtin_bit_cast(bf16x8, fa[i]), acc[j][i], 0, 0, 0);
+        }
+      }
+      if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)
+      ++gs;
+    }
+
+    // + bias (from the last low-rank slot), bf16 write: the MXFP4 kernel's
+    // epilogue. Lane h of the accumulator holds channels 32 j + 8 q + 4 h +
+    // (0..3) of token m0 + 32 i + lr; after swapping the packed pairs (q = 1,
+    // h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <-> (q = 2, h = 1), each
+    // lane stores two 16-byte runs of one row.
+    const uint8_t* bslot = smem + ((gs - 1) % kNStage) * kSlot + kScA + wn * kWN * 2;
+    const int ynrec = min(g.M - m0t, kBM) * g.N * 2;
+    const __amdgpu_buffer_rsrc_t yrs =
+        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0t * g.N, 0, ynrec, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      float bv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 bw = *reinterpret_cast<const u32x2*>(bslot + (32 * j + 8 * q + 4 * h) * 2);
+        bv[4 * q + 0] = bf16lo(bw.x);
+        bv[4 * q + 1] = bf16hi(bw.x);
+        bv[4 * q + 2] = bf16lo(bw.y);
+        bv[4 * q + 3] = bf16hi(bw.y);
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        uint32_t o[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          o[p] = cvt_bf16x2(acc[j][i][2 * p] + bv[2 * p], acc[j][i][2 * p + 1] + bv[2 * p + 1]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
+            o[4 * p + w] = r[0];
+            o[4 * p + 2 + w] = r[1];
+          }
+        }
+        // always issued (the ring waits count them); the resource drops rows
+        // past M and a block past N is sent past the end
+        const int col = n0 + 32 * j + 8 * h;
+        const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
+      }
+    }
+    stores_due = kNStage - 1;
+  }
+#undef SVDQ_ISSUE
+}
+
+hipError_t prepare_gemm_int4() {
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_int4_kernel<false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_int4_kernel<true>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+}
+
+hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
+  Geo g;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = a.K;
+  g.MB = (a.M + 31) / 32;
+  g.NB = a.N / 32;
+  g.KS = a.K / 64;
+  g.nst = a.K / 128;
+  g.act_rows = (a.M + 15) / 16 * 16;
+  g.tm_off = g.tn_off = 0;
+  int grid = num_cus > 0 ? num_cus : 256;
   if (a.p) {
-    const int tm0 = a.m0 / BM, tm1 = (a.m0 + a.mc + BM - 1) / BM;
-    const int tn0 = a.n0 / BN, tn1 = (a.n0 + a.nc + BN - 1) / BN;
-    const int tm = tm1 - tm0, tn = tn1 - tn0;
-    hipLaunchKernelGGL((gemm_int4_kernel<true>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn, tm0, tn0);
+    // group-sum hook: only the tiles that hold the window, no low-rank stages
+    g.nstt = g.nst;
+    g.tm_off = a.m0 / kBM;
+    g.tn_off = a.n0 / kBN;
+    g.tiles_m = (a.m0 + a.mc + kBM - 1) / kBM - g.tm_off;
+    g.tiles_n = (a.n0 + a.nc + kBN - 1) / kBN - g.tn_off;
+    const int ntiles = g.tiles_m * g.tiles_n;
+    if (grid > ntiles) grid = ntiles;
+    hipLaunchKernelGGL(gemm_int4_kernel<true>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
     return hipGetLastError();
   }
-  const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_int4_kernel<false>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn, 0, 0);
+  const int nlr = a.r32 > 0 ? a.r32 / 32 : 1;   // at least one: the bias rides in a low-rank stage
+  g.nstt = g.nst + nlr;
+  g.tiles_m = (a.M + kBM - 1) / kBM;
+  g.tiles_n = (a.N + kBN - 1) / kBN;
+  const int ntiles = g.tiles_m * g.tiles_n;
+  if (grid > ntiles) grid = ntiles;
+  hipLaunchKernelGGL(gemm_int4_kernel<false>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
   return hipGetLastError();
 }
 

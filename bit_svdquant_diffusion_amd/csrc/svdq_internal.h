@@ -12,9 +12,9 @@ struct Stage1Args {
   const uint16_t* x;    // bf16 [M][K]
   const float* mu;      // [K]
   const uint16_t* l1s;  // L1 in stage-1 MFMA order
-  // activation codes, scales and Z = X_hat L1: INT4 qx [M][K/2], sx fp32
-  // [K/64][Mp], z bf16 [M][r32]; MXFP4 in fragment order over round32(M) rows,
-  // the same layouts as the weight's qw, sw and l2
+  // activation codes, scales and Z = X_hat L1 over round32(M) rows: codes
+  // and Z in fragment order (the layouts of the weight's qw and l2); scales
+  // fp32 [K/64][round16(M)] (INT4) or E8M0 bytes in fragment order (MXFP4)
   uint8_t* qx;
   void* sx;
   uint16_t* z;
@@ -33,17 +33,20 @@ struct GemmArgs {
   const uint16_t* l2t;
   const uint16_t* bias;  // bf16 [N]
   uint16_t* y;           // bf16 [M][N]
-  // group-sum test hook (INT4): window and output, p == nullptr for the normal epilogue
+  // group-sum test hook (INT4): window and output [mc][nc][K/64], p ==
+  // nullptr for the normal epilogue
   int32_t* p;
   int m0, mc, n0, nc;
 };
-hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st);
-hipError_t prepare_gemm_mxfp4();   // one-time per device: kernel LDS attribute
+// one-time per device: the kernels' dynamic LDS attribute
+hipError_t prepare_gemm_int4();
+hipError_t prepare_gemm_mxfp4();
 
 inline hipError_t launch_gemm(const GemmArgs& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  return a.fmt == SVDQ_FMT_MXFP4_G32 ? launch_gemm_mxfp4(a, num_cus, st) : launch_gemm_int4(a, st);
+  return a.fmt == SVDQ_FMT_MXFP4_G32 ? launch_gemm_mxfp4(a, num_cus, st) : launch_gemm_int4(a, num_cus, st);
 }
 
 }  // namespace svdq

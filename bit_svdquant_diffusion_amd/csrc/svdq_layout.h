@@ -47,16 +47,16 @@ inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
   return s;
 }
 
-// Workspace: [qX][sX][Z: M x rank32 bf16], each 256-byte aligned. INT4: qX
-// row-major [M][K/2], sX fp32 [K/64][act_rows(M)]. MXFP4: qX and sX in
-// fragment order over round32(M) rows (see below).
+// Workspace: [qX][sX][Z], each 256-byte aligned, over round32(M) rows. qX and
+// Z in fragment order (see below) for both formats; sX fp32 [K/64][act_rows(M)]
+// (INT4) or E8M0 bytes in fragment order (MXFP4).
 struct WsLayout {
   size_t qx, sx, z, total;
 };
 inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   WsLayout w;
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
-  const int64_t rows = int4 ? M : round32(M);
+  const int64_t rows = round32(M);
   w.qx = 0;
   w.sx = align256((size_t)rows * d->K / 2);
   w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
@@ -64,17 +64,18 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   return w;
 }
 
-// Fragment order of MXFP4 codes: rows in blocks of 32, K in steps of 64; each
-// (block, step) is 1 KiB = 64 lanes x 16 bytes, lane l = 32h + r holding row
-// 32*block + r, channels 64*step + 32h + [0, 32) (even channel in the low
-// nibble). One (block, step) is exactly one MFMA operand of one wave.
+// Fragment order of 4-bit codes (both formats): rows in blocks of 32, K in
+// steps of 64; each (block, step) is 1 KiB = 64 lanes x 16 bytes, lane
+// l = 32h + r holding row 32*block + r, channels 64*step + 32h + [0, 32) (even
+// channel in the low nibble). One (block, step) is one MXFP4 MFMA operand of
+// one wave, or one INT4 group of 32 rows (two i8 MFMA operands once widened).
 inline size_t f_code_byte(int K, int64_t row, int k) {
   const int64_t b = row / 32;
   const int r = (int)(row % 32), S = k / 64, h = (k % 64) / 32, j = k % 32;
   return (((size_t)b * (K / 64) + S) * 64 + (32 * h + r)) * 16 + j / 2;
 }
-// Fragment order of a bf16 operand with rank32 columns (Z = X_hat L1 and L2^T
-// on the MXFP4 path): rows in blocks of 32, columns in steps of 16; each
+// Fragment order of a bf16 operand with rank32 columns (Z = X_hat L1 and
+// L2^T): rows in blocks of 32, columns in steps of 16; each
 // (block, step) is 1 KiB = 64 lanes x 8 bf16, lane l = 32h + r holding row
 // 32*block + r, columns 16*step + 8h + [0, 8). Returns an element index.
 inline size_t frag16_index(int r32, int64_t row, int col) {

@@ -326,10 +326,8 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
     std::memset(out->l2, 0, (size_t)N * r32 * 2);
     for (int k = 0; k < K; ++k)
       for (int c = 0; c < r; ++c) out->l1[l1_index(K, r32, k, c)] = l1b[(size_t)k * r + c];
-    const bool mx = d->format == SVDQ_FMT_MXFP4_G32;
     for (int i = 0; i < r; ++i)
-      for (int n = 0; n < N; ++n)
-        out->l2[mx ? frag16_index(r32, n, i) : (size_t)n * r32 + i] = l2b[(size_t)i * N + n];
+      for (int n = 0; n < N; ++n) out->l2[frag16_index(r32, n, i)] = l2b[(size_t)i * N + n];
   }
   for (int n = 0; n < N; ++n) {
     float b = bias ? bias[n] : 0.f;
@@ -356,14 +354,13 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
         }
         rrow[k] = (float)(what - acc);
       }
-      uint8_t* qrow = out->qw + (size_t)n * K / 2;
       for (int g = 0; g < G; ++g) {
         if (d->format == SVDQ_FMT_INT4_G64) {
           float s;
           quant_int4_group(&rrow[(size_t)g * gsz], gsz, q.data(), &s);
           sw_f[(size_t)g * N + n] = s;
           for (int j = 0; j < gsz; j += 2)
-            qrow[(g * gsz + j) / 2] = (uint8_t)((q[j] & 15) | ((q[j + 1] & 15) << 4));
+            out->qw[f_code_byte(K, n, g * gsz + j)] = (uint8_t)((q[j] & 15) | ((q[j + 1] & 15) << 4));
         } else {
           uint8_t sb;
           quant_mx_block(&rrow[(size_t)g * gsz], gsz, cq.data(), &sb);
@@ -481,7 +478,7 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
     if (!h->qw) return SVDQ_ERR_NULL;
     for (size_t n = 0; n < (size_t)N; ++n)
       for (int k = 0; k < K; ++k) {
-        uint8_t byte = int4 ? h->qw[n * K / 2 + k / 2] : h->qw[f_code_byte(K, n, k)];
+        uint8_t byte = h->qw[f_code_byte(K, n, k)];
         int nib = (k & 1) ? (byte >> 4) : (byte & 15);
         codes[n * K + k] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
       }
@@ -509,7 +506,7 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
     if (!h->l2) return SVDQ_ERR_NULL;
     for (int i = 0; i < r; ++i)
       for (int n = 0; n < N; ++n)
-        l2[(size_t)i * N + n] = h->l2[int4 ? (size_t)n * r32 + i : frag16_index(r32, n, i)];
+        l2[(size_t)i * N + n] = h->l2[frag16_index(r32, n, i)];
   }
   if (bias) {
     if (!h->bias) return SVDQ_ERR_NULL;
@@ -533,7 +530,7 @@ svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const voi
     const uint8_t* q = base + L.qx;
     for (int64_t m = 0; m < M; ++m)
       for (int k = 0; k < K; ++k) {
-        uint8_t byte = int4 ? q[(size_t)m * K / 2 + k / 2] : q[f_code_byte(K, m, k)];
+        uint8_t byte = q[f_code_byte(K, m, k)];
         int nib = (k & 1) ? (byte >> 4) : (byte & 15);
         codes[(size_t)m * K + k] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
       }
@@ -558,7 +555,7 @@ svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const voi
     for (int64_t m = 0; m < M; ++m)
       for (int i = 0; i < r; ++i)
         z[(size_t)m * r + i] =
-            (float)bf16_to_double(zb[int4 ? (size_t)m * r32 + i : frag16_index(r32, m, i)]);
+            (float)bf16_to_double(zb[frag16_index(r32, m, i)]);
   }
   return SVDQ_OK;
 }

@@ -234,7 +234,6 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
             }
           }
           if (row_ok && j == 0) reinterpret_cast<float*>(sx)[(size_t)(k0 / 64) * Mp + m] = sc;
-          if (row_ok) *reinterpret_cast<u32x2*>(qx + (size_t)m * (K / 2) + k0 / 2 + 8 * j) = u32x2{c0, c1};
         } else {
           const int e = mx_exponent(amax);       // block b = j / 2 of the quarter
           c0 = s1_e2m1x8(xh, e);
@@ -246,12 +245,12 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
             reinterpret_cast<uint8_t*>(sx)[(((size_t)(kb >> 2) * MB + m / 32) * 64 + 32 * (kb & 1) + m % 32) * 2 +
                                            ((kb >> 1) & 1)] = (uint8_t)(e + 127);
           }
-          if (row_ok) {
-            // fragment order: 64-channel step k0/64 of row block m/32; channels
-            // 32h .. 32h+31 at lane 32h + m%32, 16 channels = 8 bytes
-            uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + k0 / 64) * 1024;
-            *reinterpret_cast<u32x2*>(blk + (32 * (j >> 1) + m % 32) * 16 + (j & 1) * 8) = u32x2{c0, c1};
-          }
+        }
+        if (row_ok) {
+          // fragment order: 64-channel step k0/64 of row block m/32; channels
+          // 32h .. 32h+31 at lane 32h + m%32, 16 channels = 8 bytes
+          uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + k0 / 64) * 1024;
+          *reinterpret_cast<u32x2*>(blk + (32 * (j >> 1) + m % 32) * 16 + (j & 1) * 8) = u32x2{c0, c1};
         }
 
   }
@@ -278,14 +277,9 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
       const int l = idx & 63, e = (idx >> 6) & 3, c = idx >> 8;
       const int row = m0 + 4 * (l >> 4) + e;
       const int col = 16 * c + (l & 15);
-      if (row < M) {
-        if constexpr (FMT == SVDQ_FMT_INT4_G64) {
-          z[(size_t)row * r32 + col] = (uint16_t)f2bf(acc);
-        } else {   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
-          z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
-            col % 8] = (uint16_t)f2bf(acc);
-        }
-      }
+      if (row < M)   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
+        z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
+          col % 8] = (uint16_t)f2bf(acc);
     }
   }
 }

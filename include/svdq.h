@@ -95,18 +95,18 @@ typedef struct {
  *   mu   fp32 [K]                 runtime smoothing multiplier mu_k = fl32(1/lambda_k)
  *   l1   bf16                     L1 [K][rank], rank padded to 32, shuffled for the MFMA
  *   bias bf16 [N]
- * INT4 layers:
- *   l2   bf16 [N][rank32]         L2 transposed, rank padded to a multiple of 32 (zeros)
- *   qw   u8   [N][K/2]            codes, channel k in the low nibble when k is even
- *   sw   fp32 [K/64][N]           per-group scales (group-major)
- * MXFP4 layers, in MFMA fragment order (rows in blocks of 32; lane l = 32h + r
+ * Both formats, in MFMA fragment order (rows in blocks of 32; lane l = 32h + r
  * of a 64-lane fragment holds row 32b + r):
- *   qw   u8 [N/32][K/64][64][16]  lane 32h + r: E2M1 codes of channels
- *                                 64s + 32h + [0, 32), two per byte, low nibble first
- *   sw   u8 [K/128][N/32][64][2]  lane 32h + r of stage t: E8M0 bytes of the
- *                                 32-channel blocks 4t + h and 4t + 2 + h
- *   l2   bf16 [N/32][rank32/16][64][8]  L2 transposed; lane 32h + r of step c
- *                                 holds rank columns 16c + 8h + [0, 8)
+ *   qw   u8 [N/32][K/64][64][16]  lane 32h + r: 4-bit codes (INT4 two's
+ *                                 complement or E2M1) of channels 64s + 32h +
+ *                                 [0, 32), two per byte, low nibble first
+ *   l2   bf16 [N/32][rank32/16][64][8]  L2 transposed, rank padded to a multiple
+ *                                 of 32 (zeros); lane 32h + r of step c holds
+ *                                 rank columns 16c + 8h + [0, 8)
+ * Scales:
+ *   sw   INT4:  fp32 [K/64][N]    per-group scales (group-major)
+ *        MXFP4: u8 [K/128][N/32][64][2]  lane 32h + r of stage t: E8M0 bytes
+ *                                 of the 32-channel blocks 4t + h and 4t + 2 + h
  */
 typedef struct {
   float* mu;

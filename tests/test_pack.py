@@ -110,5 +110,7 @@ def test_device_layout_of_l1_matches_stage1_order():
         t, e = divmod(kk, 8)
         assert dev_l1[s, w, c // 16, t, 16 * j + c % 16, e] == l1[k, c]
     assert np.all(dev_l1[:, :, 3] == 0)   # columns 48..63 are padding
-    dev_l2 = host["l2"].view(np.uint16).reshape(N, 64)
-    assert np.array_equal(dev_l2[:, :r], l2.T) and np.all(dev_l2[:, r:] == 0)
+    # L2^T in 16-column fragment order: [N/32][r32/16][lane 32h + row%32][8]
+    dev_l2 = host["l2"].view(np.uint16).reshape(N // 32, 4, 2, 32, 8)
+    lin = dev_l2.transpose(0, 3, 1, 2, 4).reshape(N, 64)   # [n][16c + 8h + e]
+    assert np.array_equal(lin[:, :r], l2.T) and np.all(lin[:, r:] == 0)
