@@ -13,10 +13,9 @@
 // exactly in int32.
 //
 // Dequantization. The per-output scale s_w[n] * s_x[m] / 256 of the group is
-// an outer product, so it comes from the matrix unit as well: one
-// v_mfma_f32_32x32x2_f32 with the block's 32 weight scales and 32 activation
-// scales in the first K slot and zeros in the second. That leaves two vector
-// instructions per output and group, acc += float(256 P) * s, in fp32.
+// an outer product, so it comes from the matrix unit as well: one two-block
+// v_mfma_f32_32x32x1_2b_f32 gives it for two 32 x 32 blocks. That leaves two
+// vector instructions per output and group, acc += float(256 P) * s, in fp32.
 //
 // Data path and schedule follow the MXFP4 kernel: persistent workgroups (one
 // per CU) walk 128 x 256 tiles; direct global->LDS transfers of 16 bytes per
@@ -193,51 +192,110 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 
   f32x16 acc[kTN][kTM];
 
-  // one 64-channel group gg of the stage in `slot`: per block, two i8 MFMAs
-  // for 256 P, one fp32 MFMA for the scale outer product, then the fp32
-  // dequant (or, DEBUG_P, the group-sum writes)
-  auto group = [&](const uint8_t* slot, int gg, int gidx, int m0t, int n0t) {
-    i32x4 alo[kTM], ahi[kTM], blo[kTN], bhi[kTN];
-    float sxv[kTM], swv[kTN];
+  // The two groups of a stage are eight units u = (group u / 4, block
+  // j = (u / 2) % 2, i = u % 2). A unit is two i8 MFMAs for 256 P, one fp32
+  // MFMA for the scale outer product, and the dequant of its 16 outputs per
+  // lane (or, DEBUG_P, the group-sum writes). Units are software-pipelined
+  // within the wave: the MFMAs of unit u + 1 are issued before the vector
+  // work of unit u, so the matrix pipe and the vector ALU run side by side.
+  int gs = 0, stores_due = 0;   // ring step being computed; ring steps still to absorb Y stores
+  i32x4 alo[2][kTM], ahi[2][kTM], blo[2][kTN], bhi[2][kTN];
+  float sxv[2][kTM], swv[2][kTN];
+  i32x16 pp[2];
+  f32x16 sc[2][2];   // [block pair (u / 2) % 2][i]
+  auto mfma_unit = [&](int u) {
+    const int gg = u >> 2, j = (u >> 1) & 1, i = u & 1;
+    i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo[gg][j], alo[gg][i], i32x16{}, 0, 0, 0);
+    pp[u & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi[gg][j], ahi[gg][i], p, 0, 0, 0);
+    if (!DEBUG_P && i == 0) {
+      // scales of blocks (j, 0) and (j, 1) in one two-block outer product:
+      // block b = lane / 32 takes the 32 channel scales of block row j and
+      // the 32 token scales of block column i = b; output block b in
+      // registers 16 b .. 16 b + 15, each in the 32 x 32 accumulator layout
+      const f32x32 r = __builtin_amdgcn_mfma_f32_32x32x1f32(swv[gg][j], h ? sxv[gg][1] : sxv[gg][0], f32x32{}, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < kTM; ++t) {
-      widen(*reinterpret_cast<const i32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + gg) * 1024 + lane * 16),
-            alo[t], ahi[t]);
-      // K slot 0 (lanes 0-31): token 32 t + lr's scale / 256; K slot 1: zero
-      const float v = *reinterpret_cast<const float*>(slot + kScA + gg * (kBM * 4) + (wm * kWM + 32 * t + lr) * 4);
-      sxv[t] = h ? 0.0f : v * (1.0f / 256.0f);
-    }
-#pragma unroll
-    for (int t = 0; t < kTN; ++t) {
-      widen(*reinterpret_cast<const i32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + gg) * 1024 + lane * 16),
-            blo[t], bhi[t]);
-      const float v = *reinterpret_cast<const float*>(slot + kScB + gg * (kBN * 4) + (wn * kWN + 32 * t + lr) * 4);
-      swv[t] = h ? 0.0f : v;
-    }
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo[j], alo[i], i32x16{}, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi[j], ahi[i], p, 0, 0, 0);
-        if constexpr (DEBUG_P) {
-          const int tok = m0t + wm * kWM + 32 * i + lr;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int ch = n0t + wn * kWN + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (tok >= a.m0 && tok < a.m0 + a.mc && ch >= a.n0 && ch < a.n0 + a.nc)
-              a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (g.K / 64) + gidx] = p[e] / 256;
-          }
-        } else {
-          const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x2f32(swv[j], sxv[i], f32x16{}, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[j][i][e] = __builtin_fmaf((float)p[e], sc[e], acc[j][i][e]);
-        }
+      for (int e = 0; e < 16; ++e) {
+        sc[(u >> 1) & 1][0][e] = r[e];
+        sc[(u >> 1) & 1][1][e] = r[16 + e];
       }
     }
   };
+  auto valu_unit = [&](int u, int st, int m0t, int n0t) {
+    const int gg = u >> 2, j = (u >> 1) & 1, i = u & 1;
+    const i32x16& p = pp[u & 1];
+    if constexpr (DEBUG_P) {
+      const int tok = m0t + wm * kWM + 32 * i + lr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ch = n0t + wn * kWN + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (tok >= a.m0 && tok < a.m0 + a.mc && ch >= a.n0 && ch < a.n0 + a.nc)
+          a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (g.K / 64) + 2 * st + gg] = p[e] / 256;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = __builtin_fmaf((float)p[e], sc[(u >> 1) & 1][i][e], acc[j][i][e]);
+    }
+  };
+  // One stage: raw fragments and scales of both groups are read from LDS up
+  // front; then eight pipeline steps, each its own scheduling region: the 3
+  // MFMAs of unit u + 1 spread over the ~32 vector instructions of unit u
+  // (step 2 also widens group 1, which unit 4 needs).
+  auto stage_compute = [&](const uint8_t* slot, int st, int m0t, int n0t) {
+    i32x4 ra[2][kTM], rb[2][kTN];
+    float rsx[2][kTM], rsw[2][kTN];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+      for (int t = 0; t < kTM; ++t) {
+        ra[gg][t] = *reinterpret_cast<const i32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + gg) * 1024 + lane * 16);
+        rsx[gg][t] = *reinterpret_cast<const float*>(slot + kScA + gg * (kBM * 4) + (wm * kWM + 32 * t + lr) * 4);
+      }
+#pragma unroll
+      for (int t = 0; t < kTN; ++t) {
+        rb[gg][t] = *reinterpret_cast<const i32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + gg) * 1024 + lane * 16);
+        rsw[gg][t] = *reinterpret_cast<const float*>(slot + kScB + gg * (kBN * 4) + (wn * kWN + 32 * t + lr) * 4);
+      }
+    }
+    // int8 operands; the token scale carries the 1/256 of the widened codes
+    auto widen_group = [&](int gg) {
+#pragma unroll
+      for (int t = 0; t < kTM; ++t) {
+        widen(ra[gg][t], alo[gg][t], ahi[gg][t]);
+        sxv[gg][t] = rsx[gg][t] * (1.0f / 256.0f);
+      }
+#pragma unroll
+      for (int t = 0; t < kTN; ++t) {
+        widen(rb[gg][t], blo[gg][t], bhi[gg][t]);
+        swv[gg][t] = rsw[gg][t];
+      }
+    };
+    widen_group(0);
+    mfma_unit(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u == 2) widen_group(1);
+      if (u + 1 < 8) mfma_unit(u + 1);
+      valu_unit(u, st, m0t, n0t);
+      if (u == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+      } else if (u + 1 < 8) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  int gs = 0, stores_due = 0;
   const int nlr = g.nstt - g.nst;
   // prologue: the first kNStage - 1 ring steps in flight
   for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
@@ -252,12 +310,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     for (int st = 0; st < g.nst; ++st) {
       ring_barrier(DEBUG_P ? 0 : nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
       if (stores_due > 0) --stores_due;
-      const bool more = gs + kNStage - 1 < total;
-      if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)
-      const uint8_t* slot = smem + (gs % kNStage) * kSlot;
-      group(slot, 0, 2 * st, m0t, n0t);
-      if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)
-      group(slot, 1, 2 * st + 1, m0t, n0t);
+      if (gs + kNStage - 1 < total) SVDQ_ISSUE(gs + kNStage - 1)
+      stage_compute(smem + (gs % kNStage) * kSlot, st, m0t, n0t);
       ++gs;
     }
     if constexpr (DEBUG_P) continue;
