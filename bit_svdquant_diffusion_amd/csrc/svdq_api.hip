@@ -34,7 +34,7 @@ svdq_status check_device(int* cus = nullptr) {
     hipDeviceProp_t p;
     bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
               std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess &&
-              prepare_gemm_int4() == hipSuccess;
+              prepare_gemm_int4() == hipSuccess && prepare_stage1() == hipSuccess;
     s = ok ? 1 : 2;
     if (ok) g_dev_cus[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
     g_dev_state[dev].store(s, std::memory_order_release);

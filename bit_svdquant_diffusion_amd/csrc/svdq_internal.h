@@ -20,6 +20,7 @@ struct Stage1Args {
   uint16_t* z;
 };
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t st);
+hipError_t prepare_stage1();   // one-time per device: kernels' dynamic LDS attribute
 
 struct GemmArgs {
   int fmt, M, N, K, r32;

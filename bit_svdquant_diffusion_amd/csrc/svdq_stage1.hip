@@ -13,12 +13,12 @@
 // a wave's quarter holds exactly one INT4 group (two MXFP4 blocks) per token.
 // Lane (r = l%16, j = l/16) holds token r and channels 16j .. 16j+15 of the
 // quarter. Per step a wave
-//   1. finds its quarter of X (16 tokens x 128 bytes) and of mu in LDS, moved
-//      there by direct global->LDS transfers issued D steps ahead into a ring
-//      of D + 1 slots; loads the step's L1 fragments into registers, then
-//      issues the transfers D steps ahead. Vector-memory operations retire in
-//      issue order, so each wait names exactly the operations issued after
-//      what it waits for, and no register carries a load across iterations;
+//   1. finds its quarter of X (16 tokens x 128 bytes), of mu and of L1 in
+//      LDS, moved there by direct global->LDS transfers issued D steps ahead
+//      into a ring of D + 1 slots. Vector-memory operations retire in issue
+//      order, so each wait names exactly the operations issued after what it
+//      waits for; no register load is outstanding across a wait (a register
+//      load would make the compiler drain every transfer in flight);
 //   2. reads its 16 values of x, multiplies by mu (x_hat = fl32(x mu));
 //   3. quantizes: the group (block) absolute maximum is combined across the 4
 //      (2) lanes that share it with lane swaps; codes are stored as 8 bytes;
@@ -38,30 +38,34 @@ constexpr int S1_STEP = 256;                 // channels per step
 constexpr int S1_WAVES = 4;                  // one 64-channel quarter each
 constexpr int S1_XQ = S1_ROWS * 64 * 2;      // bytes of one wave's X quarter (2 KiB)
 constexpr int S1_MU = S1_WAVES * S1_XQ;      // offset of the step's mu in a ring slot
-constexpr int S1_SLOT = S1_MU + S1_STEP * 4; // X of all waves + mu of the step
+constexpr int S1_L1 = S1_MU + S1_STEP * 4;   // offset of the step's L1 fragments
 
 typedef __attribute__((address_space(3))) void s1_lds_void;
 // s_waitcnt operand: vmcnt n (n < 64), expcnt and lgkmcnt not waited on
 #define S1_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070 | 0x0f00)
 
-// Vector-memory operations of one step and wave, in issue order: L1
-// fragments (2 per 16 columns), the ring transfers D steps ahead (2 X, 1 mu),
-// the two stores (codes, scale; they always issue, token m0 of every
-// workgroup exists). After step i's transfers are issued, what follows them
-// when step i waits is: in the first D steps, the later prologue transfers
-// and the whole steps before i; afterwards, the rest of step i - D and the
-// D - 1 steps between. The largest count must fit the 63 operations a wave
-// can have outstanding. (The compiler itself waits for all outstanding
-// operations before the MFMAs that read the L1 registers; keeping L1 in the
-// ring instead costs more LDS than the deeper X ring gains.)
+// Ring slot: X of the four waves, mu of the step, then each wave's 2 NCB L1
+// fragments of 1 KiB. Depth: with 16 KiB of L1 or less per step the ring
+// fits two workgroups per CU (80 KiB each), otherwise one; at most 7 steps.
+// Vector-memory operations of one step and wave, in issue order: the ring
+// transfers D steps ahead (2 X, 1 mu, 2 NCB L1), then the two stores (codes,
+// scale; they always issue, token m0 of every workgroup exists). After step
+// i's transfers are issued, what follows them when step i waits is: in the
+// first D steps, the later prologue transfers and the whole steps before i;
+// afterwards, the stores of step i - D and the D - 1 steps between. The
+// largest count must fit the 63 operations a wave can have outstanding.
 template <int NCB> struct S1Cfg {
-  static constexpr int kX = 3, kSt = 2;
-  static constexpr int kPerStep = 2 * NCB + kX + kSt;
-  static constexpr int kDepth0 = 1 + (61 - kSt) / kPerStep;
-  static constexpr int kDepth = kDepth0 > 7 ? 7 : kDepth0;
+  static constexpr int kX = 3 + 2 * NCB, kSt = 2;
+  static constexpr int kPerStep = kX + kSt;
+  static constexpr int kSlot = S1_L1 + S1_WAVES * 2 * NCB * 1024;
+  static constexpr int kBudget = (NCB <= 2 ? 80 : 160) * 1024;
+  static constexpr int kDepthL = kBudget / kSlot - 1;
+  static constexpr int kDepthV = 1 + (61 - kSt) / kPerStep;
+  static constexpr int kDepth = kDepthL < kDepthV ? (kDepthL < 7 ? kDepthL : 7) : (kDepthV < 7 ? kDepthV : 7);
   static constexpr int count(int i) {   // operations issued after step i's transfers
     return i < kDepth ? kX * (kDepth - 1 - i) + i * kPerStep : kSt + (kDepth - 1) * kPerStep;
   }
+  static_assert(kDepth >= 1, "ring needs two slots");
   static_assert(count(kDepth) <= 62, "wait count out of range");
 };
 
@@ -136,11 +140,15 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
   {                                                                                                \
     const bool real_ = (I) < nsteps;                                                               \
     const size_t xo_ = real_ ? (size_t)(I) * S1_STEP : 0;                                          \
-    uint8_t* slot_ = smem + ((I) % (D + 1)) * S1_SLOT;                                             \
+    uint8_t* slot_ = smem + ((I) % (D + 1)) * Cfg::kSlot;                                          \
     __builtin_amdgcn_global_load_lds(real_ ? srcA + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ), 16, 0, 0);        \
     __builtin_amdgcn_global_load_lds(real_ ? srcB + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ + 1024), 16, 0, 0); \
     __builtin_amdgcn_global_load_lds(real_ ? mu + xo_ + wave * 64 + lane : mu,                     \
                                      (s1_lds_void*)(slot_ + S1_MU + wave * 256), 4, 0, 0);          \
+    _Pragma("unroll") for (int f_ = 0; f_ < 2 * NCB; ++f_)                                         \
+      __builtin_amdgcn_global_load_lds(                                                            \
+          l1s + (real_ ? ((((size_t)(I) * S1_WAVES + wave) * NCB * 2 + f_) * 64 + lane) * 8 : (size_t)lane * 8), \
+          (s1_lds_void*)(slot_ + S1_L1 + (wave * 2 * NCB + f_) * 1024), 16, 0, 0);                 \
   }
 #define S1_WAIT_CASE(k)                                                                            \
   case k: __builtin_amdgcn_s_waitcnt(S1_VMCNT(Cfg::count(k < D ? k : D))); break;
@@ -158,21 +166,26 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
           default: __builtin_amdgcn_s_waitcnt(S1_VMCNT(0)); break;
         }
         __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* slot = smem + (i % (D + 1)) * Cfg::kSlot;
         u32x4 l1v[NCB > 0 ? 2 * NCB : 1];
 #pragma unroll
         for (int f = 0; f < 2 * NCB; ++f)
-          l1v[f] = *reinterpret_cast<const u32x4*>(l1s + ((((size_t)i * S1_WAVES + wave) * NCB * 2 + f) * 64 + lane) * 8);
-        __builtin_amdgcn_sched_barrier(0);
-        S1_ISSUE(i + D)
-        __builtin_amdgcn_sched_barrier(0);
-        const uint8_t* slot = smem + (i % (D + 1)) * S1_SLOT;
+          l1v[f] = *reinterpret_cast<const u32x4*>(slot + S1_L1 + (wave * 2 * NCB + f) * 1024 + lane * 16);
         const u32x4 xa = *reinterpret_cast<const u32x4*>(slot + wave * S1_XQ + rd0);
         const u32x4 xb = *reinterpret_cast<const u32x4*>(slot + wave * S1_XQ + rd1);
         const float* mus = reinterpret_cast<const float*>(slot + S1_MU + wave * 256) + 16 * j;
+        f32x4 muv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) muv[t] = *reinterpret_cast<const f32x4*>(mus + 4 * t);
+        // the slot of step i + D is the one read at step i - 1: its reads are
+        // complete (they were waited on before their use)
+        __builtin_amdgcn_sched_barrier(0);
+        S1_ISSUE(i + D)
+        __builtin_amdgcn_sched_barrier(0);
         float xh[16];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const f32x4 mv = *reinterpret_cast<const f32x4*>(mus + 4 * t);
+          const f32x4 mv = muv[t];
           const u32x4& xw = t < 2 ? xa : xb;
           const uint32_t w0 = xw[(t & 1) * 2], w1 = xw[(t & 1) * 2 + 1];
           xh[4 * t + 0] = bf16lo(w0) * mv.x;
@@ -287,7 +300,7 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
 template <int FMT, int NCB>
 static hipError_t launch_t(const Stage1Args& a, hipStream_t st) {
   constexpr int D = S1Cfg<NCB>::kDepth;
-  const size_t ring = (size_t)(D + 1) * S1_SLOT;
+  const size_t ring = (size_t)(D + 1) * S1Cfg<NCB>::kSlot;
   const size_t red = (size_t)S1_WAVES * NCB * 4 * 64 * 4;
   const size_t lds = ring > red ? ring : red;
   dim3 grid((a.M + S1_ROWS - 1) / S1_ROWS);
@@ -306,6 +319,26 @@ static hipError_t launch_fmt(const Stage1Args& a, hipStream_t st) {
     case 128: return launch_t<FMT, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int FMT, int NCB>
+static hipError_t prepare_t() {
+  constexpr int D = S1Cfg<NCB>::kDepth;
+  const size_t ring = (size_t)(D + 1) * S1Cfg<NCB>::kSlot;
+  const size_t red = (size_t)S1_WAVES * NCB * 4 * 64 * 4;
+  return hipFuncSetAttribute((const void*)stage1_kernel<FMT, NCB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(ring > red ? ring : red));
+}
+
+hipError_t prepare_stage1() {
+  const hipError_t e[10] = {prepare_t<SVDQ_FMT_INT4_G64, 0>(), prepare_t<SVDQ_FMT_INT4_G64, 2>(),
+                            prepare_t<SVDQ_FMT_INT4_G64, 4>(), prepare_t<SVDQ_FMT_INT4_G64, 6>(),
+                            prepare_t<SVDQ_FMT_INT4_G64, 8>(), prepare_t<SVDQ_FMT_MXFP4_G32, 0>(),
+                            prepare_t<SVDQ_FMT_MXFP4_G32, 2>(), prepare_t<SVDQ_FMT_MXFP4_G32, 4>(),
+                            prepare_t<SVDQ_FMT_MXFP4_G32, 6>(), prepare_t<SVDQ_FMT_MXFP4_G32, 8>()};
+  for (hipError_t x : e)
+    if (x != hipSuccess) return x;
+  return hipSuccess;
 }
 
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t st) {
