@@ -1,13 +1,8 @@
-// Shared pieces of the two GEMM kernels: LDS row pitch and the workgroup ->
-// output-tile map.
+// Shared piece of the two GEMM kernels: the workgroup -> output-tile map.
 #pragma once
 #include "svdq_device.h"
 
 namespace svdq {
-
-// LDS row pitch in bytes for a 64-byte K-stage row: 16 bytes of padding put
-// the eight rows read by one 8-lane ds_read_b128 group on distinct banks.
-constexpr int G_PITCH = 80;
 
 struct TileMap {
   int tm, tn;
