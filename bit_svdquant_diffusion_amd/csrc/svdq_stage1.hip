@@ -8,17 +8,21 @@
 //     rounded to bf16 ("the low rank branch held at higher precision such as
 //     16 bit"; the branches "share inputs", same page).
 //
-// Work split: a workgroup owns 16 tokens and walks K in steps of 256
-// channels; its four waves take one 64-channel quarter of every step each, so
-// a wave's quarter holds exactly one INT4 group (two MXFP4 blocks) per token.
-// Lane (r = l%16, j = l/16) holds token r and channels 16j .. 16j+15 of the
-// quarter. Per step a wave
+// Work split: a workgroup owns 16 TH tokens (TH = 1 or 2 halves of 16) and
+// walks K in steps of 256 channels; wave w = 4 th + q takes the 64-channel
+// quarter q of every step for the 16 tokens of half th, so a wave's quarter
+// holds exactly one INT4 group (two MXFP4 blocks) per token. The two halves
+// share each step's L1 fragments (each half loads half of them), which halves
+// the L1 bytes per token. Lane (r = l%16, j = l/16) holds token r of its half
+// and channels 16j .. 16j+15 of the quarter. Per step a wave
 //   1. finds its quarter of X (16 tokens x 128 bytes), of mu and of L1 in
 //      LDS, moved there by direct global->LDS transfers issued D steps ahead
-//      into a ring of D + 1 slots. Vector-memory operations retire in issue
-//      order, so each wait names exactly the operations issued after what it
-//      waits for; no register load is outstanding across a wait (a register
-//      load would make the compiler drain every transfer in flight);
+//      into a ring of D + 1 slots (with two halves, a workgroup barrier after
+//      the wait makes the other half's L1 transfers visible). Vector-memory
+//      operations retire in issue order, so each wait names exactly the
+//      operations issued after what it waits for; no register load is
+//      outstanding across a wait (a register load would make the compiler
+//      drain every transfer in flight);
 //   2. reads its 16 values of x, multiplies by mu (x_hat = fl32(x mu));
 //   3. quantizes: the group (block) absolute maximum is combined across the 4
 //      (2) lanes that share it with lane swaps; codes are stored as 8 bytes;
@@ -37,34 +41,37 @@ constexpr int S1_ROWS = 16;
 constexpr int S1_STEP = 256;                 // channels per step
 constexpr int S1_WAVES = 4;                  // one 64-channel quarter each
 constexpr int S1_XQ = S1_ROWS * 64 * 2;      // bytes of one wave's X quarter (2 KiB)
-constexpr int S1_MU = S1_WAVES * S1_XQ;      // offset of the step's mu in a ring slot
-constexpr int S1_L1 = S1_MU + S1_STEP * 4;   // offset of the step's L1 fragments
 
 typedef __attribute__((address_space(3))) void s1_lds_void;
 // s_waitcnt operand: vmcnt n (n < 64), expcnt and lgkmcnt not waited on
 #define S1_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070 | 0x0f00)
 
-// Ring slot: X of the four waves, mu of the step, then each wave's 2 NCB L1
-// fragments of 1 KiB. Depth: with 16 KiB of L1 or less per step the ring
-// fits two workgroups per CU (80 KiB each), otherwise one; at most 7 steps.
-// Vector-memory operations of one step and wave, in issue order: the ring
-// transfers D steps ahead (2 X, 1 mu, 2 NCB L1), then the two stores (codes,
-// scale; they always issue, token m0 of every workgroup exists). After step
-// i's transfers are issued, what follows them when step i waits is: in the
-// first D steps, the later prologue transfers and the whole steps before i;
-// afterwards, the stores of step i - D and the D - 1 steps between. The
-// largest count must fit the 63 operations a wave can have outstanding.
-template <int NCB> struct S1Cfg {
-  static constexpr int kX = 3 + 2 * NCB, kSt = 2;
+// Ring slot: X of the 4 TH waves, mu of the step, then each quarter's 2 NCB
+// L1 fragments of 1 KiB. Depth: a single half with 16 KiB of L1 or less per
+// step fits two workgroups per CU (80 KiB each), otherwise one workgroup per
+// CU; at most 7 steps. Vector-memory operations of one step and wave, in
+// issue order: the ring transfers D steps ahead (2 X, 1 mu, 2 NCB / TH L1),
+// then the two stores (codes, scale; every wave issues them, lanes past M
+// repeating the identical values of token M - 1). After step i's transfers
+// are issued, what follows them when step i waits is: in the first D steps,
+// the later prologue transfers and the whole steps before i; afterwards, the
+// stores of step i - D and the D - 1 steps between. The largest count must
+// fit the 63 operations a wave can have outstanding.
+template <int NCB, int TH> struct S1Cfg {
+  static constexpr int kL1PerWave = 2 * NCB / TH;
+  static constexpr int kX = 3 + kL1PerWave, kSt = 2;
   static constexpr int kPerStep = kX + kSt;
-  static constexpr int kSlot = S1_L1 + S1_WAVES * 2 * NCB * 1024;
-  static constexpr int kBudget = (NCB <= 2 ? 80 : 160) * 1024;
+  static constexpr int kMu = TH * S1_WAVES * S1_XQ;   // offset of the step's mu
+  static constexpr int kL1 = kMu + S1_STEP * 4;       // offset of the step's L1 fragments
+  static constexpr int kSlot = kL1 + S1_WAVES * 2 * NCB * 1024;
+  static constexpr int kBudget = (TH == 1 && NCB <= 2 ? 80 : 160) * 1024;
   static constexpr int kDepthL = kBudget / kSlot - 1;
   static constexpr int kDepthV = 1 + (61 - kSt) / kPerStep;
   static constexpr int kDepth = kDepthL < kDepthV ? (kDepthL < 7 ? kDepthL : 7) : (kDepthV < 7 ? kDepthV : 7);
   static constexpr int count(int i) {   // operations issued after step i's transfers
     return i < kDepth ? kX * (kDepth - 1 - i) + i * kPerStep : kSt + (kDepth - 1) * kPerStep;
   }
+  static_assert(TH == 1 || NCB % 2 == 0, "two halves split the L1 fragments evenly");
   static_assert(kDepth >= 1, "ring needs two slots");
   static_assert(count(kDepth) <= 62, "wait count out of range");
 };
@@ -102,30 +109,33 @@ __device__ __forceinline__ uint32_t s1_e2m1x8(const float* v, int e) {
   return w;
 }
 
-template <int FMT, int NCB>
-__global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
+template <int FMT, int NCB, int TH>
+__global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
     uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, int M, int K) {
-  using Cfg = S1Cfg<NCB>;
+  using Cfg = S1Cfg<NCB, TH>;
   constexpr int D = Cfg::kDepth;
   constexpr int r32 = NCB * 16;
+  constexpr int FPW = Cfg::kL1PerWave;
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m0 = blockIdx.x * S1_ROWS;
+  const int q = wave & 3, th = wave >> 2;   // quarter and token half
+  const int m0 = blockIdx.x * S1_ROWS * TH + th * S1_ROWS;
   const int nsteps = K / S1_STEP;
   const int Mp = (M + 15) / 16 * 16;   // row stride of the INT4 scales
   const int MB = (M + 31) / 32;        // 32-row blocks (MXFP4 fragment order)
 
   const int r = lane & 15, j = lane >> 4;
-  const int m = m0 + r;
-  const bool row_ok = m < M;
+  // token of this lane; a lane past M holds token M - 1's values (its X rows
+  // are clamped below) and stores them again, so every store always issues
+  const int m = min(m0 + r, M - 1);
 
   // X transfer d (0, 1) of this lane: 16-byte unit u = 64 d + lane of the
   // quarter, token u / 8, chunk (u % 8) ^ ((token / 2) % 8)
   const int tA = lane >> 3, tB = 8 + (lane >> 3);
-  const uint16_t* srcA = x + (size_t)min(m0 + tA, M - 1) * K + wave * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
-  const uint16_t* srcB = x + (size_t)min(m0 + tB, M - 1) * K + wave * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
+  const uint16_t* srcA = x + (size_t)min(m0 + tA, M - 1) * K + q * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
+  const uint16_t* srcB = x + (size_t)min(m0 + tB, M - 1) * K + q * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
   // read-back of chunks 2j, 2j+1 of token r
   const int rd0 = (r * 8 + ((2 * j) ^ ((r >> 1) & 7))) * 16;
   const int rd1 = (r * 8 + ((2 * j + 1) ^ ((r >> 1) & 7))) * 16;
@@ -143,12 +153,12 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
     uint8_t* slot_ = smem + ((I) % (D + 1)) * Cfg::kSlot;                                          \
     __builtin_amdgcn_global_load_lds(real_ ? srcA + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ), 16, 0, 0);        \
     __builtin_amdgcn_global_load_lds(real_ ? srcB + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ + 1024), 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds(real_ ? mu + xo_ + wave * 64 + lane : mu,                     \
-                                     (s1_lds_void*)(slot_ + S1_MU + wave * 256), 4, 0, 0);          \
-    _Pragma("unroll") for (int f_ = 0; f_ < 2 * NCB; ++f_)                                         \
+    __builtin_amdgcn_global_load_lds(real_ ? mu + xo_ + q * 64 + lane : mu,                        \
+                                     (s1_lds_void*)(slot_ + Cfg::kMu + q * 256), 4, 0, 0);          \
+    _Pragma("unroll") for (int f_ = th * FPW; f_ < (th + 1) * FPW; ++f_)                           \
       __builtin_amdgcn_global_load_lds(                                                            \
-          l1s + (real_ ? ((((size_t)(I) * S1_WAVES + wave) * NCB * 2 + f_) * 64 + lane) * 8 : (size_t)lane * 8), \
-          (s1_lds_void*)(slot_ + S1_L1 + (wave * 2 * NCB + f_) * 1024), 16, 0, 0);                 \
+          l1s + (real_ ? ((((size_t)(I) * S1_WAVES + q) * NCB * 2 + f_) * 64 + lane) * 8 : (size_t)lane * 8), \
+          (s1_lds_void*)(slot_ + Cfg::kL1 + (q * 2 * NCB + f_) * 1024), 16, 0, 0);                 \
   }
 #define S1_WAIT_CASE(k)                                                                            \
   case k: __builtin_amdgcn_s_waitcnt(S1_VMCNT(Cfg::count(k < D ? k : D))); break;
@@ -165,15 +175,19 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
           S1_WAIT_CASE(4) S1_WAIT_CASE(5) S1_WAIT_CASE(6) S1_WAIT_CASE(7)
           default: __builtin_amdgcn_s_waitcnt(S1_VMCNT(0)); break;
         }
+        // both halves' L1 transfers are in: the other half's become visible
+        // at the barrier, which also means every wave is done reading the
+        // slot that the transfers below refill
+        if constexpr (TH > 1) __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const uint8_t* slot = smem + (i % (D + 1)) * Cfg::kSlot;
         u32x4 l1v[NCB > 0 ? 2 * NCB : 1];
 #pragma unroll
         for (int f = 0; f < 2 * NCB; ++f)
-          l1v[f] = *reinterpret_cast<const u32x4*>(slot + S1_L1 + (wave * 2 * NCB + f) * 1024 + lane * 16);
+          l1v[f] = *reinterpret_cast<const u32x4*>(slot + Cfg::kL1 + (q * 2 * NCB + f) * 1024 + lane * 16);
         const u32x4 xa = *reinterpret_cast<const u32x4*>(slot + wave * S1_XQ + rd0);
         const u32x4 xb = *reinterpret_cast<const u32x4*>(slot + wave * S1_XQ + rd1);
-        const float* mus = reinterpret_cast<const float*>(slot + S1_MU + wave * 256) + 16 * j;
+        const float* mus = reinterpret_cast<const float*>(slot + Cfg::kMu + q * 256) + 16 * j;
         f32x4 muv[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) muv[t] = *reinterpret_cast<const f32x4*>(mus + 4 * t);
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
           xh[4 * t + 2] = bf16lo(w1) * mv.z;
           xh[4 * t + 3] = bf16hi(w1) * mv.w;
         }
-        const int k0 = i * S1_STEP + wave * 64;   // first channel of the quarter
+        const int k0 = i * S1_STEP + q * 64;   // first channel of the quarter
 
         // 3. Z += bf16(x_hat) L1: MFMA t takes channels 16j + 8t .. +7 of each lane
         if constexpr (NCB > 0) {
@@ -221,20 +235,24 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
           // t = x_hat * rcp(s) is within 1.3e-6 of the exact quotient (|q| <= 7,
           // rcp within 1 ulp), so rint(t) is the answer unless t lies within
           // 1e-5 of a half-integer; then the lane redoes its values exactly.
-          // Zero and tiny scales always take the exact path.
+          // Zero and tiny scales always take the exact path. Adding 1.5 * 2^23
+          // rounds t to an integer (nearest, ties to even) held in the low
+          // mantissa bits, whose low nibble is the two's complement code.
+          constexpr float kRound = 12582912.0f;
           const float inv = __builtin_amdgcn_rcpf(sc);
-          bool near = !(sc >= 0x1p-100f);
+          float dmax = 0.f;   // largest |t - rint(t)| of the lane
           c0 = 0;
           c1 = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float t0 = xh[e] * inv, t1 = xh[8 + e] * inv;
-            const float r0 = __builtin_rintf(t0), r1 = __builtin_rintf(t1);
-            near |= __builtin_fabsf(t0 - r0) > 0.49999f;
-            near |= __builtin_fabsf(t1 - r1) > 0.49999f;
-            c0 |= ((uint32_t)(int)r0 & 15u) << (4 * e);
-            c1 |= ((uint32_t)(int)r1 & 15u) << (4 * e);
+            const float u0 = t0 + kRound, u1 = t1 + kRound;
+            dmax = __builtin_fmaxf(dmax, __builtin_fabsf(t0 - (u0 - kRound)));
+            dmax = __builtin_fmaxf(dmax, __builtin_fabsf(t1 - (u1 - kRound)));
+            c0 |= (__float_as_uint(u0) & 15u) << (4 * e);
+            c1 |= (__float_as_uint(u1) & 15u) << (4 * e);
           }
+          const bool near = !(sc >= 0x1p-100f) || dmax > 0.49999f;
           if (near) {
             c0 = 0;
             c1 = 0;
@@ -246,12 +264,12 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
               }
             }
           }
-          if (row_ok && j == 0) reinterpret_cast<float*>(sx)[(size_t)(k0 / 64) * Mp + m] = sc;
+          if (j == 0) reinterpret_cast<float*>(sx)[(size_t)(k0 / 64) * Mp + m] = sc;
         } else {
           const int e = mx_exponent(amax);       // block b = j / 2 of the quarter
           c0 = s1_e2m1x8(xh, e);
           c1 = s1_e2m1x8(xh + 8, e);
-          if (row_ok && (j & 1) == 0) {
+          if ((j & 1) == 0) {
             // fragment-order scale byte of 32-channel block kb = k0/32 + j/2:
             // stage kb/4, step (kb%4)/2, half kb%2
             const int kb = k0 / 32 + (j >> 1);
@@ -259,7 +277,7 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
                                            ((kb >> 1) & 1)] = (uint8_t)(e + 127);
           }
         }
-        if (row_ok) {
+        {
           // fragment order: 64-channel step k0/64 of row block m/32; channels
           // 32h .. 32h+31 at lane 32h + m%32, 16 channels = 8 bytes
           uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + k0 / 64) * 1024;
@@ -282,13 +300,14 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
       for (int e = 0; e < 4; ++e) red[((wave * NCB + c) * 4 + e) * 64 + lane] = zacc[c][e];
     }
     __syncthreads();
-    constexpr int total = NCB * 4 * 64;
-    for (int idx = threadIdx.x; idx < total; idx += 64 * S1_WAVES) {
+    constexpr int per = NCB * 4 * 64;   // one wave's partial tile
+    for (int idx = threadIdx.x; idx < TH * per; idx += 64 * S1_WAVES * TH) {
+      const int h = idx / per, rem = idx - h * per;
       float acc = 0.f;
-      for (int w = 0; w < S1_WAVES; ++w) acc += red[w * total + idx];
+      for (int w = 0; w < S1_WAVES; ++w) acc += red[(h * S1_WAVES + w) * per + rem];
       // 16x16 result layout: lane l, reg e -> row 4(l/16) + e, column l%16
-      const int l = idx & 63, e = (idx >> 6) & 3, c = idx >> 8;
-      const int row = m0 + 4 * (l >> 4) + e;
+      const int l = rem & 63, e = (rem >> 6) & 3, c = rem >> 8;
+      const int row = blockIdx.x * S1_ROWS * TH + h * S1_ROWS + 4 * (l >> 4) + e;
       const int col = 16 * c + (l & 15);
       if (row < M)   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
         z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
@@ -297,48 +316,61 @@ __global__ __launch_bounds__(64 * S1_WAVES) void stage1_kernel(
   }
 }
 
-template <int FMT, int NCB>
+template <int FMT, int NCB, int TH>
+static size_t lds_bytes() {
+  using Cfg = S1Cfg<NCB, TH>;
+  const size_t ring = (size_t)(Cfg::kDepth + 1) * Cfg::kSlot;
+  const size_t red = (size_t)TH * S1_WAVES * NCB * 4 * 64 * 4;
+  return ring > red ? ring : red;
+}
+
+template <int FMT, int NCB, int TH>
 static hipError_t launch_t(const Stage1Args& a, hipStream_t st) {
-  constexpr int D = S1Cfg<NCB>::kDepth;
-  const size_t ring = (size_t)(D + 1) * S1Cfg<NCB>::kSlot;
-  const size_t red = (size_t)S1_WAVES * NCB * 4 * 64 * 4;
-  const size_t lds = ring > red ? ring : red;
-  dim3 grid((a.M + S1_ROWS - 1) / S1_ROWS);
-  hipLaunchKernelGGL((stage1_kernel<FMT, NCB>), grid, dim3(64 * S1_WAVES), lds, st, a.x, a.mu, a.l1s,
-                     a.qx, a.sx, a.z, a.M, a.K);
+  dim3 grid((a.M + S1_ROWS * TH - 1) / (S1_ROWS * TH));
+  const size_t lds = lds_bytes<FMT, NCB, TH>();
+  hipLaunchKernelGGL((stage1_kernel<FMT, NCB, TH>), grid, dim3(64 * S1_WAVES * TH), lds, st,
+                     a.x, a.mu, a.l1s, a.qx, a.sx, a.z, a.M, a.K);
   return hipGetLastError();
 }
 
+// Two token halves per workgroup halve the L1 bytes but also the number of
+// workgroups. MXFP4 quantization is cheap, so that pays from 2048 tokens on;
+// the INT4 quantizer's vector work wants every CU, so INT4 takes two halves
+// only once 32-token workgroups fill the 256 CUs.
+constexpr int kTwoHalvesMinM[2] = {8192, 2048};   // INT4, MXFP4
+
 template <int FMT>
 static hipError_t launch_fmt(const Stage1Args& a, hipStream_t st) {
+  const bool two = a.M >= kTwoHalvesMinM[FMT == SVDQ_FMT_MXFP4_G32 ? 1 : 0];
   switch (a.r32) {
-    case 0: return launch_t<FMT, 0>(a, st);
-    case 32: return launch_t<FMT, 2>(a, st);
-    case 64: return launch_t<FMT, 4>(a, st);
-    case 96: return launch_t<FMT, 6>(a, st);
-    case 128: return launch_t<FMT, 8>(a, st);
+    case 0: return two ? launch_t<FMT, 0, 2>(a, st) : launch_t<FMT, 0, 1>(a, st);
+    case 32: return two ? launch_t<FMT, 2, 2>(a, st) : launch_t<FMT, 2, 1>(a, st);
+    case 64: return two ? launch_t<FMT, 4, 2>(a, st) : launch_t<FMT, 4, 1>(a, st);
+    case 96: return launch_t<FMT, 6, 1>(a, st);
+    case 128: return launch_t<FMT, 8, 1>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int FMT, int NCB>
+template <int FMT, int NCB, int TH>
 static hipError_t prepare_t() {
-  constexpr int D = S1Cfg<NCB>::kDepth;
-  const size_t ring = (size_t)(D + 1) * S1Cfg<NCB>::kSlot;
-  const size_t red = (size_t)S1_WAVES * NCB * 4 * 64 * 4;
-  return hipFuncSetAttribute((const void*)stage1_kernel<FMT, NCB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)(ring > red ? ring : red));
+  return hipFuncSetAttribute((const void*)stage1_kernel<FMT, NCB, TH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds_bytes<FMT, NCB, TH>());
 }
 
-hipError_t prepare_stage1() {
-  const hipError_t e[10] = {prepare_t<SVDQ_FMT_INT4_G64, 0>(), prepare_t<SVDQ_FMT_INT4_G64, 2>(),
-                            prepare_t<SVDQ_FMT_INT4_G64, 4>(), prepare_t<SVDQ_FMT_INT4_G64, 6>(),
-                            prepare_t<SVDQ_FMT_INT4_G64, 8>(), prepare_t<SVDQ_FMT_MXFP4_G32, 0>(),
-                            prepare_t<SVDQ_FMT_MXFP4_G32, 2>(), prepare_t<SVDQ_FMT_MXFP4_G32, 4>(),
-                            prepare_t<SVDQ_FMT_MXFP4_G32, 6>(), prepare_t<SVDQ_FMT_MXFP4_G32, 8>()};
+template <int FMT>
+static hipError_t prepare_fmt() {
+  const hipError_t e[8] = {prepare_t<FMT, 0, 1>(), prepare_t<FMT, 2, 1>(), prepare_t<FMT, 4, 1>(),
+                           prepare_t<FMT, 6, 1>(), prepare_t<FMT, 8, 1>(), prepare_t<FMT, 0, 2>(),
+                           prepare_t<FMT, 2, 2>(), prepare_t<FMT, 4, 2>()};
   for (hipError_t x : e)
     if (x != hipSuccess) return x;
   return hipSuccess;
+}
+
+hipError_t prepare_stage1() {
+  const hipError_t e = prepare_fmt<SVDQ_FMT_INT4_G64>();
+  return e != hipSuccess ? e : prepare_fmt<SVDQ_FMT_MXFP4_G32>();
 }
 
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t st) {
