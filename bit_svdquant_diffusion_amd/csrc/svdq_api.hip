@@ -83,6 +83,9 @@ Stage1Args stage1_args(const svdq_layer_desc* d, const svdq_packed* dev, const u
   a.qx = b + L.qx;
   a.sx = b + L.sx;
   a.z = (uint16_t*)(b + L.z);
+  const bool int4 = d->format == SVDQ_FMT_INT4_G64;
+  a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
+  a.nflags = int4 ? kSplitSlots : 0;
   return a;
 }
 
@@ -105,6 +108,9 @@ GemmArgs gemm_args(const svdq_layer_desc* d, const svdq_packed* dev, int64_t M, 
   a.l2t = dev->l2;
   a.bias = dev->bias;
   a.y = y;
+  const bool int4 = d->format == SVDQ_FMT_INT4_G64;
+  a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
+  a.part = int4 ? (float*)(b + L.part) : nullptr;
   return a;
 }
 

@@ -23,8 +23,20 @@
 // 4 (N), each own 64 x 64 (2 x 2 blocks of 32 x 32); one workgroup barrier
 // per 128-channel stage (two groups). The low-rank branch is r32/32 more
 // stages on v_mfma_f32_32x32x16_bf16 into the same accumulators.
+//
+// Work split. Whole rounds of tiles go one per workgroup. The tiles left
+// after them (between one and two rounds' worth, or all of them when there
+// are fewer tiles than workgroups) are cut into their K stages and dealt out
+// as equal contiguous runs of (tile, stage) pairs, so every workgroup ends at
+// the same time. A tile cut between runs belongs to the workgroup holding
+// its first stage; that piece is the last of its run. The other pieces come
+// first in their runs: each writes its fp32 partial to its own workspace slot
+// and raises its flag; the owner adds the partials in workgroup order (the
+// result does not depend on timing), clears the flags, and finishes the tile
+// (low-rank stages, bias, Y). Stage 1 clears the flags before every GEMM.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
+#include "svdq_layout.h"
 
 namespace svdq {
 
@@ -97,7 +109,15 @@ __device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 struct Geo {
   int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;
   int tm_off, tn_off;   // group-sum hook: the window's first tile
+  // whole rounds (tile indices below sk_base = rounds * grid), then sk_units
+  // (tile, stage) pairs from tile index sk_base dealt out over sk_grid
+  // workgroups
+  int rounds, sk_base, sk_grid;
+  long long sk_units;
 };
+constexpr int kPartFloats = kBM * kBN;   // one fp32 partial tile
+constexpr int kMinRun = 6;               // fewest stages per run of the split
+static_assert(kPartFloats * 4 == kSplitPartBytes, "workspace slot size");
 }  // namespace
 
 // DEBUG_P: instead of dequantizing, write every group sum P (exact int32) of
@@ -111,21 +131,48 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   const int wm = wave / kWGN, wn = wave % kWGN;
   const int h = lane >> 5, lr = lane & 31;
   const int ntiles = g.tiles_m * g.tiles_n;
-  const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / grid + 1 : 0;
-  const int total = my_tiles * g.nstt;   // ring steps of this workgroup
+  const int wg = (int)blockIdx.x;
+  const int nlr = g.nstt - g.nst;
   auto tile_of = [&](int t) -> TileMap {
     if (DEBUG_P) return TileMap{g.tm_off + t % g.tiles_m, g.tn_off + t / g.tiles_m};
     return map_tile(t, g.tiles_m, g.tiles_n, kGroupM);
   };
+  // whole tiles wg + k * grid for k < ncl, then the run [u0, u1) of (tile,
+  // stage) pairs; a segment is one tile's part of that: stages [ka, kb)
+  const int ncl = DEBUG_P ? (wg < ntiles ? (ntiles - 1 - wg) / grid + 1 : 0) : g.rounds;
+  auto run_begin = [&](int w) -> long long { return (long long)w * g.sk_units / g.sk_grid; };
+  const long long u0 = (!DEBUG_P && wg < g.sk_grid) ? run_begin(wg) : 0;
+  const long long u1 = (!DEBUG_P && wg < g.sk_grid) ? run_begin(wg + 1) : 0;
+  struct Seg {
+    int idx, ka, kb;
+    bool owner;
+  };
+  auto seg_at = [&](int k, long long u) -> Seg {
+    if (k < ncl) return Seg{wg + k * grid, 0, g.nst, true};
+    const int p = (int)(u / g.nst), ka = (int)(u - (long long)p * g.nst);
+    const int kb = (int)min((long long)g.nst, ka + (u1 - u));
+    return Seg{g.sk_base + p, ka, kb, ka == 0};
+  };
+  auto seg_len = [&](const Seg& sg) { return sg.kb - sg.ka + (sg.owner && !DEBUG_P ? nlr : 0); };
+  int total = 0;   // ring steps of this workgroup
+  {
+    int k = 0;
+    for (long long u = u0; k < ncl || u < u1; ++k) {
+      const Seg sg = seg_at(k, u);
+      total += seg_len(sg);
+      if (k >= ncl) u += sg.kb - sg.ka;
+    }
+  }
 
-  // issue side: next ring step to load (tile-local index is_s of tile is_t)
+  // issue side: next ring step to load (step is_s of segment is_k)
   // and this wave's per-tile transfer sources as byte offsets from uniform
   // bases: fragment item 3 w + k from src[k] (4-bit) and src[3 + k]
   // (low-rank); the scale transfer from ssrc plus the stage times sstride;
   // the bias from bsrc
   const int frag0 = kFragPerWave * wave, sop = kScaleOp(wave);
   const int nops = kOpsOf(wave);
-  int is_t = 0, is_s = 0;
+  int is_k = 0, is_s = 0, is_ka = 0, is_nk = 0, is_len = 0;   // segment, step in it, its stages
+  long long is_u = u0;
   uint32_t src[2 * kFragPerWave], ssrc = 0, bsrc = 0, sstride = 0;
   const int per_l = a.r32 / 16;
   const uint8_t* const sx_b = reinterpret_cast<const uint8_t*>(a.sx);
@@ -136,7 +183,11 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 #define SVDQ_ISSUE(GS)                                                                              \
   {                                                                                                 \
     if (is_s == 0) {                                                                                \
-      const TileMap tmi = tile_of((int)blockIdx.x + is_t * grid);                                   \
+      const Seg sg_ = seg_at(is_k, is_u);                                                           \
+      is_ka = sg_.ka;                                                                               \
+      is_nk = sg_.kb - sg_.ka;                                                                      \
+      is_len = seg_len(sg_);                                                                        \
+      const TileMap tmi = tile_of(sg_.idx);                                                         \
       const int mb0 = tmi.tm * kMB, nb0 = tmi.tn * kNBt;                                            \
       _Pragma("unroll") for (int k = 0; k < kFragPerWave; ++k) {                                    \
         const int it = frag0 + k;                          /* fragment item 0..23 */               \
@@ -160,8 +211,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       bsrc = (uint32_t)min(nb0 * 32 + 8 * lane, g.N - 8) * 2;                                       \
     }                                                                                               \
     uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
-    const bool lrs = is_s >= g.nst;                                                                 \
-    const int sl = lrs ? is_s - g.nst : is_s;                                                       \
+    const bool lrs = is_s >= is_nk;                                                                 \
+    const int sl = lrs ? is_s - is_nk : is_ka + is_s;                                               \
     if (lrs && a.r32 == 0) {                                                                        \
       /* no low-rank fragments: every transfer of the stage moves the bias */                      \
       _Pragma("unroll") for (int k = 0; k < kFragPerWave + 1; ++k)                                  \
@@ -184,9 +235,10 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
         }                                                                                           \
       }                                                                                             \
     }                                                                                               \
-    if (++is_s == g.nstt) {                                                                         \
+    if (++is_s == is_len) {                                                                         \
       is_s = 0;                                                                                     \
-      ++is_t;                                                                                       \
+      if (is_k >= ncl) is_u += is_nk;                                                               \
+      ++is_k;                                                                                       \
     }                                                                                               \
   }
 
@@ -296,18 +348,24 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     }
   };
 
-  const int nlr = g.nstt - g.nst;
   // prologue: the first kNStage - 1 ring steps in flight
   for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
-  for (int ct = 0; ct < my_tiles; ++ct) {
-    const TileMap tmc = tile_of((int)blockIdx.x + ct * grid);
+  // this lane's 16 float4 of a partial tile in a workspace slot
+  auto part_at = [&](int slot_wg, int f) -> float* {
+    return a.part + (size_t)slot_wg * kPartFloats + ((size_t)(wave * 16 + f) * 64 + lane) * 4;
+  };
+  int ck = 0;
+  for (long long cu = u0; ck < ncl || cu < u1; ++ck) {
+    const Seg sg = seg_at(ck, cu);
+    if (ck >= ncl) cu += sg.kb - sg.ka;
+    const TileMap tmc = tile_of(sg.idx);
     const int m0t = tmc.tm * kBM, n0t = tmc.tn * kBN;
     const int n0 = n0t + wn * kWN;
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
       for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
-    for (int st = 0; st < g.nst; ++st) {
+    for (int st = sg.ka; st < sg.kb; ++st) {
       ring_barrier(DEBUG_P ? 0 : nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
       if (stores_due > 0) --stores_due;
       if (gs + kNStage - 1 < total) SVDQ_ISSUE(gs + kNStage - 1)
@@ -315,6 +373,44 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       ++gs;
     }
     if constexpr (DEBUG_P) continue;
+    if (!sg.owner) {
+      // a later piece of a tile (the first segment of this run): publish the
+      // partial in this workgroup's slot, then its flag
+#pragma unroll
+      for (int f = 0; f < 16; ++f) {
+        const f32x16& v = acc[f >> 3][(f >> 2) & 1];
+        *reinterpret_cast<f32x4*>(part_at(wg, f)) = f32x4{v[4 * (f & 3)], v[4 * (f & 3) + 1], v[4 * (f & 3) + 2], v[4 * (f & 3) + 3]};
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // every store of every wave has landed ...
+      __syncthreads();                  // ... before the flag is raised
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(a.flags + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      continue;
+    }
+    if (ck >= ncl && sg.kb < g.nst) {
+      // the first piece of a tile that later runs continued: add their
+      // partials in workgroup order (the flags bound the wait; they are set
+      // early in those runs, so it is normally already over)
+      const long long tile_end = (long long)(sg.idx - g.sk_base + 1) * g.nst;
+      for (int w = wg + 1; w < g.sk_grid && run_begin(w) < tile_end; ++w) {
+        if (tid == 0) {
+          for (int spin = 0; spin < (1 << 22) && __hip_atomic_load(a.flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++spin)
+            __builtin_amdgcn_s_sleep(2);
+          __hip_atomic_store(a.flags + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(part_at(w, f));
+          f32x16& d = acc[f >> 3][(f >> 2) & 1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d[4 * (f & 3) + e] += v[e];
+        }
+      }
+    }
     for (int l = 0; l < nlr; ++l) {
       ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
       if (stores_due > 0) --stores_due;
@@ -420,6 +516,9 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
     g.tiles_n = (a.n0 + a.nc + kBN - 1) / kBN - g.tn_off;
     const int ntiles = g.tiles_m * g.tiles_n;
     if (grid > ntiles) grid = ntiles;
+    g.rounds = g.sk_base = 0;
+    g.sk_grid = 1;
+    g.sk_units = 0;
     hipLaunchKernelGGL(gemm_int4_kernel<true>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
     return hipGetLastError();
   }
@@ -428,7 +527,14 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   g.tiles_m = (a.M + kBM - 1) / kBM;
   g.tiles_n = (a.N + kBN - 1) / kBN;
   const int ntiles = g.tiles_m * g.tiles_n;
-  if (grid > ntiles) grid = ntiles;
+  if (grid > kSplitSlots) grid = kSplitSlots;
+  // whole rounds while at least one more round's worth of tiles remains
+  g.rounds = ntiles / grid > 1 ? ntiles / grid - 1 : 0;
+  g.sk_base = g.rounds * grid;
+  g.sk_units = (long long)(ntiles - g.sk_base) * g.nst;
+  // at least kMinRun stages per run, so a tile is not cut into many small pieces
+  const long long runs = g.sk_units / kMinRun;
+  g.sk_grid = (int)(runs < 1 ? 1 : (runs < grid ? runs : grid));
   hipLaunchKernelGGL(gemm_int4_kernel<false>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
   return hipGetLastError();
 }

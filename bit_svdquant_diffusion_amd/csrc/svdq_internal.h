@@ -18,6 +18,8 @@ struct Stage1Args {
   uint8_t* qx;
   void* sx;
   uint16_t* z;
+  uint32_t* flags;   // INT4 GEMM split flags to clear (nflags of them), or null
+  int nflags;
 };
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t st);
 hipError_t prepare_stage1();   // one-time per device: kernels' dynamic LDS attribute
@@ -34,6 +36,10 @@ struct GemmArgs {
   const uint16_t* l2t;
   const uint16_t* bias;  // bf16 [N]
   uint16_t* y;           // bf16 [M][N]
+  // INT4 split of the last tiles: per-workgroup flags (cleared by stage 1)
+  // and fp32 partial tiles, in the workspace
+  uint32_t* flags;
+  float* part;
   // group-sum test hook (INT4): window and output [mc][nc][K/64], p ==
   // nullptr for the normal epilogue
   int32_t* p;

@@ -47,11 +47,17 @@ inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
   return s;
 }
 
+// INT4 GEMM split of the last tiles over the workgroups: one flag and one
+// fp32 partial tile (128 x 256) per workgroup, at most kSplitSlots of them.
+constexpr int kSplitSlots = 256;
+constexpr int kSplitPartBytes = 128 * 256 * 4;
+
 // Workspace: [qX][sX][Z], each 256-byte aligned, over round32(M) rows. qX and
 // Z in fragment order (see below) for both formats; sX fp32 [K/64][act_rows(M)]
-// (INT4) or E8M0 bytes in fragment order (MXFP4).
+// (INT4) or E8M0 bytes in fragment order (MXFP4). INT4 adds the split's flags
+// (u32 [kSplitSlots], cleared by stage 1) and partial tiles.
 struct WsLayout {
-  size_t qx, sx, z, total;
+  size_t qx, sx, z, flags, part, total;
 };
 inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   WsLayout w;
@@ -60,7 +66,9 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   w.qx = 0;
   w.sx = align256((size_t)rows * d->K / 2);
   w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
-  w.total = w.z + align256((size_t)rows * rank32(d->rank) * 2);
+  w.flags = w.z + align256((size_t)rows * rank32(d->rank) * 2);
+  w.part = w.flags + (int4 ? align256((size_t)kSplitSlots * 4) : 0);
+  w.total = w.part + (int4 ? (size_t)kSplitSlots * kSplitPartBytes : 0);
   return w;
 }
 

@@ -112,7 +112,8 @@ __device__ __forceinline__ uint32_t s1_e2m1x8(const float* v, int e) {
 template <int FMT, int NCB, int TH>
 __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
-    uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, int M, int K) {
+    uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, int M, int K,
+    uint32_t* __restrict__ flags, int nflags) {
   using Cfg = S1Cfg<NCB, TH>;
   constexpr int D = Cfg::kDepth;
   constexpr int r32 = NCB * 16;
@@ -125,6 +126,10 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   const int nsteps = K / S1_STEP;
   const int Mp = (M + 15) / 16 * 16;   // row stride of the INT4 scales
   const int MB = (M + 31) / 32;        // 32-row blocks (MXFP4 fragment order)
+
+  // the INT4 GEMM that follows on the stream expects its split flags clear
+  if (blockIdx.x == 0)
+    for (int f = threadIdx.x; f < nflags; f += 64 * S1_WAVES * TH) flags[f] = 0u;
 
   const int r = lane & 15, j = lane >> 4;
   // token of this lane; a lane past M holds token M - 1's values (its X rows
@@ -329,7 +334,7 @@ static hipError_t launch_t(const Stage1Args& a, hipStream_t st) {
   dim3 grid((a.M + S1_ROWS * TH - 1) / (S1_ROWS * TH));
   const size_t lds = lds_bytes<FMT, NCB, TH>();
   hipLaunchKernelGGL((stage1_kernel<FMT, NCB, TH>), grid, dim3(64 * S1_WAVES * TH), lds, st,
-                     a.x, a.mu, a.l1s, a.qx, a.sx, a.z, a.M, a.K);
+                     a.x, a.mu, a.l1s, a.qx, a.sx, a.z, a.M, a.K, a.flags, a.nflags);
   return hipGetLastError();
 }
 
