@@ -175,7 +175,9 @@ SVDQ_API svdq_status svdq_unpack_weights(const svdq_layer_desc* desc, const svdq
 /*
  * Bytes of device workspace svdq_linear_forward needs for M tokens:
  * the 4-bit activation codes, their scales and the rank-32-padded
- * X_hat L1 product. Host only.
+ * X_hat L1 product; INT4 layers add 32 MiB of GEMM scratch (fp32 partial
+ * tiles and flags for the workgroups that share a tile's K stages, cleared
+ * by svdq_stage1). Host only.
  */
 SVDQ_API svdq_status svdq_workspace_bytes(const svdq_layer_desc* desc, int64_t M, size_t* out);
 
