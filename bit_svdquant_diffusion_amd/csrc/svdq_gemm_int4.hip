@@ -28,12 +28,15 @@
 // after them (between one and two rounds' worth, or all of them when there
 // are fewer tiles than workgroups) are cut into their K stages and dealt out
 // as equal contiguous runs of (tile, stage) pairs, so every workgroup ends at
-// the same time. A tile cut between runs belongs to the workgroup holding
-// its first stage; that piece is the last of its run. The other pieces come
-// first in their runs: each writes its fp32 partial to its own workspace slot
-// and raises its flag; the owner adds the partials in workgroup order (the
-// result does not depend on timing), clears the flags, and finishes the tile
-// (low-rank stages, bias, Y). Stage 1 clears the flags before every GEMM.
+// the same time. Each XCD deals its own share of those tiles (the ones the
+// tile map gives it) over its own workgroups, which keeps their operand
+// panels in that XCD's L2. A tile cut between runs belongs to the workgroup
+// holding its first stage; that piece is the last of its run. The other
+// pieces come first in their runs: each writes its fp32 partial to its own
+// workspace slot and raises its flag; the owner adds the partials in
+// workgroup order (the result does not depend on timing), clears the flags,
+// and finishes the tile (low-rank stages, bias, Y). Stage 1 clears the flags
+// before every GEMM.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
 #include "svdq_layout.h"
@@ -109,14 +112,13 @@ __device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 struct Geo {
   int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;
   int tm_off, tn_off;   // group-sum hook: the window's first tile
-  // whole rounds (tile indices below sk_base = rounds * grid), then sk_units
-  // (tile, stage) pairs from tile index sk_base dealt out over sk_grid
-  // workgroups
-  int rounds, sk_base, sk_grid;
-  long long sk_units;
+  // whole tiles (indices below sk_base, a multiple of 8: rounds * grid),
+  // then the sk_tiles tiles from index sk_base: tile index sk_base + 8 m + x
+  // goes to XCD x, whose workgroups share its (tile, stage) pairs
+  int rounds, sk_base, sk_tiles;
 };
 constexpr int kPartFloats = kBM * kBN;   // one fp32 partial tile
-constexpr int kMinRun = 6;               // fewest stages per run of the split
+constexpr int kMinRun = 6;               // fewest stages per run of the split (when there are that many)
 static_assert(kPartFloats * 4 == kSplitPartBytes, "workspace slot size");
 }  // namespace
 
@@ -137,21 +139,27 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     if (DEBUG_P) return TileMap{g.tm_off + t % g.tiles_m, g.tn_off + t / g.tiles_m};
     return map_tile(t, g.tiles_m, g.tiles_n, kGroupM);
   };
-  // whole tiles wg + k * grid for k < ncl, then the run [u0, u1) of (tile,
-  // stage) pairs; a segment is one tile's part of that: stages [ka, kb)
-  const int ncl = DEBUG_P ? (wg < ntiles ? (ntiles - 1 - wg) / grid + 1 : 0) : g.rounds;
-  auto run_begin = [&](int w) -> long long { return (long long)w * g.sk_units / g.sk_grid; };
-  const long long u0 = (!DEBUG_P && wg < g.sk_grid) ? run_begin(wg) : 0;
-  const long long u1 = (!DEBUG_P && wg < g.sk_grid) ? run_begin(wg + 1) : 0;
+  // whole tiles wg + k * grid for k < ncl, then the run [u0, u1) of this
+  // XCD's (tile m, stage) pairs, u = m nst + stage; a segment is one tile's
+  // part of the run: stages [ka, kb)
+  const int ncl = wg < g.sk_base ? (g.sk_base - 1 - wg) / grid + 1 : 0;
+  const int xcd = wg & 7, kx = wg >> 3;   // XCD and index among its workgroups
+  const int xtiles = DEBUG_P ? 0 : (g.sk_tiles > xcd ? (g.sk_tiles - xcd + 7) / 8 : 0);
+  const long long xunits = (long long)xtiles * g.nst;
+  // runs of this XCD: at most its workgroups, at least kMinRun stages each
+  const int xruns = (int)min((long long)(grid >> 3), max(1LL, xunits / kMinRun));
+  auto run_begin = [&](int k) -> long long { return (long long)k * xunits / xruns; };
+  const long long u0 = (xtiles > 0 && kx < xruns) ? run_begin(kx) : 0;
+  const long long u1 = (xtiles > 0 && kx < xruns) ? run_begin(kx + 1) : 0;
   struct Seg {
     int idx, ka, kb;
     bool owner;
   };
   auto seg_at = [&](int k, long long u) -> Seg {
     if (k < ncl) return Seg{wg + k * grid, 0, g.nst, true};
-    const int p = (int)(u / g.nst), ka = (int)(u - (long long)p * g.nst);
+    const int m = (int)(u / g.nst), ka = (int)(u - (long long)m * g.nst);
     const int kb = (int)min((long long)g.nst, ka + (u1 - u));
-    return Seg{g.sk_base + p, ka, kb, ka == 0};
+    return Seg{g.sk_base + 8 * m + xcd, ka, kb, ka == 0};
   };
   auto seg_len = [&](const Seg& sg) { return sg.kb - sg.ka + (sg.owner && !DEBUG_P ? nlr : 0); };
   int total = 0;   // ring steps of this workgroup
@@ -393,8 +401,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       // the first piece of a tile that later runs continued: add their
       // partials in workgroup order (the flags bound the wait; they are set
       // early in those runs, so it is normally already over)
-      const long long tile_end = (long long)(sg.idx - g.sk_base + 1) * g.nst;
-      for (int w = wg + 1; w < g.sk_grid && run_begin(w) < tile_end; ++w) {
+      const long long tile_end = (long long)((sg.idx - g.sk_base - xcd) / 8 + 1) * g.nst;
+      for (int k = kx + 1; k < xruns && run_begin(k) < tile_end; ++k) {
+        const int w = xcd + 8 * k;   // the workgroup of that run
         if (tid == 0) {
           for (int spin = 0; spin < (1 << 22) && __hip_atomic_load(a.flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++spin)
             __builtin_amdgcn_s_sleep(2);
@@ -516,9 +525,9 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
     g.tiles_n = (a.n0 + a.nc + kBN - 1) / kBN - g.tn_off;
     const int ntiles = g.tiles_m * g.tiles_n;
     if (grid > ntiles) grid = ntiles;
-    g.rounds = g.sk_base = 0;
-    g.sk_grid = 1;
-    g.sk_units = 0;
+    g.rounds = 0;
+    g.sk_base = ntiles;   // whole tiles only
+    g.sk_tiles = 0;
     hipLaunchKernelGGL(gemm_int4_kernel<true>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
     return hipGetLastError();
   }
@@ -528,13 +537,17 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   g.tiles_n = (a.N + kBN - 1) / kBN;
   const int ntiles = g.tiles_m * g.tiles_n;
   if (grid > kSplitSlots) grid = kSplitSlots;
-  // whole rounds while at least one more round's worth of tiles remains
-  g.rounds = ntiles / grid > 1 ? ntiles / grid - 1 : 0;
-  g.sk_base = g.rounds * grid;
-  g.sk_units = (long long)(ntiles - g.sk_base) * g.nst;
-  // at least kMinRun stages per run, so a tile is not cut into many small pieces
-  const long long runs = g.sk_units / kMinRun;
-  g.sk_grid = (int)(runs < 1 ? 1 : (runs < grid ? runs : grid));
+  if (grid >= 8) {
+    grid &= ~7;   // every XCD holds the same number of workgroups
+    // whole rounds while at least one more round's worth of tiles remains
+    g.rounds = ntiles / grid > 1 ? ntiles / grid - 1 : 0;
+    g.sk_base = g.rounds * grid;
+    g.sk_tiles = ntiles - g.sk_base;
+  } else {
+    g.rounds = (ntiles + grid - 1) / grid;
+    g.sk_base = ntiles;   // whole tiles only
+    g.sk_tiles = 0;
+  }
   hipLaunchKernelGGL(gemm_int4_kernel<false>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
   return hipGetLastError();
 }

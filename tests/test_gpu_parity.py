@@ -54,6 +54,9 @@ SMALL = [
     _spec("two_halves_m8194", 8194, 256, 64, 32, "int4", 16),
     _spec("two_halves_m2066_fp4", 2066, 512, 256, 32, "mxfp4", 16),
     _spec("two_halves_m2100_r48_fp4", 2100, 256, 96, 48, "mxfp4", 17),
+    # INT4 GEMM split: 4 tiles of 24 K stages on 4 XCDs, each cut into four
+    # runs of 6 stages (one owner adding three partials)
+    _spec("split_k_4_pieces", 256, 3072, 512, 16, "int4", 18),
 ]
 
 
