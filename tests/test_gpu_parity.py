@@ -140,6 +140,18 @@ def test_deterministic_and_m0(fmt):
     assert y0.shape == (0, spec.N)
 
 
+def test_split_tiles_deterministic():
+    """The INT4 GEMM's owner adds the partials of a cut tile in workgroup
+    order, so repeated calls give identical bits (four-piece split case)."""
+    spec = next(s for s in SMALL if s.name == "split_k_4_pieces")
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    ys = [S.linear_forward(layer, dev, x) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+
+
 def test_rows_are_independent():
     """A row's output does not depend on the other rows in the batch (ragged tiles)."""
     spec = _spec("indep", 300, 768, 544, 32, "int4", 11)
