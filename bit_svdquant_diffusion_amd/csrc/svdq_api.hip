@@ -59,6 +59,9 @@ svdq_status common_checks(const svdq_layer_desc* d, const svdq_packed* dev, cons
   svdq_status st = check_desc(d);
   if (st != SVDQ_OK) return st;
   if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
+  // MXFP4 activation scale bytes are addressed with 32-bit stage offsets
+  if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)d->K + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
+    return SVDQ_ERR_SHAPE;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;

@@ -12,17 +12,22 @@
 //
 // Data path. Every operand (4-bit codes, E8M0 bytes, Z = X_hat L1, L2^T) is
 // stored in MFMA fragment order, one 1 KiB block per wave operand, so each
-// global->LDS transfer is a direct `global_load_lds_dwordx4` of contiguous
-// bytes and each LDS fragment read is a contiguous, conflict-free 1 KiB.
+// global->LDS transfer is a direct `buffer_load_dwordx4 ... lds` of
+// contiguous bytes and each LDS fragment read is a contiguous,
+// conflict-free 1 KiB. (The buffer form with a 32-bit lane offset runs
+// beside the other wave's MFMAs on a SIMD; the 64-bit-address global form
+// measured mostly additive to them.)
 // Workgroups are persistent (one per CU) and walk their tiles; a ring of four
 // LDS slots runs across tile boundaries with three stages in flight, so the
 // next tile's first stages load while the current tile finishes and stores.
 //
 // Schedule. Eight waves, 2 (M) x 4 (N), each owning a 96 x 96 sub-tile of the
 // 192 x 384 tile (3 x 3 blocks of 32 x 32). One workgroup barrier per stage.
-// The second half (step 1) of each stage's MFMAs is issued right after the
-// next barrier, so every wave enters each stage with matrix work queued while
-// its LDS reads for the new stage are in flight.
+// The second half (step 1) of each stage's MFMAs is deferred past the next
+// barrier and runs while that stage's first fragments load. The per-stage
+// control is kept to a few scalar instructions (a uniform transfer count, one
+// wait form, per-wave LDS read offsets fixed once): on a SIMD the issue of
+// other instructions adds to the MFMA time rather than hiding under it.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
 
@@ -39,26 +44,28 @@ constexpr int kNStage = 4;
 constexpr int kGroupM = 8;
 constexpr int kStores = 2 * 3 * 3;                 // 16-byte Y stores per wave per tile
 // Transfers per stage: 36 fragment blocks of 1 KiB and 3 scale (or bias)
-// transfers of up to 1 KiB, spread so that each SIMD (waves w and w + 4)
-// issues 9 or 10 of them: wave w moves kFrag(w) fragment blocks starting at
-// kFrag0(w), and waves 2, 3 and 6 one scale transfer each.
-__host__ __device__ constexpr int kFrag(int w) { return (w & 2) ? 4 : 5; }
-__host__ __device__ constexpr int kFrag0(int w) {
-  return w == 0 ? 0 : w == 1 ? 5 : w == 2 ? 10 : w == 3 ? 14 : w == 4 ? 18 : w == 5 ? 23 : w == 6 ? 28 : 32;
+// transfers of 1 KiB (the scale areas of a slot are padded to whole KiB, so
+// every transfer uses all 64 lanes). Every wave issues kOps = 5 per stage:
+// waves 0-2 four of the 12 A blocks and one scale (bias) transfer, waves 3-7
+// five of the 24 B blocks (wave 7 repeats its last block: same bytes to the
+// same place). Each wave reads a single operand.
+constexpr int kOps = 5;
+__host__ __device__ constexpr int kItem(int w, int k) {   // fragment item 0..35 of transfer k of wave w
+  return w < 3 ? 4 * w + k : (12 + 5 * (w - 3) + k < 36 ? 12 + 5 * (w - 3) + k : 35);
 }
-__host__ __device__ constexpr int kScaleOp(int w) { return w == 2 ? 0 : (w == 3 ? 1 : (w == 6 ? 2 : -1)); }
-__host__ __device__ constexpr int kOpsOf(int w) { return kFrag(w) + (kScaleOp(w) >= 0 ? 1 : 0); }
 // one ring slot: A fragments (6 blocks x 2 steps x 1 KiB), B fragments (12 x 2 x 1 KiB),
-// A scale bytes (6 x 128 B), B scale bytes (12 x 128 B)
+// A scale bytes (6 x 128 B, padded to 1 KiB), B scale bytes (12 x 128 B, padded to 2 KiB);
+// low-rank stages carry the bias in the A scale area
 constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 1024;
-constexpr int kScB = kScA + kMB * 128, kSlot = kScB + kNBt * 128;
+constexpr int kScB = kScA + 1024, kSlot = kScB + 2048;
 constexpr size_t kLds = (size_t)kNStage * kSlot;
 static_assert(kTM == 3 && kTN == 3, "schedule below assumes 3 x 3 blocks per wave");
 static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
-static_assert(kFrag0(0) == 0 && kFrag0(1) == 5 && kFrag0(2) == 10 && kFrag0(3) == 14 && kFrag0(4) == 18 &&
-              kFrag0(5) == 23 && kFrag0(6) == 28 && kFrag0(7) == 32 && kFrag0(7) + kFrag(7) == 2 * (kMB + kNBt),
+static_assert((kNStage & (kNStage - 1)) == 0, "ring index is a mask");
+static_assert(kItem(2, 3) == 2 * kMB - 1 && kItem(3, 0) == 2 * kMB && kItem(7, 3) == 2 * (kMB + kNBt) - 1,
               "fragment blocks partition");
-static_assert(kMB * 128 == 768 && kNBt * 128 == 1536 && kBN * 2 == 768, "scale and bias transfer sizes");
+static_assert(kCodeB == 2 * kMB * 1024, "fragment item it sits at it KiB");
+static_assert(kMB * 128 <= 1024 && kNBt * 128 <= 2048 && kBN * 2 <= 1024, "scale and bias transfer sizes");
 
 // Ring barrier: wait until at most n of this wave's vector-memory operations
 // are outstanding, and its LDS reads have returned, then s_barrier. Vector
@@ -67,23 +74,22 @@ static_assert(kMB * 128 == 768 && kNBt * 128 == 1536 && kBN * 2 == 768, "scale a
 // fence would also drain the stages meant to stay in flight); scheduling
 // barriers keep LDS accesses on their side.
 #define SVDQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)   /* expcnt 7, lgkmcnt 0 */
-__device__ __forceinline__ void ring_barrier(int n) {
+// Every ring step issues the transfers of the step three ahead (past the
+// end of the work they repeat the last tile's), so two later steps are
+// always in flight: the wait is for all but 2 kOps of the wave's transfers,
+// plus the last tile's Y stores while they are still counted.
+__device__ __forceinline__ void ring_barrier(bool stores) {
   __builtin_amdgcn_sched_barrier(0);
-  switch (n) {
-    case 4: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(5)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(8)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(10)); break;
-    case 18: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(18)); break;
-    case 22: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(22)); break;
-    case 23: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(23)); break;
-    case 26: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(26)); break;
-    case 28: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(28)); break;
-    default: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
-  }
+  if (stores) __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps + kStores));
+  else __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
+static_assert(2 * kOps + kStores < 64, "vmcnt range");
+
+// Word 3 of the buffer resources: 32-bit data format, no swizzle, no added
+// thread id (untyped loads and stores ignore the rest).
+constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
@@ -101,13 +107,12 @@ struct Geo {
 // Ring-step transfers: direct global->LDS loads of 16 bytes per lane. A
 // fragment block is 1 KiB (both 64-channel steps of a 4-bit stage, or both
 // 16-column steps of Z and L2^T in a low-rank stage). The tile's scale bytes
-// of a stage are contiguous in the stage-major scale layout: 768 A bytes (48
-// lanes) and 1536 B bytes (64 + 32 lanes). In low-rank stages the three
-// scale transfers move the tile's 384 bias values instead (48 lanes; the
-// other two repeat it: same bytes to the same place). The number of
-// transfers of a wave is the same in every stage. The source of every
-// transfer is fixed per tile up to a per-stage offset, so each tile sets the
-// sources once.
+// of a stage are contiguous in the stage-major scale layout: 768 A bytes and
+// 1536 B bytes, moved as three full-wave transfers whose extra lanes read
+// neighbouring (clamped, in-bounds) scale bytes into the padding. In
+// low-rank stages those three transfers move the tile's 384 bias values
+// instead. The source of every transfer is fixed per tile up to a per-stage
+// offset, so each tile sets the sources once.
 }  // namespace
 
 __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g, int grid) {
@@ -118,66 +123,72 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   const int h = lane >> 5, lr = lane & 31;
   const int ntiles = g.tiles_m * g.tiles_n;
   const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / grid + 1 : 0;
-  const int total = my_tiles * g.nstt;   // ring steps of this workgroup
 
-  // issue side: next ring step to load (tile-local index, stage, tile origin)
-  // and this wave's per-tile transfer sources: fragment block k of the wave
-  // from src[k] (4-bit) and src[5 + k] (low-rank); the scale transfer from
-  // ssrc (4-bit) and bsrc (bias)
-  const int nfrag = kFrag(wave), frag0 = kFrag0(wave), sop = kScaleOp(wave);
-  const int nops = kOpsOf(wave);
-  const int slanes = sop == 0 ? 48 : (sop == 1 ? 64 : 32);   // active lanes of the scale transfer
-  int is_t = 0, is_s = 0;
-  const uint8_t* src[10];
-  const uint8_t* ssrc = nullptr;
-  const uint8_t* bsrc = nullptr;
-  int sstride = 0;   // bytes between stages of the scale transfer
+  // issue side: next ring step to load (tile-local index, stage). Transfers
+  // are buffer loads into LDS. Per tile, the rows of the wave's operand that
+  // the tile covers become a buffer resource (rcur: the 4-bit codes; rlow:
+  // the low-rank fragments, which replace them for the low-rank stages), and
+  // transfer k reads at lane offset vcur[k] from it, plus the stage offset
+  // soffs. Waves 0-2 take their scale bytes from a per-tile resource at lane
+  // offset soff plus the stage offset ssoffs (32 bits: the shape check keeps
+  // K * ceil(M / 32) below 2^31), and the bias from the whole vector at lane
+  // offset boff.
+  const bool opA = wave < 3;   // this wave's operand: A (X side) or B (W side)
   const int per_l = a.r32 / 16;
+  int is_t = 0, is_s = 0;
+  __amdgpu_buffer_rsrc_t rcur = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0), rlow = rcur;
+  __amdgpu_buffer_rsrc_t rsc = rcur;    // scale bytes of the tile's first block
+  uint32_t vcur[kOps], vlow[kOps], soffs = 0, ssoffs = 0;   // stage offsets: fragments, scale bytes
+  int sstride = 0, soff = 0, boff = 0;  // scale bytes between stages; lane offsets of the scale and bias transfers
+  const int sdst = wave == 0 ? kScA : kScB + (wave == 2 ? 1024 : 0);   // LDS offset of the scale transfer
 #define SVDQ_ISSUE(GS)                                                                              \
   {                                                                                                 \
     if (is_s == 0) {                                                                                \
-      const TileMap tmi = map_tile((int)blockIdx.x + is_t * grid, g.tiles_m, g.tiles_n, kGroupM);   \
+      const TileMap tmi = map_tile((int)blockIdx.x + min(is_t, my_tiles - 1) * grid, g.tiles_m, g.tiles_n, kGroupM); \
       const int mb0 = tmi.tm * kMB, nb0 = tmi.tn * kNBt;                                            \
-      _Pragma("unroll") for (int k = 0; k < 5; ++k) {                                               \
-        const int it = frag0 + k;                          /* fragment item 0..35 */               \
-        const bool isA = it < 2 * kMB;                                                              \
-        const int blk = isA ? (it >> 1) : ((it - 2 * kMB) >> 1);                                     \
-        const size_t b = (size_t)min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);             \
-        src[k] = (isA ? a.qx : a.qw) + (b * g.KS + (it & 1)) * 1024 + lane * 16;                    \
-        src[5 + k] = reinterpret_cast<const uint8_t*>(isA ? a.z : a.l2t) + (b * per_l + (it & 1)) * 1024 + lane * 16; \
+      const int b0 = opA ? mb0 : nb0, nbl = opA ? min(g.MB - mb0, kMB) : min(g.NB - nb0, kNBt);    \
+      rcur = __builtin_amdgcn_make_buffer_rsrc((void*)((opA ? a.qx : a.qw) + (size_t)b0 * g.KS * 1024), 0, \
+                                               nbl * g.KS * 1024, kRsrcWord3);                      \
+      rlow = __builtin_amdgcn_make_buffer_rsrc((void*)((opA ? a.z : a.l2t) + (size_t)b0 * per_l * 512), 0, \
+                                               nbl * per_l * 1024, kRsrcWord3);                     \
+      _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                            \
+        const int it = kItem(wave, k) - (opA ? 0 : 2 * kMB);   /* item within the operand */       \
+        const int bl = min(it >> 1, nbl - 1);                  /* block within the tile */         \
+        vcur[k] = (uint32_t)((bl * g.KS + (it & 1)) * 1024 + lane * 16);                            \
+        vlow[k] = (uint32_t)((bl * per_l + (it & 1)) * 1024 + lane * 16);                           \
       }                                                                                             \
+      soffs = 0;                                                                                    \
       {                                                                                             \
-        const bool isA = sop == 0;                                                                  \
-        const int blk = (sop == 2 ? 8 : 0) + (lane >> 3);                                           \
-        const int b = min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);                        \
-        ssrc = reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw) + (size_t)b * 128 + (lane & 7) * 16; \
-        sstride = (isA ? g.MB : g.NB) * 128;                                                        \
-        bsrc = reinterpret_cast<const uint8_t*>(a.bias + min(nb0 * 32 + 8 * lane, g.N - 8));        \
+        const bool isA = wave == 0;                                                                 \
+        const int base = isA ? mb0 : nb0, lim = isA ? g.MB : g.NB;                                  \
+        const int blk = (wave == 2 ? 8 : 0) + (lane >> 3);                                          \
+        sstride = lim * 128;                                                                        \
+        rsc = __builtin_amdgcn_make_buffer_rsrc(                                                    \
+            (void*)(reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw) + (size_t)base * 128), 0,    \
+            (g.nst - 1) * sstride + (lim - base) * 128, kRsrcWord3);                                \
+        soff = (min(base + blk, lim - 1) - base) * 128 + (lane & 7) * 16;                           \
+        ssoffs = 0;                                                                                 \
+        boff = min(nb0 * 32 + 8 * lane, g.N - 8) * 2;                                               \
       }                                                                                             \
+    } else if (is_s == g.nst) {                                                                     \
+      rcur = rlow;                                                                                  \
+      _Pragma("unroll") for (int k = 0; k < kOps; ++k) vcur[k] = vlow[k];                           \
+      soffs = 0;                                                                                    \
     }                                                                                               \
-    uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
-    const bool lrs = is_s >= g.nst;                                                                 \
-    const int sl = lrs ? is_s - g.nst : is_s;                                                       \
-    if (lrs && a.r32 == 0) {                                                                        \
-      /* no low-rank fragments: every transfer of the stage moves the bias */                      \
-      _Pragma("unroll") for (int k = 0; k < 6; ++k)                                                 \
-        if (k < nops && lane < 48) __builtin_amdgcn_global_load_lds(bsrc, lds_ptr(slot_w + kScA), 16, 0, 0); \
+    uint8_t* slot_w = smem + ((GS) & (kNStage - 1)) * kSlot;                                              \
+    _Pragma("unroll") for (int k = 0; k < kOps - 1; ++k)                                            \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rcur, lds_ptr(slot_w + kItem(wave, k) * 1024), 16, vcur[k], soffs, 0, 0); \
+    if (!opA) {                                                                                     \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rcur, lds_ptr(slot_w + kItem(wave, kOps - 1) * 1024), 16, \
+                                               vcur[kOps - 1], soffs, 0, 0);                        \
+    } else if (is_s < g.nst) {                                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, lds_ptr(slot_w + sdst), 16, soff, ssoffs, 0, 0); \
+      ssoffs += sstride;                                                                            \
     } else {                                                                                        \
-      _Pragma("unroll") for (int k = 0; k < 5; ++k) {                                               \
-        if (k < nfrag) {                                                                            \
-          const int it = frag0 + k;                                                                 \
-          const int dst = it < 2 * kMB ? kCodeA + it * 1024 : kCodeB + (it - 2 * kMB) * 1024;       \
-          __builtin_amdgcn_global_load_lds(src[(lrs ? 5 : 0) + k] + (size_t)sl * 2048, lds_ptr(slot_w + dst), 16, 0, 0); \
-        }                                                                                           \
-      }                                                                                             \
-      if (sop >= 0 && lane < (lrs ? 48 : slanes)) {                                                 \
-        if (lrs)                                                                                    \
-          __builtin_amdgcn_global_load_lds(bsrc, lds_ptr(slot_w + kScA), 16, 0, 0);                 \
-        else                                                                                        \
-          __builtin_amdgcn_global_load_lds(ssrc + (size_t)sl * sstride,                             \
-                                           lds_ptr(slot_w + (sop == 0 ? kScA : kScB + (sop == 2 ? 1024 : 0))), 16, 0, 0); \
-      }                                                                                             \
+      const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc((void*)a.bias, 0, g.N * 2, kRsrcWord3); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + sdst), 16, boff, 0, 0, 0);   \
     }                                                                                               \
+    soffs += 2048;                                                                                  \
     if (++is_s == g.nstt) {                                                                         \
       is_s = 0;                                                                                     \
       ++is_t;                                                                                       \
@@ -191,9 +202,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
 #define SVDQ_READ(SLOT, STEP, FA, FB)                                                               \
   {                                                                                                 \
     _Pragma("unroll") for (int t = 0; t < kTM; ++t)                                                 \
-        FA[t] = *reinterpret_cast<const i32x4*>((SLOT) + kCodeA + ((wm * kTM + t) * 2 + (STEP)) * 1024 + lane * 16); \
+        FA[t] = *reinterpret_cast<const i32x4*>(smem + rd_a + (SLOT) + (2 * t + (STEP)) * 1024);     \
     _Pragma("unroll") for (int t = 0; t < kTN; ++t)                                                 \
-        FB[t] = *reinterpret_cast<const i32x4*>((SLOT) + kCodeB + ((wn * kTN + t) * 2 + (STEP)) * 1024 + lane * 16); \
+        FB[t] = *reinterpret_cast<const i32x4*>(smem + rd_b + (SLOT) + (2 * t + (STEP)) * 1024);     \
   }
   // MFMAs of one step, weight fragment as operand A and activation fragment as
   // operand B: 4-bit (scaled, opsel = step) or low-rank (bf16)
@@ -211,36 +222,37 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
                                                              __builtin_bit_cast(bf16x8, FA[i]), acc[j][i], 0, 0, 0); \
     }                                                                                               \
   }
-  // One ring step. The deferred second half of the previous step's MFMAs goes
-  // first, so the matrix pipe has work while this step's step-0 fragments
-  // load; the step-1 fragments are read behind the step-0 MFMAs.
-  // Waves 0-3 issue their transfers for ring step gs + 3 before their LDS
-  // reads, waves 4-7 after their step-0 MFMAs, so each SIMD's two waves do
-  // not stall on transfer issue at the same time. `stores_due` counts the
-  // ring steps whose wait must also let the last tile's Y stores stay in
-  // flight.
+  // One ring step. This step's step-0 fragments (and scale bytes) are read
+  // first; the deferred second half of the previous step's MFMAs runs while
+  // they load, then the step-0 MFMAs, with the step-1 fragments read behind
+  // them for the next step's deferred half. Waves 0-3 issue their transfers
+  // for ring step gs + 3 right after the barrier, waves 4-7 after their
+  // step-0 MFMAs, so each SIMD's two waves do not issue at the same time.
+  // `stores_due` counts the ring steps whose wait must also let the last
+  // tile's Y stores stay in flight.
 #define SVDQ_STEP(LOWRANK, LAST, DO_MFMA)                                                           \
   {                                                                                                 \
-    ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));         \
+    ring_barrier(stores_due > 0);                                                                   \
     if (stores_due > 0) --stores_due;                                                               \
+    if (wave < 4) SVDQ_ISSUE(gs + kNStage - 1)                                                      \
+    const uint32_t slot = (gs & (kNStage - 1)) * kSlot;                                                   \
+    if (DO_MFMA) {                                                                                  \
+      if (!(LOWRANK)) {                                                                             \
+        _Pragma("unroll") for (int t = 0; t < kTM; ++t)                                             \
+            sa[t] = *reinterpret_cast<const uint16_t*>(smem + rs_a + slot + t * 128);                \
+        _Pragma("unroll") for (int t = 0; t < kTN; ++t)                                             \
+            sb[t] = *reinterpret_cast<const uint16_t*>(smem + rs_b + slot + t * 128);                \
+      }                                                                                             \
+      SVDQ_READ(slot, 0, f0a, f0b)                                                                  \
+    }                                                                                               \
     if (pending) {                                                                                  \
       SVDQ_MFMA(LOWRANK, 1, f1a, f1b, pa, pb)                                                       \
       pending = false;                                                                              \
     }                                                                                               \
-    const bool more = gs + kNStage - 1 < total;                                                     \
-    if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)                                              \
-    const uint8_t* slot = smem + (gs % kNStage) * kSlot;                                            \
     if (DO_MFMA) {                                                                                  \
-      if (!(LOWRANK)) {                                                                             \
-        _Pragma("unroll") for (int t = 0; t < kTM; ++t)                                             \
-            sa[t] = *reinterpret_cast<const uint16_t*>(slot + kScA + (wm * kTM + t) * 128 + lane * 2); \
-        _Pragma("unroll") for (int t = 0; t < kTN; ++t)                                             \
-            sb[t] = *reinterpret_cast<const uint16_t*>(slot + kScB + (wn * kTN + t) * 128 + lane * 2); \
-      }                                                                                             \
-      SVDQ_READ(slot, 0, f0a, f0b)                                                                  \
       SVDQ_MFMA(LOWRANK, 0, f0a, f0b, sa, sb)                                                       \
-      SVDQ_READ(slot, 1, f1a, f1b)   /* used by the deferred MFMAs: loads behind step 0 */         \
-      if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)                                           \
+      SVDQ_READ(slot, 1, f1a, f1b)                                                                  \
+      if (wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)                                                   \
       _Pragma("unroll") for (int t = 0; t < kTM; ++t) pa[t] = sa[t];                                \
       _Pragma("unroll") for (int t = 0; t < kTN; ++t) pb[t] = sb[t];                                \
       if (LAST) {                                                                                   \
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
       } else {                                                                                      \
         pending = true;                                                                             \
       }                                                                                             \
-    } else if (more && wave >= 4) {                                                                 \
+    } else if (wave >= 4) {                                                                         \
       SVDQ_ISSUE(gs + kNStage - 1)                                                                  \
     }                                                                                               \
     ++gs;                                                                                           \
@@ -257,8 +269,11 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   bool pending = false;   // deferred step-1 MFMAs of the previous ring step
   int gs = 0, stores_due = 0;
   const int nlr = g.nstt - g.nst;
+  // this wave's LDS read offsets within a slot: fragment blocks and scale bytes
+  const uint32_t rd_a = kCodeA + wm * kTM * 2048 + lane * 16, rd_b = kCodeB + wn * kTN * 2048 + lane * 16;
+  const uint32_t rs_a = kScA + wm * kTM * 128 + lane * 2, rs_b = kScB + wn * kTN * 128 + lane * 2;
   // prologue: the first kNStage - 1 ring steps in flight
-  for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
+  for (int p = 0; p < kNStage - 1; ++p) SVDQ_ISSUE(p)
   for (int ct = 0; ct < my_tiles; ++ct) {
     const TileMap tmc = map_tile((int)blockIdx.x + ct * grid, g.tiles_m, g.tiles_n, kGroupM);
     const int n0 = tmc.tn * kBN + wn * kWN;
@@ -275,11 +290,11 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
     // (q = 2, h = 1) between the lane halves leaves lane h with channels
     // 32 j + 8 h + (0..7) and 32 j + 16 + 8 h + (0..7): two 16-byte stores,
     // 32 contiguous bytes of one row per lane pair.
-    const uint8_t* bslot = smem + ((gs - 1) % kNStage) * kSlot + kScA + wn * kWN * 2;
+    const uint8_t* bslot = smem + ((gs - 1) & (kNStage - 1)) * kSlot + kScA + wn * kWN * 2;
     // Y rows of this tile as a buffer resource: stores past its end are dropped
     const int ynrec = min(g.M - tmc.tm * kBM, kBM) * g.N * 2;
     const __amdgpu_buffer_rsrc_t yrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.N, 0, ynrec, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.N, 0, ynrec, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
       float bv[16];
@@ -316,6 +331,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
     }
     stores_due = kNStage - 1;
   }
+  // the transfers issued past the end must land before the workgroup's LDS goes
+  __builtin_amdgcn_s_waitcnt(0);
 #undef SVDQ_STEP
 #undef SVDQ_READ
 #undef SVDQ_MFMA
