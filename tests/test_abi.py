@@ -90,6 +90,17 @@ def test_forward_validation_before_device():
     st = L.svdq_linear_forward(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, 1 << 25,
                                y.ctypes.data, ws.ctypes.data, ws.nbytes, None)
     assert st == 2
+    # MXFP4 activation scales use 32-bit stage offsets: (K + 128) * ceil(M / 32) < 2^31
+    big = S.LayerDesc(65536, 512, 16, 1)
+    for M, want in ((32704 * 32, 4), (32705 * 32, 2), (1 << 20, 2)):
+        st = L.svdq_linear_forward(ctypes.byref(big), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
+                                   ws.ctypes.data, ws.nbytes, None)
+        assert st == want, (M, st)
+    # the same shape in INT4 has no such bound (only the workspace is short)
+    big4 = S.LayerDesc(65536, 512, 16, 0)
+    st = L.svdq_linear_forward(ctypes.byref(big4), ctypes.byref(p), x.ctypes.data, 1 << 20, y.ctypes.data,
+                               ws.ctypes.data, ws.nbytes, None)
+    assert st == 4
     # debug hook: format and window checks
     d4 = S.LayerDesc(512, 512, 16, 1)
     pp = ctypes.byref(p)
