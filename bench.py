@@ -40,16 +40,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def make_workload(spec, rotate, torch, S, synth, seed=0):
+def make_workload(spec, rotate, torch, S, synth, seed=0, packed=None):
     """Pack the layer with the library (randomized SVD) and replicate inputs,
-    outputs, workspaces and packed weights `rotate` times in HBM."""
+    outputs, workspaces and packed weights `rotate` times in HBM. `packed`
+    (layer, host) reuses another layer's packed weights."""
     import numpy as np
     t0 = time.time()
     lay = synth.make_layer(spec)
-    ax = np.abs(lay.x).max(axis=0)
-    layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
-    host = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=seed)
-    log(f"  packed {spec.name} in {time.time() - t0:.1f}s")
+    if packed is None:
+        ax = np.abs(lay.x).max(axis=0)
+        layer = S.Layer(spec.K, spec.N, spec.rank, spec.fmt)
+        host = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=seed)
+        log(f"  packed {spec.name} in {time.time() - t0:.1f}s")
+    else:
+        layer, host = packed
     x0 = torch.from_numpy(lay.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
     sets = []
     wsb = S.workspace_bytes(layer, spec.M)
@@ -169,6 +173,44 @@ def cpu_baseline(layer, host, lay, spec, budget_s):
                        f"pack excluded")
 
 
+def bench_c4(args, torch, S, synth):
+    """Config 4: a FLUX double-stream block's linears at batch 2, 1024^2 (image
+    M=8192, text M=1024) and the decode-like M=64, 256 runs of the same four
+    shapes, which reuse the text stream's packed weights. Per layer: forward
+    time, effective TOPS and, for the weight-bound small-M runs, algorithmic
+    HBM bytes per second against 8 TB/s. Small-M runs rotate 16 weight sets
+    so that the 256 MB MALL cannot hold them."""
+    packs, rows = {}, []
+    steps = max(10, args.steps // 5)
+    for sp in synth.config_layers(4):
+        owner = sp.stream or sp.name
+        rot = 16 if sp.M <= 256 else 2
+        layer, host, _, sets = make_workload(sp, rot, torch, S, synth, packed=packs.get(owner))
+        packs[owner] = (layer, host)
+        ms, _ = time_forward(layer, sets, steps, max(20, args.warmup // 10), torch, S)
+        a1, a2 = time_split(layer, sets, steps, max(20, args.warmup // 10), torch, S)
+        del sets
+        torch.cuda.empty_cache()
+        fl = 2.0 * sp.M * sp.N * sp.K
+        hb = stage1_bytes(sp) + gemm_bytes(sp)
+        t = fl / (ms * 1e-3) / 1e12
+        gbs = hb / (ms * 1e-3) / 1e9
+        rows.append({"workload": sp.name, "M": sp.M, "K": sp.K, "N": sp.N, "rank": sp.rank, "format": sp.fmt,
+                     "us": round(ms * 1e3, 2), "effective_tops": round(t, 2),
+                     "pct_of_int8_peak": round(100 * t / PEAK_TFLOPS["int4"], 2),
+                     "hbm_algorithmic_bytes": hb, "hbm_gbs": round(gbs, 1),
+                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "stage1_us": round(a1 * 1e3, 2), "gemm_us": round(a2 * 1e3, 2)})
+        log(f"c4 {sp.name}: {ms * 1e3:.1f} us, {t:.1f} TOPS, {gbs:.0f} GB/s "
+            f"(stage1 {a1 * 1e3:.1f} us, gemm {a2 * 1e3:.1f} us)")
+    block = [r for r in rows if r["workload"].startswith(("img_", "txt_"))]
+    bus = sum(r["us"] for r in block)
+    bops = sum(2.0 * r["M"] * r["N"] * r["K"] for r in block)
+    return {"workload": "FLUX double-stream block linears, batch 2, 1024^2, INT4 g64, r32",
+            "layers": rows, "block_us": round(bus, 1),
+            "block_effective_tops": round(bops / (bus * 1e-6) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +221,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-c4", action="store_true", help="skip the FLUX block's linears (config 4)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -260,6 +303,8 @@ def main():
                         "stage1_us": round(a1 * 1e3, 2), "gemm_us": round(a2 * 1e3, 2)})
             log(f"{sp.name}: {ms2 * 1e3:.1f} us/step, {t:.1f} TOPS (stage1 {a1*1e3:.1f} us, gemm {a2*1e3:.1f} us)")
         out["secondary"] = sec
+    if not args.no_c4:
+        out["c4"] = bench_c4(args, torch, S, synth)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(layer, host, lay, spec, args.cpu_budget)

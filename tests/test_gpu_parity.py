@@ -57,6 +57,10 @@ SMALL = [
     # INT4 GEMM split: 4 tiles of 24 K stages on 4 XCDs, each cut into four
     # runs of 6 stages (one owner adding three partials)
     _spec("split_k_4_pieces", 256, 3072, 512, 16, "int4", 18),
+    # MXFP4 GEMM: 9 x 32 = 288 tiles, so 32 workgroups run two tiles of three
+    # ring steps; the next tile's bias transfer is issued before the first
+    # tile's epilogue reads its own
+    _spec("two_tiles_k256_fp4", 1728, 256, 12288, 32, "mxfp4", 19),
 ]
 
 
