@@ -89,6 +89,7 @@ Stage1Args stage1_args(const svdq_layer_desc* d, const svdq_packed* dev, const u
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
   a.nflags = int4 ? kSplitSlots : 0;
+  a.zp = (float*)(b + L.zp);
   return a;
 }
 
@@ -142,10 +143,11 @@ svdq_status svdq_stage1(const svdq_layer_desc* d, const svdq_packed* dev, const 
                         int64_t M, void* ws, size_t ws_bytes, void* stream) {
   svdq_status st = common_checks(d, dev, x, M, ws, ws_bytes);
   if (st != SVDQ_OK || M == 0) return st;
-  st = check_device();
+  int cus = 0;
+  st = check_device(&cus);
   if (st != SVDQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  return after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), s), s);
+  return after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), cus, s), s);
 }
 
 svdq_status svdq_linear_forward(const svdq_layer_desc* d, const svdq_packed* dev,
@@ -159,7 +161,7 @@ svdq_status svdq_linear_forward(const svdq_layer_desc* d, const svdq_packed* dev
   st = check_device(&cus);
   if (st != SVDQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  st = after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), s), s);
+  st = after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), cus, s), s);
   if (st != SVDQ_OK) return st;
   return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), cus, s), s);
 }

@@ -20,8 +20,11 @@ struct Stage1Args {
   uint16_t* z;
   uint32_t* flags;   // INT4 GEMM split flags to clear (nflags of them), or null
   int nflags;
+  float* zp;         // partial Z per token group and K piece (see ws_layout)
 };
-hipError_t launch_stage1(const Stage1Args& a, hipStream_t st);
+// stage 1; with few token groups its K pieces are dealt over the CUs and a
+// second kernel adds the partial Z (num_cus sizes that grid)
+hipError_t launch_stage1(const Stage1Args& a, int num_cus, hipStream_t st);
 hipError_t prepare_stage1();   // one-time per device: kernels' dynamic LDS attribute
 
 struct GemmArgs {

@@ -47,6 +47,14 @@ inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
   return s;
 }
 
+// Stage 1 sums X_hat L1 in K pieces of kPieceSteps steps of 256 channels:
+// each wave quarter's partial of a piece is complete before it is added, in
+// piece order, and the four quarter sums are added last, so a token's Z does
+// not depend on M or on whether a workgroup held the whole token group or
+// pieces of it (then a second kernel adds the stored partials).
+constexpr int kPieceSteps = 4;
+inline int s1_pieces(int K) { return (K / 256 + kPieceSteps - 1) / kPieceSteps; }
+
 // INT4 GEMM split of the last tiles over the workgroups: one flag and one
 // fp32 partial tile (128 x 256) per workgroup, at most kSplitSlots of them.
 constexpr int kSplitSlots = 256;
@@ -55,9 +63,11 @@ constexpr int kSplitPartBytes = 128 * 256 * 4;
 // Workspace: [qX][sX][Z], each 256-byte aligned, over round32(M) rows. qX and
 // Z in fragment order (see below) for both formats; sX fp32 [K/64][act_rows(M)]
 // (INT4) or E8M0 bytes in fragment order (MXFP4). INT4 adds the split's flags
-// (u32 [kSplitSlots], cleared by stage 1) and partial tiles.
+// (u32 [kSplitSlots], cleared by stage 1) and partial tiles. Last, with a
+// low-rank branch, stage 1's partial Z: fp32, per token group and piece the
+// raw MFMA accumulators of its waves, round32(M) x s1_pieces(K) x 4 x rank32.
 struct WsLayout {
-  size_t qx, sx, z, flags, part, total;
+  size_t qx, sx, z, flags, part, zp, total;
 };
 inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   WsLayout w;
@@ -68,7 +78,8 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
   w.flags = w.z + align256((size_t)rows * rank32(d->rank) * 2);
   w.part = w.flags + (int4 ? align256((size_t)kSplitSlots * 4) : 0);
-  w.total = w.part + (int4 ? (size_t)kSplitSlots * kSplitPartBytes : 0);
+  w.zp = w.part + (int4 ? (size_t)kSplitSlots * kSplitPartBytes : 0);
+  w.total = w.zp + (size_t)s1_pieces(d->K) * rows * 4 * rank32(d->rank) * 4;
   return w;
 }
 

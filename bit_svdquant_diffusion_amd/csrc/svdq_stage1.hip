@@ -34,6 +34,7 @@
 // and stored as bf16.
 #include "svdq_device.h"
 #include "svdq_internal.h"
+#include "svdq_layout.h"
 
 namespace svdq {
 
@@ -112,68 +113,104 @@ __device__ __forceinline__ uint32_t s1_e2m1x8(const float* v, int e) {
 template <int FMT, int NCB, int TH>
 __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
-    uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, int M, int K,
-    uint32_t* __restrict__ flags, int nflags) {
+    uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, float* __restrict__ zp, int M,
+    int K, uint32_t* __restrict__ flags, int nflags, int npieces, int grid, int split) {
   using Cfg = S1Cfg<NCB, TH>;
   constexpr int D = Cfg::kDepth;
   constexpr int r32 = NCB * 16;
   constexpr int FPW = Cfg::kL1PerWave;
+  constexpr int TG = S1_ROWS * TH;   // tokens per group
+  constexpr int NT = 64 * S1_WAVES * TH;
+  static_assert(NCB == 0 || TH * S1_WAVES * NCB * 4 * 64 * 4 <= Cfg::kSlot, "Z reduction fits a ring slot");
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = wave & 3, th = wave >> 2;   // quarter and token half
-  const int m0 = blockIdx.x * S1_ROWS * TH + th * S1_ROWS;
   const int nsteps = K / S1_STEP;
+  const int npc = (nsteps + kPieceSteps - 1) / kPieceSteps;   // K pieces per token group
   const int Mp = (M + 15) / 16 * 16;   // row stride of the INT4 scales
   const int MB = (M + 31) / 32;        // 32-row blocks (MXFP4 fragment order)
 
   // the INT4 GEMM that follows on the stream expects its split flags clear
   if (blockIdx.x == 0)
-    for (int f = threadIdx.x; f < nflags; f += 64 * S1_WAVES * TH) flags[f] = 0u;
+    for (int f = threadIdx.x; f < nflags; f += NT) flags[f] = 0u;
 
   const int r = lane & 15, j = lane >> 4;
-  // token of this lane; a lane past M holds token M - 1's values (its X rows
-  // are clamped below) and stores them again, so every store always issues
-  const int m = min(m0 + r, M - 1);
-
   // X transfer d (0, 1) of this lane: 16-byte unit u = 64 d + lane of the
   // quarter, token u / 8, chunk (u % 8) ^ ((token / 2) % 8)
   const int tA = lane >> 3, tB = 8 + (lane >> 3);
-  const uint16_t* srcA = x + (size_t)min(m0 + tA, M - 1) * K + q * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
-  const uint16_t* srcB = x + (size_t)min(m0 + tB, M - 1) * K + q * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
   // read-back of chunks 2j, 2j+1 of token r
   const int rd0 = (r * 8 + ((2 * j) ^ ((r >> 1) & 7))) * 16;
   const int rd1 = (r * 8 + ((2 * j + 1) ^ ((r >> 1) & 7))) * 16;
 
-  f32x4 zacc[NCB > 0 ? NCB : 1];
-#pragma unroll
-  for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
+  // This workgroup's pieces (token group g = p / npc, K piece p % npc) and
+  // the steps they hold, walked as one sequence. Without `split` the grid is
+  // one workgroup per group and holds all its pieces.
+  const int pb = (int)((int64_t)npieces * blockIdx.x / grid), pe = (int)((int64_t)npieces * (blockIdx.x + 1) / grid);
+  int T = 0;
+  for (int p = pb; p < pe; ++p) T += min(kPieceSteps, nsteps - (p % npc) * kPieceSteps);
 
-  // ring transfers of step I; past the last step they re-read the first
-  // bytes of X and mu into the slot, so every step issues the same number
-#define S1_ISSUE(I)                                                                                \
+  // issue cursor: piece ip, step is (absolute), its end, and the lane's X rows
+  int ip = pb, is = 0, iend = 0, iu = 0;
+  const uint16_t* srcA = x;
+  const uint16_t* srcB = x;
+  auto issue_piece = [&]() {
+    const int g = ip / npc;
+    is = (ip - g * npc) * kPieceSteps;
+    iend = min(is + kPieceSteps, nsteps);
+    const int m0 = g * TG + th * S1_ROWS;
+    srcA = x + (size_t)min(m0 + tA, M - 1) * K + q * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
+    srcB = x + (size_t)min(m0 + tB, M - 1) * K + q * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
+  };
+  issue_piece();
+  // compute cursor: piece cp, step cs, its end; the lane's token m (a lane
+  // past M holds token M - 1's values, its X rows being clamped, and stores
+  // them again, so every store always issues)
+  int cp = pb, cs = 0, cend = 0, cg = 0, cc = 0, m = 0;
+  f32x4 zacc[NCB > 0 ? NCB : 1];   // this piece's partial Z of the wave's quarter
+  f32x4 zrun[NCB > 0 ? NCB : 1];   // the sum over the group's pieces so far (whole-group mode)
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) zrun[c] = f32x4{};
+  auto compute_piece = [&]() {
+    cg = cp / npc;
+    cc = cp - cg * npc;
+    cs = cc * kPieceSteps;
+    cend = min(cs + kPieceSteps, nsteps);
+    m = min(cg * TG + th * S1_ROWS + r, M - 1);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
+  };
+  compute_piece();
+
+  // ring transfers of the next step of the issue cursor; past the last step
+  // they re-read the first bytes of X and mu into the slot, so every step
+  // issues the same number
+#define S1_ISSUE()                                                                                 \
   {                                                                                                \
-    const bool real_ = (I) < nsteps;                                                               \
-    const size_t xo_ = real_ ? (size_t)(I) * S1_STEP : 0;                                          \
-    uint8_t* slot_ = smem + ((I) % (D + 1)) * Cfg::kSlot;                                          \
+    const bool real_ = iu < T;                                                                     \
+    const size_t xo_ = real_ ? (size_t)is * S1_STEP : 0;                                           \
+    uint8_t* slot_ = smem + (iu % (D + 1)) * Cfg::kSlot;                                           \
     __builtin_amdgcn_global_load_lds(real_ ? srcA + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ), 16, 0, 0);        \
     __builtin_amdgcn_global_load_lds(real_ ? srcB + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ + 1024), 16, 0, 0); \
     __builtin_amdgcn_global_load_lds(real_ ? mu + xo_ + q * 64 + lane : mu,                        \
                                      (s1_lds_void*)(slot_ + Cfg::kMu + q * 256), 4, 0, 0);          \
     _Pragma("unroll") for (int f_ = th * FPW; f_ < (th + 1) * FPW; ++f_)                           \
       __builtin_amdgcn_global_load_lds(                                                            \
-          l1s + (real_ ? ((((size_t)(I) * S1_WAVES + q) * NCB * 2 + f_) * 64 + lane) * 8 : (size_t)lane * 8), \
+          l1s + (real_ ? ((((size_t)is * S1_WAVES + q) * NCB * 2 + f_) * 64 + lane) * 8 : (size_t)lane * 8), \
           (s1_lds_void*)(slot_ + Cfg::kL1 + (q * 2 * NCB + f_) * 1024), 16, 0, 0);                 \
+    if (real_ && ++is == iend && ++ip < pe) issue_piece();                                         \
+    ++iu;                                                                                          \
   }
 #define S1_WAIT_CASE(k)                                                                            \
   case k: __builtin_amdgcn_s_waitcnt(S1_VMCNT(Cfg::count(k < D ? k : D))); break;
 
 #pragma unroll
-  for (int d = 0; d < D; ++d) S1_ISSUE(d)
+  for (int d = 0; d < D; ++d) S1_ISSUE()
 
-  for (int i = 0; i < nsteps; ++i) {
+  for (int i = 0; i < T; ++i) {
         // 1. step i's transfers have landed once only the operations issued
-        //    after them are outstanding
+        //    after them are outstanding (a finished piece's partial-Z stores
+        //    only add to those: the wait gets longer, never shorter)
         __builtin_amdgcn_sched_barrier(0);
         switch (i < D ? i : D) {
           S1_WAIT_CASE(0) S1_WAIT_CASE(1) S1_WAIT_CASE(2) S1_WAIT_CASE(3)
@@ -185,7 +222,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
         // slot that the transfers below refill
         if constexpr (TH > 1) __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        const uint8_t* slot = smem + (i % (D + 1)) * Cfg::kSlot;
+        uint8_t* slot = smem + (i % (D + 1)) * Cfg::kSlot;
         u32x4 l1v[NCB > 0 ? 2 * NCB : 1];
 #pragma unroll
         for (int f = 0; f < 2 * NCB; ++f)
@@ -199,7 +236,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
         // the slot of step i + D is the one read at step i - 1: its reads are
         // complete (they were waited on before their use)
         __builtin_amdgcn_sched_barrier(0);
-        S1_ISSUE(i + D)
+        S1_ISSUE()
         __builtin_amdgcn_sched_barrier(0);
         float xh[16];
 #pragma unroll
@@ -212,7 +249,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
           xh[4 * t + 2] = bf16lo(w1) * mv.z;
           xh[4 * t + 3] = bf16hi(w1) * mv.w;
         }
-        const int k0 = i * S1_STEP + q * 64;   // first channel of the quarter
+        const int k0 = cs * S1_STEP + q * 64;   // first channel of the quarter
 
         // 3. Z += bf16(x_hat) L1: MFMA t takes channels 16j + 8t .. +7 of each lane
         if constexpr (NCB > 0) {
@@ -289,6 +326,23 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
           *reinterpret_cast<u32x2*>(blk + (32 * (j >> 1) + m % 32) * 16 + (j & 1) * 8) = u32x2{c0, c1};
         }
 
+
+        // 5. end of a piece: add the wave's partial Z to the group's running
+        //    sum, or store it (raw accumulators) for the piece-sum kernel
+        if (++cs == cend) {
+          if constexpr (NCB > 0) {
+            if (split) {
+              f32x4* dst = reinterpret_cast<f32x4*>(zp) + ((size_t)cp * (S1_WAVES * TH) + wave) * NCB * 64 + lane;
+#pragma unroll
+              for (int c = 0; c < NCB; ++c) dst[c * 64] = zacc[c];
+            } else {
+#pragma unroll
+              for (int c = 0; c < NCB; ++c) zrun[c] = cc == 0 ? zacc[c] : zrun[c] + zacc[c];
+            }
+          }
+          ++cp;
+          if (cp < pe) compute_piece();
+        }
   }
 #undef S1_ISSUE
 #undef S1_WAIT_CASE
@@ -296,45 +350,82 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   __builtin_amdgcn_s_waitcnt(S1_VMCNT(0));
 
   if constexpr (NCB > 0) {
-    // reduce the four partial Z tiles in wave order and store bf16
+    if (split) return;
+    // whole-group mode: add the four quarters' sums in wave order and store bf16
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[((wave * NCB + c) * 4 + e) * 64 + lane] = zacc[c][e];
+      for (int e = 0; e < 4; ++e) red[((wave * NCB + c) * 4 + e) * 64 + lane] = zrun[c][e];
     }
     __syncthreads();
     constexpr int per = NCB * 4 * 64;   // one wave's partial tile
-    for (int idx = threadIdx.x; idx < TH * per; idx += 64 * S1_WAVES * TH) {
+    for (int idx = threadIdx.x; idx < TH * per; idx += NT) {
       const int h = idx / per, rem = idx - h * per;
       float acc = 0.f;
       for (int w = 0; w < S1_WAVES; ++w) acc += red[(h * S1_WAVES + w) * per + rem];
       // 16x16 result layout: lane l, reg e -> row 4(l/16) + e, column l%16
       const int l = rem & 63, e = (rem >> 6) & 3, c = rem >> 8;
-      const int row = blockIdx.x * S1_ROWS * TH + h * S1_ROWS + 4 * (l >> 4) + e;
+      const int row = cg * TG + h * S1_ROWS + 4 * (l >> 4) + e;
       const int col = 16 * c + (l & 15);
       if (row < M)   // fragment order: (row block, 16-column step, lane 32h + row%32, element)
-        z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) +
-          col % 8] = (uint16_t)f2bf(acc);
+        z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) + col % 8] =
+            (uint16_t)f2bf(acc);
     }
   }
+}
+
+// Z = bf16 of the sum, over the four quarters in wave order, of each
+// quarter's sum over the K pieces in piece order (the whole-group path's
+// additions, in its order), stored in fragment order: (row block, 16-column
+// step, lane 32h + row%32, element). zp holds, per token group and piece,
+// each wave's raw accumulators [wave][16-column block][lane][4].
+__global__ __launch_bounds__(256) void zsum_kernel(const float* __restrict__ zp, uint16_t* __restrict__ z, int M,
+                                                   int r32, int npc, int th_n) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * r32) return;
+  const int row = (int)(idx / r32), col = (int)(idx - (int64_t)row * r32);
+  const int tg = S1_ROWS * th_n, ncb = r32 / 16;
+  const int g = row / tg, h = (row % tg) / S1_ROWS, rr = row % S1_ROWS;
+  const int n = col / 16, l = (rr / 4) * 16 + col % 16, e = rr % 4;
+  float acc = 0.f;
+  for (int qq = 0; qq < S1_WAVES; ++qq) {
+    const int w = h * S1_WAVES + qq;
+    const size_t base = ((size_t)(g * npc) * (S1_WAVES * th_n) + w) * ncb * 256 + ((size_t)n * 64 + l) * 4 + e;
+    const size_t pstride = (size_t)(S1_WAVES * th_n) * ncb * 256;   // next piece of the group
+    float sum = zp[base];
+    for (int c = 1; c < npc; ++c) sum += zp[base + c * pstride];
+    acc += sum;
+  }
+  z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) + col % 8] =
+      (uint16_t)f2bf(acc);
 }
 
 template <int FMT, int NCB, int TH>
 static size_t lds_bytes() {
   using Cfg = S1Cfg<NCB, TH>;
-  const size_t ring = (size_t)(Cfg::kDepth + 1) * Cfg::kSlot;
-  const size_t red = (size_t)TH * S1_WAVES * NCB * 4 * 64 * 4;
-  return ring > red ? ring : red;
+  return (size_t)(Cfg::kDepth + 1) * Cfg::kSlot;
 }
 
+// With at least half as many token groups as CUs, one workgroup per group
+// walks all of K. With fewer, the groups' K pieces are dealt over the CUs
+// (each CU then streams fewer steps) and a second kernel adds the partials.
 template <int FMT, int NCB, int TH>
-static hipError_t launch_t(const Stage1Args& a, hipStream_t st) {
-  dim3 grid((a.M + S1_ROWS * TH - 1) / (S1_ROWS * TH));
+static hipError_t launch_t(const Stage1Args& a, int num_cus, hipStream_t st) {
+  constexpr int TG = S1_ROWS * TH;
+  const int groups = (a.M + TG - 1) / TG, npc = s1_pieces(a.K);
+  const int cus = num_cus > 0 ? num_cus : 256;
   const size_t lds = lds_bytes<FMT, NCB, TH>();
-  hipLaunchKernelGGL((stage1_kernel<FMT, NCB, TH>), grid, dim3(64 * S1_WAVES * TH), lds, st,
-                     a.x, a.mu, a.l1s, a.qx, a.sx, a.z, a.M, a.K, a.flags, a.nflags);
+  const int per_cu = lds <= 80 * 1024 ? 2 : 1;   // workgroups that fit one CU's LDS
+  const bool split = NCB > 0 && npc > 1 && 2 * groups < cus;
+  const int grid = split ? min(groups * npc, cus * per_cu) : groups;
+  hipLaunchKernelGGL((stage1_kernel<FMT, NCB, TH>), dim3(grid), dim3(64 * S1_WAVES * TH), lds, st, a.x, a.mu,
+                     a.l1s, a.qx, a.sx, a.z, a.zp, a.M, a.K, a.flags, a.nflags, groups * npc, grid, split ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  hipLaunchKernelGGL(zsum_kernel, dim3((unsigned)(((int64_t)a.M * a.r32 + 255) / 256)), dim3(256), 0, st, a.zp,
+                     a.z, a.M, a.r32, npc, TH);
   return hipGetLastError();
 }
 
@@ -345,14 +436,14 @@ static hipError_t launch_t(const Stage1Args& a, hipStream_t st) {
 constexpr int kTwoHalvesMinM[2] = {8192, 2048};   // INT4, MXFP4
 
 template <int FMT>
-static hipError_t launch_fmt(const Stage1Args& a, hipStream_t st) {
+static hipError_t launch_fmt(const Stage1Args& a, int cus, hipStream_t st) {
   const bool two = a.M >= kTwoHalvesMinM[FMT == SVDQ_FMT_MXFP4_G32 ? 1 : 0];
   switch (a.r32) {
-    case 0: return two ? launch_t<FMT, 0, 2>(a, st) : launch_t<FMT, 0, 1>(a, st);
-    case 32: return two ? launch_t<FMT, 2, 2>(a, st) : launch_t<FMT, 2, 1>(a, st);
-    case 64: return two ? launch_t<FMT, 4, 2>(a, st) : launch_t<FMT, 4, 1>(a, st);
-    case 96: return launch_t<FMT, 6, 1>(a, st);
-    case 128: return launch_t<FMT, 8, 1>(a, st);
+    case 0: return two ? launch_t<FMT, 0, 2>(a, cus, st) : launch_t<FMT, 0, 1>(a, cus, st);
+    case 32: return two ? launch_t<FMT, 2, 2>(a, cus, st) : launch_t<FMT, 2, 1>(a, cus, st);
+    case 64: return two ? launch_t<FMT, 4, 2>(a, cus, st) : launch_t<FMT, 4, 1>(a, cus, st);
+    case 96: return launch_t<FMT, 6, 1>(a, cus, st);
+    case 128: return launch_t<FMT, 8, 1>(a, cus, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -378,10 +469,10 @@ hipError_t prepare_stage1() {
   return e != hipSuccess ? e : prepare_fmt<SVDQ_FMT_MXFP4_G32>();
 }
 
-hipError_t launch_stage1(const Stage1Args& a, hipStream_t st) {
+hipError_t launch_stage1(const Stage1Args& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (a.fmt == SVDQ_FMT_INT4_G64) return launch_fmt<SVDQ_FMT_INT4_G64>(a, st);
-  return launch_fmt<SVDQ_FMT_MXFP4_G32>(a, st);
+  if (a.fmt == SVDQ_FMT_INT4_G64) return launch_fmt<SVDQ_FMT_INT4_G64>(a, num_cus, st);
+  return launch_fmt<SVDQ_FMT_MXFP4_G32>(a, num_cus, st);
 }
 
 }  // namespace svdq
