@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libsvdq.so")
 
-HIP_SOURCES = ["svdq_stage1.hip", "svdq_gemm_int4.hip", "svdq_gemm_mxfp4.hip", "svdq_api.hip"]
+HIP_SOURCES = ["svdq_stage1.hip", "svdq_gemm_int4.hip", "svdq_gemm_int4_small.hip", "svdq_gemm_mxfp4.hip", "svdq_api.hip"]
 CPP_SOURCES = ["svdq_pack.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

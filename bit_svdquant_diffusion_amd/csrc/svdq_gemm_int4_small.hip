@@ -1,0 +1,253 @@
+// Kernel (2) for INT4 layers with few tokens (M <= 256): the same sums as
+// the tiled INT4 GEMM -- per 64-channel group the exact int32 sum P of code
+// products, dequantized by s_w[n] s_x[m] and accumulated in fp32 in group
+// order, then (X_hat L1) L2 and the bias before the bf16 write of Y
+// (aiflownews.com, "What SVDQuant actually does": the two-branch computation;
+// "Nunchaku: the inference engine...": the branches share the output write).
+//
+// With few tokens the layer is bound by reading the 4-bit weights once
+// (pages: inference is memory-bound). So every CU streams its own slice of
+// the weights straight into registers: a workgroup owns one 32-channel block
+// of W and the four waves split its K range (or, with few channel blocks,
+// a share of it, the workgroups of a block then leaving fp32 partials that a
+// second kernel adds in order). The activation codes (M x K/2 bytes) are
+// small and read by every workgroup from L2.
+//
+// Per 64-channel group and 32-token block a wave runs two
+// v_mfma_i32_32x32x32_i8 on nibbles widened to 16 q (256 P exactly) and one
+// two-block v_mfma_f32_32x32x1f32 for the scale outer product
+// s_w[n] * s_x[m] / 256; the four waves' sums are added in wave order.
+#include "svdq_device.h"
+#include "svdq_internal.h"
+#include "svdq_layout.h"
+
+namespace svdq {
+
+namespace {
+constexpr int kSW = 4;   // waves per workgroup
+// groups loaded ahead of the one being multiplied (fewer with more token blocks: registers)
+__host__ __device__ constexpr int kPD(int mb) { return mb <= 2 ? 4 : (mb <= 4 ? 2 : 1); }
+
+typedef __bf16 sm_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t sm_cvt_bf16x2(float lo, float hi) {
+  sm_bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// int8 operands of one 32-channel half of a group: 16*q of the even channels
+// (lo) and of the odd channels (hi) of a 16-byte fragment
+__device__ __forceinline__ void sm_widen(const i32x4& w, i32x4& lo, i32x4& hi) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    lo[d] = (int)(((uint32_t)w[d] << 4) & 0xF0F0F0F0u);
+    hi[d] = (int)((uint32_t)w[d] & 0xF0F0F0F0u);
+  }
+}
+
+// Accumulator lane layout (32 x 32 block, channels as rows, tokens as
+// columns): lane l, register e -> channel 8 (e / 4) + 4 (l / 32) + e % 4,
+// token l % 32. bf16 out: after the lane-half swap of the packed pairs
+// (q = 1, h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <-> (q = 2, h = 1),
+// lane h holds channels 8 h + (0..7) and 16 + 8 h + (0..7) of its token.
+__device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int M, int N, int n0, int m, int h) {
+  uint32_t o[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) o[p] = sm_cvt_bf16x2(v[2 * p], v[2 * p + 1]);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
+      o[4 * p + w] = r[0];
+      o[4 * p + 2 + w] = r[1];
+    }
+  }
+  if (m < M) {
+    u32x4* dst = reinterpret_cast<u32x4*>(y + (size_t)m * N + n0 + 8 * h);
+    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    dst[2] = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+}  // namespace
+
+// Workgroup b: channel block nb = b / splits, K share sp = b % splits; wave w
+// takes groups [g0, g1) of that share. part (splits > 1): raw accumulators
+// [sp][token block][channel block][64 lanes][16].
+template <int MB>
+__global__ __launch_bounds__(64 * kSW) void gemm_int4_small_kernel(GemmArgs a, int splits, float* part) {
+  __shared__ __align__(16) float red[kSW][MB][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, lr = lane & 31;
+  const int KS = a.K / 64, N = a.N, NB = N / 32;
+  const int nb = blockIdx.x / splits, sp = blockIdx.x - nb * splits;
+  const int s0 = (int)((int64_t)KS * sp / splits), s1 = (int)((int64_t)KS * (sp + 1) / splits);
+  const int g0 = s0 + (s1 - s0) * wave / kSW, g1 = s0 + (s1 - s0) * (wave + 1) / kSW;
+  const int act_rows = (a.M + 15) / 16 * 16;   // row stride of s_x
+
+  // Sources as buffer resources (no per-load address arithmetic): fragment
+  // block (row block b, group g) at ((b * KS + g) * 64 + lane) * 16 bytes,
+  // the group offset as the scalar offset; s_w [K/64][N], s_x [K/64][act_rows]
+  // fp32. The activation blocks are clamped to the tokens' rows.
+  const int MBa = (a.M + 31) / 32;
+  const __amdgpu_buffer_rsrc_t rqw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.qw + (size_t)nb * KS * 1024), 0, KS * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rqx = __builtin_amdgcn_make_buffer_rsrc((void*)a.qx, 0, MBa * KS * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)a.sw + nb * 32), 0, (KS - 1) * N * 4 + 128, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)a.sx, 0, KS * act_rows * 4, 0x00020000);
+  int sxo[(MB + 1) / 2];   // the lane's token row for each pair of token blocks (clamped to M - 1), bytes
+#pragma unroll
+  for (int p = 0; p < (MB + 1) / 2; ++p) sxo[p] = min((2 * p + h) * 32 + lr, a.M - 1) * 4;
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = f32x16{};
+
+  // PD + 1 groups of operands in registers: loads run PD groups ahead
+  constexpr int PD = kPD(MB), NP = (MB + 1) / 2;
+  i32x4 fb[PD + 1], fa[PD + 1][MB];
+  float fw[PD + 1], fx[PD + 1][NP];
+  auto load = [&](int slot, int g) {
+    const int gg = min(g, g1 - 1);   // past the end: repeat the last group (unused)
+    fb[slot] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rqw, lane * 16, gg * 1024, 0));
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+      fa[slot][b] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rqx, lane * 16, (b * KS + gg) * 1024, 0));
+    fw[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsw, lr * 4, gg * N * 4, 0));
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      fx[slot][p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsx, sxo[p], gg * act_rows * 4, 0)) *
+                    (1.0f / 256.0f);
+  };
+  if (g0 < g1) {
+#pragma unroll
+    for (int d = 0; d < PD; ++d) load(d, g0 + d);
+    // slot u holds group g + u; each step refills the slot just used with
+    // the group PD + 1 later. The last round runs whole: a group past the end
+    // repeats the last one with its token scales zeroed, so it adds exact zeros.
+    for (int g = g0; g < g1; g += PD + 1) {
+#pragma unroll
+      for (int u = 0; u <= PD; ++u) {
+        {
+          load((u + PD) % (PD + 1), g + u + PD);
+          const float live = g + u < g1 ? 1.0f : 0.0f;
+          i32x4 blo, bhi;
+          sm_widen(fb[u], blo, bhi);
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            // token block b = 2 p + lane / 32 of the pair takes the 32 channel
+            // scales and its 32 token scales: output block b in registers
+            // 16 (b - 2 p) .. + 15
+            const f32x32 r = __builtin_amdgcn_mfma_f32_32x32x1f32(fw[u], fx[u][p] * live, f32x32{}, 0, 0, 0);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+              const int b = 2 * p + bb;
+              if (b < MB) {
+                i32x4 alo, ahi;
+                sm_widen(fa[u][b], alo, ahi);
+                i32x16 pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo, alo, i32x16{}, 0, 0, 0);
+                pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi, ahi, pp, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[b][e] = __builtin_fmaf((float)pp[e], r[16 * bb + e], acc[b][e]);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // the four waves' sums, added in wave order
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wave][b][e][lane] = acc[b][e];
+  }
+  __syncthreads();
+  const int r32 = a.r32;
+  for (int b = wave; b < MB; b += kSW) {
+    f32x16 v;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSW; ++w) s += red[w][b][e][lane];
+      v[e] = s;
+    }
+    if (sp == 0) {
+      // + (X_hat L1) L2 on bf16 MFMA (Z and L2^T in 16-column fragment order) + bias
+      const i32x4* zf = reinterpret_cast<const i32x4*>(a.z) + (size_t)b * (r32 / 16) * 64 + lane;
+      const i32x4* lf = reinterpret_cast<const i32x4*>(a.l2t) + (size_t)nb * (r32 / 16) * 64 + lane;
+      for (int st = 0; st < r32 / 16; ++st)
+        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lf[st * 64]),
+                                                    __builtin_bit_cast(bf16x8, zf[st * 64]), v, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 bw = *reinterpret_cast<const u32x2*>(a.bias + nb * 32 + 8 * q + 4 * h);
+        v[4 * q + 0] += bf16lo(bw.x);
+        v[4 * q + 1] += bf16hi(bw.x);
+        v[4 * q + 2] += bf16lo(bw.y);
+        v[4 * q + 3] += bf16hi(bw.y);
+      }
+    }
+    if (splits == 1) {
+      sm_store_block(v, a.y, a.M, a.N, nb * 32, b * 32 + lr, h);
+    } else {
+      f32x4* dst = reinterpret_cast<f32x4*>(part) + ((((size_t)sp * MB + b) * NB + nb) * 64 + lane) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c] = f32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+    }
+  }
+}
+
+// Y = bf16 of the K shares' partials added in share order; one wave per
+// (token block, channel block).
+__global__ __launch_bounds__(64) void gemm_int4_small_sum(const float* __restrict__ part, uint16_t* __restrict__ y,
+                                                        int M, int N, int MB, int splits) {
+  const int lane = threadIdx.x, h = lane >> 5, lr = lane & 31;
+  const int NB = N / 32, b = blockIdx.x / NB, nb = blockIdx.x - b * NB;
+  f32x16 v = f32x16{};
+  for (int sp = 0; sp < splits; ++sp) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(part) + ((((size_t)sp * MB + b) * NB + nb) * 64 + lane) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 w = src[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * c + e] = sp == 0 ? w[e] : v[4 * c + e] + w[e];
+    }
+  }
+  sm_store_block(v, y, M, N, nb * 32, b * 32 + lr, h);
+}
+
+bool gemm_int4_small_fits(const GemmArgs& a) { return a.M <= 256 && a.p == nullptr; }
+
+template <int MB>
+static hipError_t launch_mb(const GemmArgs& a, int num_cus, hipStream_t st) {
+  const int KS = a.K / 64, NB = a.N / 32;
+  // enough workgroups for every CU, each wave keeping at least one group
+  const int cus = num_cus > 0 ? num_cus : 256;
+  int splits = max(1, min(KS / kSW, (cus + NB - 1) / NB));
+  const size_t per_split = (size_t)MB * 32 * a.N * 4;   // fp32 partial bytes of one share
+  while (splits > 1 && (size_t)splits * per_split > (size_t)kSplitSlots * kSplitPartBytes) --splits;
+  hipLaunchKernelGGL((gemm_int4_small_kernel<MB>), dim3(NB * splits), dim3(64 * kSW), 0, st, a, splits, a.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(gemm_int4_small_sum, dim3(MB * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, MB, splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_int4_small(const GemmArgs& a, int num_cus, hipStream_t st) {
+  switch ((a.M + 31) / 32) {   // exact token blocks: no read past the round32(M) rows
+    case 1: return launch_mb<1>(a, num_cus, st);
+    case 2: return launch_mb<2>(a, num_cus, st);
+    case 3: return launch_mb<3>(a, num_cus, st);
+    case 4: return launch_mb<4>(a, num_cus, st);
+    case 5: return launch_mb<5>(a, num_cus, st);
+    case 6: return launch_mb<6>(a, num_cus, st);
+    case 7: return launch_mb<7>(a, num_cus, st);
+    default: return launch_mb<8>(a, num_cus, st);
+  }
+}
+
+}  // namespace svdq

@@ -54,9 +54,12 @@ SMALL = [
     _spec("two_halves_m8194", 8194, 256, 64, 32, "int4", 16),
     _spec("two_halves_m2066_fp4", 2066, 512, 256, 32, "mxfp4", 16),
     _spec("two_halves_m2100_r48_fp4", 2100, 256, 96, 48, "mxfp4", 17),
-    # INT4 GEMM split: 4 tiles of 24 K stages on 4 XCDs, each cut into four
+    # INT4 GEMM split: 6 tiles of 24 K stages on 6 XCDs, each cut into four
     # runs of 6 stages (one owner adding three partials)
-    _spec("split_k_4_pieces", 256, 3072, 512, 16, "int4", 18),
+    _spec("split_k_4_pieces", 384, 3072, 512, 16, "int4", 18),
+    # INT4 with few tokens (weight-streaming kernel): 3 token blocks, the
+    # channel blocks' K cut into shares whose partials a second kernel adds
+    _spec("small_m70_shares", 70, 3072, 3072, 32, "int4", 20),
     # MXFP4 GEMM: 9 x 32 = 288 tiles, so 32 workgroups run two tiles of three
     # ring steps; the next tile's bias transfer is issued before the first
     # tile's epilogue reads its own
@@ -156,15 +159,21 @@ def test_split_tiles_deterministic():
         assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
 
 
-def test_rows_are_independent():
-    """A row's output does not depend on the other rows in the batch (ragged tiles)."""
-    spec = _spec("indep", 300, 768, 544, 32, "int4", 11)
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_rows_are_independent(fmt):
+    """Rows past M in a ragged last tile or token block do not leak into the
+    real rows: dropping trailing rows leaves the others' bits unchanged, for
+    the tiled GEMMs (M = 300 vs 299 and 290) and the INT4 few-token kernel
+    (M = 60 vs 43)."""
+    spec = _spec("indep", 300, 768, 544, 32, fmt, 11)
     layer, dev = C.device_layer(spec)
     x = C.x_device(spec)
     full = S.linear_forward(layer, dev, x)
-    part = S.linear_forward(layer, dev, x[257:300].contiguous())
-    torch.cuda.synchronize()
-    assert torch.equal(full[257:300].view(torch.int16), part.view(torch.int16))
+    for m, n in ((300, 299), (300, 290), (60, 43)):
+        a = full if m == 300 else S.linear_forward(layer, dev, x[:m].contiguous())
+        b = S.linear_forward(layer, dev, x[:n].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(a[:n].view(torch.int16), b.view(torch.int16)), (m, n)
 
 
 def test_library_pack_end_to_end():
