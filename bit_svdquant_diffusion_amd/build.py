@@ -29,6 +29,9 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-fvisibility=hidden",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
+# per-source extras: the small-M INT4 GEMM multiplies into VGPRs, so its
+# dequant reads the MFMA results without accumulator-register copies
+HIP_EXTRA = {"svdq_gemm_int4_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-fvisibility=hidden",
              "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 
@@ -52,7 +55,7 @@ def build(verbose: bool = False) -> str:
         jobs.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o])
     for s in HIP_SOURCES:
         o = os.path.join(BUILD_DIR, s + ".o")
-        jobs.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o])
+        jobs.append([HIPCC] + HIP_FLAGS + HIP_EXTRA.get(s, []) + ["-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:

@@ -24,7 +24,6 @@
 namespace svdq {
 
 namespace {
-constexpr int kSW = 4;   // waves per workgroup
 // groups loaded ahead of the one being multiplied (fewer with more token blocks: registers)
 __host__ __device__ constexpr int kPD(int mb) { return mb <= 2 ? 4 : (mb <= 4 ? 2 : 1); }
 
@@ -70,111 +69,119 @@ __device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int
 }
 }  // namespace
 
-// Workgroup b: channel block nb = b / splits, K share sp = b % splits; wave w
-// takes groups [g0, g1) of that share. part (splits > 1): raw accumulators
-// [sp][token block][channel block][64 lanes][16].
-template <int MB>
-__global__ __launch_bounds__(64 * kSW) void gemm_int4_small_kernel(GemmArgs a, int splits, float* part) {
-  __shared__ __align__(16) float red[kSW][MB][16][64];
+// Workgroup b: channel block nb = b / splits, K share sp = b % splits. The
+// four waves form TT token parts by 4 / TT K parts: wave w takes the token
+// blocks w % TT, w % TT + TT, ... and the groups [g0, g1) of K part w / TT.
+// part (splits > 1): raw sums [sp][token block][channel block][64 lanes][16].
+template <int MB, int TT, int PD, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_int4_small_kernel(GemmArgs a, int splits, float* part) {
+  constexpr int KK = NW / TT;               // waves along K
+  constexpr int MBW = (MB + TT - 1) / TT;   // token blocks per wave
+  constexpr int NP = (MBW + 1) / 2;         // two-block scale products per group
+  __shared__ __align__(16) float red[KK][KK > 1 ? MB : 1][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ti = wave % TT, ki = wave / TT;
   const int h = lane >> 5, lr = lane & 31;
   const int KS = a.K / 64, N = a.N, NB = N / 32;
   const int nb = blockIdx.x / splits, sp = blockIdx.x - nb * splits;
   const int s0 = (int)((int64_t)KS * sp / splits), s1 = (int)((int64_t)KS * (sp + 1) / splits);
-  const int g0 = s0 + (s1 - s0) * wave / kSW, g1 = s0 + (s1 - s0) * (wave + 1) / kSW;
+  const int g0 = s0 + (s1 - s0) * ki / KK, g1 = s0 + (s1 - s0) * (ki + 1) / KK;
   const int act_rows = (a.M + 15) / 16 * 16;   // row stride of s_x
 
   // Sources as buffer resources (no per-load address arithmetic): fragment
   // block (row block b, group g) at ((b * KS + g) * 64 + lane) * 16 bytes,
   // the group offset as the scalar offset; s_w [K/64][N], s_x [K/64][act_rows]
-  // fp32. The activation blocks are clamped to the tokens' rows.
-  const int MBa = (a.M + 31) / 32;
+  // fp32. Token blocks past MB and rows past M are clamped to the last ones
+  // (their results are dropped).
   const __amdgpu_buffer_rsrc_t rqw =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.qw + (size_t)nb * KS * 1024), 0, KS * 1024, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rqx = __builtin_amdgcn_make_buffer_rsrc((void*)a.qx, 0, MBa * KS * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rqx = __builtin_amdgcn_make_buffer_rsrc((void*)a.qx, 0, MB * KS * 1024, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsw =
       __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)a.sw + nb * 32), 0, (KS - 1) * N * 4 + 128, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)a.sx, 0, KS * act_rows * 4, 0x00020000);
-  int sxo[(MB + 1) / 2];   // the lane's token row for each pair of token blocks (clamped to M - 1), bytes
+  auto blk = [&](int j) { return min(ti + TT * min(j, MBW - 1), MB - 1); };   // the wave's j-th token block
+  int sxo[NP];   // the lane's token row in the pair's block (lanes 32 h + r: block 2 p + h), bytes
 #pragma unroll
-  for (int p = 0; p < (MB + 1) / 2; ++p) sxo[p] = min((2 * p + h) * 32 + lr, a.M - 1) * 4;
+  for (int p = 0; p < NP; ++p) sxo[p] = min(blk(2 * p + h) * 32 + lr, a.M - 1) * 4;
 
-  f32x16 acc[MB];
+  f32x16 acc[MBW];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) acc[b] = f32x16{};
+  for (int j = 0; j < MBW; ++j) acc[j] = f32x16{};
 
-  // PD + 1 groups of operands in registers: loads run PD groups ahead
-  constexpr int PD = kPD(MB), NP = (MB + 1) / 2;
-  i32x4 fb[PD + 1], fa[PD + 1][MB];
+  // PD + 1 groups of operands in registers, loads running PD groups ahead.
+  // No arithmetic touches a loaded value before its group's turn (a scale
+  // multiply at the load would make the wave wait for the load it has just
+  // issued): the 1/256 of the widened codes is applied once at the end,
+  // which is exact (a power of two) for these normal-range sums.
+  i32x4 fb[PD + 1], fa[PD + 1][MBW];
   float fw[PD + 1], fx[PD + 1][NP];
   auto load = [&](int slot, int g) {
-    const int gg = min(g, g1 - 1);   // past the end: repeat the last group (unused)
+    const int gg = min(g, g1 - 1);   // past the end: repeat the last group (not multiplied)
     fb[slot] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rqw, lane * 16, gg * 1024, 0));
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
-      fa[slot][b] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rqx, lane * 16, (b * KS + gg) * 1024, 0));
+    for (int j = 0; j < MBW; ++j)
+      fa[slot][j] =
+          __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rqx, lane * 16, (blk(j) * KS + gg) * 1024, 0));
     fw[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsw, lr * 4, gg * N * 4, 0));
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      fx[slot][p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsx, sxo[p], gg * act_rows * 4, 0)) *
-                    (1.0f / 256.0f);
+      fx[slot][p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsx, sxo[p], gg * act_rows * 4, 0));
   };
-  if (g0 < g1) {
+  auto mult = [&](int u) {
+    i32x4 blo, bhi;
+    sm_widen(fb[u], blo, bhi);
 #pragma unroll
-    for (int d = 0; d < PD; ++d) load(d, g0 + d);
-    // slot u holds group g + u; each step refills the slot just used with
-    // the group PD + 1 later. The last round runs whole: a group past the end
-    // repeats the last one with its token scales zeroed, so it adds exact zeros.
-    for (int g = g0; g < g1; g += PD + 1) {
+    for (int p = 0; p < NP; ++p) {
+      // lanes 32 h + r: the channel scales times the token scales of the
+      // pair's block 2 p + h; output block 2 p + bb in registers 16 bb .. + 15
+      const f32x32 r = __builtin_amdgcn_mfma_f32_32x32x1f32(fw[u], fx[u][p], f32x32{}, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u <= PD; ++u) {
-        {
-          load((u + PD) % (PD + 1), g + u + PD);
-          const float live = g + u < g1 ? 1.0f : 0.0f;
-          i32x4 blo, bhi;
-          sm_widen(fb[u], blo, bhi);
+      for (int bb = 0; bb < 2; ++bb) {
+        const int j = 2 * p + bb;
+        if (j < MBW) {
+          i32x4 alo, ahi;
+          sm_widen(fa[u][j], alo, ahi);
+          i32x16 pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo, alo, i32x16{}, 0, 0, 0);
+          pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi, ahi, pp, 0, 0, 0);
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            // token block b = 2 p + lane / 32 of the pair takes the 32 channel
-            // scales and its 32 token scales: output block b in registers
-            // 16 (b - 2 p) .. + 15
-            const f32x32 r = __builtin_amdgcn_mfma_f32_32x32x1f32(fw[u], fx[u][p] * live, f32x32{}, 0, 0, 0);
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-              const int b = 2 * p + bb;
-              if (b < MB) {
-                i32x4 alo, ahi;
-                sm_widen(fa[u][b], alo, ahi);
-                i32x16 pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo, alo, i32x16{}, 0, 0, 0);
-                pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi, ahi, pp, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[b][e] = __builtin_fmaf((float)pp[e], r[16 * bb + e], acc[b][e]);
-              }
-            }
-          }
+          for (int e = 0; e < 16; ++e) acc[j][e] = __builtin_fmaf((float)pp[e], r[16 * bb + e], acc[j][e]);
         }
       }
     }
+  };
+  const int n = g1 - g0;
+  if (n > 0) {
+    // the prologue's loads stay in slot order (scheduling barriers), so each
+    // slot's wait counts the same in the first round as in later ones
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+      load(d, g0 + d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole rounds: slot u holds group g + u; each step refills the slot
+    // used last with the group PD later
+    const int rounds = n / (PD + 1);
+    int g = g0;
+    for (int it = 0; it < rounds; ++it, g += PD + 1) {
+#pragma unroll
+      for (int u = 0; u <= PD; ++u) {
+        load((u + PD) % (PD + 1), g + u + PD);
+        mult(u);
+        __builtin_amdgcn_sched_barrier(0);   // keep each step's loads at its start
+      }
+    }
+    // the remaining groups already sit in slots 0 .. rem - 1
+    const int rem = n - rounds * (PD + 1);
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+      if (u < rem) mult(u);
   }
 
-  // the four waves' sums, added in wave order
-#pragma unroll
-  for (int b = 0; b < MB; ++b) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[wave][b][e][lane] = acc[b][e];
-  }
-  __syncthreads();
   const int r32 = a.r32;
-  for (int b = wave; b < MB; b += kSW) {
-    f32x16 v;
+  auto finish = [&](int b, f32x16 v) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < kSW; ++w) s += red[w][b][e][lane];
-      v[e] = s;
-    }
+    for (int e = 0; e < 16; ++e) v[e] *= 1.0f / 256.0f;
     if (sp == 0) {
       // + (X_hat L1) L2 on bf16 MFMA (Z and L2^T in 16-column fragment order) + bias
       const i32x4* zf = reinterpret_cast<const i32x4*>(a.z) + (size_t)b * (r32 / 16) * 64 + lane;
@@ -197,6 +204,33 @@ __global__ __launch_bounds__(64 * kSW) void gemm_int4_small_kernel(GemmArgs a, i
       f32x4* dst = reinterpret_cast<f32x4*>(part) + ((((size_t)sp * MB + b) * NB + nb) * 64 + lane) * 4;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dst[c] = f32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+    }
+  };
+  if constexpr (KK == 1) {
+#pragma unroll
+    for (int j = 0; j < MBW; ++j)
+      if (ti + TT * j < MB) finish(ti + TT * j, acc[j]);
+  } else {
+    // the K parts' sums, added in K-part order
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) {
+      const int b = ti + TT * j;
+      if (b < MB) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[ki][b][e][lane] = acc[j][e];
+      }
+    }
+    __syncthreads();
+    for (int b = wave; b < MB; b += NW) {
+      f32x16 v;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < KK; ++k) s += red[k][b][e][lane];
+        v[e] = s;
+      }
+      finish(b, v);
     }
   }
 }
@@ -222,31 +256,46 @@ __global__ __launch_bounds__(64) void gemm_int4_small_sum(const float* __restric
 
 bool gemm_int4_small_fits(const GemmArgs& a) { return a.M <= 256 && a.p == nullptr; }
 
-template <int MB>
-static hipError_t launch_mb(const GemmArgs& a, int num_cus, hipStream_t st) {
+// Shape of the launch for MB token blocks: token parts TT, ring depth PD.
+// With one or two token blocks the waves split K; from four blocks on they
+// split the tokens, each wave then holding two blocks' sums. The kernel is
+// bound by the dequant's vector instructions, not by the weight stream, so
+// the launch aims at busy SIMDs: eight waves per workgroup when the channel
+// blocks cannot fill half the CUs, and K shares (with an fp32 partial pass)
+// only while CUs would otherwise idle and each wave keeps 8 groups or more.
+template <int MB, int TT, int PD, int NW>
+static hipError_t launch_nw(const GemmArgs& a, int num_cus, hipStream_t st) {
   const int KS = a.K / 64, NB = a.N / 32;
-  // enough workgroups for every CU, each wave keeping at least one group
+  constexpr int KK = NW / TT;
   const int cus = num_cus > 0 ? num_cus : 256;
-  int splits = max(1, min(KS / kSW, (cus + NB - 1) / NB));
+  int splits = 1;
+  while ((splits + 1) * NB <= cus && KS / (KK * (splits + 1)) >= 8) ++splits;
   const size_t per_split = (size_t)MB * 32 * a.N * 4;   // fp32 partial bytes of one share
   while (splits > 1 && (size_t)splits * per_split > (size_t)kSplitSlots * kSplitPartBytes) --splits;
-  hipLaunchKernelGGL((gemm_int4_small_kernel<MB>), dim3(NB * splits), dim3(64 * kSW), 0, st, a, splits, a.part);
+  hipLaunchKernelGGL((gemm_int4_small_kernel<MB, TT, PD, NW>), dim3(NB * splits), dim3(64 * NW), 0, st, a, splits,
+                     a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(gemm_int4_small_sum, dim3(MB * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, MB, splits);
   return hipGetLastError();
 }
 
+template <int MB, int TT>
+static hipError_t launch_shape(const GemmArgs& a, int num_cus, hipStream_t st) {
+  const int cus = num_cus > 0 ? num_cus : 256;
+  return 2 * (a.N / 32) <= cus ? launch_nw<MB, TT, 2, 8>(a, num_cus, st) : launch_nw<MB, TT, 2, 4>(a, num_cus, st);
+}
+
 hipError_t launch_gemm_int4_small(const GemmArgs& a, int num_cus, hipStream_t st) {
   switch ((a.M + 31) / 32) {   // exact token blocks: no read past the round32(M) rows
-    case 1: return launch_mb<1>(a, num_cus, st);
-    case 2: return launch_mb<2>(a, num_cus, st);
-    case 3: return launch_mb<3>(a, num_cus, st);
-    case 4: return launch_mb<4>(a, num_cus, st);
-    case 5: return launch_mb<5>(a, num_cus, st);
-    case 6: return launch_mb<6>(a, num_cus, st);
-    case 7: return launch_mb<7>(a, num_cus, st);
-    default: return launch_mb<8>(a, num_cus, st);
+    case 1: return launch_shape<1, 1>(a, num_cus, st);
+    case 2: return launch_shape<2, 1>(a, num_cus, st);
+    case 3: return launch_shape<3, 1>(a, num_cus, st);
+    case 4: return launch_shape<4, 2>(a, num_cus, st);
+    case 5: return launch_shape<5, 4>(a, num_cus, st);
+    case 6: return launch_shape<6, 4>(a, num_cus, st);
+    case 7: return launch_shape<7, 4>(a, num_cus, st);
+    default: return launch_shape<8, 4>(a, num_cus, st);
   }
 }
 

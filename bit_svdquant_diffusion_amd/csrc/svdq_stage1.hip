@@ -389,15 +389,31 @@ __global__ __launch_bounds__(256) void zsum_kernel(const float* __restrict__ zp,
   const int tg = S1_ROWS * th_n, ncb = r32 / 16;
   const int g = row / tg, h = (row % tg) / S1_ROWS, rr = row % S1_ROWS;
   const int n = col / 16, l = (rr / 4) * 16 + col % 16, e = rr % 4;
-  float acc = 0.f;
-  for (int qq = 0; qq < S1_WAVES; ++qq) {
-    const int w = h * S1_WAVES + qq;
-    const size_t base = ((size_t)(g * npc) * (S1_WAVES * th_n) + w) * ncb * 256 + ((size_t)n * 64 + l) * 4 + e;
-    const size_t pstride = (size_t)(S1_WAVES * th_n) * ncb * 256;   // next piece of the group
-    float sum = zp[base];
-    for (int c = 1; c < npc; ++c) sum += zp[base + c * pstride];
-    acc += sum;
+  const size_t pstride = (size_t)(S1_WAVES * th_n) * ncb * 256;   // next piece of the group
+  const size_t base0 = ((size_t)(g * npc) * (S1_WAVES * th_n) + h * S1_WAVES) * ncb * 256 + ((size_t)n * 64 + l) * 4 + e;
+  // the loads of 8 pieces of all four quarters go out together (the sums
+  // themselves stay in piece order per quarter)
+  float sum[S1_WAVES];
+  for (int c0 = 0; c0 < npc; c0 += 8) {
+    float v[8][S1_WAVES];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = min(c0 + j, npc - 1);
+#pragma unroll
+      for (int qq = 0; qq < S1_WAVES; ++qq) v[j][qq] = zp[base0 + (size_t)qq * ncb * 256 + c * pstride];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int qq = 0; qq < S1_WAVES; ++qq) {
+        if (c0 + j == 0) sum[qq] = v[j][qq];
+        else if (c0 + j < npc) sum[qq] += v[j][qq];
+      }
+    }
   }
+  float acc = 0.f;
+#pragma unroll
+  for (int qq = 0; qq < S1_WAVES; ++qq) acc += sum[qq];
   z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) + col % 8] =
       (uint16_t)f2bf(acc);
 }

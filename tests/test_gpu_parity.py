@@ -57,9 +57,15 @@ SMALL = [
     # INT4 GEMM split: 6 tiles of 24 K stages on 6 XCDs, each cut into four
     # runs of 6 stages (one owner adding three partials)
     _spec("split_k_4_pieces", 384, 3072, 512, 16, "int4", 18),
-    # INT4 with few tokens (weight-streaming kernel): 3 token blocks, the
-    # channel blocks' K cut into shares whose partials a second kernel adds
-    _spec("small_m70_shares", 70, 3072, 3072, 32, "int4", 20),
+    # INT4 with few tokens (weight-streaming kernel). 3 token blocks over
+    # eight K parts, K cut into two shares whose partials a second kernel
+    # adds; 7 token blocks in four token parts by two K parts, three shares;
+    # more channel blocks than half the CUs: four-wave workgroups, K parts
+    # (2 token blocks) or token parts (8 token blocks, the last one ragged)
+    _spec("small_m70_shares", 70, 8192, 512, 32, "int4", 20),
+    _spec("small_m200_shares", 200, 3072, 256, 32, "int4", 21),
+    _spec("small_m40_four_waves", 40, 512, 4160, 16, "int4", 22),
+    _spec("small_m250_four_waves", 250, 256, 8224, 32, "int4", 23),
     # MXFP4 GEMM: 9 x 32 = 288 tiles, so 32 workgroups run two tiles of three
     # ring steps; the next tile's bias transfer is issued before the first
     # tile's epilogue reads its own
