@@ -107,6 +107,30 @@ def time_split(layer, sets, steps, warmup, torch, S):
     return t1, t2
 
 
+def time_graph(calls, reps, torch):
+    """Per-call GPU time of `calls` (each launches on the current stream),
+    captured once into a HIP graph and replayed `reps` times: the launch
+    cost of the host is out of the measurement."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * len(calls))
+    del g
+    return ms
+
+
 def stage1_bytes(spec):
     """Algorithmic HBM bytes of kernel 1: read X (bf16) and mu, L1; write codes, scales, Z."""
     r32 = (spec.rank + 31) // 32 * 32
@@ -177,9 +201,10 @@ def bench_c4(args, torch, S, synth):
     """Config 4: a FLUX double-stream block's linears at batch 2, 1024^2 (image
     M=8192, text M=1024) and the decode-like M=64, 256 runs of the same four
     shapes, which reuse the text stream's packed weights. Per layer: forward
-    time, effective TOPS and, for the weight-bound small-M runs, algorithmic
-    HBM bytes per second against 8 TB/s. Small-M runs rotate 16 weight sets
-    so that the 256 MB MALL cannot hold them."""
+    time (GPU time from HIP graph replays, with the rate of eager launches
+    beside it), effective TOPS and, for the small-M runs, algorithmic HBM
+    bytes per second against 8 TB/s. Small-M runs rotate 16 weight sets so
+    that the 256 MB MALL cannot hold them."""
     packs, rows = {}, []
     steps = max(10, args.steps // 5)
     for sp in synth.config_layers(4):
@@ -187,8 +212,16 @@ def bench_c4(args, torch, S, synth):
         rot = 16 if sp.M <= 256 else 2
         layer, host, _, sets = make_workload(sp, rot, torch, S, synth, packed=packs.get(owner))
         packs[owner] = (layer, host)
-        ms, _ = time_forward(layer, sets, steps, max(20, args.warmup // 10), torch, S)
-        a1, a2 = time_split(layer, sets, steps, max(20, args.warmup // 10), torch, S)
+        ms_eager, _ = time_forward(layer, sets, steps, max(20, args.warmup // 10), torch, S)
+        # GPU time per call from graph replays of one call per buffer set
+        # (the few-token layers launch faster than the host can issue them)
+        reps = max(4, steps // len(sets))
+        fwd = [lambda s=s: S.linear_forward(layer, s["dev"], s["x"], y=s["y"], workspace=s["ws"]) for s in sets]
+        s1 = [lambda s=s: S.stage1(layer, s["dev"], s["x"], s["ws"]) for s in sets]
+        gm = [lambda s=s: S.gemm(layer, s["dev"], s["ws"], sp.M, s["y"]) for s in sets]
+        ms = time_graph(fwd, reps, torch)
+        a1 = time_graph(s1, reps, torch)
+        a2 = time_graph(gm, reps, torch)
         del sets
         torch.cuda.empty_cache()
         fl = 2.0 * sp.M * sp.N * sp.K
@@ -196,12 +229,13 @@ def bench_c4(args, torch, S, synth):
         t = fl / (ms * 1e-3) / 1e12
         gbs = hb / (ms * 1e-3) / 1e9
         rows.append({"workload": sp.name, "M": sp.M, "K": sp.K, "N": sp.N, "rank": sp.rank, "format": sp.fmt,
-                     "us": round(ms * 1e3, 2), "effective_tops": round(t, 2),
+                     "us": round(ms * 1e3, 2), "us_eager_launches": round(ms_eager * 1e3, 2),
+                     "effective_tops": round(t, 2),
                      "pct_of_int8_peak": round(100 * t / PEAK_TFLOPS["int4"], 2),
                      "hbm_algorithmic_bytes": hb, "hbm_gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                      "stage1_us": round(a1 * 1e3, 2), "gemm_us": round(a2 * 1e3, 2)})
-        log(f"c4 {sp.name}: {ms * 1e3:.1f} us, {t:.1f} TOPS, {gbs:.0f} GB/s "
+        log(f"c4 {sp.name}: {ms * 1e3:.1f} us (eager {ms_eager * 1e3:.1f}), {t:.1f} TOPS, {gbs:.0f} GB/s "
             f"(stage1 {a1 * 1e3:.1f} us, gemm {a2 * 1e3:.1f} us)")
     block = [r for r in rows if r["workload"].startswith(("img_", "txt_"))]
     bus = sum(r["us"] for r in block)

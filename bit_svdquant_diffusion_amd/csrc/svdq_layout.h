@@ -47,13 +47,17 @@ inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
   return s;
 }
 
-// Stage 1 sums X_hat L1 in K pieces of kPieceSteps steps of 256 channels:
-// each wave quarter's partial of a piece is complete before it is added, in
-// piece order, and the four quarter sums are added last, so a token's Z does
-// not depend on M or on whether a workgroup held the whole token group or
-// pieces of it (then a second kernel adds the stored partials).
-constexpr int kPieceSteps = 4;
-inline int s1_pieces(int K) { return (K / 256 + kPieceSteps - 1) / kPieceSteps; }
+// Stage 1 sums X_hat L1 in K pieces of s1_piece_steps(K) steps of 256
+// channels, about twelve pieces whatever K: each wave quarter's partial of a
+// piece is complete before it is added, in piece order, and the four quarter
+// sums are added last, so a token's Z does not depend on M or on whether a
+// workgroup held the whole token group or pieces of it (then a second kernel
+// adds the stored partials). The pieces of fewer than 128 token groups are
+// dealt over the CUs, so the stored partials cover at most kS1SplitRows rows.
+constexpr int kS1Pieces = 12;
+inline int s1_piece_steps(int K) { return (K / 256 + kS1Pieces - 1) / kS1Pieces; }
+inline int s1_pieces(int K) { return (K / 256 + s1_piece_steps(K) - 1) / s1_piece_steps(K); }
+constexpr int64_t kS1SplitRows = 4096;
 
 // INT4 GEMM split of the last tiles over the workgroups: one flag and one
 // fp32 partial tile (128 x 256) per workgroup, at most kSplitSlots of them.
@@ -65,7 +69,8 @@ constexpr int kSplitPartBytes = 128 * 256 * 4;
 // (INT4) or E8M0 bytes in fragment order (MXFP4). INT4 adds the split's flags
 // (u32 [kSplitSlots], cleared by stage 1) and partial tiles. Last, with a
 // low-rank branch, stage 1's partial Z: fp32, per token group and piece the
-// raw MFMA accumulators of its waves, round32(M) x s1_pieces(K) x 4 x rank32.
+// raw MFMA accumulators of its waves, min(round32(M), kS1SplitRows) x
+// s1_pieces(K) x 4 x rank32.
 struct WsLayout {
   size_t qx, sx, z, flags, part, zp, total;
 };
@@ -79,7 +84,7 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   w.flags = w.z + align256((size_t)rows * rank32(d->rank) * 2);
   w.part = w.flags + (int4 ? align256((size_t)kSplitSlots * 4) : 0);
   w.zp = w.part + (int4 ? (size_t)kSplitSlots * kSplitPartBytes : 0);
-  w.total = w.zp + (size_t)s1_pieces(d->K) * rows * 4 * rank32(d->rank) * 4;
+  w.total = w.zp + (size_t)s1_pieces(d->K) * (rows < kS1SplitRows ? rows : kS1SplitRows) * 4 * rank32(d->rank) * 4;
   return w;
 }
 

@@ -114,7 +114,7 @@ template <int FMT, int NCB, int TH>
 __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
     uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, float* __restrict__ zp, int M,
-    int K, uint32_t* __restrict__ flags, int nflags, int npieces, int grid, int split) {
+    int K, uint32_t* __restrict__ flags, int nflags, int ps, int npieces, int grid, int split) {
   using Cfg = S1Cfg<NCB, TH>;
   constexpr int D = Cfg::kDepth;
   constexpr int r32 = NCB * 16;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = wave & 3, th = wave >> 2;   // quarter and token half
   const int nsteps = K / S1_STEP;
-  const int npc = (nsteps + kPieceSteps - 1) / kPieceSteps;   // K pieces per token group
+  const int npc = (nsteps + ps - 1) / ps;   // K pieces (of ps steps) per token group
   const int Mp = (M + 15) / 16 * 16;   // row stride of the INT4 scales
   const int MB = (M + 31) / 32;        // 32-row blocks (MXFP4 fragment order)
 
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   // one workgroup per group and holds all its pieces.
   const int pb = (int)((int64_t)npieces * blockIdx.x / grid), pe = (int)((int64_t)npieces * (blockIdx.x + 1) / grid);
   int T = 0;
-  for (int p = pb; p < pe; ++p) T += min(kPieceSteps, nsteps - (p % npc) * kPieceSteps);
+  for (int p = pb; p < pe; ++p) T += min(ps, nsteps - (p % npc) * ps);
 
   // issue cursor: piece ip, step is (absolute), its end, and the lane's X rows
   int ip = pb, is = 0, iend = 0, iu = 0;
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   const uint16_t* srcB = x;
   auto issue_piece = [&]() {
     const int g = ip / npc;
-    is = (ip - g * npc) * kPieceSteps;
-    iend = min(is + kPieceSteps, nsteps);
+    is = (ip - g * npc) * ps;
+    iend = min(is + ps, nsteps);
     const int m0 = g * TG + th * S1_ROWS;
     srcA = x + (size_t)min(m0 + tA, M - 1) * K + q * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
     srcB = x + (size_t)min(m0 + tB, M - 1) * K + q * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
@@ -174,8 +174,8 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   auto compute_piece = [&]() {
     cg = cp / npc;
     cc = cp - cg * npc;
-    cs = cc * kPieceSteps;
-    cend = min(cs + kPieceSteps, nsteps);
+    cs = cc * ps;
+    cend = min(cs + ps, nsteps);
     m = min(cg * TG + th * S1_ROWS + r, M - 1);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
@@ -380,40 +380,36 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
 // quarter's sum over the K pieces in piece order (the whole-group path's
 // additions, in its order), stored in fragment order: (row block, 16-column
 // step, lane 32h + row%32, element). zp holds, per token group and piece,
-// each wave's raw accumulators [wave][16-column block][lane][4].
+// each wave's raw accumulators [wave][16-column block][lane][4]. Four lanes
+// per element, one per quarter, each load all pieces of their quarter at
+// once; lane 0 of the four then adds the quarter sums in order.
 __global__ __launch_bounds__(256) void zsum_kernel(const float* __restrict__ zp, uint16_t* __restrict__ z, int M,
                                                    int r32, int npc, int th_n) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = t >> 2;   // output element; the four lanes of a quad share it
+  const int qq = (int)(t & 3);
   if (idx >= (int64_t)M * r32) return;
   const int row = (int)(idx / r32), col = (int)(idx - (int64_t)row * r32);
   const int tg = S1_ROWS * th_n, ncb = r32 / 16;
   const int g = row / tg, h = (row % tg) / S1_ROWS, rr = row % S1_ROWS;
   const int n = col / 16, l = (rr / 4) * 16 + col % 16, e = rr % 4;
   const size_t pstride = (size_t)(S1_WAVES * th_n) * ncb * 256;   // next piece of the group
-  const size_t base0 = ((size_t)(g * npc) * (S1_WAVES * th_n) + h * S1_WAVES) * ncb * 256 + ((size_t)n * 64 + l) * 4 + e;
-  // the loads of 8 pieces of all four quarters go out together (the sums
-  // themselves stay in piece order per quarter)
-  float sum[S1_WAVES];
-  for (int c0 = 0; c0 < npc; c0 += 8) {
-    float v[8][S1_WAVES];
+  const size_t base = ((size_t)(g * npc) * (S1_WAVES * th_n) + h * S1_WAVES + qq) * ncb * 256 + ((size_t)n * 64 + l) * 4 + e;
+  float v[kS1Pieces];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = min(c0 + j, npc - 1);
+  for (int c = 0; c < kS1Pieces; ++c) v[c] = zp[base + (size_t)min(c, npc - 1) * pstride];
+  float sum = v[0];
 #pragma unroll
-      for (int qq = 0; qq < S1_WAVES; ++qq) v[j][qq] = zp[base0 + (size_t)qq * ncb * 256 + c * pstride];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int qq = 0; qq < S1_WAVES; ++qq) {
-        if (c0 + j == 0) sum[qq] = v[j][qq];
-        else if (c0 + j < npc) sum[qq] += v[j][qq];
-      }
-    }
-  }
+  for (int c = 1; c < kS1Pieces; ++c)
+    if (c < npc) sum += v[c];
+  const int q0 = (int)(threadIdx.x & 60u);   // lane of quarter 0 of this quad
+  const float s0 = __shfl(sum, q0), s1 = __shfl(sum, q0 + 1), s2 = __shfl(sum, q0 + 2), s3 = __shfl(sum, q0 + 3);
+  if (qq != 0) return;
   float acc = 0.f;
-#pragma unroll
-  for (int qq = 0; qq < S1_WAVES; ++qq) acc += sum[qq];
+  acc += s0;
+  acc += s1;
+  acc += s2;
+  acc += s3;
   z[((((size_t)(row / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + row % 32) * 8) + col % 8] =
       (uint16_t)f2bf(acc);
 }
@@ -430,17 +426,17 @@ static size_t lds_bytes() {
 template <int FMT, int NCB, int TH>
 static hipError_t launch_t(const Stage1Args& a, int num_cus, hipStream_t st) {
   constexpr int TG = S1_ROWS * TH;
-  const int groups = (a.M + TG - 1) / TG, npc = s1_pieces(a.K);
+  const int groups = (a.M + TG - 1) / TG, npc = s1_pieces(a.K), ps = s1_piece_steps(a.K);
   const int cus = num_cus > 0 ? num_cus : 256;
   const size_t lds = lds_bytes<FMT, NCB, TH>();
   const int per_cu = lds <= 80 * 1024 ? 2 : 1;   // workgroups that fit one CU's LDS
-  const bool split = NCB > 0 && npc > 1 && 2 * groups < cus;
+  const bool split = NCB > 0 && npc > 1 && 2 * groups < cus && (int64_t)groups * TG <= kS1SplitRows;
   const int grid = split ? min(groups * npc, cus * per_cu) : groups;
   hipLaunchKernelGGL((stage1_kernel<FMT, NCB, TH>), dim3(grid), dim3(64 * S1_WAVES * TH), lds, st, a.x, a.mu,
-                     a.l1s, a.qx, a.sx, a.z, a.zp, a.M, a.K, a.flags, a.nflags, groups * npc, grid, split ? 1 : 0);
+                     a.l1s, a.qx, a.sx, a.z, a.zp, a.M, a.K, a.flags, a.nflags, ps, groups * npc, grid, split ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
-  hipLaunchKernelGGL(zsum_kernel, dim3((unsigned)(((int64_t)a.M * a.r32 + 255) / 256)), dim3(256), 0, st, a.zp,
+  hipLaunchKernelGGL(zsum_kernel, dim3((unsigned)(((int64_t)a.M * a.r32 * 4 + 255) / 256)), dim3(256), 0, st, a.zp,
                      a.z, a.M, a.r32, npc, TH);
   return hipGetLastError();
 }

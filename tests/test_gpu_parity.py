@@ -182,6 +182,53 @@ def test_rows_are_independent(fmt):
         assert torch.equal(a[:n].view(torch.int16), b.view(torch.int16)), (m, n)
 
 
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_stage1_z_same_in_both_modes(fmt):
+    """Z = X_hat L1 of a token does not depend on the batch: 100 tokens (their
+    K pieces dealt over the CUs, partials added by a second kernel) and 4200
+    tokens (one workgroup walks a token group's whole K) give the same bits
+    for the shared rows, as do the codes and scales."""
+    spec = _spec("zmodes", 4200, 3072, 64, 32, fmt, 25)
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    got = {}
+    for m in (100, 4200):
+        _say(f"[z modes] {fmt} M={m}")
+        ws = torch.full((S.workspace_bytes(layer, m),), 0xFF, dtype=torch.uint8, device="cuda")
+        S.stage1(layer, dev, x[:m].contiguous(), ws)
+        torch.cuda.synchronize()
+        got[m] = S.unpack_workspace(layer, m, ws.cpu().numpy())
+    for key in ("z", "codes", "scales"):
+        a, b = np.asarray(got[100][key]), np.asarray(got[4200][key])
+        assert np.array_equal(a, b[:a.shape[0]]), key
+
+
+@pytest.mark.parametrize("fmt,M", [("int4", 70), ("int4", 300), ("mxfp4", 300)])
+def test_graph_replays_match_eager(fmt, M):
+    """svdq_linear_forward captured in a HIP graph: each replay, with eager
+    work and synchronizations between replays and the workspace refilled with
+    0xFF each time, gives the eager result's bits. The forward records kernel
+    nodes only (stage 1 clears the INT4 split flags in a kernel)."""
+    _say(f"[graph] {fmt} M={M}")
+    spec = _spec("graph", M, 768, 544, 32, fmt, 24)
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    want = S.linear_forward(layer, dev, x)
+    ws = torch.empty(S.workspace_bytes(layer, M), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, spec.N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.linear_forward(layer, dev, x, y=y, workspace=ws)
+    for i in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+
+
 def test_library_pack_end_to_end():
     """svdq_pack_weights (randomized SVD) + forward stays within the Y bar of the oracle."""
     spec = SMALL[0]
