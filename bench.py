@@ -207,7 +207,12 @@ def bench_c4(args, torch, S, synth):
     that the 256 MB MALL cannot hold them."""
     packs, rows = {}, []
     steps = max(10, args.steps // 5)
-    for sp in synth.config_layers(4):
+    for li, sp in enumerate(synth.config_layers(4)):
+        if args.layer_markers:
+            # a one-kernel fill of a byte buffer: in a rocprofv3 trace the
+            # dispatches of layer li follow the (li + 1)-th such fill
+            torch.full((4096,), li, dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
         owner = sp.stream or sp.name
         rot = 16 if sp.M <= 256 else 2
         layer, host, _, sets = make_workload(sp, rot, torch, S, synth, packed=packs.get(owner))
@@ -256,6 +261,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-c4", action="store_true", help="skip the FLUX block's linears (config 4)")
+    ap.add_argument("--layer-markers", action="store_true",
+                    help="launch one byte-fill kernel before each config-4 layer (layer boundaries in profiler traces)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args()
