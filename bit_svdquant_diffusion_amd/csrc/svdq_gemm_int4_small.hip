@@ -1,4 +1,5 @@
-// Kernel (2) for INT4 layers with few tokens (M <= 256): the same sums as
+// Kernel (2) for INT4 layers with few tokens (M <= 256, and 769 to 1024
+// unless the channel blocks overfill one round of CUs): the same sums as
 // the tiled INT4 GEMM -- per 64-channel group the exact int32 sum P of code
 // products, dequantized by s_w[n] s_x[m] and accumulated in fp32 in group
 // order, then (X_hat L1) L2 and the bias before the bf16 write of Y
@@ -70,9 +71,11 @@ __device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int
 }  // namespace
 
 // Workgroup b: channel block nb = b / splits, K share sp = b % splits. The
-// four waves form TT token parts by 4 / TT K parts: wave w takes the token
+// NW waves form TT token parts by NW / TT K parts: wave w takes the token
 // blocks w % TT, w % TT + TT, ... and the groups [g0, g1) of K part w / TT.
-// part (splits > 1): raw sums [sp][token block][channel block][64 lanes][16].
+// MB is the most token blocks the instance serves; the layer has
+// mb = ceil(M / 32) of them. part (splits > 1): sums [sp][token block][channel
+// block][64 lanes][16].
 template <int MB, int TT, int PD, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_int4_small_kernel(GemmArgs a, int splits, float* part) {
   constexpr int KK = NW / TT;               // waves along K
@@ -88,6 +91,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_int4_small_kernel(GemmArgs a, in
   const int s0 = (int)((int64_t)KS * sp / splits), s1 = (int)((int64_t)KS * (sp + 1) / splits);
   const int g0 = s0 + (s1 - s0) * ki / KK, g1 = s0 + (s1 - s0) * (ki + 1) / KK;
   const int act_rows = (a.M + 15) / 16 * 16;   // row stride of s_x
+  const int mb = (a.M + 31) / 32;
 
   // Sources as buffer resources (no per-load address arithmetic): fragment
   // block (row block b, group g) at ((b * KS + g) * 64 + lane) * 16 bytes,
@@ -96,11 +100,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_int4_small_kernel(GemmArgs a, in
   // (their results are dropped).
   const __amdgpu_buffer_rsrc_t rqw =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.qw + (size_t)nb * KS * 1024), 0, KS * 1024, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rqx = __builtin_amdgcn_make_buffer_rsrc((void*)a.qx, 0, MB * KS * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rqx = __builtin_amdgcn_make_buffer_rsrc((void*)a.qx, 0, mb * KS * 1024, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsw =
       __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)a.sw + nb * 32), 0, (KS - 1) * N * 4 + 128, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)a.sx, 0, KS * act_rows * 4, 0x00020000);
-  auto blk = [&](int j) { return min(ti + TT * min(j, MBW - 1), MB - 1); };   // the wave's j-th token block
+  auto blk = [&](int j) { return min(ti + TT * min(j, MBW - 1), mb - 1); };   // the wave's j-th token block
   int sxo[NP];   // the lane's token row in the pair's block (lanes 32 h + r: block 2 p + h), bytes
 #pragma unroll
   for (int p = 0; p < NP; ++p) sxo[p] = min(blk(2 * p + h) * 32 + lr, a.M - 1) * 4;
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_int4_small_kernel(GemmArgs a, in
     if (splits == 1) {
       sm_store_block(v, a.y, a.M, a.N, nb * 32, b * 32 + lr, h);
     } else {
-      f32x4* dst = reinterpret_cast<f32x4*>(part) + ((((size_t)sp * MB + b) * NB + nb) * 64 + lane) * 4;
+      f32x4* dst = reinterpret_cast<f32x4*>(part) + ((((size_t)sp * mb + b) * NB + nb) * 64 + lane) * 4;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dst[c] = f32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
     }
@@ -209,19 +213,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_int4_small_kernel(GemmArgs a, in
   if constexpr (KK == 1) {
 #pragma unroll
     for (int j = 0; j < MBW; ++j)
-      if (ti + TT * j < MB) finish(ti + TT * j, acc[j]);
+      if (ti + TT * j < mb) finish(ti + TT * j, acc[j]);
   } else {
     // the K parts' sums, added in K-part order
 #pragma unroll
     for (int j = 0; j < MBW; ++j) {
       const int b = ti + TT * j;
-      if (b < MB) {
+      if (b < mb) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) red[ki][b][e][lane] = acc[j][e];
       }
     }
     __syncthreads();
-    for (int b = wave; b < MB; b += NW) {
+    for (int b = wave; b < mb; b += NW) {
       f32x16 v;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -254,7 +258,15 @@ __global__ __launch_bounds__(64) void gemm_int4_small_sum(const float* __restric
   sm_store_block(v, y, M, N, nb * 32, b * 32 + lr, h);
 }
 
-bool gemm_int4_small_fits(const GemmArgs& a) { return a.M <= 256 && a.p == nullptr; }
+bool gemm_int4_small_fits(const GemmArgs& a, int num_cus) {
+  if (a.p != nullptr || a.M > 1024 || (a.M > 256 && a.M <= 768)) return false;
+  if (a.M <= 256) return true;
+  // 769 to 1024 tokens run one eight-wave workgroup per CU at a time: a
+  // little over one round of channel blocks would leave most CUs idle in
+  // the second round, and the tiled kernel does better there
+  const int cus = num_cus > 0 ? num_cus : 256, NB = a.N / 32;
+  return !(NB > cus && 4 * NB <= 5 * cus);
+}
 
 // Shape of the launch for MB token blocks: token parts TT, ring depth PD.
 // With one or two token blocks the waves split K; from four blocks on they
@@ -270,13 +282,14 @@ static hipError_t launch_nw(const GemmArgs& a, int num_cus, hipStream_t st) {
   const int cus = num_cus > 0 ? num_cus : 256;
   int splits = 1;
   while ((splits + 1) * NB <= cus && KS / (KK * (splits + 1)) >= 8) ++splits;
-  const size_t per_split = (size_t)MB * 32 * a.N * 4;   // fp32 partial bytes of one share
+  const int mb = (a.M + 31) / 32;
+  const size_t per_split = (size_t)mb * 32 * a.N * 4;   // fp32 partial bytes of one share
   while (splits > 1 && (size_t)splits * per_split > (size_t)kSplitSlots * kSplitPartBytes) --splits;
   hipLaunchKernelGGL((gemm_int4_small_kernel<MB, TT, PD, NW>), dim3(NB * splits), dim3(64 * NW), 0, st, a, splits,
                      a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(gemm_int4_small_sum, dim3(MB * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, MB, splits);
+  hipLaunchKernelGGL(gemm_int4_small_sum, dim3(mb * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, mb, splits);
   return hipGetLastError();
 }
 
@@ -287,6 +300,9 @@ static hipError_t launch_shape(const GemmArgs& a, int num_cus, hipStream_t st) {
 }
 
 hipError_t launch_gemm_int4_small(const GemmArgs& a, int num_cus, hipStream_t st) {
+  // 769 to 1024 tokens: eight token parts of four blocks each (the last
+  // parts' surplus blocks repeat the last block and are dropped)
+  if (a.M > 256) return launch_nw<32, 8, 2, 8>(a, num_cus, st);
   switch ((a.M + 31) / 32) {   // exact token blocks: no read past the round32(M) rows
     case 1: return launch_shape<1, 1>(a, num_cus, st);
     case 2: return launch_shape<2, 1>(a, num_cus, st);

@@ -66,6 +66,11 @@ SMALL = [
     _spec("small_m200_shares", 200, 3072, 256, 32, "int4", 21),
     _spec("small_m40_four_waves", 40, 512, 4160, 16, "int4", 22),
     _spec("small_m250_four_waves", 250, 256, 8224, 32, "int4", 23),
+    # 769 to 1024 tokens: eight token parts of four blocks (M = 1000: the
+    # last block ragged, K cut into two shares; M = 800: 25 blocks, the
+    # surplus parts repeating the last block)
+    _spec("small_m1000_shares", 1000, 1024, 512, 32, "int4", 27),
+    _spec("small_m800", 800, 512, 4160, 16, "int4", 28),
     # MXFP4 GEMM: 9 x 32 = 288 tiles, so 32 workgroups run two tiles of three
     # ring steps; the next tile's bias transfer is issued before the first
     # tile's epilogue reads its own
