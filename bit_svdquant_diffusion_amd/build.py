@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libsvdq.so")
 
-HIP_SOURCES = ["svdq_stage1.hip", "svdq_gemm_int4.hip", "svdq_gemm_int4_small.hip", "svdq_gemm_mxfp4.hip", "svdq_api.hip"]
+HIP_SOURCES = ["svdq_stage1.hip", "svdq_gemm_int4.hip", "svdq_gemm_small.hip", "svdq_gemm_mxfp4.hip", "svdq_api.hip"]
 CPP_SOURCES = ["svdq_pack.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,9 +29,9 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-fvisibility=hidden",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
-# per-source extras: the small-M INT4 GEMM multiplies into VGPRs, so its
+# per-source extras: the few-token GEMM multiplies into VGPRs, so its INT4
 # dequant reads the MFMA results without accumulator-register copies
-HIP_EXTRA = {"svdq_gemm_int4_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+HIP_EXTRA = {"svdq_gemm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-fvisibility=hidden",
              "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 

@@ -114,7 +114,7 @@ GemmArgs gemm_args(const svdq_layer_desc* d, const svdq_packed* dev, int64_t M, 
   a.y = y;
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
-  a.part = int4 ? (float*)(b + L.part) : nullptr;
+  a.part = int4 || M <= kFewTokens ? (float*)(b + L.part) : nullptr;
   return a;
 }
 

@@ -49,10 +49,10 @@ struct GemmArgs {
   int m0, mc, n0, nc;
 };
 hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st);
-// INT4 with at most 256 tokens, or 769 to 1024 (and no group-sum hook): the
-// weight-streaming kernel
-bool gemm_int4_small_fits(const GemmArgs& a, int num_cus);
-hipError_t launch_gemm_int4_small(const GemmArgs& a, int num_cus, hipStream_t st);
+// few tokens (INT4: at most 256, or 769 to 1024; MXFP4: at most 256; no
+// group-sum hook): the weight-streaming kernel of either format
+bool gemm_small_fits(const GemmArgs& a, int num_cus);
+hipError_t launch_gemm_small(const GemmArgs& a, int num_cus, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st);
 // one-time per device: the kernels' dynamic LDS attribute
 hipError_t prepare_gemm_int4();
@@ -60,8 +60,8 @@ hipError_t prepare_gemm_mxfp4();
 
 inline hipError_t launch_gemm(const GemmArgs& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (a.fmt == SVDQ_FMT_MXFP4_G32) return launch_gemm_mxfp4(a, num_cus, st);
-  return gemm_int4_small_fits(a, num_cus) ? launch_gemm_int4_small(a, num_cus, st) : launch_gemm_int4(a, num_cus, st);
+  if (gemm_small_fits(a, num_cus)) return launch_gemm_small(a, num_cus, st);
+  return a.fmt == SVDQ_FMT_MXFP4_G32 ? launch_gemm_mxfp4(a, num_cus, st) : launch_gemm_int4(a, num_cus, st);
 }
 
 }  // namespace svdq

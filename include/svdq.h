@@ -177,8 +177,8 @@ SVDQ_API svdq_status svdq_unpack_weights(const svdq_layer_desc* desc, const svdq
  * the 4-bit activation codes, their scales and the rank-32-padded
  * X_hat L1 product; INT4 layers add 32 MiB of GEMM scratch (fp32 partial
  * tiles and flags for the workgroups that share a tile's K stages, cleared
- * by svdq_stage1; with few tokens the weight-streaming GEMM keeps its fp32 K-share
- * partials there). With a low-rank branch, a last area holds kernel (1)'s
+ * by svdq_stage1), and so do MXFP4 layers with M <= 256: with few tokens
+ * the weight-streaming GEMM keeps its fp32 K-share partials there. With a low-rank branch, a last area holds kernel (1)'s
  * fp32 partial X_hat L1 per K piece (about twelve pieces) for up to 4096
  * rows, used when few token groups have their K pieces dealt over the CUs.
  * Host only.

@@ -66,6 +66,13 @@ SMALL = [
     _spec("small_m200_shares", 200, 3072, 256, 32, "int4", 21),
     _spec("small_m40_four_waves", 40, 512, 4160, 16, "int4", 22),
     _spec("small_m250_four_waves", 250, 256, 8224, 32, "int4", 23),
+    # MXFP4 with few tokens, the same kernel on block-scaled MFMA: two K
+    # shares over eight K parts, three shares over token parts, four-wave
+    # workgroups, and a decode-like QKV projection
+    _spec("small_m70_shares_fp4", 70, 8192, 512, 32, "mxfp4", 20),
+    _spec("small_m200_shares_fp4", 200, 3072, 256, 32, "mxfp4", 21),
+    _spec("small_m250_four_waves_fp4", 250, 256, 8224, 32, "mxfp4", 23),
+    _spec("small_m64_qkv_fp4", 64, 3072, 9216, 32, "mxfp4", 29),
     # 769 to 1024 tokens: eight token parts of four blocks (M = 1000: the
     # last block ragged, K cut into two shares; M = 800: 25 blocks, the
     # surplus parts repeating the last block)
