@@ -128,6 +128,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
 #pragma unroll
   for (int j = 0; j < MBW; ++j) acc[j] = f32x16{};
 
+  // The epilogue's operands (the first two 16-column steps of Z and L2^T,
+  // the bias) do not depend on the main loop. When a wave finishes at most
+  // two blocks they are loaded before it, so their latency hides under it.
+  constexpr int FB = KK == 1 ? MBW : (MB + NW - 1) / NW;   // blocks this wave finishes
+  constexpr bool PRE = FB <= 2;
+  const int r32 = a.r32, nlr = r32 / 16;
+  const i32x4* lf = reinterpret_cast<const i32x4*>(a.l2t) + (size_t)nb * nlr * 64 + lane;
+  // the wave's i-th finished block (not past the last one)
+  auto fin_block = [&](int i) { return min(KK == 1 ? ti + TT * i : wave + NW * i, mb - 1); };
+  i32x4 zpre[PRE ? FB : 1][2], lpre[2];
+  u32x2 bpre[4];
+  if (PRE && sp == 0) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      if (st < nlr) lpre[st] = lf[st * 64];
+#pragma unroll
+    for (int i = 0; i < (PRE ? FB : 1); ++i) {
+      const i32x4* zf = reinterpret_cast<const i32x4*>(a.z) + (size_t)fin_block(i) * nlr * 64 + lane;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        if (st < nlr) zpre[i][st] = zf[st * 64];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bpre[q] = *reinterpret_cast<const u32x2*>(a.bias + nb * 32 + 8 * q + 4 * h);
+  }
+
   // PD + 1 units of operands in registers, loads running PD units ahead.
   // No arithmetic touches a loaded value before its unit's turn (a scale
   // multiply at the load would make the wave wait for the load it has just
@@ -224,22 +250,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
       if (u < rem) mult(u);
   }
 
-  const int r32 = a.r32;
-  auto finish = [&](int b, f32x16 v) {
+  // block b, the wave's i-th finished block
+  auto finish = [&](int b, int i, f32x16 v) {
     if constexpr (!FP4) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] *= 1.0f / 256.0f;
     }
     if (sp == 0) {
       // + (X_hat L1) L2 on bf16 MFMA (Z and L2^T in 16-column fragment order) + bias
-      const i32x4* zf = reinterpret_cast<const i32x4*>(a.z) + (size_t)b * (r32 / 16) * 64 + lane;
-      const i32x4* lf = reinterpret_cast<const i32x4*>(a.l2t) + (size_t)nb * (r32 / 16) * 64 + lane;
-      for (int st = 0; st < r32 / 16; ++st)
+      const i32x4* zf = reinterpret_cast<const i32x4*>(a.z) + (size_t)b * nlr * 64 + lane;
+      int st = 0;
+      if constexpr (PRE) {
+#pragma unroll
+        for (; st < 2; ++st)
+          if (st < nlr)
+            v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lpre[st]),
+                                                        __builtin_bit_cast(bf16x8, zpre[i][st]), v, 0, 0, 0);
+      }
+      for (; st < nlr; ++st)
         v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lf[st * 64]),
                                                     __builtin_bit_cast(bf16x8, zf[st * 64]), v, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x2 bw = *reinterpret_cast<const u32x2*>(a.bias + nb * 32 + 8 * q + 4 * h);
+        const u32x2 bw = PRE ? bpre[q] : *reinterpret_cast<const u32x2*>(a.bias + nb * 32 + 8 * q + 4 * h);
         v[4 * q + 0] += bf16lo(bw.x);
         v[4 * q + 1] += bf16hi(bw.x);
         v[4 * q + 2] += bf16lo(bw.y);
@@ -257,7 +290,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
   if constexpr (KK == 1) {
 #pragma unroll
     for (int j = 0; j < MBW; ++j)
-      if (ti + TT * j < mb) finish(ti + TT * j, acc[j]);
+      if (ti + TT * j < mb) finish(ti + TT * j, j, acc[j]);
   } else {
     // the K parts' sums, added in K-part order
 #pragma unroll
@@ -269,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
       }
     }
     __syncthreads();
-    for (int b = wave; b < mb; b += NW) {
+    for (int b = wave, i = 0; b < mb; b += NW, ++i) {
       f32x16 v;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -278,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
         for (int k = 0; k < KK; ++k) s += red[k][b][e][lane];
         v[e] = s;
       }
-      finish(b, v);
+      finish(b, i, v);
     }
   }
 }
