@@ -274,12 +274,11 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
         if constexpr (FMT == SVDQ_FMT_INT4_G64) {
           amax = s1_max32(amax);                 // the 4 lanes of the 64-channel group
           const float sc = amax / 7.0f;          // IEEE-rounded division
-          // t = x_hat * rcp(s) is within 1.3e-6 of the exact quotient (|q| <= 7,
+          // t = x_hat * rcp(s) is within 2e-6 of the exact quotient (|q| <= 7,
           // rcp within 1 ulp), so rint(t) is the answer unless t lies within
-          // 1e-5 of a half-integer; then the lane redoes its values exactly.
-          // Zero and tiny scales always take the exact path. Adding 1.5 * 2^23
-          // rounds t to an integer (nearest, ties to even) held in the low
-          // mantissa bits, whose low nibble is the two's complement code.
+          // 1e-5 of a half-integer. Adding 1.5 * 2^23 rounds t to an integer
+          // (nearest, ties to even) held in the low mantissa bits, whose low
+          // nibble is the two's complement code.
           constexpr float kRound = 12582912.0f;
           const float inv = __builtin_amdgcn_rcpf(sc);
           float dmax = 0.f;   // largest |t - rint(t)| of the lane
@@ -294,8 +293,8 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
             c0 |= (__float_as_uint(u0) & 15u) << (4 * e);
             c1 |= (__float_as_uint(u1) & 15u) << (4 * e);
           }
-          const bool near = !(sc >= 0x1p-100f) || dmax > 0.49999f;
-          if (near) {
+          if (!(sc >= 0x1p-100f)) {
+            // zero and tiny scales (rcp out of range): one comparison per level
             c0 = 0;
             c1 = 0;
             if (sc > 0.f) {
@@ -304,6 +303,31 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
                 c0 |= ((uint32_t)q_int4_slow(xh[e], sc) & 15u) << (4 * e);
                 c1 |= ((uint32_t)q_int4_slow(xh[8 + e], sc) & 15u) << (4 * e);
               }
+            }
+          } else if (dmax > 0.49999f) {
+            // a value near a half-integer: redo the lane's values exactly.
+            // With k = floor(|t|) the answer is k or k + 1, and the sign of
+            // the fused |x_hat| - (k + 1/2) s, the sign of the exact
+            // difference, decides: above goes up, below stays, zero is an
+            // exact tie and goes to the even one. Where |t| and the exact
+            // quotient lie on two sides of an integer n the pair tested is
+            // (n - 1, n) or (n, n + 1), whose midpoint is still on the right
+            // side of the quotient. k + 1 never passes 7: |x_hat| <= amax <
+            // 7.5 s.
+            c0 = 0;
+            c1 = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float ax = __builtin_fabsf(xh[e]);
+              const float k = __builtin_floorf(ax * inv);
+              const float d = __builtin_fmaf(-(k + 0.5f), sc, ax);
+              const bool up = d > 0.f || (d == 0.f && (__float_as_uint(k + kRound) & 1u));
+              const float q = up ? k + 1.f : k;
+              const uint32_t code = __float_as_uint(__builtin_copysignf(q, xh[e]) + kRound) & 15u;
+              if (e < 8)
+                c0 |= code << (4 * e);
+              else
+                c1 |= code << (4 * (e - 8));
             }
           }
           if (j == 0) reinterpret_cast<float*>(sx)[(size_t)(k0 / 64) * Mp + m] = sc;
