@@ -150,17 +150,26 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   int T = 0;
   for (int p = pb; p < pe; ++p) T += min(ps, nsteps - (p % npc) * ps);
 
-  // issue cursor: piece ip, step is (absolute), its end, and the lane's X rows
+  // issue cursor: piece ip, step is (absolute), its end. The transfers are
+  // buffer loads into LDS: X through a resource over the half's 16 rows
+  // (set per piece), mu and L1 through resources over the whole vectors;
+  // each lane's offset is fixed per piece and the step adds a scalar offset
+  // (no per-transfer address arithmetic).
   int ip = pb, is = 0, iend = 0, iu = 0;
-  const uint16_t* srcA = x;
-  const uint16_t* srcB = x;
+  __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rmu = __builtin_amdgcn_make_buffer_rsrc((void*)mu, 0, K * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rl1 = __builtin_amdgcn_make_buffer_rsrc((void*)l1s, 0, K * NCB * 32, 0x00020000);
+  int vA = 0, vB = 0;   // the lane's X offsets (bytes) in the half's rows
+  const int vmu = (q * 64 + lane) * 4;
   auto issue_piece = [&]() {
     const int g = ip / npc;
     is = (ip - g * npc) * ps;
     iend = min(is + ps, nsteps);
-    const int m0 = g * TG + th * S1_ROWS;
-    srcA = x + (size_t)min(m0 + tA, M - 1) * K + q * 64 + (((lane & 7) ^ ((tA >> 1) & 7)) * 8);
-    srcB = x + (size_t)min(m0 + tB, M - 1) * K + q * 64 + (((lane & 7) ^ ((tB >> 1) & 7)) * 8);
+    // rows past M read row M - 1 (a half wholly past M reads it throughout)
+    const int m0 = g * TG + th * S1_ROWS, m0c = min(m0, M - 1);
+    rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)m0c * K), 0, S1_ROWS * K * 2, 0x00020000);
+    vA = ((min(m0 + tA, M - 1) - m0c) * K + q * 64 + ((lane & 7) ^ ((tA >> 1) & 7)) * 8) * 2;
+    vB = ((min(m0 + tB, M - 1) - m0c) * K + q * 64 + ((lane & 7) ^ ((tB >> 1) & 7)) * 8) * 2;
   };
   issue_piece();
   // compute cursor: piece cp, step cs, its end; the lane's token m (a lane
@@ -187,18 +196,15 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   // issues the same number
 #define S1_ISSUE()                                                                                 \
   {                                                                                                \
-    const bool real_ = iu < T;                                                                     \
-    const size_t xo_ = real_ ? (size_t)is * S1_STEP : 0;                                           \
+    const int st_ = iu < T ? is : 0;   /* past the last step: step 0 of the current rows */        \
     uint8_t* slot_ = smem + (iu % (D + 1)) * Cfg::kSlot;                                           \
-    __builtin_amdgcn_global_load_lds(real_ ? srcA + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ), 16, 0, 0);        \
-    __builtin_amdgcn_global_load_lds(real_ ? srcB + xo_ : x, (s1_lds_void*)(slot_ + wave * S1_XQ + 1024), 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds(real_ ? mu + xo_ + q * 64 + lane : mu,                        \
-                                     (s1_lds_void*)(slot_ + Cfg::kMu + q * 256), 4, 0, 0);          \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (s1_lds_void*)(slot_ + wave * S1_XQ), 16, vA, st_ * S1_STEP * 2, 0, 0);        \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (s1_lds_void*)(slot_ + wave * S1_XQ + 1024), 16, vB, st_ * S1_STEP * 2, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rmu, (s1_lds_void*)(slot_ + Cfg::kMu + q * 256), 4, vmu, st_ * S1_STEP * 4, 0, 0); \
     _Pragma("unroll") for (int f_ = th * FPW; f_ < (th + 1) * FPW; ++f_)                           \
-      __builtin_amdgcn_global_load_lds(                                                            \
-          l1s + (real_ ? ((((size_t)is * S1_WAVES + q) * NCB * 2 + f_) * 64 + lane) * 8 : (size_t)lane * 8), \
-          (s1_lds_void*)(slot_ + Cfg::kL1 + (q * 2 * NCB + f_) * 1024), 16, 0, 0);                 \
-    if (real_ && ++is == iend && ++ip < pe) issue_piece();                                         \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl1, (s1_lds_void*)(slot_ + Cfg::kL1 + (q * 2 * NCB + f_) * 1024), 16,   \
+                                               ((q * NCB * 2 + f_) * 64 + lane) * 16, st_ * S1_WAVES * NCB * 2048, 0, 0); \
+    if (iu < T && ++is == iend && ++ip < pe) issue_piece();                                        \
     ++iu;                                                                                          \
   }
 #define S1_WAIT_CASE(k)                                                                            \
