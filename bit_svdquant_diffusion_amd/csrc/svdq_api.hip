@@ -59,9 +59,11 @@ svdq_status common_checks(const svdq_layer_desc* d, const svdq_packed* dev, cons
   svdq_status st = check_desc(d);
   if (st != SVDQ_OK) return st;
   if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
-  // MXFP4 activation scale bytes are addressed with 32-bit stage offsets
+  // MXFP4 activation scale bytes are addressed with 32-bit stage offsets,
+  // the tiled INT4 GEMM's activation codes with 32-bit byte offsets
   if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)d->K + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
     return SVDQ_ERR_SHAPE;
+  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * d->K > ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
@@ -186,7 +188,7 @@ svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_pack
   svdq_status st = check_desc(d);
   if (st != SVDQ_OK) return st;
   if (d->format != SVDQ_FMT_INT4_G64) return SVDQ_ERR_FORMAT;
-  if (M <= 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
+  if (M <= 0 || M > (1 << 24) || round32(M) * d->K > ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (!ws || !p) return SVDQ_ERR_NULL;

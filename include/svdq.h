@@ -38,7 +38,8 @@
  *     pointer after returning.
  *   - Shapes: K % 256 == 0, N % 32 == 0, 0 <= rank <= 128 with rank % 16 == 0,
  *     rank <= min(K, N); M >= 0 (M == 0 is a no-op returning SVDQ_OK).
- *     K, N <= 65536; M <= 2^24; MXFP4 also (K + 128) * ceil(M / 32) < 2^31.
+ *     K, N <= 65536; M <= 2^24; MXFP4 also (K + 128) * ceil(M / 32) < 2^31,
+ *     INT4 also 32 * ceil(M / 32) * K <= 2^33 (activation codes of at most 4 GiB).
  *   - Device pointers (x, y, workspace and every packed buffer) must be
  *     16-byte aligned; a misaligned pointer returns SVDQ_ERR_SHAPE.
  *   - All functions are thread-safe; the only global state is a per-device

@@ -96,11 +96,15 @@ def test_forward_validation_before_device():
         st = L.svdq_linear_forward(ctypes.byref(big), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
                                    ws.ctypes.data, ws.nbytes, None)
         assert st == want, (M, st)
-    # the same shape in INT4 has no such bound (only the workspace is short)
+    # INT4 activation codes use 32-bit byte offsets: round32(M) * K <= 2^33
     big4 = S.LayerDesc(65536, 512, 16, 0)
-    st = L.svdq_linear_forward(ctypes.byref(big4), ctypes.byref(p), x.ctypes.data, 1 << 20, y.ctypes.data,
-                               ws.ctypes.data, ws.nbytes, None)
-    assert st == 4
+    for M, want in ((1 << 17, 4), ((1 << 17) + 1, 2), (1 << 20, 2)):
+        st = L.svdq_linear_forward(ctypes.byref(big4), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
+                                   ws.ctypes.data, ws.nbytes, None)
+        assert st == want, (M, st)
+        st = L.svdq_debug_int4_group_sums(ctypes.byref(big4), ctypes.byref(p), ws.ctypes.data, ws.nbytes, M,
+                                          0, 1, 0, 1, ws.ctypes.data, None)
+        assert st == want, ("group sums", M, st)
     # debug hook: format and window checks
     d4 = S.LayerDesc(512, 512, 16, 1)
     pp = ctypes.byref(p)
