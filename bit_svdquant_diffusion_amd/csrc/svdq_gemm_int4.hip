@@ -18,7 +18,7 @@
 // vector instructions per output and group, acc += float(256 P) * s, in fp32.
 //
 // Data path and schedule follow the MXFP4 kernel: persistent workgroups (one
-// per CU) walk 128 x 256 tiles; direct global->LDS transfers of 16 bytes per
+// per CU) walk 128 x 256 tiles; direct buffer loads into LDS of 16 bytes per
 // lane fill a ring of LDS slots across tile boundaries; eight waves, 2 (M) x
 // 4 (N), each own 64 x 64 (2 x 2 blocks of 32 x 32); one workgroup barrier
 // per 128-channel stage (two groups). The low-rank branch is r32/32 more
@@ -183,11 +183,20 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   long long is_u = u0;
   uint32_t src[2 * kFragPerWave], ssrc = 0, bsrc = 0, sstride = 0;
   const int per_l = a.r32 / 16;
-  const uint8_t* const sx_b = reinterpret_cast<const uint8_t*>(a.sx);
-  const uint8_t* const sw_b = reinterpret_cast<const uint8_t*>(a.sw);
-  const uint8_t* const z_b = reinterpret_cast<const uint8_t*>(a.z);
-  const uint8_t* const l2_b = reinterpret_cast<const uint8_t*>(a.l2t);
-  const uint8_t* const bias_b = reinterpret_cast<const uint8_t*>(a.bias);
+  // every source as a buffer resource over the whole operand: a transfer is
+  // one buffer load into LDS with the lane's 32-bit offset and the stage as
+  // a scalar offset (the API keeps the codes below 4 GiB)
+  auto rsrc = [](const void* p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)(uint32_t)min(bytes, (uint64_t)0xFFFFFFFFu),
+                                             0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rqx = rsrc(a.qx, (uint64_t)g.MB * g.KS * 1024);
+  const __amdgpu_buffer_rsrc_t rqw = rsrc(a.qw, (uint64_t)g.NB * g.KS * 1024);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(a.z, (uint64_t)g.MB * per_l * 1024);
+  const __amdgpu_buffer_rsrc_t rl2 = rsrc(a.l2t, (uint64_t)g.NB * per_l * 1024);
+  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, (uint64_t)g.KS * g.act_rows * 4);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, (uint64_t)g.KS * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rbias = rsrc(a.bias, (uint64_t)g.N * 2);
 #define SVDQ_ISSUE(GS)                                                                              \
   {                                                                                                 \
     if (is_s == 0) {                                                                                \
@@ -224,22 +233,23 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     if (lrs && a.r32 == 0) {                                                                        \
       /* no low-rank fragments: every transfer of the stage moves the bias */                      \
       _Pragma("unroll") for (int k = 0; k < kFragPerWave + 1; ++k)                                  \
-        if (k < nops && lane < 32) __builtin_amdgcn_global_load_lds(bias_b + bsrc, lds_ptr(slot_w + kScA), 16, 0, 0); \
+        if (k < nops && lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
     } else {                                                                                        \
       _Pragma("unroll") for (int k = 0; k < kFragPerWave; ++k) {                                    \
         const int it = frag0 + k;                                                                   \
         const bool isA = it < 2 * kMB;                                                              \
         const int dst = isA ? kCodeA + it * 1024 : kCodeB + (it - 2 * kMB) * 1024;                  \
-        const uint8_t* base = lrs ? (isA ? z_b : l2_b) : (isA ? a.qx : a.qw);                       \
-        __builtin_amdgcn_global_load_lds(base + (src[(lrs ? kFragPerWave : 0) + k] + (uint32_t)sl * 2048), \
-                                         lds_ptr(slot_w + dst), 16, 0, 0);                          \
+        const __amdgpu_buffer_rsrc_t rs = lrs ? (isA ? rz : rl2) : (isA ? rqx : rqw);                \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(slot_w + dst), 16, src[(lrs ? kFragPerWave : 0) + k], \
+                                                 sl * 2048, 0, 0);                                  \
       }                                                                                             \
       if (sop >= 0) {                                                                               \
         if (lrs) {                                                                                  \
-          if (lane < 32) __builtin_amdgcn_global_load_lds(bias_b + bsrc, lds_ptr(slot_w + kScA), 16, 0, 0); \
+          if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
         } else {                                                                                    \
-          __builtin_amdgcn_global_load_lds((sop == 0 ? sx_b : sw_b) + (ssrc + (uint32_t)sl * sstride), \
-                                           lds_ptr(slot_w + (sop == 0 ? kScA : kScB + 1024 * (sop - 1))), 16, 0, 0); \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(sop == 0 ? rsx : rsw,                            \
+                                                   lds_ptr(slot_w + (sop == 0 ? kScA : kScB + 1024 * (sop - 1))), 16, \
+                                                   ssrc, sl * sstride, 0, 0);                       \
         }                                                                                           \
       }                                                                                             \
     }                                                                                               \
