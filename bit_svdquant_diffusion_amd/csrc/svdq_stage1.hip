@@ -150,46 +150,51 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   int T = 0;
   for (int p = pb; p < pe; ++p) T += min(ps, nsteps - (p % npc) * ps);
 
-  // issue cursor: piece ip, step is (absolute), its end. The transfers are
-  // buffer loads into LDS: X through a resource over the half's 16 rows
-  // (set per piece), mu and L1 through resources over the whole vectors;
-  // each lane's offset is fixed per piece and the step adds a scalar offset
-  // (no per-transfer address arithmetic).
-  int ip = pb, is = 0, iend = 0, iu = 0;
+  // issue cursor: piece ip (group ig, piece ic in it), step is (absolute),
+  // its end. The cursors advance by increments: a group's rows are set up
+  // only when the group changes. The transfers are buffer loads into LDS: X
+  // through a resource over the half's 16 rows, mu and L1 through resources
+  // over the whole vectors; each lane's offset is fixed per group and the
+  // step adds a scalar offset (no per-transfer address arithmetic).
+  int ip = pb, ig = pb / npc, ic = pb - (pb / npc) * npc, is = 0, iend = 0, iu = 0;
   __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t rmu = __builtin_amdgcn_make_buffer_rsrc((void*)mu, 0, K * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rl1 = __builtin_amdgcn_make_buffer_rsrc((void*)l1s, 0, K * NCB * 32, 0x00020000);
   int vA = 0, vB = 0;   // the lane's X offsets (bytes) in the half's rows
   const int vmu = (q * 64 + lane) * 4;
-  auto issue_piece = [&]() {
-    const int g = ip / npc;
-    is = (ip - g * npc) * ps;
-    iend = min(is + ps, nsteps);
+  auto issue_group = [&]() {
     // rows past M read row M - 1 (a half wholly past M reads it throughout)
-    const int m0 = g * TG + th * S1_ROWS, m0c = min(m0, M - 1);
+    const int m0 = ig * TG + th * S1_ROWS, m0c = min(m0, M - 1);
     rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)m0c * K), 0, S1_ROWS * K * 2, 0x00020000);
     vA = ((min(m0 + tA, M - 1) - m0c) * K + q * 64 + ((lane & 7) ^ ((tA >> 1) & 7)) * 8) * 2;
     vB = ((min(m0 + tB, M - 1) - m0c) * K + q * 64 + ((lane & 7) ^ ((tB >> 1) & 7)) * 8) * 2;
   };
-  issue_piece();
-  // compute cursor: piece cp, step cs, its end; the lane's token m (a lane
-  // past M holds token M - 1's values, its X rows being clamped, and stores
-  // them again, so every store always issues)
-  int cp = pb, cs = 0, cend = 0, cg = 0, cc = 0, m = 0;
+  is = ic * ps;
+  iend = min(is + ps, nsteps);
+  issue_group();
+  // compute cursor: piece cp (group cg, piece cc in it), step cs, its end;
+  // the lane's token m (a lane past M holds token M - 1's values, its X rows
+  // being clamped, and stores them again, so every store always issues)
+  int cp = pb, cg = ig, cc = ic, cs = is, cend = iend, m = 0;
   f32x4 zacc[NCB > 0 ? NCB : 1];   // this piece's partial Z of the wave's quarter
   f32x4 zrun[NCB > 0 ? NCB : 1];   // the sum over the group's pieces so far (whole-group mode)
 #pragma unroll
   for (int c = 0; c < NCB; ++c) zrun[c] = f32x4{};
-  auto compute_piece = [&]() {
-    cg = cp / npc;
-    cc = cp - cg * npc;
-    cs = cc * ps;
+  m = min(cg * TG + th * S1_ROWS + r, M - 1);
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
+  // the next piece of the compute cursor (cs is already its first step)
+  auto compute_next = [&]() {
+    if (++cc == npc) {
+      cc = 0;
+      cs = 0;
+      ++cg;
+      m = min(cg * TG + th * S1_ROWS + r, M - 1);
+    }
     cend = min(cs + ps, nsteps);
-    m = min(cg * TG + th * S1_ROWS + r, M - 1);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
   };
-  compute_piece();
 
   // ring transfers of the next step of the issue cursor; past the last step
   // they re-read the first bytes of X and mu into the slot, so every step
@@ -204,7 +209,15 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     _Pragma("unroll") for (int f_ = th * FPW; f_ < (th + 1) * FPW; ++f_)                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl1, (s1_lds_void*)(slot_ + Cfg::kL1 + (q * 2 * NCB + f_) * 1024), 16,   \
                                                ((q * NCB * 2 + f_) * 64 + lane) * 16, st_ * S1_WAVES * NCB * 2048, 0, 0); \
-    if (iu < T && ++is == iend && ++ip < pe) issue_piece();                                        \
+    if (iu < T && ++is == iend && ++ip < pe) {                                                     \
+      if (++ic == npc) {                                                                           \
+        ic = 0;                                                                                    \
+        is = 0;                                                                                    \
+        ++ig;                                                                                      \
+        issue_group();                                                                             \
+      }                                                                                            \
+      iend = min(is + ps, nsteps);                                                                 \
+    }                                                                                              \
     ++iu;                                                                                          \
   }
 #define S1_WAIT_CASE(k)                                                                            \
@@ -371,7 +384,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
             }
           }
           ++cp;
-          if (cp < pe) compute_piece();
+          if (cp < pe) compute_next();
         }
   }
 #undef S1_ISSUE
