@@ -180,7 +180,26 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   f32x4 zrun[NCB > 0 ? NCB : 1];   // the sum over the group's pieces so far (whole-group mode)
 #pragma unroll
   for (int c = 0; c < NCB; ++c) zrun[c] = f32x4{};
-  m = min(cg * TG + th * S1_ROWS + r, M - 1);
+  // Stores as buffer stores: the codes through a resource over the group
+  // half's 32-row block (every lane's m lies in it, rows past M included),
+  // the scales through one over the whole scale area; each lane's offset is
+  // fixed per group and the step adds a scalar offset.
+  __amdgpu_buffer_rsrc_t rcode = rx;
+  int vcode = 0, vsx = 0;
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
+      sx, 0, FMT == SVDQ_FMT_INT4_G64 ? (K / 64) * Mp * 4 : (K / 128) * MB * 128, 0x00020000);
+  auto compute_group = [&]() {
+    m = min(cg * TG + th * S1_ROWS + r, M - 1);
+    const int rb = min(cg * TG + th * S1_ROWS, M - 1) / 32;
+    rcode = __builtin_amdgcn_make_buffer_rsrc(qx + (size_t)rb * (K / 64) * 1024, 0, K * 16, 0x00020000);
+    vcode = (32 * (j >> 1) + m % 32) * 16 + (j & 1) * 8;
+    // INT4: fp32 [K/64][Mp]; MXFP4: the byte of 32-channel block
+    // kb = k0 / 32 + j / 2, k0 = 256 cs + 64 q, at ((kb / 4) MB + m / 32) 128
+    // + (32 (kb % 2) + m % 32) 2 + (kb / 2) % 2, whose step part is 256 MB cs
+    vsx = FMT == SVDQ_FMT_INT4_G64 ? m * 4
+                                   : ((q >> 1) * MB + m / 32) * 128 + (32 * (j >> 1) + m % 32) * 2 + (q & 1);
+  };
+  compute_group();
 #pragma unroll
   for (int c = 0; c < NCB; ++c) zacc[c] = f32x4{};
   // the next piece of the compute cursor (cs is already its first step)
@@ -189,7 +208,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
       cc = 0;
       cs = 0;
       ++cg;
-      m = min(cg * TG + th * S1_ROWS + r, M - 1);
+      compute_group();
     }
     cend = min(cs + ps, nsteps);
 #pragma unroll
@@ -349,7 +368,7 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
                 c1 |= code << (4 * (e - 8));
             }
           }
-          if (j == 0) reinterpret_cast<float*>(sx)[(size_t)(k0 / 64) * Mp + m] = sc;
+          if (j == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsx, vsx, (cs * 4 + q) * Mp * 4, 0);
         } else {
           const int e = mx_exponent(amax);       // block b = j / 2 of the quarter
           c0 = s1_e2m1x8(xh, e);
@@ -357,16 +376,13 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
           if ((j & 1) == 0) {
             // fragment-order scale byte of 32-channel block kb = k0/32 + j/2:
             // stage kb/4, step (kb%4)/2, half kb%2
-            const int kb = k0 / 32 + (j >> 1);
-            reinterpret_cast<uint8_t*>(sx)[(((size_t)(kb >> 2) * MB + m / 32) * 64 + 32 * (kb & 1) + m % 32) * 2 +
-                                           ((kb >> 1) & 1)] = (uint8_t)(e + 127);
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(e + 127), rsx, vsx, cs * MB * 256, 0);
           }
         }
         {
           // fragment order: 64-channel step k0/64 of row block m/32; channels
           // 32h .. 32h+31 at lane 32h + m%32, 16 channels = 8 bytes
-          uint8_t* blk = qx + ((size_t)(m / 32) * (K / 64) + k0 / 64) * 1024;
-          *reinterpret_cast<u32x2*>(blk + (32 * (j >> 1) + m % 32) * 16 + (j & 1) * 8) = u32x2{c0, c1};
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, rcode, vcode, (cs * 4 + q) * 1024, 0);
         }
 
 
