@@ -50,6 +50,18 @@ constexpr int kStores = 2 * 3 * 3;                 // 16-byte Y stores per wave 
 // five of the 24 B blocks (wave 7 repeats its last block: same bytes to the
 // same place). Each wave reads a single operand.
 constexpr int kOps = 5;
+// LDS position p of a B block (0..11 in a tile) holds the tile's block
+// bperm(p): odd wave columns take their three blocks in reverse. Two waves
+// share a 128-byte line of a Y row (tile blocks 2 and 3, and 8 and 9); with
+// the reversal both store their halves of it at the same epilogue step
+// (j = 2), so the line is whole when it leaves L2. An involution; positions
+// past the tile's blocks (scale and bias padding) map to themselves.
+__host__ __device__ constexpr int bperm(int p) {
+  return p < kNBt && ((p / kTN) & 1) ? p / kTN * kTN + (kTN - 1) - p % kTN : p;
+}
+static_assert(bperm(2) == 2 && bperm(3) == 5 && bperm(5) == 3 && bperm(8) == 8 && bperm(9) == 11 &&
+                  bperm(11) == 9 && bperm(12) == 12,
+              "shared lines (blocks 2|3, 8|9) at the same step of both waves");
 __host__ __device__ constexpr int kItem(int w, int k) {   // fragment item 0..35 of transfer k of wave w
   return w < 3 ? 4 * w + k : (12 + 5 * (w - 3) + k < 36 ? 12 + 5 * (w - 3) + k : 35);
 }
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
                                                nbl * per_l * 1024, kRsrcWord3);                     \
       _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                            \
         const int it = kItem(wave, k) - (opA ? 0 : 2 * kMB);   /* item within the operand */       \
-        const int bl = min(it >> 1, nbl - 1);                  /* block within the tile */         \
+        const int bl = min(opA ? it >> 1 : bperm(it >> 1), nbl - 1);   /* block within the tile */ \
         vcur[k] = (uint32_t)((bl * g.KS + (it & 1)) * 1024 + lane * 16);                            \
         vlow[k] = (uint32_t)((bl * per_l + (it & 1)) * 1024 + lane * 16);                           \
       }                                                                                             \
@@ -166,9 +178,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
         rsc = __builtin_amdgcn_make_buffer_rsrc(                                                    \
             (void*)(reinterpret_cast<const uint8_t*>(isA ? a.sx : a.sw) + (size_t)base * 128), 0,    \
             (g.nst - 1) * sstride + (lim - base) * 128, kRsrcWord3);                                \
-        soff = (min(base + blk, lim - 1) - base) * 128 + (lane & 7) * 16;                           \
+        soff = (min(base + (isA ? blk : bperm(blk)), lim - 1) - base) * 128 + (lane & 7) * 16;      \
         ssoffs = 0;                                                                                 \
-        boff = min(nb0 * 32 + 8 * lane, g.N - 8) * 2;                                               \
+        boff = min(nb0 * 32 + 32 * bperm(lane >> 2) + 8 * (lane & 3), g.N - 8) * 2;                 \
       }                                                                                             \
     } else if (is_s == g.nst) {                                                                     \
       rcur = rlow;                                                                                  \
@@ -276,7 +288,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   for (int p = 0; p < kNStage - 1; ++p) SVDQ_ISSUE(p)
   for (int ct = 0; ct < my_tiles; ++ct) {
     const TileMap tmc = map_tile((int)blockIdx.x + ct * grid, g.tiles_m, g.tiles_n, kGroupM);
-    const int n0 = tmc.tn * kBN + wn * kWN;
+    const int n0 = tmc.tn * kBN;
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
@@ -323,7 +335,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
         }
         // always issued (the ring waits count them); the resource drops rows
         // past M and a block past N is sent past the end
-        const int col = n0 + 32 * j + 8 * h;
+        const int col = n0 + 32 * bperm(wn * kTN + j) + 8 * h;
         const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
