@@ -116,7 +116,7 @@ def time_graph(calls, reps, torch):
     with torch.cuda.graph(g):
         for c in calls:
             c()
-    for _ in range(3):
+    for _ in range(max(3, reps)):   # untimed replays as many as the timed ones
         g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
