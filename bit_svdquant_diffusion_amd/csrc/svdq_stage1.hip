@@ -503,12 +503,16 @@ static hipError_t launch_t(const Stage1Args& a, int num_cus, hipStream_t st) {
 // Two token halves per workgroup halve the L1 bytes but also the number of
 // workgroups. MXFP4 quantization is cheap, so that pays from 2048 tokens on;
 // the INT4 quantizer's vector work wants every CU, so INT4 takes two halves
-// only once 32-token workgroups fill the 256 CUs.
+// only once 32-token workgroups fill the 256 CUs, and only for long K: at
+// K = 3072 one half per workgroup (two workgroups per CU) is the faster up
+// to 16384 tokens at least, at K = 12288 two halves are.
 constexpr int kTwoHalvesMinM[2] = {8192, 2048};   // INT4, MXFP4
+constexpr int kTwoHalvesMinKInt4 = 6144;
 
 template <int FMT>
 static hipError_t launch_fmt(const Stage1Args& a, int cus, hipStream_t st) {
-  const bool two = a.M >= kTwoHalvesMinM[FMT == SVDQ_FMT_MXFP4_G32 ? 1 : 0];
+  const bool two = FMT == SVDQ_FMT_MXFP4_G32 ? a.M >= kTwoHalvesMinM[1]
+                                             : a.M >= kTwoHalvesMinM[0] && a.K >= kTwoHalvesMinKInt4;
   switch (a.r32) {
     case 0: return two ? launch_t<FMT, 0, 2>(a, cus, st) : launch_t<FMT, 0, 1>(a, cus, st);
     case 32: return two ? launch_t<FMT, 2, 2>(a, cus, st) : launch_t<FMT, 2, 1>(a, cus, st);

@@ -48,10 +48,12 @@ SMALL = [
     _spec("r128", 200, 256, 160, 128, "int4", 14),
     _spec("r128_fp4", 200, 256, 160, 128, "mxfp4", 14),
     _spec("wide_k", 96, 2048, 64, 48, "int4", 15),
-    # 32-token stage-1 workgroups (MXFP4 from M = 2048, INT4 from M = 8192):
-    # the last workgroup's second half holds 2 tokens (M = 2066, 8194) or 4
-    # (M = 2100, rank32 = 64)
-    _spec("two_halves_m8194", 8194, 256, 64, 32, "int4", 16),
+    # 32-token stage-1 workgroups (MXFP4 from M = 2048, INT4 from M = 8192
+    # with K >= 6144): the last workgroup's second half holds 2 tokens
+    # (M = 2066, 8194) or 4 (M = 2100, rank32 = 64). INT4 with a short K
+    # keeps 16-token workgroups at M = 8194, the last one holding 2 tokens.
+    _spec("two_halves_m8194", 8194, 6144, 64, 32, "int4", 16),
+    _spec("one_half_m8194_short_k", 8194, 256, 64, 32, "int4", 16),
     _spec("two_halves_m2066_fp4", 2066, 512, 256, 32, "mxfp4", 16),
     _spec("two_halves_m2100_r48_fp4", 2100, 256, 96, 48, "mxfp4", 17),
     # INT4 GEMM split: 6 tiles of 24 K stages on 6 XCDs, each cut into four
