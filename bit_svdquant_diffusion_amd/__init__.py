@@ -279,9 +279,14 @@ def unpack_workspace(layer: Layer, M: int, ws_host: np.ndarray) -> dict:
 
 
 def debug_int4_group_sums(layer: Layer, dev: dict, workspace, M: int, m0: int, mc: int,
-                          n0: int, nc: int, stream=None):
+                          n0: int, nc: int, stream=None, out=None):
+    """int32 group sums P [mc][nc][K/64] of the window, from the GEMM kernel the
+    forward runs for this M. ``out`` (int32 device tensor of that shape) is
+    written in place when given."""
     import torch
-    p_out = torch.empty((mc, nc, layer.K // 64), dtype=torch.int32, device=workspace.device)
+    p_out = out if out is not None else torch.empty((mc, nc, layer.K // 64), dtype=torch.int32,
+                                                    device=workspace.device)
+    assert p_out.dtype == torch.int32 and p_out.is_contiguous() and p_out.numel() == mc * nc * (layer.K // 64)
     p = _packed_struct(layer, dev)
     d = layer.desc
     _check(lib().svdq_debug_int4_group_sums(ctypes.byref(d), ctypes.byref(p), _ptr(workspace),

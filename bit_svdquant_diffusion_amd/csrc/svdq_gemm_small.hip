@@ -81,7 +81,11 @@ __device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int
 // MB is the most token blocks the instance serves; the layer has
 // mb = ceil(M / 32) of them. part (splits > 1): sums [sp][token block][channel
 // block][64 lanes][16].
-template <int FMT, int MB, int TT, int PD, int NW>
+// DEBUG_P (INT4 only): the same loads, widening and i8 MFMAs, but each group's
+// exact sum P = (256 P) / 256 of the outputs inside the window [m0, m0 + mc)
+// x [n0, n0 + nc) is written to a.p ([mc][nc][K/64] int32) instead of being
+// dequantized; no epilogue.
+template <int FMT, int MB, int TT, int PD, int NW, bool DEBUG_P>
 __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int splits, float* part) {
   constexpr bool FP4 = FMT == SVDQ_FMT_MXFP4_G32;
   constexpr int FPU = FP4 ? 2 : 1;          // 64-channel fragments per K unit
@@ -183,7 +187,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
       for (int p = 0; p < NP; ++p) fx[slot][p] = __builtin_amdgcn_raw_buffer_load_b32(rsx, sxo[p], gg * act_rows * 4, 0);
     }
   };
-  auto mult = [&](int u) {
+  // unit u of the ring holds K unit (group) grp
+  auto mult = [&](int u, int grp) {
     if constexpr (FP4) {
       // weight fragment as operand A (channels as rows), the scale bytes of
       // step f selected by opsel f
@@ -215,8 +220,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
             sm_widen(fa[u][j][0], alo, ahi);
             i32x16 pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo, alo, i32x16{}, 0, 0, 0);
             pp = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi, ahi, pp, 0, 0, 0);
+            if constexpr (DEBUG_P) {
+              // token (ti + TT j) 32 + lr, channel nb 32 + 8 (e / 4) + 4 h + e % 4;
+              // surplus parts (a clamped, repeated block) write nothing
+              const int tok = (ti + TT * j) * 32 + lr;
+              if (ti + TT * j < mb && tok >= a.m0 && tok < a.m0 + a.mc && tok < a.M) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[j][e] = __builtin_fmaf((float)pp[e], r[16 * bb + e], acc[j][e]);
+                for (int e = 0; e < 16; ++e) {
+                  const int ch = nb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                  if (ch >= a.n0 && ch < a.n0 + a.nc)
+                    a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * KS + grp] = pp[e] / 256;
+                }
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[j][e] = __builtin_fmaf((float)pp[e], r[16 * bb + e], acc[j][e]);
+            }
           }
         }
       }
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
 #pragma unroll
       for (int u = 0; u <= PD; ++u) {
         load((u + PD) % (PD + 1), g + u + PD);
-        mult(u);
+        mult(u, g + u);
         __builtin_amdgcn_sched_barrier(0);   // keep each step's loads at its start
       }
     }
@@ -247,8 +266,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
     const int rem = n - rounds * (PD + 1);
 #pragma unroll
     for (int u = 0; u < PD; ++u)
-      if (u < rem) mult(u);
+      if (u < rem) mult(u, g + u);
   }
+  if constexpr (DEBUG_P) return;
 
   // block b, the wave's i-th finished block
   auto finish = [&](int b, int i, f32x16 v) {
@@ -336,7 +356,6 @@ __global__ __launch_bounds__(64) void gemm_small_sum(const float* __restrict__ p
 }
 
 bool gemm_small_fits(const GemmArgs& a, int num_cus) {
-  if (a.p != nullptr) return false;
   if (a.M <= kFewTokens) return true;
   if (a.fmt != SVDQ_FMT_INT4_G64 || a.M <= 768 || a.M > 1024) return false;
   // 769 to 1024 INT4 tokens run one eight-wave workgroup per CU at a time:
@@ -354,7 +373,7 @@ bool gemm_small_fits(const GemmArgs& a, int num_cus) {
 // the channel blocks cannot fill half the CUs, and K shares (with an fp32
 // partial pass) only while CUs would otherwise idle and each wave keeps 512
 // channels or more.
-template <int FMT, int MB, int TT, int PD, int NW>
+template <int FMT, int MB, int TT, int PD, int NW, bool DBG>
 static hipError_t launch_nw(const GemmArgs& a, int num_cus, hipStream_t st) {
   constexpr int KK = NW / TT, FPU = FMT == SVDQ_FMT_MXFP4_G32 ? 2 : 1;
   const int KU = a.K / 64 / FPU, NB = a.N / 32;
@@ -365,41 +384,47 @@ static hipError_t launch_nw(const GemmArgs& a, int num_cus, hipStream_t st) {
   const size_t per_split = (size_t)mb * 32 * a.N * 4;   // fp32 partial bytes of one share
   while (splits > 1 && (size_t)splits * per_split > (size_t)kSplitSlots * kSplitPartBytes) --splits;
   if (a.part == nullptr) splits = 1;   // no partial area: whole K per workgroup
-  hipLaunchKernelGGL((gemm_small_kernel<FMT, MB, TT, PD, NW>), dim3(NB * splits), dim3(64 * NW), 0, st, a, splits,
-                     a.part);
+  hipLaunchKernelGGL((gemm_small_kernel<FMT, MB, TT, PD, NW, DBG>), dim3(NB * splits), dim3(64 * NW), 0, st, a,
+                     splits, a.part);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || splits == 1 || DBG) return e;
   hipLaunchKernelGGL(gemm_small_sum, dim3(mb * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, mb, splits);
   return hipGetLastError();
 }
 
-template <int FMT, int MB, int TT>
+template <int FMT, int MB, int TT, bool DBG>
 static hipError_t launch_shape(const GemmArgs& a, int num_cus, hipStream_t st) {
   const int cus = num_cus > 0 ? num_cus : 256;
-  return 2 * (a.N / 32) <= cus ? launch_nw<FMT, MB, TT, 2, 8>(a, num_cus, st)
-                               : launch_nw<FMT, MB, TT, 2, 4>(a, num_cus, st);
+  return 2 * (a.N / 32) <= cus ? launch_nw<FMT, MB, TT, 2, 8, DBG>(a, num_cus, st)
+                               : launch_nw<FMT, MB, TT, 2, 4, DBG>(a, num_cus, st);
 }
 
-template <int FMT>
+template <int FMT, bool DBG>
 static hipError_t launch_fmt(const GemmArgs& a, int num_cus, hipStream_t st) {
   switch ((a.M + 31) / 32) {   // exact token blocks: no read past the round32(M) rows
-    case 1: return launch_shape<FMT, 1, 1>(a, num_cus, st);
-    case 2: return launch_shape<FMT, 2, 1>(a, num_cus, st);
-    case 3: return launch_shape<FMT, 3, 1>(a, num_cus, st);
-    case 4: return launch_shape<FMT, 4, 2>(a, num_cus, st);
-    case 5: return launch_shape<FMT, 5, 4>(a, num_cus, st);
-    case 6: return launch_shape<FMT, 6, 4>(a, num_cus, st);
-    case 7: return launch_shape<FMT, 7, 4>(a, num_cus, st);
-    default: return launch_shape<FMT, 8, 4>(a, num_cus, st);
+    case 1: return launch_shape<FMT, 1, 1, DBG>(a, num_cus, st);
+    case 2: return launch_shape<FMT, 2, 1, DBG>(a, num_cus, st);
+    case 3: return launch_shape<FMT, 3, 1, DBG>(a, num_cus, st);
+    case 4: return launch_shape<FMT, 4, 2, DBG>(a, num_cus, st);
+    case 5: return launch_shape<FMT, 5, 4, DBG>(a, num_cus, st);
+    case 6: return launch_shape<FMT, 6, 4, DBG>(a, num_cus, st);
+    case 7: return launch_shape<FMT, 7, 4, DBG>(a, num_cus, st);
+    default: return launch_shape<FMT, 8, 4, DBG>(a, num_cus, st);
   }
 }
 
-hipError_t launch_gemm_small(const GemmArgs& a, int num_cus, hipStream_t st) {
-  if (a.fmt == SVDQ_FMT_MXFP4_G32) return launch_fmt<SVDQ_FMT_MXFP4_G32>(a, num_cus, st);
+template <bool DBG>
+static hipError_t launch_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   // 769 to 1024 INT4 tokens: eight token parts of four blocks each (the last
   // parts' surplus blocks repeat the last block and are dropped)
-  if (a.M > 256) return launch_nw<SVDQ_FMT_INT4_G64, 32, 8, 2, 8>(a, num_cus, st);
-  return launch_fmt<SVDQ_FMT_INT4_G64>(a, num_cus, st);
+  if (a.M > 256) return launch_nw<SVDQ_FMT_INT4_G64, 32, 8, 2, 8, DBG>(a, num_cus, st);
+  return launch_fmt<SVDQ_FMT_INT4_G64, DBG>(a, num_cus, st);
+}
+
+hipError_t launch_gemm_small(const GemmArgs& a, int num_cus, hipStream_t st) {
+  if (a.fmt == SVDQ_FMT_MXFP4_G32) return launch_fmt<SVDQ_FMT_MXFP4_G32, false>(a, num_cus, st);
+  // the group-sum hook runs the forward's own launch shape with DEBUG_P
+  return a.p != nullptr ? launch_int4<true>(a, num_cus, st) : launch_int4<false>(a, num_cus, st);
 }
 
 }  // namespace svdq

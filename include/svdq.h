@@ -18,7 +18,8 @@
  * quantization and X_hat L1, and the 4-bit GEMM's epilogue adds (X_hat L1) L2
  * and b before the only write of Y.
  *
- * Formats ("SVDQuant supports both INT4 and FP4 data types", aiflownews.com):
+ * Formats (the pages give both a 4-bit integer and a 4-bit float variant;
+ * aiflownews.com, "What SVDQuant actually does"):
  *   SVDQ_FMT_INT4_G64 : symmetric INT4 codes in [-7, 7] with an fp32 scale
  *                       max|v|/7 per 64 consecutive input channels (per token
  *                       for X, per output channel for R); codes are rounded
@@ -39,7 +40,7 @@
  *   - Shapes: K % 256 == 0, N % 32 == 0, 0 <= rank <= 128 with rank % 16 == 0,
  *     rank <= min(K, N); M >= 0 (M == 0 is a no-op returning SVDQ_OK).
  *     K, N <= 65536; M <= 2^24; MXFP4 also (K + 128) * ceil(M / 32) < 2^31,
- *     INT4 also 32 * ceil(M / 32) * K <= 2^33 (activation codes of at most 4 GiB).
+ *     INT4 also 32 * ceil(M / 32) * K < 2^33 (activation codes below 4 GiB).
  *   - Device pointers (x, y, workspace and every packed buffer) must be
  *     16-byte aligned; a misaligned pointer returns SVDQ_ERR_SHAPE.
  *   - All functions are thread-safe; the only global state is a per-device
@@ -131,9 +132,9 @@ SVDQ_API int32_t svdq_version(void);
 SVDQ_API svdq_status svdq_packed_bytes(const svdq_layer_desc* desc, svdq_packed_sizes* out);
 
 /*
- * Offline preparation of one layer, host only (the pages' "calibration,
- * quantization, packaging" step; aiflownews.com, "Deep integration with
- * Hugging Face Diffusers"):
+ * Offline preparation of one layer, host only (the offline calibrate, quantize
+ * and package step of aiflownews.com, "Deep integration with Hugging Face
+ * Diffusers"):
  *   1. lambda_k = sqrt(act_absmax[k] / max_n |W[k,n]|) (1 where either is 0),
  *      mu_k = fl32(1/lambda_k); W_hat[k,n] = W[k,n] / mu_k in fp64;
  *   2. the top-`rank` singular triplets of W_hat by randomized subspace
@@ -232,8 +233,12 @@ SVDQ_API svdq_status svdq_unpack_workspace(const svdq_layer_desc* desc, int64_t 
 /*
  * Test hook (INT4 only): the int32 group sums P[m][n][g] = sum over the 64
  * channels of group g of qx[m,k] qw[n,k] for the window m0 <= m < m0+mc,
- * n0 <= n < n0+nc, computed by the INT4 GEMM main loop (same kernel, an
- * epilogue that stores the raw per-group sums instead of dequantizing).
+ * n0 <= n < n0+nc. They come from the GEMM kernel svdq_linear_forward runs
+ * for this M (the same dispatch): the tiled kernel, over the window's tiles
+ * as whole tiles, or with few tokens the weight-streaming kernel in the
+ * forward's own launch shape (K shares, K parts, token parts). Both use the
+ * forward's loads, nibble widening and i8 MFMAs and store each group's sum
+ * instead of dequantizing it. Only entries inside the window are written.
  * The workspace must hold svdq_stage1 output for M tokens.
  * p: int32 device [mc][nc][K/64]. Errors: as svdq_linear_forward.
  */

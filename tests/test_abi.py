@@ -96,9 +96,10 @@ def test_forward_validation_before_device():
         st = L.svdq_linear_forward(ctypes.byref(big), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
                                    ws.ctypes.data, ws.nbytes, None)
         assert st == want, (M, st)
-    # INT4 activation codes use 32-bit byte offsets: round32(M) * K <= 2^33
+    # INT4 activation codes use 32-bit byte offsets: round32(M) * K < 2^33
+    # (codes below 4 GiB; exactly 4 GiB is refused)
     big4 = S.LayerDesc(65536, 512, 16, 0)
-    for M, want in ((1 << 17, 4), ((1 << 17) + 1, 2), (1 << 20, 2)):
+    for M, want in (((1 << 17) - 32, 4), ((1 << 17) - 31, 2), (1 << 17, 2), (1 << 20, 2)):
         st = L.svdq_linear_forward(ctypes.byref(big4), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
                                    ws.ctypes.data, ws.nbytes, None)
         assert st == want, (M, st)

@@ -129,28 +129,45 @@ def test_forward_matches_oracle(spec):
     _say(f"  rel_fro={fro:.2e} max_rel={mx:.2e}")
 
 
+SENTINEL = -(2 ** 31)
+
+
+def _group_sums(layer, dev, ws, M, m0, mc, n0, nc):
+    """The hook's int32 sums into a buffer pre-filled with a value no sum can
+    take, so a group the kernel skipped shows up as a mismatch."""
+    out = torch.full((mc, nc, layer.K // 64), SENTINEL, dtype=torch.int32, device="cuda")
+    S.debug_int4_group_sums(layer, dev, ws, M, m0, mc, n0, nc, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
 @pytest.mark.parametrize("spec", [s for s in SMALL if s.fmt == "int4"], ids=lambda s: s.name)
 def test_int4_group_sums_bit_exact(spec):
+    """Every INT4 launch shape, through the same dispatch as the forward (the
+    tiled kernel, or the few-token kernel for M <= 256 and 769..1024 with its
+    K shares, K parts and token parts)."""
     _say(f"[group sums] {spec}")
     layer, dev, x, ws = _run_stage1(spec)
-    p = S.debug_int4_group_sums(layer, dev, ws, spec.M, 0, spec.M, 0, spec.N)
-    torch.cuda.synchronize()
+    p = _group_sums(layer, dev, ws, spec.M, 0, spec.M, 0, spec.N)
     ref = C.oracle_pack(spec)
     xh = O.smooth_activations(C.layer_data(spec).x, ref["mu"])
     qx, _ = O.quant_int4_rows(xh)
     want = O.int4_group_sums(qx, ref["qw"])
-    assert np.array_equal(p.cpu().numpy(), want)
+    assert np.array_equal(p, want)
 
 
-def test_group_sums_window():
-    spec = SMALL[2]
+@pytest.mark.parametrize("name,win", [("ragged_m300", (131, 150, 67, 200)),
+                                      ("small_m200_shares", (37, 150, 67, 120)),
+                                      ("small_m1000_shares", (500, 333, 200, 77))])
+def test_group_sums_window(name, win):
+    spec = next(s for s in SMALL if s.name == name)
+    m0, mc, n0, nc = win
     layer, dev, x, ws = _run_stage1(spec)
-    p = S.debug_int4_group_sums(layer, dev, ws, spec.M, 131, 150, 67, 200)
-    torch.cuda.synchronize()
+    p = _group_sums(layer, dev, ws, spec.M, m0, mc, n0, nc)
     ref = C.oracle_pack(spec)
     qx, _ = O.quant_int4_rows(O.smooth_activations(C.layer_data(spec).x, ref["mu"]))
-    want = O.int4_group_sums(qx[131:281], ref["qw"][67:267])
-    assert np.array_equal(p.cpu().numpy(), want)
+    want = O.int4_group_sums(qx[m0:m0 + mc], ref["qw"][n0:n0 + nc])
+    assert np.array_equal(p, want)
 
 
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
@@ -301,12 +318,18 @@ def test_full_size_sampled(spec):
     fro, mx = C.check_y(yg, yr, spec.name)
     _say(f"  rows={len(rows)} rel_fro={fro:.2e} max_rel={mx:.2e}")
     if spec.fmt == "int4":
-        m0 = int(rows[len(rows) // 2])
-        mc = min(64, spec.M - m0)
-        p = S.debug_int4_group_sums(layer, dev, ws, spec.M, m0, mc, spec.N - 96, 96)
-        torch.cuda.synchronize()
-        want = O.int4_group_sums(qx[m0:m0 + mc], ref["qw"][spec.N - 96:])
-        assert np.array_equal(p.cpu().numpy(), want)
+        # int32 group sums bit-exact, from the kernel this M's forward runs:
+        # with at most 1024 tokens every row (the few-token kernel's token
+        # parts), else a 64-row window; the first 128 and last 96 channels
+        if spec.M <= 1024:
+            m0, mc = 0, spec.M
+        else:
+            m0 = int(rows[len(rows) // 2])
+            mc = min(64, spec.M - m0)
+        for n0, nc in ((0, 128), (spec.N - 96, 96)):
+            p = _group_sums(layer, dev, ws, spec.M, m0, mc, n0, nc)
+            want = O.int4_group_sums(qx[m0:m0 + mc], ref["qw"][n0:n0 + nc])
+            assert np.array_equal(p, want), (n0, nc)
 
 
 def _tie_rows(fmt: str, K: int, M: int) -> np.ndarray:

@@ -319,3 +319,50 @@ def test_generator_recipe():
     # seeded: same draw twice; first rows of a full draw equal a partial draw
     lay2 = synth.make_layer(spec, m_rows=16)
     assert np.array_equal(lay2.x, lay.x[:16]) and np.array_equal(lay2.w_lin, lay.w_lin)
+
+
+def test_sigma_goes_into_l1():
+    """The singular values ride in L1, not L2: before bf16 rounding the rows of
+    L2 are orthonormal and the columns of L1 have the singular values as
+    norms (taken here from the Gram matrix's eigenvalues, not from the SVD);
+    L1 = W_hat L2^T, the projection of W_hat onto the kept right singular
+    vectors. Moving Sigma into L2, splitting it, or transposing a factor
+    fails one of these."""
+    lay = _tiny(8, 128, 96, seed=31)
+    ax = np.abs(lay.x).max(axis=0)
+    _, mu = O.smoothing_factors(ax, lay.w_lin)
+    wh = O.smoothed_weight(lay.w_lin, mu)
+    r = 12
+    l1, l2 = O.low_rank_factors(wh, r, round_bf16=False)
+    assert l1.shape == (128, r) and l2.shape == (r, 96)
+    np.testing.assert_allclose(l2 @ l2.T, np.eye(r), atol=1e-12)
+    sig = np.sqrt(np.sort(np.linalg.eigvalsh(wh.T @ wh))[::-1][:r])
+    np.testing.assert_allclose(np.linalg.norm(l1, axis=0), sig, rtol=1e-10)
+    np.testing.assert_allclose(l1, wh @ l2.T, rtol=0, atol=1e-12 * np.abs(l1).max())
+    # the bf16 factors are the roundings of these
+    b1, b2 = O.low_rank_factors(wh, r)
+    assert np.array_equal(b1, O.to_bf16(l1)) and np.array_equal(b2, O.to_bf16(l2))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_brute_matches_oracle_config0(fmt):
+    """Brute force on the tiny configuration (256 x 512 -> 512, rank 16): the
+    whole pack (smoothing factors, residual, weight codes and scales), and the
+    forward on a sample of token rows (rows are independent in every step)."""
+    spec = synth.config_layers(0)[0]
+    lay = synth.make_layer(spec)
+    ax = np.abs(lay.x).max(axis=0)
+    p = O.pack(lay.w_lin, lay.bias, ax, spec.rank, fmt)
+    bp = brute.pack(lay.w_lin.tolist(), lay.bias.tolist(), ax.tolist(),
+                    p["l1"].tolist(), p["l2"].tolist(), fmt)
+    assert np.array_equal(np.array(bp["mu"], np.float32), p["mu"])
+    assert np.array_equal(np.array(bp["R"], np.float32), p["r"])
+    assert np.array_equal(np.array(bp["codes"]), p["qw"].astype(np.int64))
+    assert np.array_equal(np.array(bp["scales"], dtype=p["sw"].dtype), p["sw"])
+    rows = np.array([0, 1, 77, 128, 255])
+    y, parts = O.forward(p, lay.x[rows], return_parts=True)
+    by, bxc, bxs, bz = brute.forward(bp, lay.x[rows].tolist())
+    assert np.array_equal(np.array(bxc), parts["qx"].astype(np.int64))
+    assert np.array_equal(np.array(bxs, dtype=parts["sx"].dtype), parts["sx"])
+    np.testing.assert_allclose(np.array(bz), parts["z"], rtol=1e-12, atol=1e-12 * np.abs(parts["z"]).max())
+    np.testing.assert_allclose(np.array(by), y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
