@@ -17,7 +17,7 @@ import numpy as np
 __all__ = [
     "SvdqError", "FMT_INT4", "FMT_MXFP4", "LayerDesc", "lib", "lib_path", "status_string",
     "packed_bytes", "pack_weights", "quantize_residual", "unpack_weights", "workspace_bytes",
-    "to_device", "linear_forward", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
+    "to_device", "linear_forward", "linear_forward_noalloc", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer",
 ]
 
@@ -32,8 +32,11 @@ EXPORTED_SYMBOLS = [
     "svdq_status_string", "svdq_version", "svdq_packed_bytes", "svdq_pack_weights",
     "svdq_quantize_residual", "svdq_unpack_weights", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_stage1", "svdq_unpack_workspace",
-    "svdq_debug_int4_group_sums", "svdq_gemm",
+    "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc",
 ]
+
+# bytes of the library-owned device workspace of svdq_linear_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class SvdqError(RuntimeError):
@@ -87,6 +90,7 @@ def lib() -> ctypes.CDLL:
         "svdq_unpack_weights": [D, P(Packed), vp, vp, vp, vp, vp],
         "svdq_workspace_bytes": [D, i64, P(sz)],
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
+        "svdq_linear_forward_noalloc": [D, P(Packed), vp, i64, vp, vp],
         "svdq_stage1": [D, P(Packed), vp, i64, vp, sz, vp],
         "svdq_gemm": [D, P(Packed), vp, sz, i64, vp, vp],
         "svdq_unpack_workspace": [D, i64, vp, sz, vp, vp, vp],
@@ -240,6 +244,20 @@ def linear_forward(layer: Layer, dev: dict, x, y=None, workspace=None, stream=No
     _check(lib().svdq_linear_forward(ctypes.byref(d), ctypes.byref(p), _ptr(x), M, _ptr(y),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
            "svdq_linear_forward")
+    return y
+
+
+def linear_forward_noalloc(layer: Layer, dev: dict, x, y, stream=None):
+    """svdq_linear_forward_noalloc: y (caller's bf16 tensor [M][N]) = layer(x),
+    with the library's own device workspace (no allocation by the call)."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape[-1] == layer.K
+    assert y.dtype == torch.bfloat16 and y.is_contiguous() and tuple(y.shape) == (x.shape[0], layer.N)
+    p = _packed_struct(layer, dev)
+    d = layer.desc
+    _check(lib().svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), _ptr(x), x.shape[0],
+                                             _ptr(y), _stream(stream)),
+           "svdq_linear_forward_noalloc")
     return y
 
 

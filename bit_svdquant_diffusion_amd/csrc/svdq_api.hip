@@ -12,35 +12,49 @@
 
 namespace svdq {
 
+// Workspace of svdq_linear_forward_noalloc: a library-owned device array, one
+// copy per GPU (each device that loads the library holds it until the process
+// ends). In host code `scratch` names a host-side stand-in, not device memory:
+// the host uses only the per-device address hipGetSymbolAddress returns.
+constexpr size_t kNoAllocScratchBytes = (size_t)SVDQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950 ready, 2 unsupported
 std::atomic<int> g_dev_cus[kMaxDevices];     // compute units of each ready device
+std::atomic<void*> g_dev_scratch[kMaxDevices];   // device address of `scratch` on each ready device
 std::mutex g_dev_mu;
 
-svdq_status check_device(int* cus = nullptr) {
+// One-time set-up per device, with that device current: the gfx950 check,
+// the kernels' LDS attributes and the address of this device's `scratch`.
+svdq_status check_device(int* cus = nullptr, void** scratch_ptr = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SVDQ_ERR_DEVICE;
   int s = g_dev_state[dev].load(std::memory_order_acquire);
-  if (s == 1) {
-    if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
-    return SVDQ_OK;
-  }
-  if (s == 2) return SVDQ_ERR_DEVICE;
-  std::lock_guard<std::mutex> lock(g_dev_mu);
-  s = g_dev_state[dev].load(std::memory_order_acquire);
   if (s == 0) {
-    hipDeviceProp_t p;
-    bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
-              std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess &&
-              prepare_gemm_int4() == hipSuccess && prepare_stage1() == hipSuccess;
-    s = ok ? 1 : 2;
-    if (ok) g_dev_cus[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
-    g_dev_state[dev].store(s, std::memory_order_release);
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    s = g_dev_state[dev].load(std::memory_order_acquire);
+    if (s == 0) {
+      hipDeviceProp_t p;
+      void* sp = nullptr;
+      bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
+                std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess &&
+                prepare_gemm_int4() == hipSuccess && prepare_stage1() == hipSuccess &&
+                hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) == hipSuccess && sp != nullptr;
+      s = ok ? 1 : 2;
+      if (ok) {
+        g_dev_cus[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
+        g_dev_scratch[dev].store(sp, std::memory_order_relaxed);
+      }
+      g_dev_state[dev].store(s, std::memory_order_release);
+    }
   }
-  if (s == 1 && cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
-  return s == 1 ? SVDQ_OK : SVDQ_ERR_DEVICE;
+  if (s != 1) return SVDQ_ERR_DEVICE;
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  if (scratch_ptr) *scratch_ptr = g_dev_scratch[dev].load(std::memory_order_relaxed);
+  return SVDQ_OK;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -166,6 +180,21 @@ svdq_status svdq_linear_forward(const svdq_layer_desc* d, const svdq_packed* dev
   st = after_launch(launch_stage1(stage1_args(d, dev, x, M, ws), cus, s), s);
   if (st != SVDQ_OK) return st;
   return after_launch(launch_gemm(gemm_args(d, dev, M, ws, y), cus, s), s);
+}
+
+svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* d, const svdq_packed* dev,
+                                        const uint16_t* x, int64_t M, uint16_t* y, void* stream) {
+  svdq_status st = check_desc(d);
+  if (st != SVDQ_OK) return st;
+  if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
+  // the workspace this M needs must fit the device array (host arithmetic only)
+  if (M > 0 && ws_layout(d, M).total > kNoAllocScratchBytes) return SVDQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (M > 0) {
+    st = check_device(nullptr, &ws);
+    if (st != SVDQ_OK) return st;
+  }
+  return svdq_linear_forward(d, dev, x, M, y, ws, kNoAllocScratchBytes, stream);
 }
 
 svdq_status svdq_gemm(const svdq_layer_desc* d, const svdq_packed* dev, const void* ws,

@@ -44,8 +44,10 @@
  *   - Device pointers (x, y, workspace and every packed buffer) must be
  *     16-byte aligned; a misaligned pointer returns SVDQ_ERR_SHAPE.
  *   - All functions are thread-safe; the only global state is a per-device
- *     cache of the "is this a gfx950 device" check. Two calls that share a
- *     workspace must be ordered (same stream or an event between them).
+ *     cache of the "is this a gfx950 device" check and, per device, the
+ *     address of the array svdq_linear_forward_noalloc uses as its workspace.
+ *     Two calls that share a workspace must be ordered (same stream or an
+ *     event between them).
  *   - Environment: SVDQ_SYNC_DEBUG=1 synchronizes the stream after every
  *     launch and reports asynchronous faults as SVDQ_ERR_DEVICE;
  *     SVDQ_JACOBI_MAX_SWEEPS=n caps the pack's Jacobi sweeps (tests use 0 to
@@ -203,6 +205,25 @@ SVDQ_API svdq_status svdq_workspace_bytes(const svdq_layer_desc* desc, int64_t M
 SVDQ_API svdq_status svdq_linear_forward(const svdq_layer_desc* desc, const svdq_packed* dev,
                                 const uint16_t* x, int64_t M, uint16_t* y, void* workspace,
                                 size_t workspace_bytes, void* hip_stream);
+
+/*
+ * svdq_linear_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same kernels and result as svdq_linear_forward; the workspace is
+ * a device array the library owns, SVDQ_NOALLOC_SCRATCH_BYTES (128 MiB) per
+ * GPU, set aside when the library first runs on that GPU and held until the
+ * process ends. Nothing is allocated here, and M is limited to the M for which
+ * svdq_workspace_bytes(desc, M) <= SVDQ_NOALLOC_SCRATCH_BYTES (every layer of
+ * up to 4608 tokens with K <= 12288). Every call on one GPU uses the same
+ * array and leaves this call's codes, scales and X_hat L1 in it: calls that
+ * overlap on one GPU (two streams, or two host threads without ordering)
+ * race and give wrong results, so order them.
+ * Errors: as svdq_linear_forward; SVDQ_ERR_WORKSPACE when the workspace for M
+ * exceeds the array.
+ */
+#define SVDQ_NOALLOC_SCRATCH_BYTES (128u << 20)
+SVDQ_API svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* desc, const svdq_packed* dev,
+                                                 const uint16_t* x, int64_t M, uint16_t* y, void* hip_stream);
 
 /*
  * Test hook: only kernel (1) of svdq_linear_forward, filling the workspace.

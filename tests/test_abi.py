@@ -147,3 +147,25 @@ def test_pack_svd_nonconvergence_reported(monkeypatch):
     assert e.value.status == 5
     monkeypatch.delenv("SVDQ_JACOBI_MAX_SWEEPS")
     S.pack_weights(layer, w, None, ax)
+
+
+def test_noalloc_host_checks():
+    """svdq_linear_forward_noalloc refuses, on the host and before touching a
+    device, an M whose workspace exceeds the library's array, and treats
+    M == 0 as a no-op."""
+    L = S.lib()
+    assert S.NOALLOC_SCRATCH_BYTES == 128 << 20
+    buf = np.zeros(1 << 16, np.uint8)
+    p = S.Packed(*([buf.ctypes.data] * 6))
+    x = np.zeros(16, np.uint16)
+    for K, N, fmt in ((3072, 9216, 0), (12288, 3072, 0), (3072, 12288, 1)):
+        d = S.LayerDesc(K, N, 32, fmt)
+        # 4608 tokens fit (the documented bound); far more do not
+        assert S.workspace_bytes(S.Layer(K, N, 32, "int4" if fmt == 0 else "mxfp4"), 4608) <= S.NOALLOC_SCRATCH_BYTES
+        big = 1 << 16
+        assert L.svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, big,
+                                             x.ctypes.data, None) == 4
+        assert L.svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, 0,
+                                             x.ctypes.data, None) == 0
+        assert L.svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, -1,
+                                             x.ctypes.data, None) == 2
