@@ -104,7 +104,7 @@ Stage1Args stage1_args(const svdq_layer_desc* d, const svdq_packed* dev, const u
   a.z = (uint16_t*)(b + L.z);
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
-  a.nflags = int4 ? kSplitSlots : 0;
+  a.nflags = int4 ? kSplitCounters : 0;
   a.zp = (float*)(b + L.zp);
   return a;
 }

@@ -30,13 +30,15 @@
 // as equal contiguous runs of (tile, stage) pairs, so every workgroup ends at
 // the same time. Each XCD deals its own share of those tiles (the ones the
 // tile map gives it) over its own workgroups, which keeps their operand
-// panels in that XCD's L2. A tile cut between runs belongs to the workgroup
-// holding its first stage; that piece is the last of its run. The other
-// pieces come first in their runs: each writes its fp32 partial to its own
-// workspace slot and raises its flag; the owner adds the partials in
-// workgroup order (the result does not depend on timing), clears the flags,
-// and finishes the tile (low-rank stages, bias, Y). Stage 1 clears the flags
-// before every GEMM.
+// panels in that XCD's L2. A run's part of a tile is a piece (a run that
+// covers a whole tile just finishes it). Every piece writes its fp32 partial
+// to its own workspace slot and then takes a ticket from the tile's counter;
+// the piece that takes the last ticket adds all the tile's partials in piece
+// (K) order, so the result does not depend on which piece came last, resets
+// the counter and finishes the tile (low-rank product, bias, Y) with direct
+// loads. No workgroup ever waits for another, so nothing assumes that the
+// grid's workgroups run at the same time. Stage 1 clears the counters before
+// every GEMM; the finishers leave them at zero as well.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
 #include "svdq_layout.h"
@@ -111,6 +113,7 @@ __device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 
 struct Geo {
   int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;
+  int r32;
   int tm_off, tn_off;   // group-sum hook: the window's first tile
   // whole tiles (indices below sk_base, a multiple of 8: rounds * grid),
   // then the sk_tiles tiles from index sk_base: tile index sk_base + 8 m + x
@@ -120,6 +123,7 @@ struct Geo {
 constexpr int kPartFloats = kBM * kBN;   // one fp32 partial tile
 constexpr int kMinRun = 6;               // fewest stages per run of the split (when there are that many)
 static_assert(kPartFloats * 4 == kSplitPartBytes, "workspace slot size");
+static_assert(kSplitPieces == 2, "a run holds at most two pieces: its first and its last segment");
 }  // namespace
 
 // DEBUG_P: instead of dequantizing, write every group sum P (exact int32) of
@@ -151,17 +155,21 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   auto run_begin = [&](int k) -> long long { return (long long)k * xunits / xruns; };
   const long long u0 = (xtiles > 0 && kx < xruns) ? run_begin(kx) : 0;
   const long long u1 = (xtiles > 0 && kx < xruns) ? run_begin(kx + 1) : 0;
+  // a segment: tile idx, its stages [ka, kb); whole (all K stages) or a
+  // piece, m the tile's index among this XCD's split tiles
   struct Seg {
-    int idx, ka, kb;
-    bool owner;
+    int idx, ka, kb, m;
+    bool whole;
   };
   auto seg_at = [&](int k, long long u) -> Seg {
-    if (k < ncl) return Seg{wg + k * grid, 0, g.nst, true};
+    if (k < ncl) return Seg{wg + k * grid, 0, g.nst, -1, true};
     const int m = (int)(u / g.nst), ka = (int)(u - (long long)m * g.nst);
     const int kb = (int)min((long long)g.nst, ka + (u1 - u));
-    return Seg{g.sk_base + 8 * m + xcd, ka, kb, ka == 0};
+    return Seg{g.sk_base + 8 * m + xcd, ka, kb, m, ka == 0 && kb == g.nst};
   };
-  auto seg_len = [&](const Seg& sg) { return sg.kb - sg.ka + (sg.owner && !DEBUG_P ? nlr : 0); };
+  // the run holding unit u of this XCD
+  auto run_of = [&](long long u) -> int { return (int)min((long long)xruns - 1, ((u + 1) * xruns - 1) / xunits); };
+  auto seg_len = [&](const Seg& sg) { return sg.kb - sg.ka + (sg.whole && !DEBUG_P ? nlr : 0); };
   int total = 0;   // ring steps of this workgroup
   {
     int k = 0;
@@ -366,6 +374,43 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     }
   };
 
+  // acc + bias, bf16 write of the wave's 64 x 64 (the MXFP4 kernel's
+  // epilogue). Lane h of the accumulator holds channels 32 j + 8 q + 4 h +
+  // (0..3) of token m0 + 32 i + lr; after swapping the packed pairs (q = 1,
+  // h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <-> (q = 2, h = 1), each
+  // lane stores two 16-byte runs of one row.
+  auto store_tile = [&](int m0t, int n0, const float (&bv)[kTN][16]) {
+    const int ynrec = min(g.M - m0t, kBM) * g.N * 2;
+    const __amdgpu_buffer_rsrc_t yrs =
+        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0t * g.N, 0, ynrec, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        uint32_t o[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          o[p] = cvt_bf16x2(acc[j][i][2 * p] + bv[j][2 * p], acc[j][i][2 * p + 1] + bv[j][2 * p + 1]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
+            o[4 * p + w] = r[0];
+            o[4 * p + 2 + w] = r[1];
+          }
+        }
+        // always issued (the ring waits count them); the resource drops rows
+        // past M and a block past N is sent past the end
+        const int col = n0 + 32 * j + 8 * h;
+        const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
+      }
+    }
+  };
+  __shared__ int ticket_last;   // the workgroup took a tile's last ticket
+
   // prologue: the first kNStage - 1 ring steps in flight
   for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
   // this lane's 16 float4 of a partial tile in a workspace slot
@@ -391,44 +436,80 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       ++gs;
     }
     if constexpr (DEBUG_P) continue;
-    if (!sg.owner) {
-      // a later piece of a tile (the first segment of this run): publish the
-      // partial in this workgroup's slot, then its flag
+    if (!sg.whole) {
+      // a piece: publish the partial in this run's slot for it (its first
+      // segment, else its last), then take the tile's ticket
+      const int myslot = kSplitPieces * wg + (ck == ncl ? 0 : 1);
 #pragma unroll
       for (int f = 0; f < 16; ++f) {
         const f32x16& v = acc[f >> 3][(f >> 2) & 1];
-        *reinterpret_cast<f32x4*>(part_at(wg, f)) = f32x4{v[4 * (f & 3)], v[4 * (f & 3) + 1], v[4 * (f & 3) + 2], v[4 * (f & 3) + 3]};
+        *reinterpret_cast<f32x4*>(part_at(myslot, f)) = f32x4{v[4 * (f & 3)], v[4 * (f & 3) + 1], v[4 * (f & 3) + 2], v[4 * (f & 3) + 3]};
       }
-      __builtin_amdgcn_s_waitcnt(0);   // every store of every wave has landed ...
-      __syncthreads();                  // ... before the flag is raised
+      __builtin_amdgcn_s_waitcnt(0);   // every wave's stores (and transfers) have landed ...
+      __syncthreads();                  // ... before one release covers them all
+      const int k0 = run_of((long long)sg.m * g.nst), k1 = run_of((long long)(sg.m + 1) * g.nst - 1);
+      uint32_t* ctr = a.flags + (sg.idx - g.sk_base);
       if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_store(a.flags + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = t + 1 == (uint32_t)(k1 - k0 + 1);
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket_last = last ? 1 : 0;
       }
-      continue;
-    }
-    if (ck >= ncl && sg.kb < g.nst) {
-      // the first piece of a tile that later runs continued: add their
-      // partials in workgroup order (the flags bound the wait; they are set
-      // early in those runs, so it is normally already over)
-      const long long tile_end = (long long)((sg.idx - g.sk_base - xcd) / 8 + 1) * g.nst;
-      for (int k = kx + 1; k < xruns && run_begin(k) < tile_end; ++k) {
-        const int w = xcd + 8 * k;   // the workgroup of that run
-        if (tid == 0) {
-          for (int spin = 0; spin < (1 << 22) && __hip_atomic_load(a.flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++spin)
-            __builtin_amdgcn_s_sleep(2);
-          __hip_atomic_store(a.flags + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+      if (!ticket_last) continue;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // the last piece: the tile's partials in piece order. A run's piece is
+      // its first segment when the run starts inside this tile (or at its
+      // first stage), else its last segment.
+      for (int k = k0; k <= k1; ++k) {
+        const int slot = kSplitPieces * (xcd + 8 * k) + (run_begin(k) >= (long long)sg.m * g.nst ? 0 : 1);
 #pragma unroll
         for (int f = 0; f < 16; ++f) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(part_at(w, f));
+          const f32x4 v = *reinterpret_cast<const f32x4*>(part_at(slot, f));
           f32x16& d = acc[f >> 3][(f >> 2) & 1];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d[4 * (f & 3) + e] += v[e];
+          for (int e = 0; e < 4; ++e) d[4 * (f & 3) + e] = k == k0 ? v[e] : d[4 * (f & 3) + e] + v[e];
         }
       }
+      // + (X_hat L1) L2 from fragments loaded straight from memory, in the
+      // ring's order of 16-column steps, then the bias
+      const int per_l = g.r32 / 16;
+      for (int c = 0; c < per_l; ++c) {
+        i32x4 fa[kTM], fb[kTN];
+#pragma unroll
+        for (int t = 0; t < kTM; ++t) {
+          const int b = min(tmc.tm * kMB + wm * kTM + t, g.MB - 1);
+          fa[t] = *reinterpret_cast<const i32x4*>(a.z + ((size_t)(b * per_l + c) * 64 + lane) * 8);
+        }
+#pragma unroll
+        for (int t = 0; t < kTN; ++t) {
+          const int b = min(tmc.tn * kNBt + wn * kTN + t, g.NB - 1);
+          fb[t] = *reinterpret_cast<const i32x4*>(a.l2t + ((size_t)(b * per_l + c) * 64 + lane) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+          for (int i = 0; i < kTM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[j]),
+                                                                __builtin_bit_cast(bf16x8, fa[i]), acc[j][i], 0, 0, 0);
+      }
+      float bv[kTN][16];
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = min(n0 + 32 * j + 8 * q + 4 * h, g.N - 4);
+          const u32x2 bw = *reinterpret_cast<const u32x2*>(a.bias + ch);
+          bv[j][4 * q + 0] = bf16lo(bw.x);
+          bv[j][4 * q + 1] = bf16hi(bw.x);
+          bv[j][4 * q + 2] = bf16lo(bw.y);
+          bv[j][4 * q + 3] = bf16hi(bw.y);
+        }
+      __builtin_amdgcn_s_waitcnt(0);   // no transfer is in flight: the next ring waits stay exact
+      store_tile(m0t, n0, bv);
+      stores_due = kNStage - 1;
+      continue;
     }
     for (int l = 0; l < nlr; ++l) {
       ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
@@ -458,49 +539,20 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       ++gs;
     }
 
-    // + bias (from the last low-rank slot), bf16 write: the MXFP4 kernel's
-    // epilogue. Lane h of the accumulator holds channels 32 j + 8 q + 4 h +
-    // (0..3) of token m0 + 32 i + lr; after swapping the packed pairs (q = 1,
-    // h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <-> (q = 2, h = 1), each
-    // lane stores two 16-byte runs of one row.
+    // + bias (from the last low-rank slot), bf16 write
     const uint8_t* bslot = smem + ((gs - 1) % kNStage) * kSlot + kScA + wn * kWN * 2;
-    const int ynrec = min(g.M - m0t, kBM) * g.N * 2;
-    const __amdgpu_buffer_rsrc_t yrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0t * g.N, 0, ynrec, 0x00020000);
+    float bv[kTN][16];
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      float bv[16];
+    for (int j = 0; j < kTN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x2 bw = *reinterpret_cast<const u32x2*>(bslot + (32 * j + 8 * q + 4 * h) * 2);
-        bv[4 * q + 0] = bf16lo(bw.x);
-        bv[4 * q + 1] = bf16hi(bw.x);
-        bv[4 * q + 2] = bf16lo(bw.y);
-        bv[4 * q + 3] = bf16hi(bw.y);
+        bv[j][4 * q + 0] = bf16lo(bw.x);
+        bv[j][4 * q + 1] = bf16hi(bw.x);
+        bv[j][4 * q + 2] = bf16lo(bw.y);
+        bv[j][4 * q + 3] = bf16hi(bw.y);
       }
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        uint32_t o[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          o[p] = cvt_bf16x2(acc[j][i][2 * p] + bv[2 * p], acc[j][i][2 * p + 1] + bv[2 * p + 1]);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
-            o[4 * p + w] = r[0];
-            o[4 * p + 2 + w] = r[1];
-          }
-        }
-        // always issued (the ring waits count them); the resource drops rows
-        // past M and a block past N is sent past the end
-        const int col = n0 + 32 * j + 8 * h;
-        const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
-      }
-    }
+    store_tile(m0t, n0, bv);
     stores_due = kNStage - 1;
   }
 #undef SVDQ_ISSUE
@@ -524,6 +576,7 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   g.KS = a.K / 64;
   g.nst = a.K / 128;
   g.act_rows = (a.M + 15) / 16 * 16;
+  g.r32 = a.r32;
   g.tm_off = g.tn_off = 0;
   int grid = num_cus > 0 ? num_cus : 256;
   if (a.p) {

@@ -382,7 +382,7 @@ static hipError_t launch_nw(const GemmArgs& a, int num_cus, hipStream_t st) {
   while ((splits + 1) * NB <= cus && KU / (KK * (splits + 1)) >= 8 / FPU) ++splits;
   const int mb = (a.M + 31) / 32;
   const size_t per_split = (size_t)mb * 32 * a.N * 4;   // fp32 partial bytes of one share
-  while (splits > 1 && (size_t)splits * per_split > (size_t)kSplitSlots * kSplitPartBytes) --splits;
+  while (splits > 1 && (size_t)splits * per_split > kPartAreaBytes) --splits;
   if (a.part == nullptr) splits = 1;   // no partial area: whole K per workgroup
   hipLaunchKernelGGL((gemm_small_kernel<FMT, MB, TT, PD, NW, DBG>), dim3(NB * splits), dim3(64 * NW), 0, st, a,
                      splits, a.part);

@@ -18,7 +18,7 @@ struct Stage1Args {
   uint8_t* qx;
   void* sx;
   uint16_t* z;
-  uint32_t* flags;   // INT4 GEMM split flags to clear (nflags of them), or null
+  uint32_t* flags;   // INT4 GEMM split ticket counters to clear (nflags of them), or null
   int nflags;
   float* zp;         // partial Z per token group and K piece (see ws_layout)
 };
@@ -39,8 +39,8 @@ struct GemmArgs {
   const uint16_t* l2t;
   const uint16_t* bias;  // bf16 [N]
   uint16_t* y;           // bf16 [M][N]
-  // INT4 split of the last tiles: per-workgroup flags (cleared by stage 1)
-  // and fp32 partial tiles, in the workspace
+  // INT4 split of the last tiles: per-tile ticket counters (cleared by
+  // stage 1) and fp32 partial tiles, in the workspace
   uint32_t* flags;
   float* part;
   // group-sum test hook (INT4): window and output [mc][nc][K/64], p ==

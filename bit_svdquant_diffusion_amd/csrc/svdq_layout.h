@@ -59,18 +59,24 @@ inline int s1_piece_steps(int K) { return (K / 256 + kS1Pieces - 1) / kS1Pieces;
 inline int s1_pieces(int K) { return (K / 256 + s1_piece_steps(K) - 1) / s1_piece_steps(K); }
 constexpr int64_t kS1SplitRows = 4096;
 
-// INT4 GEMM split of the last tiles over the workgroups: one flag and one
-// fp32 partial tile (128 x 256) per workgroup, at most kSplitSlots of them.
+// INT4 GEMM split of the last tiles over the workgroups (at most
+// kSplitSlots of them): two fp32 partial tiles (128 x 256) per workgroup, one
+// for the first and one for the last piece of its run, and one ticket counter
+// per split tile (fewer than two rounds of tiles, so at most kSplitCounters).
 // The few-token GEMM (both formats, M <= kFewTokens) keeps the fp32 partials
 // of its K shares in the same area.
 constexpr int64_t kFewTokens = 256;
 constexpr int kSplitSlots = 256;
+constexpr int kSplitPieces = 2;
+constexpr int kSplitCounters = 2 * kSplitSlots;
 constexpr int kSplitPartBytes = 128 * 256 * 4;
+constexpr size_t kPartAreaBytes = (size_t)kSplitPieces * kSplitSlots * kSplitPartBytes;
 
 // Workspace: [qX][sX][Z], each 256-byte aligned, over round32(M) rows. qX and
 // Z in fragment order (see below) for both formats; sX fp32 [K/64][act_rows(M)]
 // (INT4) or E8M0 bytes in fragment order (MXFP4). INT4 adds the split's flags
-// (u32 [kSplitSlots], cleared by stage 1) and partial tiles, which MXFP4 with
+// ticket counters (u32 [kSplitCounters], cleared by stage 1) and partial
+// tiles (kPartAreaBytes), which MXFP4 with
 // M <= kFewTokens has as well (flags unused). Last, with a
 // low-rank branch, stage 1's partial Z: fp32, per token group and piece the
 // raw MFMA accumulators of its waves, min(round32(M), kS1SplitRows) x
@@ -86,8 +92,8 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   w.sx = align256((size_t)rows * d->K / 2);
   w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
   w.flags = w.z + align256((size_t)rows * rank32(d->rank) * 2);
-  w.part = w.flags + (int4 ? align256((size_t)kSplitSlots * 4) : 0);
-  w.zp = w.part + (int4 || M <= kFewTokens ? (size_t)kSplitSlots * kSplitPartBytes : 0);
+  w.part = w.flags + (int4 ? align256((size_t)kSplitCounters * 4) : 0);
+  w.zp = w.part + (int4 || M <= kFewTokens ? kPartAreaBytes : 0);
   w.total = w.zp + (size_t)s1_pieces(d->K) * (rows < kS1SplitRows ? rows : kS1SplitRows) * 4 * rank32(d->rank) * 4;
   return w;
 }

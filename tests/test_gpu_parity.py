@@ -185,8 +185,9 @@ def test_deterministic_and_m0(fmt):
 
 
 def test_split_tiles_deterministic():
-    """The INT4 GEMM's owner adds the partials of a cut tile in workgroup
-    order, so repeated calls give identical bits (four-piece split case)."""
+    """The last piece of a cut INT4 tile adds the tile's partials in piece
+    order, whichever piece it is, so repeated calls give identical bits
+    (four-piece split case)."""
     spec = next(s for s in SMALL if s.name == "split_k_4_pieces")
     layer, dev = C.device_layer(spec)
     x = C.x_device(spec)
@@ -194,6 +195,35 @@ def test_split_tiles_deterministic():
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,M,K,N", [("split_k_4_pieces", 384, 3072, 512),
+                                        ("split_two_pieces_per_tile", 1024, 1536, 4096),
+                                        ("split_after_rounds", 2304, 1024, 9216)])
+def test_split_tiles_beside_a_concurrent_kernel(name, M, K, N):
+    """The INT4 GEMM's split needs no workgroups to run at the same time:
+    pieces publish partials and the last one finishes the tile, nobody waits.
+    With a long bf16 GEMM on another stream holding CUs, the layer gives the
+    bits it gives alone, and both match the oracle."""
+    _say(f"[split concurrent] {name}")
+    spec = _spec(name, M, K, N, 32, "int4", 18)
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    alone = S.linear_forward(layer, dev, x)
+    torch.cuda.synchronize()
+    big = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    other = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(other):
+            for _ in range(2):
+                big = (big @ big) * (1.0 / 128)
+        outs.append(S.linear_forward(layer, dev, x))
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y.view(torch.int16), alone.view(torch.int16))
+    rows = C.sample_rows(M, n=48)
+    C.check_y(C.bf16_tensor_to_f32(alone)[rows], O.forward(C.oracle_pack(spec), C.layer_data(spec).x[rows]), name)
 
 
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
