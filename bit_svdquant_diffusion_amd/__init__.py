@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "SvdqError", "FMT_INT4", "FMT_MXFP4", "LayerDesc", "lib", "lib_path", "status_string",
-    "packed_bytes", "pack_weights", "quantize_residual", "unpack_weights", "workspace_bytes",
+    "packed_bytes", "pack_weights", "quantize_residual", "lora_extend", "unpack_weights", "workspace_bytes",
     "to_device", "linear_forward", "linear_forward_noalloc", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer",
 ]
@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = [
     "svdq_status_string", "svdq_version", "svdq_packed_bytes", "svdq_pack_weights",
     "svdq_quantize_residual", "svdq_unpack_weights", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_stage1", "svdq_unpack_workspace",
-    "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc",
+    "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc", "svdq_lora_extend",
 ]
 
 # bytes of the library-owned device workspace of svdq_linear_forward_noalloc
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "svdq_pack_weights": [D, vp, vp, vp, ctypes.c_uint64, P(Packed)],
         "svdq_quantize_residual": [D, vp, vp, vp, vp, vp, P(Packed)],
         "svdq_unpack_weights": [D, P(Packed), vp, vp, vp, vp, vp],
+        "svdq_lora_extend": [D, P(Packed), ctypes.c_int32, vp, vp, ctypes.c_float, P(Packed)],
         "svdq_workspace_bytes": [D, i64, P(sz)],
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
         "svdq_linear_forward_noalloc": [D, P(Packed), vp, i64, vp, vp],
@@ -181,6 +182,28 @@ def quantize_residual(layer: Layer, w_lin, bias, mu, l1_bits, l2_bits) -> dict:
                                         _ptr(l2) if layer.rank else None, ctypes.byref(p)),
            "svdq_quantize_residual")
     return bufs
+
+
+def lora_extend(layer: Layer, host: dict, lora_a, lora_b, scale: float, share_base: bool = False):
+    """svdq_lora_extend: (extended Layer, host buffers) of `layer` with the LoRA
+    adapter scale * X A B (A fp32 [K][r_a], B fp32 [r_a][N]) in its 16-bit
+    branch. With share_base, only l1 and l2 are returned (the rest of the base
+    layer's buffers are used as they are)."""
+    a = np.ascontiguousarray(lora_a, dtype=np.float32)
+    b = np.ascontiguousarray(lora_b, dtype=np.float32)
+    ra = a.shape[1]
+    assert a.shape == (layer.K, ra) and b.shape == (ra, layer.N)
+    ext = Layer(layer.K, layer.N, layer.rank + ra, layer.fmt)
+    bufs, p = _alloc_host(ext)
+    if share_base:
+        for n in ("mu", "qw", "sw", "bias"):
+            setattr(p, n, None)
+    base = _packed_struct(layer, host)
+    _check(lib().svdq_lora_extend(ctypes.byref(layer.desc), ctypes.byref(base), int(ra), _ptr(a), _ptr(b),
+                                  float(scale), ctypes.byref(p)), "svdq_lora_extend")
+    if share_base:
+        bufs = {n: (bufs[n] if n in ("l1", "l2") else host[n]) for n in PACKED_FIELDS}
+    return ext, bufs
 
 
 def _packed_struct(layer: Layer, bufs: dict) -> Packed:

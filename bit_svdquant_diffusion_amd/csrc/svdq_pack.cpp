@@ -515,6 +515,60 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
   return SVDQ_OK;
 }
 
+svdq_status svdq_lora_extend(const svdq_layer_desc* base, const svdq_packed* h, int32_t lora_rank,
+                             const float* lora_a, const float* lora_b, float scale, svdq_packed* out) {
+  svdq_status st = check_desc(base);
+  if (st != SVDQ_OK) return st;
+  if (!h || !out || !lora_a || !lora_b || !h->mu) return SVDQ_ERR_NULL;
+  if (lora_rank <= 0) return SVDQ_ERR_SHAPE;
+  svdq_layer_desc ed = *base;
+  ed.rank = base->rank + lora_rank;
+  st = check_desc(&ed);
+  if (st != SVDQ_OK) return st;
+  if (!out->l1 || !out->l2 || (base->rank > 0 && (!h->l1 || !h->l2))) return SVDQ_ERR_NULL;
+  const int K = base->K, N = base->N, r0 = base->rank, r = ed.rank, r32 = rank32(r);
+  const int r032 = rank32(r0);
+  if (!all_finite(lora_a, (size_t)K * lora_rank) || !all_finite(lora_b, (size_t)lora_rank * N) ||
+      !std::isfinite(scale))
+    return SVDQ_ERR_NUMERIC;
+  for (int k = 0; k < K; ++k)
+    if (!(h->mu[k] > 0.f) || !std::isfinite(h->mu[k])) return SVDQ_ERR_NUMERIC;
+  // the base factors (logical), then the adapter's columns of L1 and rows of L2
+  std::vector<uint16_t> l1((size_t)K * r), l2((size_t)r * N);
+  for (int k = 0; k < K; ++k) {
+    for (int c = 0; c < r0; ++c) l1[(size_t)k * r + c] = h->l1[l1_index(K, r032, k, c)];
+    for (int c = 0; c < lora_rank; ++c)
+      l1[(size_t)k * r + r0 + c] =
+          bf16_from_double(((double)lora_a[(size_t)k * lora_rank + c] * (double)scale) / (double)h->mu[k]);
+  }
+  for (int i = 0; i < r0; ++i)
+    for (int n = 0; n < N; ++n) l2[(size_t)i * N + n] = h->l2[frag16_index(r032, n, i)];
+  for (int i = 0; i < lora_rank; ++i)
+    for (int n = 0; n < N; ++n) l2[(size_t)(r0 + i) * N + n] = bf16_from_double((double)lora_b[(size_t)i * N + n]);
+  // device layout of the extended factors; the 4-bit side is copied as it is
+  std::memset(out->l1, 0, (size_t)K * r32 * 2);
+  std::memset(out->l2, 0, (size_t)N * r32 * 2);
+  for (int k = 0; k < K; ++k)
+    for (int c = 0; c < r; ++c) out->l1[l1_index(K, r32, k, c)] = l1[(size_t)k * r + c];
+  for (int i = 0; i < r; ++i)
+    for (int n = 0; n < N; ++n) out->l2[frag16_index(r32, n, i)] = l2[(size_t)i * N + n];
+  const svdq_packed_sizes sz = packed_sizes(base);
+  if (out->mu && out->mu != h->mu) std::memcpy(out->mu, h->mu, sz.mu);
+  if (out->qw && out->qw != h->qw) {
+    if (!h->qw) return SVDQ_ERR_NULL;
+    std::memcpy(out->qw, h->qw, sz.qw);
+  }
+  if (out->sw && out->sw != h->sw) {
+    if (!h->sw) return SVDQ_ERR_NULL;
+    std::memcpy(out->sw, h->sw, sz.sw);
+  }
+  if (out->bias && out->bias != h->bias) {
+    if (!h->bias) return SVDQ_ERR_NULL;
+    std::memcpy(out->bias, h->bias, sz.bias);
+  }
+  return SVDQ_OK;
+}
+
 svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const void* ws,
                                   size_t ws_bytes, int8_t* codes, void* scales, float* z) {
   svdq_status st = check_desc(d);

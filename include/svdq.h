@@ -165,6 +165,31 @@ SVDQ_API svdq_status svdq_quantize_residual(const svdq_layer_desc* desc, const f
                                    const uint16_t* l2, svdq_packed* host_out);
 
 /*
+ * A LoRA adapter on a packed layer, without quantizing again (aiflownews.com,
+ * "What SVDQuant actually does": pre-trained low-rank adapters work on the
+ * 4-bit model as they are). Host only.
+ * The adapter adds scale * X A B to the layer's output (A fp32 [K][lora_rank],
+ * B fp32 [lora_rank][N], row-major; the usual LoRA down and up projections,
+ * with scale = alpha / rank of the adapter). Since the layer sees X_hat =
+ * X diag(mu), the adapter joins the 16-bit branch: the result is the layer of
+ * rank base->rank + lora_rank with
+ *   L1' = [L1 | bf16(A[k][i] * scale / mu_k)]  (fp64 multiply, then divide)
+ *   L2' = [L2 ; bf16(B)]
+ * and mu, the 4-bit codes and scales and the bias of `host_base` unchanged.
+ * host_out->l1 and ->l2 must hold svdq_packed_bytes() of the extended
+ * descriptor ({K, N, base->rank + lora_rank, format}). host_out->mu, ->qw, ->sw
+ * and ->bias receive byte copies of the base's buffers, or may be NULL: the
+ * extended layer can share the base's device buffers for them, so switching
+ * adapters re-uploads only L1 and L2.
+ * Errors: SVDQ_ERR_NULL; SVDQ_ERR_SHAPE (lora_rank <= 0, or the extended rank
+ * outside the supported set: a multiple of 16, <= 128, <= min(K, N));
+ * SVDQ_ERR_FORMAT; SVDQ_ERR_NUMERIC (non-finite adapter or scale, mu <= 0).
+ */
+SVDQ_API svdq_status svdq_lora_extend(const svdq_layer_desc* base, const svdq_packed* host_base,
+                                      int32_t lora_rank, const float* lora_a, const float* lora_b,
+                                      float scale, svdq_packed* host_out);
+
+/*
  * Logical view of a host packed layer (inverse of the device layout).
  * Any output pointer may be NULL to skip it.
  *   codes  int8 [N][K]: INT4 values in [-7,7], or E2M1 code bits 0..15

@@ -34,6 +34,10 @@ exponent floor(log2 amax) - 2, sign kept on E2M1 zeros).
 
 Every function here is pinned by tests/test_oracle.py against brute force,
 closed forms and invariants; none is "parity unpinned".
+
+A packed layer can also take a LoRA adapter without re-quantization
+(lora_extend): the adapter joins the 16-bit low-rank branch and the 4-bit
+residual is kept (same page, same section).
 """
 from __future__ import annotations
 
@@ -297,6 +301,35 @@ def forward(packed: dict, x: np.ndarray, return_parts: bool = False):
     if return_parts:
         return y, dict(x_hat=x_hat, qx=qx, sx=sx, z=z, y_lr=y_lr, y_q=y_q)
     return y
+
+
+# ----------------------------------------------------------------------------
+# LoRA adapters on a packed layer, without re-quantization
+# ----------------------------------------------------------------------------
+def lora_extend(packed: dict, lora_a: np.ndarray, lora_b: np.ndarray, scale: float) -> dict:
+    """A packed layer that also applies a LoRA adapter, with its 4-bit residual
+    left as it is (aiflownews.com, "What SVDQuant actually does": pre-trained
+    low-rank adapters are used without quantizing again).
+
+    The adapter adds scale * X A B to Y (A [K][r_a], B [r_a][N], math layout).
+    The layer sees X_hat = X diag(mu), so X = X_hat diag(1/mu) and the adapter
+    is the low-rank product X_hat (diag(1/mu) A scale) B, which joins the
+    16-bit branch: L1' = [L1 | bf16(A[k,i] * scale / mu_k)] (taken in float64,
+    multiply then divide, one bf16 rounding) and L2' = [L2 ; bf16(B)]. mu, the
+    residual's codes and scales and the bias are the base layer's.
+    """
+    a = np.asarray(lora_a, dtype=np.float32).astype(np.float64)
+    b = np.asarray(lora_b, dtype=np.float32).astype(np.float64)
+    K, ra = a.shape
+    assert b.shape == (ra, packed["N"]) and K == packed["K"]
+    mu = np.asarray(packed["mu"], dtype=np.float32).astype(np.float64)
+    l1a = to_bf16((a * np.float64(np.float32(scale))) / mu[:, None])
+    l2a = to_bf16(b)
+    out = dict(packed)
+    out["rank"] = packed["rank"] + ra
+    out["l1"] = np.concatenate([np.asarray(packed["l1"], np.float32).reshape(K, -1), l1a], axis=1)
+    out["l2"] = np.concatenate([np.asarray(packed["l2"], np.float32).reshape(-1, packed["N"]), l2a], axis=0)
+    return out
 
 
 def forward_rows(packed: dict, x_rows: np.ndarray) -> np.ndarray:

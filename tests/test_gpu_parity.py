@@ -414,3 +414,45 @@ def test_stage1_quantizer_tie_points(fmt):
     qx, sx = O.quantize_activations(xr.astype(np.float32), fmt)
     assert np.array_equal(got["codes"], qx.astype(np.int8)), "activation codes at tie points"
     assert np.array_equal(got["scales"], sx), "activation scales at tie points"
+
+
+# ----------------------------------------------------------------------------
+# LoRA adapter without re-quantization
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name,M,K,N,fmt", [("qkv", 4608, 3072, 9216, "int4"),
+                                            ("lora_m64", 64, 3072, 3072, "int4"),
+                                            ("lora_fp4", 700, 1536, 2048, "mxfp4"),
+                                            ("lora_m40_fp4", 40, 1024, 2048, "mxfp4")])
+def test_lora_extended_forward(name, M, K, N, fmt):
+    """A rank-16 adapter on a rank-32 layer (rank 48 in all): only L1 and L2
+    are re-laid and uploaded, the device buffers of mu, the 4-bit codes and
+    scales and the bias are the base layer's. Y matches the oracle's
+    extended layer (sampled rows at full size) to the Y bar."""
+    _say(f"[lora] {name}")
+    if name == "qkv":
+        spec = synth.config_layers(1)[0]
+    else:
+        spec = _spec(name, M, K, N, 32, fmt, 43)
+    layer, host = C.library_host(spec)
+    _, dev = C.device_layer(spec)
+    rng = np.random.default_rng(77)
+    A = (rng.standard_normal((K, 16)) / np.sqrt(K)).astype(np.float32)
+    B = (rng.standard_normal((16, N)) * 0.5).astype(np.float32)
+    ext_layer, ext_host = S.lora_extend(layer, host, A, B, 2.0, share_base=True)
+    ext_dev = dict(dev)
+    for n in ("l1", "l2"):
+        ext_dev[n] = torch.from_numpy(ext_host[n].copy()).cuda()
+    x = C.x_device(spec)
+    y = torch.full((spec.M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    S.linear_forward(ext_layer, ext_dev, x, y=y)
+    torch.cuda.synchronize()
+    ref = O.lora_extend(C.oracle_pack(spec), A, B, 2.0)
+    rows = C.sample_rows(spec.M, n=64)
+    lay = C.layer_data(spec)
+    C.check_y(C.bf16_tensor_to_f32(y)[rows], O.forward(ref, lay.x[rows]), f"lora {name}")
+    # the adapter's share of the output is really there: the base layer differs
+    yb = S.linear_forward(layer, dev, x)
+    torch.cuda.synchronize()
+    d = C.bf16_tensor_to_f32(y)[rows].astype(np.float64) - C.bf16_tensor_to_f32(yb)[rows]
+    want = 2.0 * (lay.x[rows].astype(np.float64) @ A) @ B
+    assert np.linalg.norm(d - want) <= 0.05 * np.linalg.norm(want)

@@ -366,3 +366,62 @@ def test_brute_matches_oracle_config0(fmt):
     assert np.array_equal(np.array(bxs, dtype=parts["sx"].dtype), parts["sx"])
     np.testing.assert_allclose(np.array(bz), parts["z"], rtol=1e-12, atol=1e-12 * np.abs(parts["z"]).max())
     np.testing.assert_allclose(np.array(by), y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+# --------------------------------------------------------------------------
+# LoRA without re-quantization
+# --------------------------------------------------------------------------
+def _pow2_smoothed_layer(K=128, N=48, rank=16, fmt="int4", seed=33):
+    """A packed layer whose smoothing factors are exact powers of two (the
+    calibration maxima are max|W_k| times 4^j, so lambda_k = 2^j exactly)."""
+    lay = _tiny(6, K, N, seed=seed, fmt=fmt)
+    aw = np.abs(lay.w_lin).max(axis=0).astype(np.float64)
+    j = (np.arange(K) % 5) - 2
+    ax = (aw * 4.0 ** j).astype(np.float32)
+    assert np.array_equal(ax.astype(np.float64), aw * 4.0 ** j)   # exact in float32
+    p = O.pack(lay.w_lin, lay.bias, ax, rank, fmt)
+    assert np.array_equal(p["mu"].astype(np.float64), 2.0 ** -j)
+    return lay, p
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_lora_extend_adds_scaled_adapter_exactly(fmt):
+    """With power-of-two smoothing, bf16 adapter factors and a power-of-two
+    scale, every bf16 rounding in the extension is exact, so the extended
+    layer's output minus the base layer's is scale * X A B to float64
+    rounding, on any input; the residual's codes and scales, mu and the bias
+    are untouched. A wrong side of mu (diag(mu) instead of diag(1/mu)), a
+    dropped scale or a transposed factor fails this."""
+    lay, p = _pow2_smoothed_layer(fmt=fmt)
+    rng = np.random.default_rng(4)
+    ra = 16
+    A = O.to_bf16(rng.standard_normal((128, ra)) * 0.1)
+    B = O.to_bf16(rng.standard_normal((ra, 48)) * 0.1)
+    ext = O.lora_extend(p, A, B, 0.5)
+    assert ext["rank"] == p["rank"] + ra and ext["l1"].shape == (128, p["rank"] + ra)
+    assert np.array_equal(ext["l1"][:, :p["rank"]], p["l1"]) and np.array_equal(ext["l2"][:p["rank"]], p["l2"])
+    for key in ("qw", "sw", "mu", "bias", "r"):
+        assert np.array_equal(ext[key], p[key]), key
+    x = rng.standard_normal((9, 128)).astype(np.float32)
+    d = O.forward(ext, x) - O.forward(p, x)
+    want = 0.5 * (x.astype(np.float64) @ A.astype(np.float64)) @ B.astype(np.float64)
+    np.testing.assert_allclose(d, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_lora_extend_general_within_bf16():
+    """General smoothing and fp32 adapter factors: the added output is
+    scale * X A B up to the bf16 rounding of the two new factors."""
+    lay = _tiny(16, 256, 64, seed=35)
+    ax = np.abs(lay.x).max(axis=0)
+    p = O.pack(lay.w_lin, lay.bias, ax, 16, "int4")
+    rng = np.random.default_rng(5)
+    A = (rng.standard_normal((256, 32)) / 16).astype(np.float32)
+    B = (rng.standard_normal((32, 64)) / 4).astype(np.float32)
+    ext = O.lora_extend(p, A, B, 0.75)
+    d = O.forward(ext, lay.x) - O.forward(p, lay.x)
+    want = 0.75 * (lay.x.astype(np.float64) @ A) @ B
+    err = np.linalg.norm(d - want) / np.linalg.norm(want)
+    assert err < 2 ** -7, err
+    # the appended L1 columns are bf16 of A * scale / mu, row by row
+    k = 17
+    assert np.array_equal(ext["l1"][k, 16:], O.to_bf16(A[k].astype(np.float64) * 0.75 / float(p["mu"][k])))

@@ -114,3 +114,61 @@ def test_device_layout_of_l1_matches_stage1_order():
     dev_l2 = host["l2"].view(np.uint16).reshape(N // 32, 4, 2, 32, 8)
     lin = dev_l2.transpose(0, 3, 1, 2, 4).reshape(N, 64)   # [n][16c + 8h + e]
     assert np.array_equal(lin[:, :r], l2.T) and np.all(lin[:, r:] == 0)
+
+
+@pytest.mark.parametrize("fmt,r0,ra", [("int4", 16, 16), ("mxfp4", 32, 16), ("int4", 0, 32), ("mxfp4", 96, 32)])
+def test_lora_extend_matches_oracle(fmt, r0, ra):
+    """svdq_lora_extend: the extended L1 and L2 are bit-exact with the
+    oracle's (base factors kept, adapter columns bf16(A scale / mu) and rows
+    bf16(B)); codes, scales, mu and bias are the base layer's bytes."""
+    spec, lay = _layer(K=512, N=256, r=r0, M=64, seed=7, fmt=fmt)
+    ax = np.abs(lay.x).max(axis=0)
+    ref = O.pack(lay.w_lin, lay.bias, ax, r0, fmt)
+    layer = S.Layer(512, 256, r0, fmt)
+    host = S.quantize_residual(layer, lay.w_lin, lay.bias, ref["mu"],
+                               O.bf16_to_bits(ref["l1"]), O.bf16_to_bits(ref["l2"]))
+    rng = np.random.default_rng(9)
+    A = (rng.standard_normal((512, ra)) / 20).astype(np.float32)
+    B = (rng.standard_normal((ra, 256)) / 5).astype(np.float32)
+    ext_layer, ext = S.lora_extend(layer, host, A, B, 0.625)
+    assert ext_layer.rank == r0 + ra
+    want = O.lora_extend(ref, A, B, 0.625)
+    u = S.unpack_weights(ext_layer, ext)
+    assert np.array_equal(u["l1"], O.bf16_to_bits(want["l1"]))
+    assert np.array_equal(u["l2"], O.bf16_to_bits(want["l2"]))
+    for n in ("qw", "sw", "mu", "bias"):
+        assert np.array_equal(ext[n], host[n]), n
+    # sharing the base's buffers: only l1 and l2 are written
+    _, shared = S.lora_extend(layer, host, A, B, 0.625, share_base=True)
+    assert np.array_equal(shared["l1"], ext["l1"]) and np.array_equal(shared["l2"], ext["l2"])
+    assert shared["qw"] is host["qw"]
+
+
+def test_lora_extend_errors():
+    import ctypes
+    spec, lay = _layer(K=256, N=128, r=112, M=16, seed=8)
+    ax = np.abs(lay.x).max(axis=0)
+    ref = O.pack(lay.w_lin, lay.bias, ax, 112, "int4")
+    layer = S.Layer(256, 128, 112, "int4")
+    host = S.quantize_residual(layer, lay.w_lin, lay.bias, ref["mu"],
+                               O.bf16_to_bits(ref["l1"]), O.bf16_to_bits(ref["l2"]))
+    A = np.ones((256, 32), np.float32)
+    B = np.ones((32, 128), np.float32)
+    with pytest.raises(S.SvdqError) as e:          # 112 + 32 > 128
+        S.lora_extend(layer, host, A, B, 1.0)
+    assert e.value.status == 2
+    with pytest.raises(S.SvdqError) as e:          # rank not a multiple of 16
+        S.lora_extend(layer, host, A[:, :8], B[:8], 1.0)
+    assert e.value.status == 2
+    A16, B16 = A[:, :16].copy(), B[:16].copy()
+    A16[3, 2] = np.nan
+    with pytest.raises(S.SvdqError) as e:
+        S.lora_extend(layer, host, A16, B16, 1.0)
+    assert e.value.status == 5
+    L = S.lib()
+    p = S._packed_struct(layer, host)
+    out = S.Packed()
+    assert L.svdq_lora_extend(ctypes.byref(layer.desc), ctypes.byref(p), 0, A.ctypes.data, B.ctypes.data,
+                              1.0, ctypes.byref(out)) == 2
+    assert L.svdq_lora_extend(ctypes.byref(layer.desc), ctypes.byref(p), 16, A.ctypes.data, B.ctypes.data,
+                              1.0, ctypes.byref(out)) == 1
