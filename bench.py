@@ -163,9 +163,34 @@ def traffic_from_profile():
     return float(m_b.group(1))
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _blas_info():
+    """(vendor, threads) of the BLAS numpy uses, from threadpoolctl when present."""
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                return f"{p.get('internal_api')} {p.get('version') or ''}".strip(), p.get("num_threads")
+    except Exception:
+        pass
+    return "unknown", None
+
+
 def cpu_baseline(layer, host, lay, spec, budget_s):
     """The oracle's forward on a bounded sample of the same workload's rows,
-    with the same packed weights (logical values), on the host's cores."""
+    with the same packed weights (logical values), on all of the host cores
+    this process may use; the median of three timed runs of that sample."""
+    import contextlib
     import numpy as np
     from oracle import svdq_oracle as O
     try:
@@ -173,28 +198,86 @@ def cpu_baseline(layer, host, lay, spec, budget_s):
     except ImportError:
         threadpool_limits = None
     import bit_svdquant_diffusion_amd as S
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = len(os.sched_getaffinity(0))
     u = S.unpack_weights(layer, host)
     packed = dict(fmt=spec.fmt, mu=u["mu"], l1=O.bf16_from_bits(u["l1"]),
                   l2=O.bf16_from_bits(u["l2"]), bias=O.bf16_from_bits(u["bias"]),
                   qw=u["codes"] if spec.fmt == "int4" else u["codes"].astype(np.uint8),
                   sw=u["scales"])
-    import contextlib
     ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
     with ctx:
+        vendor, threads = _blas_info()
+        # size the sample so that one run takes about a third of the budget
         rows = 64
         while True:
             t0 = time.perf_counter()
             O.forward(packed, lay.x[:rows])
             t = time.perf_counter() - t0
-            if t >= 0.5 * budget_s or rows >= spec.M:
+            if t >= budget_s / 6 or rows >= spec.M:
                 break
-            rows = int(min(spec.M, max(2 * rows, rows * 0.8 * budget_s / max(t, 1e-3)) // 64 * 64))
+            rows = int(min(spec.M, max(2 * rows, rows * 0.3 * budget_s / max(t, 1e-3)) // 64 * 64))
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.forward(packed, lay.x[:rows])
+            times.append(time.perf_counter() - t0)
+    t = sorted(times)[1]
     tops = 2.0 * rows * spec.N * spec.K / t / 1e12
     return dict(value=round(tops, 6), unit="TOPS", cores=cores, kind="oracle",
                 sample=f"{rows} of {spec.M} token rows of the same layer ({spec.M}x{spec.K}->{spec.N}, "
-                       f"r{spec.rank}, {spec.fmt}); oracle forward (NumPy float64) took {t:.1f}s; "
-                       f"pack excluded")
+                       f"r{spec.rank}, {spec.fmt}); oracle forward (NumPy float64), median of 3 runs "
+                       f"({', '.join(f'{x:.2f}' for x in times)} s); pack excluded",
+                cpu_model=_cpu_model(), blas=vendor, blas_threads=threads)
+
+
+def measured_peaks(torch, S, reps=5):
+    """Measured ceilings of this GPU in the same process: the MFMA-only loop
+    of each matrix instruction the GEMMs use (random and constant operand
+    bits) and a 2 GiB device copy, each the median of `reps` event-timed runs."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            v = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return v, sorted(ts)[len(ts) // 2]
+
+    out = {}
+    for kind, iters in (("mxfp4", 20000), ("int8", 10000), ("bf16", 10000)):
+        for const in (False, True):
+            fl, t = timed(lambda: S.measure_mfma_peak(kind, iters, constant=const, stream=stream))
+            out[f"{kind}_{'constant' if const else 'random'}_tflops"] = round(fl / t / 1e12, 1)
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    _, t = timed(lambda: S.measure_copy(src, dst, stream=stream))
+    out["copy_gbs"] = round(2 * n / t / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def settle(layer, sets, torch, S, seconds=0.5):
+    """Run forwards untimed for a fixed time before the warm-up steps: after
+    the host-side pack the GPU has been idle and its clocks take tens of
+    milliseconds to come back up."""
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            s = sets[i % len(sets)]
+            S.linear_forward(layer, s["dev"], s["x"], y=s["y"], workspace=s["ws"], stream=stream)
+            i += 1
+        torch.cuda.synchronize()
+    return i
 
 
 def bench_c4(args, torch, S, synth):
@@ -261,6 +344,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-c4", action="store_true", help="skip the FLUX block's linears (config 4)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and copy ceilings")
     ap.add_argument("--layer-markers", action="store_true",
                     help="launch one byte-fill kernel before each config-4 layer (layer boundaries in profiler traces)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -286,6 +370,7 @@ def main():
     layer, host, lay, sets = make_workload(spec, args.rotate, torch, S, synth)
     flops = 2.0 * spec.M * spec.N * spec.K
 
+    nsettle = settle(layer, sets, torch, S)
     ms, wall_ms = time_forward(layer, sets, args.steps, args.warmup, torch, S)
     tops = flops / (ms * 1e-3) / 1e12
     log(f"forward: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us), {tops:.1f} effective TOPS")
@@ -302,6 +387,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     traffic = traffic_from_profile()
+    peaks = None if args.no_peaks else measured_peaks(torch, S)
+    if peaks:
+        log(f"measured peaks: {peaks}")
     out = {
         "metric": METRIC,
         "value": round(tops, 3),
@@ -322,11 +410,18 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_TFLOPS["mxfp4"],
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_TFLOPS["mxfp4"], 4),
                      "traffic": traffic, "kernel": "svdq::gemm_mxfp4_kernel (persistent, 192x384 tiles)",
-                     "kernel_avg_us": round(t2 * 1e3, 2), "algorithmic_bytes": gemm_bytes(spec)},
+                     "kernel_avg_us": round(t2 * 1e3, 2), "algorithmic_bytes": gemm_bytes(spec),
+                     "measured_peak": peaks["mxfp4_random_tflops"] if peaks else None,
+                     "frac_of_measured": round(gemm_tflops / peaks["mxfp4_random_tflops"], 4) if peaks else None},
         "stage1": {"kernel": "stage1_kernel<MXFP4>", "avg_us": round(t1 * 1e3, 2), "bound": "hbm",
                    "achieved": round(s1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": round(s1_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": stage1_bytes(spec)},
+                   "frac": round(s1_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": stage1_bytes(spec),
+                   "measured_peak": peaks["copy_gbs"] if peaks else None,
+                   "frac_of_measured": round(s1_gbs / peaks["copy_gbs"], 4) if peaks else None},
+        "settle_steps": nsettle,
     }
+    if peaks:
+        out["measured_peaks"] = peaks
     if not args.no_secondary:
         sec = []
         for idx in (3, 1):

@@ -18,7 +18,7 @@ __all__ = [
     "SvdqError", "FMT_INT4", "FMT_MXFP4", "LayerDesc", "lib", "lib_path", "status_string",
     "packed_bytes", "pack_weights", "quantize_residual", "lora_extend", "unpack_weights", "workspace_bytes",
     "to_device", "linear_forward", "linear_forward_noalloc", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
-    "SVDQLinear", "EXPORTED_SYMBOLS", "Layer",
+    "SVDQLinear", "EXPORTED_SYMBOLS", "Layer", "measure_mfma_peak", "measure_copy",
 ]
 
 FMT_INT4 = 0
@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = [
     "svdq_quantize_residual", "svdq_unpack_weights", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_stage1", "svdq_unpack_workspace",
     "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc", "svdq_lora_extend",
+    "svdq_measure_mfma_peak", "svdq_measure_copy",
 ]
 
 # bytes of the library-owned device workspace of svdq_linear_forward_noalloc
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
         "svdq_quantize_residual": [D, vp, vp, vp, vp, vp, P(Packed)],
         "svdq_unpack_weights": [D, P(Packed), vp, vp, vp, vp, vp],
         "svdq_lora_extend": [D, P(Packed), ctypes.c_int32, vp, vp, ctypes.c_float, P(Packed)],
+        "svdq_measure_mfma_peak": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_double), vp],
+        "svdq_measure_copy": [vp, vp, sz, vp],
         "svdq_workspace_bytes": [D, i64, P(sz)],
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
         "svdq_linear_forward_noalloc": [D, P(Packed), vp, i64, vp, vp],
@@ -335,6 +338,25 @@ def debug_int4_group_sums(layer: Layer, dev: dict, workspace, M: int, m0: int, m
                                             int(nc), _ptr(p_out), _stream(stream)),
            "svdq_debug_int4_group_sums")
     return p_out
+
+
+MFMA_KINDS = {"mxfp4": 0, "int8": 1, "bf16": 2}
+
+
+def measure_mfma_peak(kind: str, iters: int, constant: bool = False, stream=None) -> float:
+    """Enqueue the MFMA-only loop of `kind` on the current stream; returns its
+    flop count (time it with events on the same stream)."""
+    f = ctypes.c_double()
+    _check(lib().svdq_measure_mfma_peak(MFMA_KINDS[kind], 1 if constant else 0, int(iters), ctypes.byref(f),
+                                        _stream(stream)), "svdq_measure_mfma_peak")
+    return f.value
+
+
+def measure_copy(src, dst, stream=None):
+    """Enqueue dst = src (device tensors of the same byte size) on the stream."""
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nbytes
+    _check(lib().svdq_measure_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "svdq_measure_copy")
 
 
 class SVDQLinear:

@@ -75,9 +75,9 @@ svdq_status common_checks(const svdq_layer_desc* d, const svdq_packed* dev, cons
   if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
   // MXFP4 activation scale bytes are addressed with 32-bit stage offsets,
   // the tiled INT4 GEMM's activation codes with 32-bit byte offsets
-  if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)d->K + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
+  if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)kpad(d) + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
     return SVDQ_ERR_SHAPE;
-  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * d->K >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
+  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * kpad(d) >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
@@ -94,7 +94,8 @@ Stage1Args stage1_args(const svdq_layer_desc* d, const svdq_packed* dev, const u
   Stage1Args a;
   a.fmt = d->format;
   a.M = (int)M;
-  a.K = d->K;
+  a.K = kpad(d);
+  a.xk = d->K;
   a.r32 = rank32(d->rank);
   a.x = x;
   a.mu = dev->mu;
@@ -117,8 +118,10 @@ GemmArgs gemm_args(const svdq_layer_desc* d, const svdq_packed* dev, int64_t M, 
   std::memset(&a, 0, sizeof(a));
   a.fmt = d->format;
   a.M = (int)M;
-  a.N = d->N;
-  a.K = d->K;
+  a.N = npad(d);
+  a.K = kpad(d);
+  a.ldy = d->N;
+  a.ldk = d->K;
   a.r32 = rank32(d->rank);
   a.qx = b + L.qx;
   a.sx = b + L.sx;
@@ -197,6 +200,28 @@ svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* d, const svdq_pac
   return svdq_linear_forward(d, dev, x, M, y, ws, kNoAllocScratchBytes, stream);
 }
 
+svdq_status svdq_measure_mfma_peak(int32_t kind, int32_t constant_operands, int32_t iters, double* flops,
+                                   void* stream) {
+  if (!flops) return SVDQ_ERR_NULL;
+  if (kind < 0 || kind > 2 || iters < 1 || iters > (1 << 24)) return SVDQ_ERR_SHAPE;
+  int cus = 0;
+  svdq_status st = check_device(&cus);
+  if (st != SVDQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return after_launch(launch_mfma_peak(kind, constant_operands ? 1 : 0, iters, cus, nullptr, s, flops), s);
+}
+
+svdq_status svdq_measure_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return SVDQ_OK;
+  if (!src || !dst) return SVDQ_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst) || bytes % 16 != 0) return SVDQ_ERR_SHAPE;
+  int cus = 0;
+  svdq_status st = check_device(&cus);
+  if (st != SVDQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return after_launch(launch_copy(src, dst, bytes, cus, s), s);
+}
+
 svdq_status svdq_gemm(const svdq_layer_desc* d, const svdq_packed* dev, const void* ws,
                       size_t ws_bytes, int64_t M, uint16_t* y, void* stream) {
   svdq_status st = common_checks(d, dev, ws, M, ws, ws_bytes);
@@ -217,7 +242,7 @@ svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_pack
   svdq_status st = check_desc(d);
   if (st != SVDQ_OK) return st;
   if (d->format != SVDQ_FMT_INT4_G64) return SVDQ_ERR_FORMAT;
-  if (M <= 0 || M > (1 << 24) || round32(M) * d->K >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
+  if (M <= 0 || M > (1 << 24) || round32(M) * kpad(d) >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (!ws || !p) return SVDQ_ERR_NULL;

@@ -112,8 +112,9 @@ __device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 }
 
 struct Geo {
-  int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;
+  int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;   // N, K padded
   int r32;
+  int ldy;   // Y's row stride and width (the layer's N)
   int tm_off, tn_off;   // group-sum hook: the window's first tile
   // whole tiles (indices below sk_base, a multiple of 8: rounds * grid),
   // then the sk_tiles tiles from index sk_base: tile index sk_base + 8 m + x
@@ -307,7 +308,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       for (int e = 0; e < 16; ++e) {
         const int ch = n0t + wn * kWN + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
         if (tok >= a.m0 && tok < a.m0 + a.mc && ch >= a.n0 && ch < a.n0 + a.nc)
-          a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (g.K / 64) + 2 * st + gg] = p[e] / 256;
+          if (2 * st + gg < a.ldk / 64)   // the layer's groups (not the padding)
+            a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (a.ldk / 64) + 2 * st + gg] = p[e] / 256;
       }
     } else {
 #pragma unroll
@@ -380,9 +382,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   // h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <-> (q = 2, h = 1), each
   // lane stores two 16-byte runs of one row.
   auto store_tile = [&](int m0t, int n0, const float (&bv)[kTN][16]) {
-    const int ynrec = min(g.M - m0t, kBM) * g.N * 2;
+    const int ynrec = min(g.M - m0t, kBM) * g.ldy * 2;
     const __amdgpu_buffer_rsrc_t yrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0t * g.N, 0, ynrec, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0t * g.ldy, 0, ynrec, 0x00020000);
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
 #pragma unroll
@@ -401,11 +403,12 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
           }
         }
         // always issued (the ring waits count them); the resource drops rows
-        // past M and a block past N is sent past the end
+        // past M, and an 8-channel run past the layer's N is sent past the end
         const int col = n0 + 32 * j + 8 * h;
-        const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
+        const int off = ((wm * kWM + 32 * i + lr) * g.ldy + col) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, col < g.ldy ? off : ynrec, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col + 16 < g.ldy ? off + 32 : ynrec,
+                                               0, 0);
       }
     }
   };
@@ -577,6 +580,7 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   g.nst = a.K / 128;
   g.act_rows = (a.M + 15) / 16 * 16;
   g.r32 = a.r32;
+  g.ldy = a.ldy;
   g.tm_off = g.tn_off = 0;
   int grid = num_cus > 0 ? num_cus : 256;
   if (a.p) {

@@ -113,7 +113,8 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 }
 
 struct Geo {
-  int M, N, K, MB, NB, KS, nst, nlr, nstt, tiles_m, tiles_n;
+  int M, N, K, MB, NB, KS, nst, nlr, nstt, tiles_m, tiles_n;   // N, K padded
+  int ldy;   // Y's row stride and width (the layer's N)
 };
 
 // Ring-step transfers: direct global->LDS loads of 16 bytes per lane. A
@@ -304,9 +305,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
     // 32 contiguous bytes of one row per lane pair.
     const uint8_t* bslot = smem + ((gs - 1) & (kNStage - 1)) * kSlot + kScA + wn * kWN * 2;
     // Y rows of this tile as a buffer resource: stores past its end are dropped
-    const int ynrec = min(g.M - tmc.tm * kBM, kBM) * g.N * 2;
+    const int ynrec = min(g.M - tmc.tm * kBM, kBM) * g.ldy * 2;
     const __amdgpu_buffer_rsrc_t yrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.N, 0, ynrec, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.ldy, 0, ynrec, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
       float bv[16];
@@ -334,11 +335,12 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
           }
         }
         // always issued (the ring waits count them); the resource drops rows
-        // past M and a block past N is sent past the end
+        // past M, and an 8-channel run past the layer's N is sent past the end
         const int col = n0 + 32 * bperm(wn * kTN + j) + 8 * h;
-        const int off = col < g.N ? ((wm * kWM + 32 * i + lr) * g.N + col) * 2 : ynrec;
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col < g.N ? off + 32 : ynrec, 0, 0);
+        const int off = ((wm * kWM + 32 * i + lr) * g.ldy + col) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, col < g.ldy ? off : ynrec, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col + 16 < g.ldy ? off + 32 : ynrec,
+                                               0, 0);
       }
     }
     stores_due = kNStage - 1;
@@ -371,6 +373,7 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st) {
   g.nstt = g.nst + g.nlr;
   g.tiles_m = (a.M + kBM - 1) / kBM;
   g.tiles_n = (a.N + kBN - 1) / kBN;
+  g.ldy = a.ldy;
   const int ntiles = g.tiles_m * g.tiles_n;
   // persistent grid: one workgroup per CU, a multiple of 8 so each stays on its XCD's tiles
   int grid = num_cus > 0 ? num_cus : 256;

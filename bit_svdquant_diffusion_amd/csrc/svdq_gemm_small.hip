@@ -53,7 +53,8 @@ __device__ __forceinline__ void sm_widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 // token l % 32. bf16 out: after the lane-half swap of the packed pairs
 // (q = 1, h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <-> (q = 2, h = 1),
 // lane h holds channels 8 h + (0..7) and 16 + 8 h + (0..7) of its token.
-__device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int M, int N, int n0, int m, int h) {
+// Y has ldy channels per row; 8-channel runs past them are not stored.
+__device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int M, int ldy, int n0, int m, int h) {
   uint32_t o[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) o[p] = sm_cvt_bf16x2(v[2 * p], v[2 * p + 1]);
@@ -67,9 +68,9 @@ __device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int
     }
   }
   if (m < M) {
-    u32x4* dst = reinterpret_cast<u32x4*>(y + (size_t)m * N + n0 + 8 * h);
-    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-    dst[2] = u32x4{o[4], o[5], o[6], o[7]};
+    u32x4* dst = reinterpret_cast<u32x4*>(y + (size_t)m * ldy + n0 + 8 * h);
+    if (n0 + 8 * h < ldy) dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    if (n0 + 16 + 8 * h < ldy) dst[2] = u32x4{o[4], o[5], o[6], o[7]};
   }
 }
 }  // namespace
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                   const int ch = nb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                  if (ch >= a.n0 && ch < a.n0 + a.nc)
-                    a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * KS + grp] = pp[e] / 256;
+                  if (ch >= a.n0 && ch < a.n0 + a.nc && grp < a.ldk / 64)
+                    a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (a.ldk / 64) + grp] = pp[e] / 256;
                 }
               }
             } else {
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
       }
     }
     if (splits == 1) {
-      sm_store_block(v, a.y, a.M, a.N, nb * 32, b * 32 + lr, h);
+      sm_store_block(v, a.y, a.M, a.ldy, nb * 32, b * 32 + lr, h);
     } else {
       f32x4* dst = reinterpret_cast<f32x4*>(part) + ((((size_t)sp * mb + b) * NB + nb) * 64 + lane) * 4;
 #pragma unroll
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs a, int spl
 // Y = bf16 of the K shares' partials added in share order; one wave per
 // (token block, channel block).
 __global__ __launch_bounds__(64) void gemm_small_sum(const float* __restrict__ part, uint16_t* __restrict__ y,
-                                                        int M, int N, int MB, int splits) {
+                                                        int M, int N, int ldy, int MB, int splits) {
   const int lane = threadIdx.x, h = lane >> 5, lr = lane & 31;
   const int NB = N / 32, b = blockIdx.x / NB, nb = blockIdx.x - b * NB;
   f32x16 v = f32x16{};
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(64) void gemm_small_sum(const float* __restrict__ p
       for (int e = 0; e < 4; ++e) v[4 * c + e] = sp == 0 ? w[e] : v[4 * c + e] + w[e];
     }
   }
-  sm_store_block(v, y, M, N, nb * 32, b * 32 + lr, h);
+  sm_store_block(v, y, M, ldy, nb * 32, b * 32 + lr, h);
 }
 
 bool gemm_small_fits(const GemmArgs& a, int num_cus) {
@@ -388,7 +389,7 @@ static hipError_t launch_nw(const GemmArgs& a, int num_cus, hipStream_t st) {
                      splits, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1 || DBG) return e;
-  hipLaunchKernelGGL(gemm_small_sum, dim3(mb * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, mb, splits);
+  hipLaunchKernelGGL(gemm_small_sum, dim3(mb * NB), dim3(64), 0, st, a.part, a.y, a.M, a.N, a.ldy, mb, splits);
   return hipGetLastError();
 }
 

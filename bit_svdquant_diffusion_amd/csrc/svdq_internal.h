@@ -8,8 +8,9 @@
 namespace svdq {
 
 struct Stage1Args {
-  int fmt, M, K, r32;
-  const uint16_t* x;    // bf16 [M][K]
+  int fmt, M, K, r32;   // K: padded to whole 256-channel steps
+  int xk;               // the layer's K: X's row stride, and its channels (the rest read as zero)
+  const uint16_t* x;    // bf16 [M][xk]
   const float* mu;      // [K]
   const uint16_t* l1s;  // L1 in stage-1 MFMA order
   // activation codes, scales and Z = X_hat L1 over round32(M) rows: codes
@@ -28,7 +29,9 @@ hipError_t launch_stage1(const Stage1Args& a, int num_cus, hipStream_t st);
 hipError_t prepare_stage1();   // one-time per device: kernels' dynamic LDS attribute
 
 struct GemmArgs {
-  int fmt, M, N, K, r32;
+  int fmt, M, N, K, r32;   // N, K: padded (whole 32-row blocks, whole 256-channel steps)
+  int ldy;                 // the layer's N: Y's row stride and width (stores past it are dropped)
+  int ldk;                 // the layer's K (the group-sum hook's groups)
   // operands in the layouts of Stage1Args and the packed layer (z and l2t
   // unused when r32 == 0)
   const uint8_t* qx;
@@ -38,7 +41,7 @@ struct GemmArgs {
   const void* sw;
   const uint16_t* l2t;
   const uint16_t* bias;  // bf16 [N]
-  uint16_t* y;           // bf16 [M][N]
+  uint16_t* y;           // bf16 [M][ldy]
   // INT4 split of the last tiles: per-tile ticket counters (cleared by
   // stage 1) and fp32 partial tiles, in the workspace
   uint32_t* flags;
@@ -57,6 +60,11 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st);
 // one-time per device: the kernels' dynamic LDS attribute
 hipError_t prepare_gemm_int4();
 hipError_t prepare_gemm_mxfp4();
+
+// measured ceilings of the part (not part of the layer): an MFMA-only loop
+// (kind 0 scaled FP4, 1 i8, 2 bf16; *flops = its flop count) and a device copy
+hipError_t launch_mfma_peak(int kind, int constant, int iters, int grid, float* sink, hipStream_t st, double* flops);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, int num_cus, hipStream_t st);
 
 inline hipError_t launch_gemm(const GemmArgs& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;

@@ -17,10 +17,13 @@ constexpr int kMaxRank = 128;
 inline int rank32(int r) { return (r + 31) / 32 * 32; }
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+// K must hold whole scale groups of the 4-bit GEMM's K step: 64 channels
+// (INT4) or 128 (MXFP4); N whole 16-byte runs of bf16 Y (8 channels).
 inline svdq_status check_desc(const svdq_layer_desc* d) {
   if (!d) return SVDQ_ERR_NULL;
   if (d->format != SVDQ_FMT_INT4_G64 && d->format != SVDQ_FMT_MXFP4_G32) return SVDQ_ERR_FORMAT;
-  if (d->K <= 0 || d->N <= 0 || d->K % 256 != 0 || d->N % 32 != 0) return SVDQ_ERR_SHAPE;
+  const int kq = d->format == SVDQ_FMT_INT4_G64 ? 64 : 128;
+  if (d->K <= 0 || d->N <= 0 || d->K % kq != 0 || d->N % 8 != 0) return SVDQ_ERR_SHAPE;
   if (d->K > 65536 || d->N > 65536) return SVDQ_ERR_SHAPE;
   if (d->rank < 0 || d->rank > kMaxRank || d->rank % 16 != 0) return SVDQ_ERR_SHAPE;
   if (d->rank > d->K || d->rank > d->N) return SVDQ_ERR_SHAPE;
@@ -29,9 +32,17 @@ inline svdq_status check_desc(const svdq_layer_desc* d) {
 
 inline int64_t round32(int64_t v) { return (v + 31) / 32 * 32; }
 
+// Device layouts hold K padded to whole 256-channel stage-1 steps and N
+// padded to whole 32-row blocks: the padding's codes, scales, L1 rows, L2
+// columns and bias are zero, and stage 1 gives the padded channels of X zero
+// codes and scales, so they add nothing. The kernels run on the padded sizes;
+// only X's row stride and Y's row stride and width are the layer's own.
+inline int kpad(const svdq_layer_desc* d) { return (d->K + 255) / 256 * 256; }
+inline int npad(const svdq_layer_desc* d) { return (d->N + 31) / 32 * 32; }
+
 inline size_t scale_bytes(const svdq_layer_desc* d, int64_t rows) {
-  return d->format == SVDQ_FMT_INT4_G64 ? (size_t)rows * (d->K / kGroupInt4) * 4
-                                        : (size_t)rows * (d->K / kBlockMx);
+  return d->format == SVDQ_FMT_INT4_G64 ? (size_t)rows * (kpad(d) / kGroupInt4) * 4
+                                        : (size_t)rows * (kpad(d) / kBlockMx);
 }
 // Row stride of the INT4 activation scales [K/64][act_rows(M)] in the workspace.
 inline int64_t act_rows(int64_t M) { return (M + 15) / 16 * 16; }
@@ -39,11 +50,11 @@ inline int64_t act_rows(int64_t M) { return (M + 15) / 16 * 16; }
 inline svdq_packed_sizes packed_sizes(const svdq_layer_desc* d) {
   svdq_packed_sizes s;
   s.mu = (size_t)d->K * 4;
-  s.l1 = (size_t)d->K * rank32(d->rank) * 2;
-  s.l2 = (size_t)d->N * rank32(d->rank) * 2;
-  s.qw = (size_t)d->N * d->K / 2;
-  s.sw = scale_bytes(d, d->N);
-  s.bias = (size_t)d->N * 2;
+  s.l1 = (size_t)kpad(d) * rank32(d->rank) * 2;
+  s.l2 = (size_t)npad(d) * rank32(d->rank) * 2;
+  s.qw = (size_t)npad(d) * kpad(d) / 2;
+  s.sw = scale_bytes(d, npad(d));
+  s.bias = (size_t)npad(d) * 2;
   return s;
 }
 
@@ -89,12 +100,12 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   const int64_t rows = round32(M);
   w.qx = 0;
-  w.sx = align256((size_t)rows * d->K / 2);
+  w.sx = align256((size_t)rows * kpad(d) / 2);
   w.z = w.sx + align256(scale_bytes(d, int4 ? act_rows(M) : rows));
   w.flags = w.z + align256((size_t)rows * rank32(d->rank) * 2);
   w.part = w.flags + (int4 ? align256((size_t)kSplitCounters * 4) : 0);
   w.zp = w.part + (int4 || M <= kFewTokens ? kPartAreaBytes : 0);
-  w.total = w.zp + (size_t)s1_pieces(d->K) * (rows < kS1SplitRows ? rows : kS1SplitRows) * 4 * rank32(d->rank) * 4;
+  w.total = w.zp + (size_t)s1_pieces(kpad(d)) * (rows < kS1SplitRows ? rows : kS1SplitRows) * 4 * rank32(d->rank) * 4;
   return w;
 }
 

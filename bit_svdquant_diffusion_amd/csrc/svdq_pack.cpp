@@ -318,14 +318,20 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
                         const float* mu, const uint16_t* l1b, const uint16_t* l2b,
                         svdq_packed* out) {
   const int K = d->K, N = d->N, r = d->rank, r32 = rank32(r);
+  const int Kp = kpad(d), Np = npad(d);
   if (r32 > 0 && (!out->l1 || !out->l2)) return SVDQ_ERR_NULL;
+  const svdq_packed_sizes sz = packed_sizes(d);
   std::memcpy(out->mu, mu, (size_t)K * 4);
+  // the padding (channels K..Kp, rows N..Np) stays zero
+  std::memset(out->qw, 0, sz.qw);
+  std::memset(out->sw, 0, sz.sw);
+  std::memset(out->bias, 0, sz.bias);
   // factors in device layout
   if (r32 > 0) {
-    std::memset(out->l1, 0, (size_t)K * r32 * 2);
-    std::memset(out->l2, 0, (size_t)N * r32 * 2);
+    std::memset(out->l1, 0, sz.l1);
+    std::memset(out->l2, 0, sz.l2);
     for (int k = 0; k < K; ++k)
-      for (int c = 0; c < r; ++c) out->l1[l1_index(K, r32, k, c)] = l1b[(size_t)k * r + c];
+      for (int c = 0; c < r; ++c) out->l1[l1_index(Kp, r32, k, c)] = l1b[(size_t)k * r + c];
     for (int i = 0; i < r; ++i)
       for (int n = 0; n < N; ++n) out->l2[frag16_index(r32, n, i)] = l2b[(size_t)i * N + n];
   }
@@ -358,15 +364,15 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
         if (d->format == SVDQ_FMT_INT4_G64) {
           float s;
           quant_int4_group(&rrow[(size_t)g * gsz], gsz, q.data(), &s);
-          sw_f[(size_t)g * N + n] = s;
+          sw_f[(size_t)g * Np + n] = s;
           for (int j = 0; j < gsz; j += 2)
-            out->qw[f_code_byte(K, n, g * gsz + j)] = (uint8_t)((q[j] & 15) | ((q[j + 1] & 15) << 4));
+            out->qw[f_code_byte(Kp, n, g * gsz + j)] = (uint8_t)((q[j] & 15) | ((q[j + 1] & 15) << 4));
         } else {
           uint8_t sb;
           quant_mx_block(&rrow[(size_t)g * gsz], gsz, cq.data(), &sb);
-          sw_b[f_scale_index(N, n, g)] = sb;
+          sw_b[f_scale_index(Np, n, g)] = sb;
           for (int j = 0; j < gsz; j += 2)
-            out->qw[f_code_byte(K, n, g * gsz + j)] = (uint8_t)((cq[j] & 15) | ((cq[j + 1] & 15) << 4));
+            out->qw[f_code_byte(Kp, n, g * gsz + j)] = (uint8_t)((cq[j] & 15) | ((cq[j + 1] & 15) << 4));
         }
       }
     }
@@ -473,12 +479,13 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
   if (st != SVDQ_OK) return st;
   if (!h) return SVDQ_ERR_NULL;
   const int K = d->K, N = d->N, r = d->rank, r32 = rank32(r);
+  const int Kp = kpad(d), Np = npad(d);
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   if (codes) {
     if (!h->qw) return SVDQ_ERR_NULL;
     for (size_t n = 0; n < (size_t)N; ++n)
       for (int k = 0; k < K; ++k) {
-        uint8_t byte = h->qw[f_code_byte(K, n, k)];
+        uint8_t byte = h->qw[f_code_byte(Kp, n, k)];
         int nib = (k & 1) ? (byte >> 4) : (byte & 15);
         codes[n * K + k] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
       }
@@ -489,18 +496,18 @@ svdq_status svdq_unpack_weights(const svdq_layer_desc* d, const svdq_packed* h, 
       const int G = K / kGroupInt4;
       for (int n = 0; n < N; ++n)
         for (int g = 0; g < G; ++g)
-          ((float*)scales)[(size_t)n * G + g] = ((const float*)h->sw)[(size_t)g * N + n];
+          ((float*)scales)[(size_t)n * G + g] = ((const float*)h->sw)[(size_t)g * Np + n];
     } else {
       const int G = K / kBlockMx;
       for (int n = 0; n < N; ++n)
         for (int g = 0; g < G; ++g)
-          ((uint8_t*)scales)[(size_t)n * G + g] = ((const uint8_t*)h->sw)[f_scale_index(N, n, g)];
+          ((uint8_t*)scales)[(size_t)n * G + g] = ((const uint8_t*)h->sw)[f_scale_index(Np, n, g)];
     }
   }
   if (l1 && r > 0) {
     if (!h->l1) return SVDQ_ERR_NULL;
     for (int k = 0; k < K; ++k)
-      for (int c = 0; c < r; ++c) l1[(size_t)k * r + c] = h->l1[l1_index(K, r32, k, c)];
+      for (int c = 0; c < r; ++c) l1[(size_t)k * r + c] = h->l1[l1_index(Kp, r32, k, c)];
   }
   if (l2 && r > 0) {
     if (!h->l2) return SVDQ_ERR_NULL;
@@ -527,7 +534,7 @@ svdq_status svdq_lora_extend(const svdq_layer_desc* base, const svdq_packed* h, 
   if (st != SVDQ_OK) return st;
   if (!out->l1 || !out->l2 || (base->rank > 0 && (!h->l1 || !h->l2))) return SVDQ_ERR_NULL;
   const int K = base->K, N = base->N, r0 = base->rank, r = ed.rank, r32 = rank32(r);
-  const int r032 = rank32(r0);
+  const int r032 = rank32(r0), Kp = kpad(base);
   if (!all_finite(lora_a, (size_t)K * lora_rank) || !all_finite(lora_b, (size_t)lora_rank * N) ||
       !std::isfinite(scale))
     return SVDQ_ERR_NUMERIC;
@@ -536,7 +543,7 @@ svdq_status svdq_lora_extend(const svdq_layer_desc* base, const svdq_packed* h, 
   // the base factors (logical), then the adapter's columns of L1 and rows of L2
   std::vector<uint16_t> l1((size_t)K * r), l2((size_t)r * N);
   for (int k = 0; k < K; ++k) {
-    for (int c = 0; c < r0; ++c) l1[(size_t)k * r + c] = h->l1[l1_index(K, r032, k, c)];
+    for (int c = 0; c < r0; ++c) l1[(size_t)k * r + c] = h->l1[l1_index(Kp, r032, k, c)];
     for (int c = 0; c < lora_rank; ++c)
       l1[(size_t)k * r + r0 + c] =
           bf16_from_double(((double)lora_a[(size_t)k * lora_rank + c] * (double)scale) / (double)h->mu[k]);
@@ -546,10 +553,11 @@ svdq_status svdq_lora_extend(const svdq_layer_desc* base, const svdq_packed* h, 
   for (int i = 0; i < lora_rank; ++i)
     for (int n = 0; n < N; ++n) l2[(size_t)(r0 + i) * N + n] = bf16_from_double((double)lora_b[(size_t)i * N + n]);
   // device layout of the extended factors; the 4-bit side is copied as it is
-  std::memset(out->l1, 0, (size_t)K * r32 * 2);
-  std::memset(out->l2, 0, (size_t)N * r32 * 2);
+  const svdq_packed_sizes esz = packed_sizes(&ed);
+  std::memset(out->l1, 0, esz.l1);
+  std::memset(out->l2, 0, esz.l2);
   for (int k = 0; k < K; ++k)
-    for (int c = 0; c < r; ++c) out->l1[l1_index(K, r32, k, c)] = l1[(size_t)k * r + c];
+    for (int c = 0; c < r; ++c) out->l1[l1_index(Kp, r32, k, c)] = l1[(size_t)k * r + c];
   for (int i = 0; i < r; ++i)
     for (int n = 0; n < N; ++n) out->l2[frag16_index(r32, n, i)] = l2[(size_t)i * N + n];
   const svdq_packed_sizes sz = packed_sizes(base);
@@ -578,13 +586,13 @@ svdq_status svdq_unpack_workspace(const svdq_layer_desc* d, int64_t M, const voi
   WsLayout L = ws_layout(d, M);
   if (ws_bytes < L.total) return SVDQ_ERR_WORKSPACE;
   const uint8_t* base = (const uint8_t*)ws;
-  const int K = d->K, r = d->rank, r32 = rank32(r);
+  const int K = d->K, Kp = kpad(d), r = d->rank, r32 = rank32(r);
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   if (codes) {
     const uint8_t* q = base + L.qx;
     for (int64_t m = 0; m < M; ++m)
       for (int k = 0; k < K; ++k) {
-        uint8_t byte = q[f_code_byte(K, m, k)];
+        uint8_t byte = q[f_code_byte(Kp, m, k)];
         int nib = (k & 1) ? (byte >> 4) : (byte & 15);
         codes[(size_t)m * K + k] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
       }

@@ -114,7 +114,7 @@ template <int FMT, int NCB, int TH>
 __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
     uint8_t* __restrict__ qx, void* __restrict__ sx, uint16_t* __restrict__ z, float* __restrict__ zp, int M,
-    int K, uint32_t* __restrict__ flags, int nflags, int ps, int npieces, int grid, int split) {
+    int K, int XK, uint32_t* __restrict__ flags, int nflags, int ps, int npieces, int grid, int split) {
   using Cfg = S1Cfg<NCB, TH>;
   constexpr int D = Cfg::kDepth;
   constexpr int r32 = NCB * 16;
@@ -158,16 +158,20 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
   // step adds a scalar offset (no per-transfer address arithmetic).
   int ip = pb, ig = pb / npc, ic = pb - (pb / npc) * npc, is = 0, iend = 0, iu = 0;
   __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rmu = __builtin_amdgcn_make_buffer_rsrc((void*)mu, 0, K * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rmu = __builtin_amdgcn_make_buffer_rsrc((void*)mu, 0, XK * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rl1 = __builtin_amdgcn_make_buffer_rsrc((void*)l1s, 0, K * NCB * 32, 0x00020000);
   int vA = 0, vB = 0;   // the lane's X offsets (bytes) in the half's rows
   const int vmu = (q * 64 + lane) * 4;
   auto issue_group = [&]() {
-    // rows past M read row M - 1 (a half wholly past M reads it throughout)
+    // rows past M read row M - 1 (a half wholly past M reads it throughout).
+    // X's rows are XK channels; the steps run over K >= XK, and the reads of
+    // channels past XK (zeroed after the read) stay inside the resource,
+    // which ends with X's last row, or read zeros past it.
     const int m0 = ig * TG + th * S1_ROWS, m0c = min(m0, M - 1);
-    rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)m0c * K), 0, S1_ROWS * K * 2, 0x00020000);
-    vA = ((min(m0 + tA, M - 1) - m0c) * K + q * 64 + ((lane & 7) ^ ((tA >> 1) & 7)) * 8) * 2;
-    vB = ((min(m0 + tB, M - 1) - m0c) * K + q * 64 + ((lane & 7) ^ ((tB >> 1) & 7)) * 8) * 2;
+    rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)m0c * XK), 0, (min(M, m0c + S1_ROWS) - m0c) * XK * 2,
+                                           0x00020000);
+    vA = ((min(m0 + tA, M - 1) - m0c) * XK + q * 64 + ((lane & 7) ^ ((tA >> 1) & 7)) * 8) * 2;
+    vB = ((min(m0 + tB, M - 1) - m0c) * XK + q * 64 + ((lane & 7) ^ ((tB >> 1) & 7)) * 8) * 2;
   };
   is = ic * ps;
   iend = min(is + ps, nsteps);
@@ -276,18 +280,20 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
         __builtin_amdgcn_sched_barrier(0);
         S1_ISSUE()
         __builtin_amdgcn_sched_barrier(0);
+        const int k0 = cs * S1_STEP + q * 64;   // first channel of the quarter
+        // a quarter past the layer's channels (padding up to whole steps) is zero
+        const bool live = k0 < XK;
         float xh[16];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const f32x4 mv = muv[t];
           const u32x4& xw = t < 2 ? xa : xb;
           const uint32_t w0 = xw[(t & 1) * 2], w1 = xw[(t & 1) * 2 + 1];
-          xh[4 * t + 0] = bf16lo(w0) * mv.x;
-          xh[4 * t + 1] = bf16hi(w0) * mv.y;
-          xh[4 * t + 2] = bf16lo(w1) * mv.z;
-          xh[4 * t + 3] = bf16hi(w1) * mv.w;
+          xh[4 * t + 0] = live ? bf16lo(w0) * mv.x : 0.f;
+          xh[4 * t + 1] = live ? bf16hi(w0) * mv.y : 0.f;
+          xh[4 * t + 2] = live ? bf16lo(w1) * mv.z : 0.f;
+          xh[4 * t + 3] = live ? bf16hi(w1) * mv.w : 0.f;
         }
-        const int k0 = cs * S1_STEP + q * 64;   // first channel of the quarter
 
         // 3. Z += bf16(x_hat) L1: MFMA t takes channels 16j + 8t .. +7 of each lane
         if constexpr (NCB > 0) {
@@ -492,7 +498,8 @@ static hipError_t launch_t(const Stage1Args& a, int num_cus, hipStream_t st) {
   const bool split = NCB > 0 && npc > 1 && 2 * groups < cus && (int64_t)groups * TG <= kS1SplitRows;
   const int grid = split ? min(groups * npc, cus * per_cu) : groups;
   hipLaunchKernelGGL((stage1_kernel<FMT, NCB, TH>), dim3(grid), dim3(64 * S1_WAVES * TH), lds, st, a.x, a.mu,
-                     a.l1s, a.qx, a.sx, a.z, a.zp, a.M, a.K, a.flags, a.nflags, ps, groups * npc, grid, split ? 1 : 0);
+                     a.l1s, a.qx, a.sx, a.z, a.zp, a.M, a.K, a.xk, a.flags, a.nflags, ps, groups * npc, grid,
+                     split ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   hipLaunchKernelGGL(zsum_kernel, dim3((unsigned)(((int64_t)a.M * a.r32 * 4 + 255) / 256)), dim3(256), 0, st, a.zp,

@@ -37,10 +37,13 @@
  *     the default stream) and return without synchronizing; buffers must stay
  *     alive until that stream has finished the work. The library keeps no
  *     pointer after returning.
- *   - Shapes: K % 256 == 0, N % 32 == 0, 0 <= rank <= 128 with rank % 16 == 0,
- *     rank <= min(K, N); M >= 0 (M == 0 is a no-op returning SVDQ_OK).
- *     K, N <= 65536; M <= 2^24; MXFP4 also (K + 128) * ceil(M / 32) < 2^31,
- *     INT4 also 32 * ceil(M / 32) * K < 2^33 (activation codes below 4 GiB).
+ *   - Shapes: K % 64 == 0 (INT4) or K % 128 == 0 (MXFP4), N % 8 == 0,
+ *     0 <= rank <= 128 with rank % 16 == 0, rank <= min(K, N); M >= 0 (M == 0
+ *     is a no-op returning SVDQ_OK). K, N <= 65536; M <= 2^24. The packed
+ *     layer and the workspace hold K padded to Kp = 256 ceil(K / 256) and N
+ *     padded to Np = 32 ceil(N / 32) (the padding is zero and adds nothing);
+ *     MXFP4 also (Kp + 128) * ceil(M / 32) < 2^31, INT4 also
+ *     32 * ceil(M / 32) * Kp < 2^33 (activation codes below 4 GiB).
  *   - Device pointers (x, y, workspace and every packed buffer) must be
  *     16-byte aligned; a misaligned pointer returns SVDQ_ERR_SHAPE.
  *   - All functions are thread-safe; the only global state is a per-device
@@ -96,7 +99,10 @@ typedef struct {
  * calls and the device copy read by the forward call (copy each buffer
  * byte-for-byte to the device). Layouts are the library's own ("device
  * layout"); svdq_unpack_weights() returns the logical values.
+ * K and N below are the padded Kp and Np of the shape rules above (zeros in
+ * the padding), except for mu.
  *   mu   fp32 [K]                 runtime smoothing multiplier mu_k = fl32(1/lambda_k)
+ *                                 (the layer's K)
  *   l1   bf16                     L1 [K][rank], rank padded to 32, shuffled for the MFMA
  *   bias bf16 [N]
  * Both formats, in MFMA fragment order (rows in blocks of 32; lane l = 32h + r
@@ -292,6 +298,30 @@ SVDQ_API svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* desc, con
                                        const void* workspace, size_t workspace_bytes, int64_t M,
                                        int64_t m0, int64_t mc, int64_t n0, int64_t nc,
                                        int32_t* p, void* hip_stream);
+
+/*
+ * Measured ceilings of the GPU (not part of the layer; the benchmark reports
+ * the kernels against them beside the published peaks).
+ * svdq_measure_mfma_peak enqueues one MFMA-only loop on every compute unit:
+ * kind 0 v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 operands (the MXFP4 GEMM's
+ * instruction), 1 v_mfma_i32_32x32x32_i8 (the INT4 GEMM's), 2
+ * v_mfma_f32_32x32x16_bf16 (the low-rank branch's), `iters` steps of four
+ * independent accumulators per wave, operand bits random per lane or, with
+ * constant_operands, one fixed pattern. *flops receives the loop's operation
+ * count (2 per multiply-add); time it with events on hip_stream.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE (kind outside 0..2, iters outside
+ * 1..2^24), SVDQ_ERR_DEVICE.
+ */
+SVDQ_API svdq_status svdq_measure_mfma_peak(int32_t kind, int32_t constant_operands, int32_t iters,
+                                            double* flops, void* hip_stream);
+
+/*
+ * Enqueues dst = src for `bytes` device bytes (16-byte loads and stores over
+ * eight workgroups per compute unit): 2 * bytes of HBM traffic when neither
+ * buffer fits the caches. Both pointers 16-byte aligned, bytes % 16 == 0, the
+ * buffers must not overlap. Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_DEVICE.
+ */
+SVDQ_API svdq_status svdq_measure_copy(const void* src, void* dst, size_t bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -36,8 +36,12 @@ def test_status_strings():
 
 @pytest.mark.parametrize("K,N,r,fmt,status", [
     (512, 512, 16, 0, 0), (3072, 12288, 32, 1, 0),
-    (500, 512, 16, 0, 2),      # K % 256
-    (512, 500, 16, 0, 2),      # N % 32
+    (320, 40, 16, 0, 0),       # INT4 takes K % 64, N % 8 (padded inside)
+    (384, 72, 32, 1, 0),       # MXFP4 takes K % 128
+    (500, 512, 16, 0, 2),      # K % 64
+    (320, 64, 16, 1, 2),       # MXFP4 K % 128
+    (512, 500, 16, 0, 2),      # N % 8
+    (512, 36, 16, 0, 2),       # N % 8
     (512, 512, 17, 0, 2),      # rank % 16
     (512, 512, 144, 0, 2),     # rank > 128
     (256, 32, 48, 0, 2),       # rank > N
@@ -50,9 +54,10 @@ def test_desc_validation(K, N, r, fmt, status):
     assert S.lib().svdq_packed_bytes(ctypes.byref(d), ctypes.byref(out)) == status
     if status == 0:
         r32 = (r + 31) // 32 * 32
-        assert out.mu == 4 * K and out.qw == N * K // 2
-        assert out.l1 == K * r32 * 2 and out.l2 == N * r32 * 2 and out.bias == 2 * N
-        assert out.sw == (N * K // 64 * 4 if fmt == 0 else N * K // 32)
+        Kp, Np = (K + 255) // 256 * 256, (N + 31) // 32 * 32
+        assert out.mu == 4 * K and out.qw == Np * Kp // 2
+        assert out.l1 == Kp * r32 * 2 and out.l2 == Np * r32 * 2 and out.bias == 2 * Np
+        assert out.sw == (Np * Kp // 64 * 4 if fmt == 0 else Np * Kp // 32)
 
 
 def test_null_pointers():

@@ -84,6 +84,19 @@ SMALL = [
     # ring steps; the next tile's bias transfer is issued before the first
     # tile's epilogue reads its own
     _spec("two_tiles_k256_fp4", 1728, 256, 12288, 32, "mxfp4", 19),
+    # K and N that are not whole 256-channel steps or 32-row blocks (K % 64
+    # for INT4, K % 128 for MXFP4, N % 8): the tiled kernels (with the INT4
+    # split and both stage-1 modes), the few-token kernel with K shares and
+    # its 769-1024 token shape
+    _spec("k320_n40", 300, 320, 40, 16, "int4", 30),
+    _spec("k192_n72", 600, 192, 72, 16, "int4", 31),
+    _spec("k1088_n4104_split", 4200, 1088, 4104, 32, "int4", 32),
+    _spec("k384_n72_fp4", 300, 384, 72, 32, "mxfp4", 33),
+    _spec("k640_n1544_fp4", 2100, 640, 1544, 32, "mxfp4", 34),
+    _spec("k320_n40_few", 70, 320, 40, 16, "int4", 35),
+    _spec("k4160_n200_few_shares", 100, 4160, 200, 32, "int4", 36),
+    _spec("k384_n40_few_fp4", 50, 384, 40, 16, "mxfp4", 37),
+    _spec("k576_n1000_m1000", 1000, 576, 1000, 32, "int4", 38),
 ]
 
 

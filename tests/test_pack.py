@@ -26,6 +26,8 @@ CASES = [
     dict(K=256, N=96, r=0, M=40, seed=3),    # no low-rank branch
     dict(K=256, N=128, r=128, M=40, seed=4), # rank == min(K, N) limit of the ABI
     dict(K=768, N=224, r=48, M=64, seed=5, fmt="mxfp4"),
+    dict(K=320, N=40, r=16, M=32, seed=6),                  # K % 64, N % 8: padded inside
+    dict(K=384, N=72, r=32, M=32, seed=6, fmt="mxfp4"),     # K % 128
 ]
 
 
@@ -172,3 +174,27 @@ def test_lora_extend_errors():
                               1.0, ctypes.byref(out)) == 2
     assert L.svdq_lora_extend(ctypes.byref(layer.desc), ctypes.byref(p), 16, A.ctypes.data, B.ctypes.data,
                               1.0, ctypes.byref(out)) == 1
+
+
+@pytest.mark.parametrize("fmt,K,N", [("int4", 320, 40), ("mxfp4", 384, 72)])
+def test_padding_is_zero(fmt, K, N):
+    """Channels K..Kp and rows N..Np of the device layout are zero (codes,
+    scales, L1 rows, L2 columns, bias), so they add nothing to the GEMM."""
+    spec, lay = _layer(K=K, N=N, r=16, M=32, seed=9, fmt=fmt)
+    ax = np.abs(lay.x).max(axis=0)
+    layer = S.Layer(K, N, 16, fmt)
+    host = S.pack_weights(layer, lay.w_lin, lay.bias, ax, seed=1)
+    Kp, Np = 512, (N + 31) // 32 * 32
+    qw = host["qw"].reshape(Np // 32, Kp // 64, 64, 16)
+    # rows past N: lanes 32h + r with 32 b + r >= N
+    for b in range(Np // 32):
+        for lane in range(64):
+            if 32 * b + lane % 32 >= N:
+                assert not qw[b, :, lane].any()
+    # channels past K: whole 64-channel steps past K // 64
+    assert not qw[:, K // 64:].any()
+    bias = host["bias"].view(np.uint16)
+    assert not bias[N:Np].any()
+    if fmt == "int4":
+        sw = host["sw"].view(np.float32).reshape(Kp // 64, Np)
+        assert not sw[K // 64:].any() and not sw[:, N:].any()
