@@ -70,6 +70,26 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+SANITIZED_HOST_LIB = os.path.join(BUILD_DIR, "libsvdq_host_asan.so")
+
+
+def build_host_sanitized() -> str:
+    """The host-only part of the library (pack, unpack, LoRA extension, sizes
+    and workspace queries) built by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer, every finding fatal. For tests that load it
+    in a process started with libasan preloaded; no GPU code is in it."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = SANITIZED_HOST_LIB + ".tmp"
+    _run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-fsanitize=address,undefined",
+          "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-ffp-contract=off", "-Wall",
+          "-I" + INCLUDE, "-I" + CSRC] + [os.path.join(CSRC, s) for s in CPP_SOURCES] + ["-o", tmp, "-lpthread"])
+    os.replace(tmp, SANITIZED_HOST_LIB)
+    return SANITIZED_HOST_LIB
+
+
 if __name__ == "__main__":
-    p = build(verbose="-v" in sys.argv)
-    print(p)
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        p = build(verbose="-v" in sys.argv)
+        print(p)
