@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "LayerSpec", "CONFIGS", "config_layers", "make_layer", "bf16_bits",
-    "bf16_value", "round_to_bf16",
+    "bf16_value", "round_to_bf16", "calibration_rows", "awq_layers",
 ]
 
 
@@ -60,9 +60,9 @@ class LayerSpec:
     K: int
     N: int
     rank: int
-    fmt: str                    # "int4" (INT4, group 64) or "mxfp4" (E2M1 + E8M0 per 32)
+    fmt: str                    # "int4" (INT4, group 64), "mxfp4" (E2M1 + E8M0 per 32), or "w4a16" (AWQ-style)
     seed: int
-    x_kind: str = "normal"      # "normal" or "gelu"
+    x_kind: str = "normal"      # "normal", "gelu" or "silu"
     x_outlier_frac: float = 0.01
     x_outlier_scale: float = 50.0
     w_outlier_frac: float = 0.02
@@ -135,6 +135,20 @@ def _gelu(a: np.ndarray) -> np.ndarray:
     return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
 
 
+def _silu(a: np.ndarray) -> np.ndarray:
+    return a / (1.0 + np.exp(-a))
+
+
+def _draw_x(spec: LayerSpec, rng, rows: int, xo: np.ndarray) -> np.ndarray:
+    xf = rng.standard_normal((rows, spec.K), dtype=np.float64)
+    if spec.x_kind == "gelu":
+        xf = _gelu(xf)
+    elif spec.x_kind == "silu":
+        xf = _silu(2.0 * xf)
+    xf[:, xo] *= spec.x_outlier_scale
+    return xf
+
+
 @dataclass
 class Layer:
     spec: LayerSpec
@@ -159,10 +173,7 @@ def make_layer(spec: LayerSpec, m_rows: int | None = None, with_x: bool = True) 
     x_bits = x = None
     if with_x:
         rows = M if m_rows is None else min(m_rows, M)
-        xf = r_x.standard_normal((rows, K), dtype=np.float64)
-        if spec.x_kind == "gelu":
-            xf = _gelu(xf)
-        xf[:, xo] *= spec.x_outlier_scale
+        xf = _draw_x(spec, r_x, rows, xo)
         x_bits = bf16_bits(xf.astype(np.float32))
         x = bf16_value(x_bits)
 
@@ -172,6 +183,30 @@ def make_layer(spec: LayerSpec, m_rows: int | None = None, with_x: bool = True) 
     w_lin = np.ascontiguousarray(w.T.astype(np.float32))
     bias = round_to_bf16(r_b.standard_normal(N).astype(np.float32) * np.float32(0.1))
     return Layer(spec, x_bits, x, w_lin, bias, xo, wo)
+
+
+def calibration_rows(spec: LayerSpec, rows: int) -> np.ndarray:
+    """`rows` held-out activation rows of the layer's distribution (the same
+    outlier channels, drawn from the layer's spare stream), bf16 values as
+    float32: calibration data for a layer whose own batch is a few rows."""
+    r_out, _, _, _, r_spare = _streams(spec)
+    n_xo = int(round(spec.x_outlier_frac * spec.K))
+    xo = np.sort(r_out.choice(spec.K, size=n_xo, replace=False)) if n_xo else np.zeros(0, np.int64)
+    return bf16_value(bf16_bits(_draw_x(spec, r_spare, rows, xo).astype(np.float32)))
+
+
+def awq_layers() -> list[LayerSpec]:
+    """FLUX-shaped adaptive-normalization and modulation linears (the pages'
+    W4A16 layers), batch 2: a double-stream block's per-stream modulation
+    3072 -> 6 x 3072, a single-stream block's 3072 -> 3 x 3072, the final
+    norm's 3072 -> 2 x 3072, and the double-stream one at 16 rows. Inputs
+    are SiLU(2 N(0,1)) (a conditioning vector after its SiLU) with 1% of
+    channels x8; weights N(0, 1/K), no outlier rows."""
+    kw = dict(x_kind="silu", x_outlier_frac=0.01, x_outlier_scale=8.0, w_outlier_frac=0.0)
+    return [_layer("mod_double", 2, 3072, 18432, 0, "w4a16", 5, **kw),
+            _layer("mod_single", 2, 3072, 9216, 0, "w4a16", 6, **kw),
+            _layer("norm_out", 2, 3072, 6144, 0, "w4a16", 7, **kw),
+            _layer("mod_double_m16", 16, 3072, 18432, 0, "w4a16", 5, **kw)]
 
 
 def ragged_spec(name: str, M: int, K: int, N: int, rank: int, fmt: str, seed: int) -> LayerSpec:
