@@ -19,6 +19,7 @@ __all__ = [
     "packed_bytes", "pack_weights", "quantize_residual", "lora_extend", "unpack_weights", "workspace_bytes",
     "to_device", "linear_forward", "linear_forward_noalloc", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer", "measure_mfma_peak", "measure_copy",
+    "awq_packed_bytes", "awq_pack", "awq_unpack", "awq_to_device", "awq_forward",
 ]
 
 FMT_INT4 = 0
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = [
     "svdq_linear_forward", "svdq_stage1", "svdq_unpack_workspace",
     "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc", "svdq_lora_extend",
     "svdq_measure_mfma_peak", "svdq_measure_copy",
+    "svdq_awq_packed_bytes", "svdq_awq_pack", "svdq_awq_unpack", "svdq_awq_forward",
 ]
 
 # bytes of the library-owned device workspace of svdq_linear_forward_noalloc
@@ -60,6 +62,21 @@ class Packed(ctypes.Structure):
 
 
 PACKED_FIELDS = ("mu", "l1", "l2", "qw", "sw", "bias")
+
+
+class AwqDesc(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32)]
+
+
+AWQ_FIELDS = ("inv_s", "qw", "scales", "zeros", "bias")
+
+
+class AwqSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in AWQ_FIELDS]
+
+
+class AwqPacked(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in AWQ_FIELDS]
 
 _lib = None
 
@@ -92,6 +109,10 @@ def lib() -> ctypes.CDLL:
         "svdq_lora_extend": [D, P(Packed), ctypes.c_int32, vp, vp, ctypes.c_float, P(Packed)],
         "svdq_measure_mfma_peak": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_double), vp],
         "svdq_measure_copy": [vp, vp, sz, vp],
+        "svdq_awq_packed_bytes": [P(AwqDesc), P(AwqSizes)],
+        "svdq_awq_pack": [P(AwqDesc), vp, vp, vp, i64, ctypes.c_float, P(ctypes.c_double), vp, P(AwqPacked)],
+        "svdq_awq_unpack": [P(AwqDesc), P(AwqPacked), vp, vp, vp],
+        "svdq_awq_forward": [P(AwqDesc), P(AwqPacked), vp, i64, vp, vp],
         "svdq_workspace_bytes": [D, i64, P(sz)],
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
         "svdq_linear_forward_noalloc": [D, P(Packed), vp, i64, vp, vp],
@@ -357,6 +378,69 @@ def measure_copy(src, dst, stream=None):
     nbytes = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() == nbytes
     _check(lib().svdq_measure_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "svdq_measure_copy")
+
+
+# ----------------------------------------------------------------------------
+# AWQ-style W4A16 linear (adaptive-normalization and modulation layers)
+# ----------------------------------------------------------------------------
+def awq_packed_bytes(K: int, N: int) -> dict:
+    s = AwqSizes()
+    d = AwqDesc(int(K), int(N))
+    _check(lib().svdq_awq_packed_bytes(ctypes.byref(d), ctypes.byref(s)), "svdq_awq_packed_bytes")
+    return {n: getattr(s, n) for n in AWQ_FIELDS}
+
+
+def awq_pack(w_lin: np.ndarray, bias, x_cal: np.ndarray, alpha: float | None = None):
+    """svdq_awq_pack on host arrays: (host buffers, chosen alpha, s float64 [K])."""
+    w = np.ascontiguousarray(w_lin, dtype=np.float32)
+    N, K = w.shape
+    xc = np.ascontiguousarray(x_cal, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    sizes = awq_packed_bytes(K, N)
+    bufs = {n: np.zeros(max(sizes[n], 1), np.uint8) for n in AWQ_FIELDS}
+    p = AwqPacked(*[bufs[n].ctypes.data for n in AWQ_FIELDS])
+    a_out = ctypes.c_double()
+    s_out = np.zeros(K, np.float64)
+    d = AwqDesc(K, N)
+    _check(lib().svdq_awq_pack(ctypes.byref(d), _ptr(w), _ptr(b), _ptr(xc), xc.shape[0],
+                               -1.0 if alpha is None else float(alpha), ctypes.byref(a_out), _ptr(s_out),
+                               ctypes.byref(p)), "svdq_awq_pack")
+    return bufs, a_out.value, s_out
+
+
+def _awq_struct(bufs: dict) -> AwqPacked:
+    return AwqPacked(*[_ptr(bufs[n]) for n in AWQ_FIELDS])
+
+
+def awq_unpack(K: int, N: int, host: dict) -> dict:
+    codes = np.zeros((N, K), np.uint8)
+    scales = np.zeros((N, K // 128), np.float32)
+    zeros = np.zeros((N, K // 128), np.uint8)
+    d = AwqDesc(int(K), int(N))
+    p = _awq_struct(host)
+    _check(lib().svdq_awq_unpack(ctypes.byref(d), ctypes.byref(p), _ptr(codes), _ptr(scales), _ptr(zeros)),
+           "svdq_awq_unpack")
+    return dict(codes=codes, scales=scales, zeros=zeros, inv_s=host["inv_s"].view(np.float32)[:K].copy(),
+                bias=host["bias"].view(np.uint16)[:N].copy())
+
+
+def awq_to_device(host: dict, device="cuda") -> dict:
+    import torch
+    return {n: torch.from_numpy(host[n].copy()).to(device) for n in AWQ_FIELDS}
+
+
+def awq_forward(K: int, N: int, dev: dict, x, y=None, stream=None):
+    """y[M][N] bf16 = AWQ layer(x[M][K] bf16) via svdq_awq_forward."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape[-1] == K
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    d = AwqDesc(int(K), int(N))
+    p = _awq_struct(dev)
+    _check(lib().svdq_awq_forward(ctypes.byref(d), ctypes.byref(p), _ptr(x), M, _ptr(y), _stream(stream)),
+           "svdq_awq_forward")
+    return y
 
 
 class SVDQLinear:

@@ -41,7 +41,7 @@ svdq_status check_device(int* cus = nullptr, void** scratch_ptr = nullptr) {
       void* sp = nullptr;
       bool ok = hipGetDeviceProperties(&p, dev) == hipSuccess &&
                 std::strncmp(p.gcnArchName, "gfx950", 6) == 0 && prepare_gemm_mxfp4() == hipSuccess &&
-                prepare_gemm_int4() == hipSuccess && prepare_stage1() == hipSuccess &&
+                prepare_gemm_int4() == hipSuccess && prepare_stage1() == hipSuccess && prepare_awq() == hipSuccess &&
                 hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) == hipSuccess && sp != nullptr;
       s = ok ? 1 : 2;
       if (ok) {
@@ -198,6 +198,35 @@ svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* d, const svdq_pac
     if (st != SVDQ_OK) return st;
   }
   return svdq_linear_forward(d, dev, x, M, y, ws, kNoAllocScratchBytes, stream);
+}
+
+svdq_status svdq_awq_forward(const svdq_awq_desc* d, const svdq_awq_packed* dev, const uint16_t* x, int64_t M,
+                             uint16_t* y, void* stream) {
+  if (!d) return SVDQ_ERR_NULL;
+  if (d->K <= 0 || d->N <= 0 || d->K % 128 != 0 || d->K > 4096 || d->N % 16 != 0 || d->N > 65536)
+    return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
+  if (!dev || !dev->inv_s || !dev->qw || !dev->scales || !dev->zeros || !dev->bias) return SVDQ_ERR_NULL;
+  if (!aligned16(dev->inv_s) || !aligned16(dev->qw) || !aligned16(dev->scales)) return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!x || !y) return SVDQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return SVDQ_ERR_SHAPE;
+  int cus = 0;
+  svdq_status st = check_device(&cus);
+  if (st != SVDQ_OK) return st;
+  AwqArgs a;
+  a.M = (int)M;
+  a.K = d->K;
+  a.N = d->N;
+  a.x = x;
+  a.inv_s = dev->inv_s;
+  a.qw = dev->qw;
+  a.scales = dev->scales;
+  a.zeros = dev->zeros;
+  a.bias = dev->bias;
+  a.y = y;
+  hipStream_t s = (hipStream_t)stream;
+  return after_launch(launch_awq(a, cus, s), s);
 }
 
 svdq_status svdq_measure_mfma_peak(int32_t kind, int32_t constant_operands, int32_t iters, double* flops,

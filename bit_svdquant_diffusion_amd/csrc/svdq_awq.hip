@@ -1,0 +1,188 @@
+// The AWQ-style W4A16 linear on the GPU: 4-bit weights with a scale and a
+// zero point per 128 input channels, 16-bit activations (aiflownews.com, "How
+// Nunchaku four bit quantization actually works": the adaptive-normalization
+// and modulation layers). Its inputs are a few conditioning rows, so the
+// layer is a GEMV over 4-bit weights and its time is the weight stream.
+//
+// y[m,n] = b[n] + sum_g scale[n,g] sum_{k in g} x_hat[m,k] (q[n,k] - zero[n,g]),
+// x_hat = fl32(x inv_s) rounded to bf16 for the matrix unit. Per group the
+// inner sum runs on v_mfma_f32_16x16x32_bf16 as
+//   P = sum_k x_hat[m,k] (128 + q[n,k])   (128 + q is exact in bf16, and its
+//       bits come from the nibble with one and-or: 0x4300 | q)
+// and the zero point is taken out once per output and group:
+//   y += scale (P - (128 + zero) S),  S = sum_k x_hat[m,k] (per token and group).
+// So a weight costs under one vector instruction to unpack (seven per eight
+// nibbles) and the matrix unit does the multiply-adds.
+//
+// A workgroup of eight waves covers NB n-blocks of 16 output channels; the
+// waves of one n-block split its groups (K parts) and add their sums in
+// K-part order through LDS. Tokens go in chunks of 16 (the MFMA's rows): the
+// chunk's x_hat (bf16, rows padded by 8 channels against LDS bank conflicts)
+// and S sit in LDS. Each wave keeps up to eight groups of weights in flight
+// (16-byte loads, 1 KiB per n-block and group).
+#include "svdq_device.h"
+#include "svdq_internal.h"
+
+namespace svdq {
+
+namespace {
+constexpr int kAwqWaves = 8;
+constexpr int kAwqBatch = 8;    // groups of weights loaded ahead per wave
+constexpr int kAwqPadK = 8;     // bf16 padding of an x_hat row in LDS
+
+typedef __bf16 awq_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t awq_cvt_bf16x2(float lo, float hi) {
+  awq_bf16x2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+}  // namespace
+
+size_t awq_lds_bytes(int K) {
+  return (size_t)16 * (K + kAwqPadK) * 2 + (size_t)(K / 128) * 16 * 4 + (size_t)kAwqWaves * 4 * 64 * 4;
+}
+
+template <int NB>
+__global__ __launch_bounds__(64 * kAwqWaves) void awq_kernel(AwqArgs a) {
+  constexpr int KP = kAwqWaves / NB;   // waves (K parts) per n-block
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int K = a.K, G = K / 128, ldx = K + kAwqPadK;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [16][ldx] bf16
+  float* sxg = reinterpret_cast<float*>(smem + (size_t)16 * ldx * 2);            // [G][16]
+  float* red = sxg + G * 16;                                                     // [waves][4][64]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nbl = wave % NB, kp = wave / NB;
+  const int nb = blockIdx.x * NB + nbl;   // this wave's n-block
+  const bool live = nb * 16 < a.N;
+  const int g0 = G * kp / KP, g1 = G * (kp + 1) / KP;
+  const int r = lane & 15, c = lane >> 4;
+  const i32x4* wsrc = reinterpret_cast<const i32x4*>(a.qw) + ((size_t)min(nb, a.N / 16 - 1) * G) * 64 + lane;
+  const float* ssrc = a.scales + (size_t)min(nb, a.N / 16 - 1) * G * 16 + r;
+  const uint8_t* zsrc = a.zeros + (size_t)min(nb, a.N / 16 - 1) * G * 16 + r;
+
+  for (int t0 = 0; t0 < a.M; t0 += 16) {
+    if (t0 > 0) __syncthreads();   // the last chunk's LDS reads are done
+    // x_hat of the chunk's 16 rows (rows past M are zero), eight channels a thread
+    for (int i = tid; i < 16 * (K / 8); i += 64 * kAwqWaves) {
+      const int t = i / (K / 8), k = (i - t * (K / 8)) * 8;
+      u32x4 o = u32x4{0, 0, 0, 0};
+      if (t0 + t < a.M) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + t) * K + k);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.inv_s + k);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.inv_s + k + 4);
+        o[0] = awq_cvt_bf16x2(bf16lo(xv[0]) * s0[0], bf16hi(xv[0]) * s0[1]);
+        o[1] = awq_cvt_bf16x2(bf16lo(xv[1]) * s0[2], bf16hi(xv[1]) * s0[3]);
+        o[2] = awq_cvt_bf16x2(bf16lo(xv[2]) * s1[0], bf16hi(xv[2]) * s1[1]);
+        o[3] = awq_cvt_bf16x2(bf16lo(xv[3]) * s1[2], bf16hi(xv[3]) * s1[3]);
+      }
+      *reinterpret_cast<u32x4*>(xs + (size_t)t * ldx + k) = o;
+    }
+    __syncthreads();
+    // S[g][t] = sum of the group's bf16 x_hat, channels in order
+    for (int i = tid; i < G * 16; i += 64 * kAwqWaves) {
+      const int g = i / 16, t = i - g * 16;
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(xs + (size_t)t * ldx + g * 128);
+      float s = 0.f;
+      for (int j = 0; j < 64; ++j) {
+        s += bf16lo(row[j]);
+        s += bf16hi(row[j]);
+      }
+      sxg[i] = s;
+    }
+    __syncthreads();
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x4 wq[kAwqBatch];
+    float sc[kAwqBatch];
+    uint32_t zp[kAwqBatch];
+    auto load = [&](int gb) {
+#pragma unroll
+      for (int u = 0; u < kAwqBatch; ++u) {
+        const int g = min(gb + u, g1 - 1);   // past the part's end: repeat its last group (not used)
+        wq[u] = wsrc[(size_t)g * 64];
+        sc[u] = ssrc[g * 16];
+        zp[u] = zsrc[g * 16];
+      }
+    };
+    if (g0 < g1) load(g0);
+    for (int gb = g0; gb < g1; gb += kAwqBatch) {
+      i32x4 cw[kAwqBatch];
+      float csc[kAwqBatch];
+      uint32_t czp[kAwqBatch];
+#pragma unroll
+      for (int u = 0; u < kAwqBatch; ++u) {
+        cw[u] = wq[u];
+        csc[u] = sc[u];
+        czp[u] = zp[u];
+      }
+      if (gb + kAwqBatch < g1) load(gb + kAwqBatch);   // the next batch flies while this one is used
+#pragma unroll
+      for (int u = 0; u < kAwqBatch; ++u) {
+        const int g = gb + u;
+        if (g < g1) {
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            // A: token r, channels 128 g + 32 t + 8 c + (0..7); B: the same
+            // channels of output 16 nb + r as bf16 128 + q
+            const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (size_t)r * ldx + g * 128 + 32 * t + 8 * c);
+            const uint32_t w = (uint32_t)cw[u][t];
+            const u32x4 bv = u32x4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
+                                   ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
+                                                        p, 0, 0, 0);
+          }
+          // lane l holds tokens 4 c + (0..3) of output 16 nb + r
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(sxg + g * 16 + 4 * c);
+          const float zf = 128.f + (float)czp[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(csc[u], __builtin_fmaf(-zf, s4[e], p[e]), acc[e]);
+        }
+      }
+    }
+    // the K parts' sums in K-part order, + bias, bf16 out
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(wave * 4 + e) * 64 + lane] = acc[e];
+    __syncthreads();
+    if (kp == 0 && live) {
+      const int n = nb * 16 + r;
+      const float bv = __uint_as_float((uint32_t)a.bias[n] << 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < KP; ++k2) s += red[((nbl + NB * k2) * 4 + e) * 64 + lane];
+        const int m = t0 + 4 * c + e;
+        if (m < a.M) a.y[(size_t)m * a.N + n] = (uint16_t)f2bf(s + bv);
+      }
+    }
+  }
+}
+
+hipError_t prepare_awq() {
+  hipError_t e = hipFuncSetAttribute((const void*)awq_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)awq_lds_bytes(4096));
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)awq_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)awq_lds_bytes(4096));
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)awq_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)awq_lds_bytes(4096));
+}
+
+// The most n-blocks per workgroup that still gives every CU a workgroup.
+hipError_t launch_awq(const AwqArgs& a, int num_cus, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const int cus = num_cus > 0 ? num_cus : 256, nblk = a.N / 16;
+  const size_t lds = awq_lds_bytes(a.K);
+  if (nblk >= 4 * cus) {
+    hipLaunchKernelGGL(awq_kernel<4>, dim3((nblk + 3) / 4), dim3(64 * kAwqWaves), lds, st, a);
+  } else if (nblk >= 2 * cus) {
+    hipLaunchKernelGGL(awq_kernel<2>, dim3((nblk + 1) / 2), dim3(64 * kAwqWaves), lds, st, a);
+  } else {
+    hipLaunchKernelGGL(awq_kernel<1>, dim3(nblk), dim3(64 * kAwqWaves), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svdq

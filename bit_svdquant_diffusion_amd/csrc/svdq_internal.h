@@ -61,6 +61,20 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st);
 hipError_t prepare_gemm_int4();
 hipError_t prepare_gemm_mxfp4();
 
+// The AWQ-style W4A16 linear (layouts in svdq.h): y [M][N] bf16.
+struct AwqArgs {
+  int M, K, N;
+  const uint16_t* x;       // bf16 [M][K]
+  const float* inv_s;      // [K]
+  const uint8_t* qw;       // [N/16][K/128][64][16]
+  const float* scales;     // [N/16][K/128][16]
+  const uint8_t* zeros;    // [N/16][K/128][16]
+  const uint16_t* bias;    // bf16 [N]
+  uint16_t* y;
+};
+hipError_t launch_awq(const AwqArgs& a, int num_cus, hipStream_t st);
+hipError_t prepare_awq();
+
 // measured ceilings of the part (not part of the layer): an MFMA-only loop
 // (kind 0 scaled FP4, 1 i8, 2 bf16; *flops = its flop count) and a device copy
 hipError_t launch_mfma_peak(int kind, int constant, int iters, int grid, float* sink, hipStream_t st, double* flops);

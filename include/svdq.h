@@ -300,6 +300,78 @@ SVDQ_API svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* desc, con
                                        int32_t* p, void* hip_stream);
 
 /*
+ * ---------------------------------------------------------------------------
+ * AWQ-style W4A16 linear: 4-bit weights, 16-bit activations, for the
+ * adaptive-normalization and modulation layers the pages keep at higher
+ * precision (aiflownews.com, "How Nunchaku four bit quantization actually
+ * works"). y = x diag(inv_s) dequant(Q)^T + b with inv_s = fl32(1/s), s the
+ * activation-aware channel scales, and Q the 4-bit codes of W diag(s):
+ * per output channel and group of 128 input channels an fp32 scale and a
+ * u8 zero point, w = scale * (q - zero) with q in [0, 15].
+ * Shapes: K % 128 == 0, K <= 4096, N % 16 == 0, N <= 65536; M >= 0.
+ * Device layout (the host copy written by svdq_awq_pack, copied byte for byte):
+ *   inv_s  fp32 [K]
+ *   qw     u8 [N/16][K/128][64][16]: lane l = 16c + r holds output row 16b + r;
+ *          its 4-byte word t holds channels 128g + 32t + 8c + (0..7), element
+ *          2i in bits 4i..4i+3 and element 2i+1 in bits 16+4i..16+4i+3
+ *   scales fp32 [N/16][K/128][16], zeros u8 [N/16][K/128][16]  (row 16b + r at r)
+ *   bias   bf16 [N]
+ * ---------------------------------------------------------------------------
+ */
+typedef struct {
+  int32_t K, N;
+} svdq_awq_desc;
+
+typedef struct {
+  size_t inv_s, qw, scales, zeros, bias;
+} svdq_awq_sizes;
+
+typedef struct {
+  float* inv_s;
+  uint8_t* qw;
+  float* scales;
+  uint8_t* zeros;
+  uint16_t* bias;
+} svdq_awq_packed;
+
+/* Byte sizes of the buffers of an AWQ layer. Host only.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE. */
+SVDQ_API svdq_status svdq_awq_packed_bytes(const svdq_awq_desc* desc, svdq_awq_sizes* out);
+
+/*
+ * Offline preparation of an AWQ layer, host only. a_k = mean over the m_cal
+ * calibration rows x_cal (fp32 [m_cal][K]) of |x_cal[m,k]|; for alpha on the
+ * grid 0, 1/20, ..., 19/20 (or `alpha` when it is in [0, 1]; a negative value
+ * searches): s_k = max(a_k, 1e-4)^alpha / sqrt(max s * min s), W diag(s)
+ * quantized per group as above (fp32: scale = max(max - min, 1e-5) / 15,
+ * zero = clamp(-rint(min / scale), 0, 15), q = clamp(rint(w / scale) + zero,
+ * 0, 15)), and the candidate's loss the squared error of its output against
+ * x_cal W^T; the first alpha of least loss is kept.
+ * w_lin fp32 [N][K]; bias fp32 [N] or NULL. alpha_out and s_out (fp64 [K],
+ * the chosen s) may be NULL. host_out: buffers of svdq_awq_packed_bytes().
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE (also m_cal <= 0, alpha > 1),
+ * SVDQ_ERR_NUMERIC (non-finite input).
+ */
+SVDQ_API svdq_status svdq_awq_pack(const svdq_awq_desc* desc, const float* w_lin, const float* bias,
+                                   const float* x_cal, int64_t m_cal, float alpha, double* alpha_out,
+                                   double* s_out, svdq_awq_packed* host_out);
+
+/* Logical view of a host AWQ layer: codes u8 [N][K] (0..15), scales fp32
+ * [N][K/128], zeros u8 [N][K/128]; any output may be NULL. */
+SVDQ_API svdq_status svdq_awq_unpack(const svdq_awq_desc* desc, const svdq_awq_packed* host, uint8_t* codes,
+                                     float* scales, uint8_t* zeros);
+
+/*
+ * Runtime forward on the GPU: y bf16 [M][N] = layer(x bf16 [M][K]), one
+ * kernel on hip_stream. x_hat = fl32(x inv_s) is rounded to bf16 for the
+ * bf16 MFMA; sums in fp32. Built for a few rows (it streams the weights once
+ * per 16 rows). No workspace, nothing allocated. Device pointers 16-byte
+ * aligned. Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_DEVICE.
+ */
+SVDQ_API svdq_status svdq_awq_forward(const svdq_awq_desc* desc, const svdq_awq_packed* dev, const uint16_t* x,
+                                      int64_t M, uint16_t* y, void* hip_stream);
+
+/*
  * Measured ceilings of the GPU (not part of the layer; the benchmark reports
  * the kernels against them beside the published peaks).
  * svdq_measure_mfma_peak enqueues one MFMA-only loop on every compute unit:
