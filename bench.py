@@ -280,6 +280,41 @@ def settle(layer, sets, torch, S, seconds=0.5):
     return i
 
 
+def awq_bytes(spec):
+    """Algorithmic HBM bytes of one W4A16 launch: codes, scales and zero
+    points, inv_s, bias, x in and y out."""
+    return (spec.N * spec.K // 2 + spec.N * (spec.K // 128) * 5 + spec.K * 4 + spec.N * 2
+            + spec.M * spec.K * 2 + spec.M * spec.N * 2)
+
+
+def bench_awq(args, torch, S, synth):
+    """The AWQ-style W4A16 layers (FLUX modulation and final-norm shapes):
+    library pack with the alpha search on 32 held-out calibration rows, then
+    GPU time per call from graph replays over 16 weight sets (far more bytes
+    than the 256 MB MALL), against 8 TB/s."""
+    import numpy as np
+    rows = []
+    for sp in synth.awq_layers():
+        lay = synth.make_layer(sp)
+        t0 = time.time()
+        host, alpha, _ = S.awq_pack(lay.w_lin, lay.bias, synth.calibration_rows(sp, 32))
+        log(f"  packed {sp.name} (alpha {alpha}) in {time.time() - t0:.1f}s")
+        x = torch.from_numpy(lay.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        sets = [dict(dev=S.awq_to_device(host), y=torch.empty((sp.M, sp.N), dtype=torch.bfloat16, device="cuda"))
+                for _ in range(16)]
+        calls = [lambda s=s: S.awq_forward(sp.K, sp.N, s["dev"], x, y=s["y"]) for s in sets]
+        ms = time_graph(calls, max(8, args.steps // 4), torch)
+        b = awq_bytes(sp)
+        gbs = b / (ms * 1e-3) / 1e9
+        rows.append({"workload": sp.name, "M": sp.M, "K": sp.K, "N": sp.N, "alpha": alpha, "us": round(ms * 1e3, 2),
+                     "hbm_algorithmic_bytes": b, "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        log(f"awq {sp.name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+        del sets
+        torch.cuda.empty_cache()
+    return {"workload": "AWQ-style W4A16 linears, FLUX modulation and final-norm shapes, batch 2 and 16",
+            "kernel": "svdq::awq_kernel", "bound": "hbm", "layers": rows}
+
+
 def bench_c4(args, torch, S, synth):
     """Config 4: a FLUX double-stream block's linears at batch 2, 1024^2 (image
     M=8192, text M=1024) and the decode-like M=64, 256 runs of the same four
@@ -345,6 +380,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-c4", action="store_true", help="skip the FLUX block's linears (config 4)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and copy ceilings")
+    ap.add_argument("--no-awq", action="store_true", help="skip the W4A16 (AWQ-style) layers")
     ap.add_argument("--layer-markers", action="store_true",
                     help="launch one byte-fill kernel before each config-4 layer (layer boundaries in profiler traces)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -441,6 +477,8 @@ def main():
         out["secondary"] = sec
     if not args.no_c4:
         out["c4"] = bench_c4(args, torch, S, synth)
+    if not args.no_awq:
+        out["awq"] = bench_awq(args, torch, S, synth)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(layer, host, lay, spec, args.cpu_budget)

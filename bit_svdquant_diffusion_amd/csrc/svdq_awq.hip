@@ -16,18 +16,23 @@
 //
 // A workgroup of eight waves covers NB n-blocks of 16 output channels; the
 // waves of one n-block split its groups (K parts) and add their sums in
-// K-part order through LDS. Tokens go in chunks of 16 (the MFMA's rows): the
-// chunk's x_hat (bf16, rows padded by 8 channels against LDS bank conflicts)
-// and S sit in LDS. Each wave keeps up to eight groups of weights in flight
-// (16-byte loads, 1 KiB per n-block and group).
+// K-part order through LDS. Tokens go in chunks of up to 16 (the MFMA's
+// rows): the chunk's live rows of x_hat (bf16, rows padded by 8 channels
+// against LDS bank conflicts) and their S sit in LDS, so with a couple of
+// rows the LDS is small and several workgroups share a CU; rows past the
+// chunk enter the MFMA as zeros. Each wave keeps six groups of weights in
+// flight (16-byte loads, 1 KiB per n-block and group), the first ones issued
+// before the staging.
 #include "svdq_device.h"
 #include "svdq_internal.h"
+
+#include <algorithm>
 
 namespace svdq {
 
 namespace {
 constexpr int kAwqWaves = 8;
-constexpr int kAwqBatch = 8;    // groups of weights loaded ahead per wave
+constexpr int kAwqRing = 6;     // groups of weights in flight per wave
 constexpr int kAwqPadK = 8;     // bf16 padding of an x_hat row in LDS
 
 typedef __bf16 awq_bf16x2 __attribute__((ext_vector_type(2)));
@@ -37,17 +42,19 @@ __device__ __forceinline__ uint32_t awq_cvt_bf16x2(float lo, float hi) {
 }
 }  // namespace
 
-size_t awq_lds_bytes(int K) {
-  return (size_t)16 * (K + kAwqPadK) * 2 + (size_t)(K / 128) * 16 * 4 + (size_t)kAwqWaves * 4 * 64 * 4;
+// rows: x_hat rows staged at once (min(16, M))
+size_t awq_lds_bytes(int K, int rows) {
+  return (size_t)rows * (K + kAwqPadK) * 2 + (size_t)(K / 128) * 16 * 4 + (size_t)kAwqWaves * 4 * 64 * 4;
 }
 
 template <int NB>
-__global__ __launch_bounds__(64 * kAwqWaves) void awq_kernel(AwqArgs a) {
+__global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(4))) void awq_kernel(AwqArgs a) {
   constexpr int KP = kAwqWaves / NB;   // waves (K parts) per n-block
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K, G = K / 128, ldx = K + kAwqPadK;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [16][ldx] bf16
-  float* sxg = reinterpret_cast<float*>(smem + (size_t)16 * ldx * 2);            // [G][16]
+  const int rows = min(16, a.M);   // rows of x_hat staged at once
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                              // [rows][ldx] bf16
+  float* sxg = reinterpret_cast<float*>(smem + (size_t)rows * ldx * 2);          // [G][16]
   float* red = sxg + G * 16;                                                     // [waves][4][64]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -60,64 +67,64 @@ __global__ __launch_bounds__(64 * kAwqWaves) void awq_kernel(AwqArgs a) {
   const float* ssrc = a.scales + (size_t)min(nb, a.N / 16 - 1) * G * 16 + r;
   const uint8_t* zsrc = a.zeros + (size_t)min(nb, a.N / 16 - 1) * G * 16 + r;
 
+  // a ring of kAwqRing groups of weights (and their scales and zero points),
+  // each slot refilled with the group kAwqRing later as soon as it is used
+  i32x4 wq[kAwqRing];
+  float sc[kAwqRing];
+  uint32_t zp[kAwqRing];
+  auto load = [&](int u, int g) {
+    g = min(g, g1 - 1);   // past the part's end: repeat its last group (not used)
+    wq[u] = wsrc[(size_t)g * 64];
+    sc[u] = ssrc[g * 16];
+    zp[u] = zsrc[g * 16];
+  };
   for (int t0 = 0; t0 < a.M; t0 += 16) {
-    if (t0 > 0) __syncthreads();   // the last chunk's LDS reads are done
-    // x_hat of the chunk's 16 rows (rows past M are zero), eight channels a thread
-    for (int i = tid; i < 16 * (K / 8); i += 64 * kAwqWaves) {
-      const int t = i / (K / 8), k = (i - t * (K / 8)) * 8;
-      u32x4 o = u32x4{0, 0, 0, 0};
-      if (t0 + t < a.M) {
+    const int rc = min(16, a.M - t0);   // live rows of this chunk
+    if (t0 > 0) __syncthreads();         // the last chunk's LDS reads are done
+    // the first weights do not depend on x_hat: in flight during the staging
+    if (g0 < g1) {
+#pragma unroll
+      for (int u = 0; u < kAwqRing; ++u) load(u, g0 + u);
+    }
+    // x_hat of the live rows, eight channels a thread; the sixteen threads of
+    // a 128-channel group (consecutive lanes) then add their partial sums of
+    // the bf16 values in a fixed butterfly order into S
+    for (int i0 = 0; i0 < rc * (K / 8); i0 += 64 * kAwqWaves) {
+      const int i = i0 + tid;
+      const bool in = i < rc * (K / 8);
+      const int t = in ? i / (K / 8) : 0, k = in ? (i - t * (K / 8)) * 8 : 0;
+      float part = 0.f;
+      if (in) {
         const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + t) * K + k);
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.inv_s + k);
         const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.inv_s + k + 4);
+        u32x4 o;
         o[0] = awq_cvt_bf16x2(bf16lo(xv[0]) * s0[0], bf16hi(xv[0]) * s0[1]);
         o[1] = awq_cvt_bf16x2(bf16lo(xv[1]) * s0[2], bf16hi(xv[1]) * s0[3]);
         o[2] = awq_cvt_bf16x2(bf16lo(xv[2]) * s1[0], bf16hi(xv[2]) * s1[1]);
         o[3] = awq_cvt_bf16x2(bf16lo(xv[3]) * s1[2], bf16hi(xv[3]) * s1[3]);
+        *reinterpret_cast<u32x4*>(xs + (size_t)t * ldx + k) = o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          part += bf16lo(o[d]);
+          part += bf16hi(o[d]);
+        }
       }
-      *reinterpret_cast<u32x4*>(xs + (size_t)t * ldx + k) = o;
-    }
-    __syncthreads();
-    // S[g][t] = sum of the group's bf16 x_hat, channels in order
-    for (int i = tid; i < G * 16; i += 64 * kAwqWaves) {
-      const int g = i / 16, t = i - g * 16;
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(xs + (size_t)t * ldx + g * 128);
-      float s = 0.f;
-      for (int j = 0; j < 64; ++j) {
-        s += bf16lo(row[j]);
-        s += bf16hi(row[j]);
-      }
-      sxg[i] = s;
+      // i0 and the group's first thread are multiples of 16: a group's
+      // sixteen threads are lanes 16 j .. 16 j + 15 of one wave
+      part += __shfl_xor(part, 8, 16);
+      part += __shfl_xor(part, 4, 16);
+      part += __shfl_xor(part, 2, 16);
+      part += __shfl_xor(part, 1, 16);
+      if (in && (i & 15) == 0) sxg[(k / 128) * 16 + t] = part;
     }
     __syncthreads();
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x4 wq[kAwqBatch];
-    float sc[kAwqBatch];
-    uint32_t zp[kAwqBatch];
-    auto load = [&](int gb) {
+    const bool arow = r < rc;   // this lane's MFMA row is a live token
+    for (int gb = g0; gb < g1; gb += kAwqRing) {
 #pragma unroll
-      for (int u = 0; u < kAwqBatch; ++u) {
-        const int g = min(gb + u, g1 - 1);   // past the part's end: repeat its last group (not used)
-        wq[u] = wsrc[(size_t)g * 64];
-        sc[u] = ssrc[g * 16];
-        zp[u] = zsrc[g * 16];
-      }
-    };
-    if (g0 < g1) load(g0);
-    for (int gb = g0; gb < g1; gb += kAwqBatch) {
-      i32x4 cw[kAwqBatch];
-      float csc[kAwqBatch];
-      uint32_t czp[kAwqBatch];
-#pragma unroll
-      for (int u = 0; u < kAwqBatch; ++u) {
-        cw[u] = wq[u];
-        csc[u] = sc[u];
-        czp[u] = zp[u];
-      }
-      if (gb + kAwqBatch < g1) load(gb + kAwqBatch);   // the next batch flies while this one is used
-#pragma unroll
-      for (int u = 0; u < kAwqBatch; ++u) {
+      for (int u = 0; u < kAwqRing; ++u) {
         const int g = gb + u;
         if (g < g1) {
           f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -125,18 +132,21 @@ __global__ __launch_bounds__(64 * kAwqWaves) void awq_kernel(AwqArgs a) {
           for (int t = 0; t < 4; ++t) {
             // A: token r, channels 128 g + 32 t + 8 c + (0..7); B: the same
             // channels of output 16 nb + r as bf16 128 + q
-            const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (size_t)r * ldx + g * 128 + 32 * t + 8 * c);
-            const uint32_t w = (uint32_t)cw[u][t];
+            const u32x4 av = arow ? *reinterpret_cast<const u32x4*>(xs + (size_t)r * ldx + g * 128 + 32 * t + 8 * c)
+                                  : u32x4{0, 0, 0, 0};
+            const uint32_t w = (uint32_t)wq[u][t];
             const u32x4 bv = u32x4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
                                    ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
             p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
                                                         p, 0, 0, 0);
           }
-          // lane l holds tokens 4 c + (0..3) of output 16 nb + r
+          // lane l holds tokens 4 c + (0..3) of output 16 nb + r (S of rows
+          // past the chunk is never written: their sums are not stored)
           const f32x4 s4 = *reinterpret_cast<const f32x4*>(sxg + g * 16 + 4 * c);
-          const float zf = 128.f + (float)czp[u];
+          const float zf = 128.f + (float)zp[u], scu = sc[u];
+          if (g + kAwqRing < g1) load(u, g + kAwqRing);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(csc[u], __builtin_fmaf(-zf, s4[e], p[e]), acc[e]);
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(scu, __builtin_fmaf(-zf, s4[e], p[e]), acc[e]);
         }
       }
     }
@@ -160,27 +170,31 @@ __global__ __launch_bounds__(64 * kAwqWaves) void awq_kernel(AwqArgs a) {
 }
 
 hipError_t prepare_awq() {
-  hipError_t e = hipFuncSetAttribute((const void*)awq_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)awq_lds_bytes(4096));
+  const int most = (int)awq_lds_bytes(4096, 16);
+  hipError_t e = hipFuncSetAttribute((const void*)awq_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)awq_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)awq_lds_bytes(4096));
+  e = hipFuncSetAttribute((const void*)awq_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)awq_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)awq_lds_bytes(4096));
+  return hipFuncSetAttribute((const void*)awq_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
 }
 
-// The most n-blocks per workgroup that still gives every CU a workgroup.
+// n-blocks per workgroup. While two workgroups fit a CU (a few rows keep the
+// LDS small; two is the register file's limit at four waves per SIMD): one
+// n-block up to two per CU, two above. Measured on the FLUX shapes (graph
+// replays): 576 n-blocks 9.7 us with one, 8.9 with two; 1152 n-blocks 15.7,
+// 13.8 and 15.2 with one, two and four; 384 n-blocks the same with any.
+// When the LDS holds one workgroup per CU (16-row chunks), four n-blocks.
 hipError_t launch_awq(const AwqArgs& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int cus = num_cus > 0 ? num_cus : 256, nblk = a.N / 16;
-  const size_t lds = awq_lds_bytes(a.K);
-  if (nblk >= 4 * cus) {
-    hipLaunchKernelGGL(awq_kernel<4>, dim3((nblk + 3) / 4), dim3(64 * kAwqWaves), lds, st, a);
-  } else if (nblk >= 2 * cus) {
+  const size_t lds = awq_lds_bytes(a.K, a.M < 16 ? a.M : 16);
+  const bool two_per_cu = 2 * lds <= 160 * 1024;
+  if (two_per_cu && nblk <= 2 * cus) {
+    hipLaunchKernelGGL(awq_kernel<1>, dim3(nblk), dim3(64 * kAwqWaves), lds, st, a);
+  } else if (two_per_cu) {
     hipLaunchKernelGGL(awq_kernel<2>, dim3((nblk + 1) / 2), dim3(64 * kAwqWaves), lds, st, a);
   } else {
-    hipLaunchKernelGGL(awq_kernel<1>, dim3(nblk), dim3(64 * kAwqWaves), lds, st, a);
+    hipLaunchKernelGGL(awq_kernel<4>, dim3((nblk + 3) / 4), dim3(64 * kAwqWaves), lds, st, a);
   }
   return hipGetLastError();
 }
