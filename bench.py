@@ -381,6 +381,8 @@ def main():
     ap.add_argument("--no-c4", action="store_true", help="skip the FLUX block's linears (config 4)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and copy ceilings")
     ap.add_argument("--no-awq", action="store_true", help="skip the W4A16 (AWQ-style) layers")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the half second of untimed forwards before the warm-up (profiler runs)")
     ap.add_argument("--layer-markers", action="store_true",
                     help="launch one byte-fill kernel before each config-4 layer (layer boundaries in profiler traces)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -406,7 +408,7 @@ def main():
     layer, host, lay, sets = make_workload(spec, args.rotate, torch, S, synth)
     flops = 2.0 * spec.M * spec.N * spec.K
 
-    nsettle = settle(layer, sets, torch, S)
+    nsettle = 0 if args.no_settle else settle(layer, sets, torch, S)
     ms, wall_ms = time_forward(layer, sets, args.steps, args.warmup, torch, S)
     tops = flops / (ms * 1e-3) / 1e12
     log(f"forward: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us), {tops:.1f} effective TOPS")

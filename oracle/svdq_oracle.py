@@ -86,6 +86,46 @@ def smoothing_factors(act_absmax: np.ndarray, w_lin: np.ndarray):
     return lam, mu
 
 
+def smoothing_factors_alpha(act_absmax: np.ndarray, w_lin: np.ndarray, alpha: float):
+    """Smoothing of strength alpha: lambda_k = ax_k^alpha / aw_k^(1 - alpha)
+    (float64; 1 where either maximum is 0), mu = fl32(1 / lambda). At alpha =
+    1/2 this is the default rule and is computed as it is, sqrt(ax / aw).
+    Returns (lam float64 [K], mu float32 [K])."""
+    if alpha == 0.5:
+        return smoothing_factors(act_absmax, w_lin)
+    ax = np.asarray(act_absmax, dtype=np.float32).astype(np.float64)
+    aw = np.abs(np.asarray(w_lin, dtype=np.float32)).max(axis=0).astype(np.float64)
+    lam = np.ones_like(ax)
+    ok = (ax > 0) & (aw > 0)
+    lam[ok] = np.power(ax[ok], alpha) / np.power(aw[ok], 1.0 - alpha)
+    return lam, (1.0 / lam).astype(np.float32)
+
+
+def calibrate_alpha(w_lin, bias, x_cal, rank: int, fmt: str, alphas) -> dict:
+    """Calibrated smoothing strength (aiflownews.com, "What SVDQuant actually
+    does": the method is calibrated on representative data before it is
+    quantized): for each alpha the whole pack (smoothing of strength alpha,
+    SVD, residual, quantization) and the layer's output on the calibration
+    rows; the loss is the squared error against x W^T + b, and the first
+    alpha of least loss is kept. Returns dict(alpha, losses, packed)."""
+    w_lin = np.asarray(w_lin, np.float32)
+    x = np.asarray(x_cal, np.float32)
+    ax = np.abs(x).max(axis=0)
+    ref = x.astype(np.float64) @ w_lin.T.astype(np.float64)
+    if bias is not None:
+        ref = ref + np.asarray(bias, np.float32).astype(np.float64)[None, :]
+    losses, packs = [], []
+    for al in alphas:
+        _, mu = smoothing_factors_alpha(ax, w_lin, float(al))
+        w_hat = smoothed_weight(w_lin, mu)
+        l1, l2 = low_rank_factors(w_hat, rank)
+        p = pack(w_lin, bias, ax, rank, fmt, factors=(mu, l1, l2))
+        losses.append(float(np.sum((forward(p, x) - ref) ** 2)))
+        packs.append(p)
+    i = int(np.argmin(losses))
+    return dict(alpha=float(alphas[i]), losses=np.array(losses), packed=packs[i])
+
+
 def smoothed_weight(w_lin: np.ndarray, mu: np.ndarray) -> np.ndarray:
     """W_hat [K][N] float64, W_hat[k,n] = W[k,n] / mu_k (the exact inverse of the runtime multiply)."""
     w = np.asarray(w_lin, dtype=np.float32).astype(np.float64).T  # math layout K x N

@@ -425,3 +425,45 @@ def test_lora_extend_general_within_bf16():
     # the appended L1 columns are bf16 of A * scale / mu, row by row
     k = 17
     assert np.array_equal(ext["l1"][k, 16:], O.to_bf16(A[k].astype(np.float64) * 0.75 / float(p["mu"][k])))
+
+
+# --------------------------------------------------------------------------
+# calibrated smoothing strength
+# --------------------------------------------------------------------------
+def test_smoothing_alpha_closed_forms():
+    """alpha = 1/2 is the default rule bit for bit; alpha = 1 moves all of
+    each channel's activation range into the weights (max |x_hat| = 1);
+    alpha = 0 scales the weights' rows to max 1 (max |W_hat| = 1)."""
+    lay = _tiny(16, 128, 24, seed=41)
+    ax = np.abs(lay.x).max(axis=0)
+    assert np.array_equal(O.smoothing_factors_alpha(ax, lay.w_lin, 0.5)[1], O.smoothing_factors(ax, lay.w_lin)[1])
+    _, mu1 = O.smoothing_factors_alpha(ax, lay.w_lin, 1.0)
+    xh = O.smooth_activations(lay.x, mu1)
+    np.testing.assert_allclose(np.abs(xh).max(axis=0), 1.0, rtol=2 ** -22)
+    _, mu0 = O.smoothing_factors_alpha(ax, lay.w_lin, 0.0)
+    wh = O.smoothed_weight(lay.w_lin, mu0)
+    np.testing.assert_allclose(np.abs(wh).max(axis=1), 1.0, rtol=2 ** -22)
+    # the strengths in between lie between, channel by channel (monotone in alpha)
+    lam = [O.smoothing_factors_alpha(ax, lay.w_lin, a)[0] for a in (0.0, 0.25, 0.5, 0.75, 1.0)]
+    aw = np.abs(lay.w_lin).max(axis=0).astype(np.float64)
+    up = ax.astype(np.float64) * aw >= 1.0
+    for a, b in zip(lam, lam[1:]):
+        assert np.all((b >= a * (1 - 1e-12))[up]) and np.all((b <= a * (1 + 1e-12))[~up])
+
+
+def test_calibrate_alpha_is_the_argmin():
+    """The kept alpha is the grid's first least loss, each loss recomputed
+    here from the kept pieces by a separate route: the dequantized weight
+    plus the low-rank product, applied to the smoothed rows."""
+    spec = synth.LayerSpec("cal", 48, 256, 64, 16, "int4", 44)
+    lay = synth.make_layer(spec)
+    grid = [0.3, 0.5, 0.7]
+    res = O.calibrate_alpha(lay.w_lin, lay.bias, lay.x, 16, "int4", grid)
+    assert res["alpha"] == grid[int(np.argmin(res["losses"]))]
+    p = res["packed"]
+    xh = O.smooth_activations(lay.x, p["mu"]).astype(np.float64)
+    qx, sx = O.quant_int4_rows(xh.astype(np.float32))
+    w_eff = (O.dequant_int4(p["qw"], p["sw"]).T, p["l1"].astype(np.float64) @ p["l2"].astype(np.float64))
+    y = O.dequant_int4(qx, sx) @ w_eff[0] + xh @ w_eff[1] + lay.bias.astype(np.float64)
+    ref = lay.x.astype(np.float64) @ lay.w_lin.T.astype(np.float64) + lay.bias
+    np.testing.assert_allclose(np.sum((y - ref) ** 2), res["losses"].min(), rtol=1e-9)
