@@ -20,6 +20,7 @@ __all__ = [
     "to_device", "linear_forward", "linear_forward_noalloc", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer", "measure_mfma_peak", "measure_copy",
     "awq_packed_bytes", "awq_pack", "awq_unpack", "awq_to_device", "awq_forward",
+    "pack_weights_gpu", "calibrate_alpha", "to_host",
 ]
 
 FMT_INT4 = 0
@@ -36,6 +37,8 @@ EXPORTED_SYMBOLS = [
     "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc", "svdq_lora_extend",
     "svdq_measure_mfma_peak", "svdq_measure_copy",
     "svdq_awq_packed_bytes", "svdq_awq_pack", "svdq_awq_unpack", "svdq_awq_forward",
+    "svdq_pack_gpu_workspace_bytes", "svdq_pack_weights_gpu", "svdq_calibrate_workspace_bytes",
+    "svdq_calibrate_alpha",
 ]
 
 # bytes of the library-owned device workspace of svdq_linear_forward_noalloc
@@ -113,6 +116,11 @@ def lib() -> ctypes.CDLL:
         "svdq_awq_pack": [P(AwqDesc), vp, vp, vp, i64, ctypes.c_float, P(ctypes.c_double), vp, P(AwqPacked)],
         "svdq_awq_unpack": [P(AwqDesc), P(AwqPacked), vp, vp, vp],
         "svdq_awq_forward": [P(AwqDesc), P(AwqPacked), vp, i64, vp, vp],
+        "svdq_pack_gpu_workspace_bytes": [D, P(sz)],
+        "svdq_pack_weights_gpu": [D, vp, vp, vp, ctypes.c_float, ctypes.c_uint64, P(Packed), vp, sz, vp],
+        "svdq_calibrate_workspace_bytes": [D, i64, P(sz)],
+        "svdq_calibrate_alpha": [D, vp, vp, vp, i64, vp, ctypes.c_int32, ctypes.c_uint64, P(ctypes.c_float),
+                                 vp, P(Packed), vp, sz, vp],
         "svdq_workspace_bytes": [D, i64, P(sz)],
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
         "svdq_linear_forward_noalloc": [D, P(Packed), vp, i64, vp, vp],
@@ -378,6 +386,56 @@ def measure_copy(src, dst, stream=None):
     nbytes = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() == nbytes
     _check(lib().svdq_measure_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "svdq_measure_copy")
+
+
+# ----------------------------------------------------------------------------
+# GPU-side pack and the calibrated smoothing strength
+# ----------------------------------------------------------------------------
+def _alloc_device(layer: Layer, device="cuda") -> dict:
+    import torch
+    sizes = packed_bytes(layer)
+    return {n: torch.zeros(max(sizes[n], 1), dtype=torch.uint8, device=device) for n in PACKED_FIELDS}
+
+
+def pack_weights_gpu(layer: Layer, w_lin, bias, act_absmax, alpha: float = 0.5, seed: int = 0, stream=None):
+    """svdq_pack_weights_gpu: device tensors in (fp32 w_lin [N][K], bias [N] or
+    None, act_absmax [K]); returns the packed layer as device uint8 tensors."""
+    import torch
+    dev = _alloc_device(layer, w_lin.device)
+    d = layer.desc
+    n = ctypes.c_size_t()
+    _check(lib().svdq_pack_gpu_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "svdq_pack_gpu_workspace_bytes")
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=w_lin.device)
+    p = _packed_struct(layer, dev)
+    _check(lib().svdq_pack_weights_gpu(ctypes.byref(d), _ptr(w_lin), _ptr(bias), _ptr(act_absmax), float(alpha),
+                                       int(seed), ctypes.byref(p), _ptr(ws), ws.numel(), _stream(stream)),
+           "svdq_pack_weights_gpu")
+    return dev
+
+
+def calibrate_alpha(layer: Layer, w_lin, bias, x_cal, alphas, seed: int = 0, stream=None):
+    """svdq_calibrate_alpha: (packed device layer of the best alpha, alpha, losses)."""
+    import torch
+    dev = _alloc_device(layer, w_lin.device)
+    d = layer.desc
+    M = x_cal.shape[0]
+    n = ctypes.c_size_t()
+    _check(lib().svdq_calibrate_workspace_bytes(ctypes.byref(d), M, ctypes.byref(n)),
+           "svdq_calibrate_workspace_bytes")
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=w_lin.device)
+    al = np.ascontiguousarray(alphas, dtype=np.float32)
+    losses = np.zeros(len(al), np.float64)
+    a_out = ctypes.c_float()
+    p = _packed_struct(layer, dev)
+    _check(lib().svdq_calibrate_alpha(ctypes.byref(d), _ptr(w_lin), _ptr(bias), _ptr(x_cal), M, _ptr(al), len(al),
+                                      int(seed), ctypes.byref(a_out), _ptr(losses), ctypes.byref(p), _ptr(ws),
+                                      ws.numel(), _stream(stream)), "svdq_calibrate_alpha")
+    return dev, a_out.value, losses
+
+
+def to_host(dev: dict) -> dict:
+    """Device packed buffers back to host uint8 arrays (byte for byte)."""
+    return {n: t.cpu().numpy() for n, t in dev.items()}
 
 
 # ----------------------------------------------------------------------------

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libsvdq.so")
 
 HIP_SOURCES = ["svdq_stage1.hip", "svdq_gemm_int4.hip", "svdq_gemm_small.hip", "svdq_gemm_mxfp4.hip", "svdq_awq.hip",
-               "svdq_peak.hip", "svdq_api.hip"]
+               "svdq_pack_gpu.hip", "svdq_peak.hip", "svdq_api.hip"]
 CPP_SOURCES = ["svdq_pack.cpp", "svdq_awq_pack.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

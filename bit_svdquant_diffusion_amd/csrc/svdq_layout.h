@@ -7,6 +7,15 @@
 
 #include "svdq.h"
 
+// The fragment-order helpers below are also called from device code (the
+// GPU-side pack) when this header is compiled by hipcc; g++ sees plain
+// inline functions.
+#if defined(__HIPCC__)
+#define SVDQ_HD __host__ __device__
+#else
+#define SVDQ_HD
+#endif
+
 namespace svdq {
 
 constexpr int kGroupInt4 = 64;    // INT4 scale group along K
@@ -114,7 +123,7 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
 // l = 32h + r holding row 32*block + r, channels 64*step + 32h + [0, 32) (even
 // channel in the low nibble). One (block, step) is one MXFP4 MFMA operand of
 // one wave, or one INT4 group of 32 rows (two i8 MFMA operands once widened).
-inline size_t f_code_byte(int K, int64_t row, int k) {
+SVDQ_HD inline size_t f_code_byte(int K, int64_t row, int k) {
   const int64_t b = row / 32;
   const int r = (int)(row % 32), S = k / 64, h = (k % 64) / 32, j = k % 32;
   return (((size_t)b * (K / 64) + S) * 64 + (32 * h + r)) * 16 + j / 2;
@@ -123,7 +132,7 @@ inline size_t f_code_byte(int K, int64_t row, int k) {
 // L2^T): rows in blocks of 32, columns in steps of 16; each
 // (block, step) is 1 KiB = 64 lanes x 8 bf16, lane l = 32h + r holding row
 // 32*block + r, columns 16*step + 8h + [0, 8). Returns an element index.
-inline size_t frag16_index(int r32, int64_t row, int col) {
+SVDQ_HD inline size_t frag16_index(int r32, int64_t row, int col) {
   const int64_t b = row / 32;
   const int r = (int)(row % 32), c = col / 16, h = (col % 16) / 8, j = col % 8;
   return (((size_t)b * (r32 / 16) + c) * 64 + (32 * h + r)) * 8 + j;
@@ -132,7 +141,7 @@ inline size_t frag16_index(int r32, int64_t row, int col) {
 // Fragment order of MXFP4 scale bytes: [K/128 stage][rows32/32 block][64 lanes][2];
 // lane l = 32h + r of block b at stage st holds the bytes of the 32-channel
 // blocks kb = 4 st + 2 step + h (step = 0, 1) of row 32 b + r.
-inline size_t f_scale_index(int64_t rows32, int64_t row, int kb) {
+SVDQ_HD inline size_t f_scale_index(int64_t rows32, int64_t row, int kb) {
   const int st = kb / 4, step = (kb % 4) / 2, h = kb % 2;
   return (((size_t)st * (rows32 / 32) + row / 32) * 64 + (32 * h + row % 32)) * 2 + step;
 }

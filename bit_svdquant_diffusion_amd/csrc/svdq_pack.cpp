@@ -22,6 +22,7 @@
 
 #include "svdq.h"
 #include "svdq_layout.h"
+#include "svdq_pack_host.h"
 
 namespace svdq {
 namespace {
@@ -47,6 +48,8 @@ void parallel_for(int64_t n, const std::function<void(int64_t, int64_t)>& fn) {
   for (auto& x : th) x.join();
 }
 
+}  // namespace
+
 // ---------------- bf16 ----------------
 // Round a real to the nearest bf16 (8 significant bits), ties to even, in one
 // rounding: v = f 2^e with f in [0.5, 1) -> nearbyint(f 2^8) 2^(e-8).
@@ -70,6 +73,8 @@ double bf16_to_double(uint16_t b) {
   std::memcpy(&f, &u, 4);
   return (double)f;
 }
+
+namespace {
 
 // ---------------- seeded Gaussian (splitmix64 + Box-Muller) ----------------
 struct Rng {
@@ -192,9 +197,14 @@ bool one_sided_jacobi(double* A, int64_t R, int L, double* J, int max_sweeps) {
 
 int jacobi_sweeps();
 
-// Top-r factors of W_hat [K][N]: L1 [K][r] = U_r Sigma_r, L2 [r][N] = V_r^T (fp64).
-svdq_status truncated_svd(const double* W, int64_t K, int64_t N, int r, uint64_t seed,
-                          std::vector<double>& L1, std::vector<double>& L2) {
+}  // namespace
+
+// Top-r factors of the K x N matrix W_hat that AX (W_hat X, X [N][L] -> [K][L])
+// and AtX (W_hat^T X, X [K][L] -> [N][L]) apply: L1 [K][r] = U_r Sigma_r,
+// L2 [r][N] = V_r^T (fp64), by randomized subspace iteration (Halko,
+// Martinsson and Tropp) with the small factorizations on the host.
+svdq_status truncated_svd_ops(int64_t K, int64_t N, int r, uint64_t seed, const PanelOp& AX, const PanelOp& AtX,
+                              std::vector<double>& L1, std::vector<double>& L2) {
   // oversampled subspace; power iterations until the captured energy
   // ||W Z||_F^2 stops growing (relative change below 1e-9), at most 60
   const int L = (int)std::min<int64_t>(r + std::max(16, r / 2), std::min(K, N));
@@ -202,13 +212,14 @@ svdq_status truncated_svd(const double* W, int64_t K, int64_t N, int r, uint64_t
   Rng rng{seed ^ 0x5EED5EED12345678ull};
   std::vector<double> Om((size_t)N * L), Y((size_t)K * L), Z((size_t)N * L);
   for (auto& v : Om) v = rng.normal();
-  mul_AX(W, K, N, Om.data(), L, Y.data());
+  svdq_status st = AX(Om.data(), Y.data());
+  if (st != SVDQ_OK) return st;
   orthonormalize(Y.data(), K, L);
   double prev = -1.0;
   for (int it = 0; it < max_power_iters; ++it) {
-    mul_AtX(W, K, N, Y.data(), L, Z.data());
+    if ((st = AtX(Y.data(), Z.data())) != SVDQ_OK) return st;
     orthonormalize(Z.data(), N, L);
-    mul_AX(W, K, N, Z.data(), L, Y.data());
+    if ((st = AX(Z.data(), Y.data())) != SVDQ_OK) return st;
     double energy = 0.0;
     for (size_t i = 0; i < Y.size(); ++i) energy += Y[i] * Y[i];
     orthonormalize(Y.data(), K, L);
@@ -217,7 +228,7 @@ svdq_status truncated_svd(const double* W, int64_t K, int64_t N, int r, uint64_t
     prev = energy;
   }
   // B^T = W^T Q  [N][L]; B = Q^T W
-  mul_AtX(W, K, N, Y.data(), L, Z.data());
+  if ((st = AtX(Y.data(), Z.data())) != SVDQ_OK) return st;
   std::vector<double> J((size_t)L * L);
   if (!one_sided_jacobi(Z.data(), N, L, J.data(), jacobi_sweeps())) return SVDQ_ERR_NUMERIC;
   // B^T = (V Sigma) J^T  ->  B = J Sigma V^T, W ~= Q B = (Q J) Sigma V^T
@@ -246,6 +257,48 @@ svdq_status truncated_svd(const double* W, int64_t K, int64_t N, int r, uint64_t
     for (int64_t n = 0; n < N; ++n) L2[c * N + n] = Z[n * L + j] * inv;
   }
   return SVDQ_OK;
+}
+
+svdq_status smoothing_mu(int K, const float* ax, const float* aw, double alpha, float* mu) {
+  for (int k = 0; k < K; ++k) {
+    const double a = (double)ax[k], w = (double)aw[k];
+    double lam = 1.0;
+    if (a > 0 && w > 0) lam = alpha == 0.5 ? std::sqrt(a / w) : std::pow(a, alpha) / std::pow(w, 1.0 - alpha);
+    mu[k] = (float)(1.0 / lam);
+    if (!(mu[k] > 0.f) || !std::isfinite(mu[k])) return SVDQ_ERR_NUMERIC;
+  }
+  return SVDQ_OK;
+}
+
+void factor_layout(const svdq_layer_desc* d, const uint16_t* l1b, const uint16_t* l2b, uint16_t* l1_out,
+                   uint16_t* l2_out) {
+  const int K = d->K, N = d->N, r = d->rank, r32 = rank32(r), Kp = kpad(d);
+  const svdq_packed_sizes sz = packed_sizes(d);
+  std::memset(l1_out, 0, sz.l1);
+  std::memset(l2_out, 0, sz.l2);
+  for (int k = 0; k < K; ++k)
+    for (int c = 0; c < r; ++c) l1_out[l1_index(Kp, r32, k, c)] = l1b[(size_t)k * r + c];
+  for (int i = 0; i < r; ++i)
+    for (int n = 0; n < N; ++n) l2_out[frag16_index(r32, n, i)] = l2b[(size_t)i * N + n];
+}
+
+namespace {
+
+// Top-r factors of W_hat [K][N] in host memory.
+svdq_status truncated_svd(const double* W, int64_t K, int64_t N, int r, uint64_t seed,
+                          std::vector<double>& L1, std::vector<double>& L2) {
+  const int L = (int)std::min<int64_t>(r + std::max(16, r / 2), std::min(K, N));
+  return truncated_svd_ops(
+      K, N, r, seed,
+      [&](const double* X, double* Y) {
+        mul_AX(W, K, N, X, L, Y);
+        return SVDQ_OK;
+      },
+      [&](const double* X, double* Y) {
+        mul_AtX(W, K, N, X, L, Y);
+        return SVDQ_OK;
+      },
+      L1, L2);
 }
 
 // ---------------- 4-bit quantizers (definitions as in svdq.h) ----------------
@@ -327,14 +380,7 @@ svdq_status finish_pack(const svdq_layer_desc* d, const float* w_lin, const floa
   std::memset(out->sw, 0, sz.sw);
   std::memset(out->bias, 0, sz.bias);
   // factors in device layout
-  if (r32 > 0) {
-    std::memset(out->l1, 0, sz.l1);
-    std::memset(out->l2, 0, sz.l2);
-    for (int k = 0; k < K; ++k)
-      for (int c = 0; c < r; ++c) out->l1[l1_index(Kp, r32, k, c)] = l1b[(size_t)k * r + c];
-    for (int i = 0; i < r; ++i)
-      for (int n = 0; n < N; ++n) out->l2[frag16_index(r32, n, i)] = l2b[(size_t)i * N + n];
-  }
+  if (r32 > 0) factor_layout(d, l1b, l2b, out->l1, out->l2);
   for (int n = 0; n < N; ++n) {
     float b = bias ? bias[n] : 0.f;
     out->bias[n] = bf16_from_double((double)b);
@@ -448,12 +494,8 @@ svdq_status svdq_pack_weights(const svdq_layer_desc* d, const float* w_lin, cons
   std::vector<float> aw(K, 0.f), mu(K);
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) aw[k] = std::max(aw[k], std::fabs(w_lin[n * K + k]));
-  for (int64_t k = 0; k < K; ++k) {
-    double ax = (double)act_absmax[k], a_w = (double)aw[k];
-    double lam = (ax > 0 && a_w > 0) ? std::sqrt(ax / a_w) : 1.0;
-    mu[k] = (float)(1.0 / lam);
-    if (!(mu[k] > 0.f) || !std::isfinite(mu[k])) return SVDQ_ERR_NUMERIC;
-  }
+  st = smoothing_mu((int)K, act_absmax, aw.data(), 0.5, mu.data());
+  if (st != SVDQ_OK) return st;
   // 2. low-rank branch of W_hat = diag(1/mu) W  (math layout [K][N], fp64)
   std::vector<uint16_t> l1b((size_t)K * r), l2b((size_t)r * N);
   if (r > 0) {

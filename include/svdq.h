@@ -300,6 +300,50 @@ SVDQ_API svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* desc, con
                                        int32_t* p, void* hip_stream);
 
 /*
+ * GPU-side pack (the calibrate-quantize-package step on the device; the pages'
+ * offline workflow, aiflownews.com, "Native Diffusers integration and the new
+ * workflow"): the steps of svdq_pack_weights with the column maxima, the
+ * randomized SVD's products with W_hat, the residual and its quantization on
+ * the GPU (the panel orthonormalizations and the small Jacobi SVD on the
+ * host). The smoothing has strength alpha: lambda_k = ax_k^alpha /
+ * aw_k^(1 - alpha) (fp64; at alpha = 0.5 computed as sqrt(ax / aw), which is
+ * svdq_pack_weights' rule; 1 where either maximum is 0). Given the same mu and
+ * bf16 factors the codes and scales are the host pack's bits.
+ * w_lin fp32 [N][K], bias fp32 [N] or NULL, act_absmax fp32 [K]: DEVICE
+ * pointers. dev_out: device buffers of svdq_packed_bytes() sizes. workspace:
+ * >= svdq_pack_gpu_workspace_bytes() device bytes. Runs on hip_stream and
+ * synchronizes it (host steps in between); not for graph capture.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE (also alpha outside [0, 1]),
+ * SVDQ_ERR_FORMAT, SVDQ_ERR_WORKSPACE, SVDQ_ERR_NUMERIC, SVDQ_ERR_DEVICE.
+ */
+SVDQ_API svdq_status svdq_pack_gpu_workspace_bytes(const svdq_layer_desc* desc, size_t* out);
+SVDQ_API svdq_status svdq_pack_weights_gpu(const svdq_layer_desc* desc, const float* w_lin, const float* bias,
+                                           const float* act_absmax, float alpha, uint64_t seed,
+                                           svdq_packed* dev_out, void* workspace, size_t workspace_bytes,
+                                           void* hip_stream);
+
+/*
+ * Calibrated smoothing strength (aiflownews.com, "What SVDQuant actually
+ * does": a calibration pass on representative data): for each alpha of
+ * alphas[n_alpha] (host, each in [0, 1], at most 64) the layer is packed on
+ * the GPU as svdq_pack_weights_gpu does (act_absmax = max over the
+ * calibration rows) and run on the calibration rows x_cal (bf16 [m_cal][K],
+ * device); the loss is the squared error of its bf16 output against
+ * x_cal W^T + b (fp64). The first alpha of least loss is kept: dev_out holds
+ * that layer, *alpha_out (may be NULL) its alpha, losses_out (host
+ * [n_alpha], may be NULL) every loss. workspace: >=
+ * svdq_calibrate_workspace_bytes(desc, m_cal). Synchronizes hip_stream.
+ * Errors: as svdq_pack_weights_gpu, and SVDQ_ERR_SHAPE for m_cal outside
+ * 1..65536 or n_alpha outside 1..64.
+ */
+SVDQ_API svdq_status svdq_calibrate_workspace_bytes(const svdq_layer_desc* desc, int64_t m_cal, size_t* out);
+SVDQ_API svdq_status svdq_calibrate_alpha(const svdq_layer_desc* desc, const float* w_lin, const float* bias,
+                                          const uint16_t* x_cal, int64_t m_cal, const float* alphas,
+                                          int32_t n_alpha, uint64_t seed, float* alpha_out, double* losses_out,
+                                          svdq_packed* dev_out, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream);
+
+/*
  * ---------------------------------------------------------------------------
  * AWQ-style W4A16 linear: 4-bit weights, 16-bit activations, for the
  * adaptive-normalization and modulation layers the pages keep at higher
