@@ -20,7 +20,8 @@ __all__ = [
     "to_device", "linear_forward", "linear_forward_noalloc", "stage1", "gemm", "unpack_workspace", "debug_int4_group_sums",
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer", "measure_mfma_peak", "measure_copy",
     "awq_packed_bytes", "awq_pack", "awq_unpack", "awq_to_device", "awq_forward",
-    "pack_weights_gpu", "calibrate_alpha", "to_host",
+    "pack_weights_gpu", "calibrate_alpha", "to_host", "mlp_workspace_bytes", "mlp_fused", "mlp_forward",
+    "MLP_AUTO", "MLP_UNFUSED",
 ]
 
 FMT_INT4 = 0
@@ -38,8 +39,12 @@ EXPORTED_SYMBOLS = [
     "svdq_measure_mfma_peak", "svdq_measure_copy",
     "svdq_awq_packed_bytes", "svdq_awq_pack", "svdq_awq_unpack", "svdq_awq_forward",
     "svdq_pack_gpu_workspace_bytes", "svdq_pack_weights_gpu", "svdq_calibrate_workspace_bytes",
-    "svdq_calibrate_alpha",
+    "svdq_calibrate_alpha", "svdq_mlp_workspace_bytes", "svdq_mlp_fused", "svdq_mlp_forward",
 ]
+
+# svdq_mlp_forward modes
+MLP_AUTO = 0
+MLP_UNFUSED = 1
 
 # bytes of the library-owned device workspace of svdq_linear_forward_noalloc
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -128,6 +133,9 @@ def lib() -> ctypes.CDLL:
         "svdq_gemm": [D, P(Packed), vp, sz, i64, vp, vp],
         "svdq_unpack_workspace": [D, i64, vp, sz, vp, vp, vp],
         "svdq_debug_int4_group_sums": [D, P(Packed), vp, sz, i64, i64, i64, i64, i64, vp, vp],
+        "svdq_mlp_workspace_bytes": [D, D, i64, P(sz), P(sz)],
+        "svdq_mlp_fused": [D, D, i64, P(ctypes.c_int32)],
+        "svdq_mlp_forward": [D, P(Packed), D, P(Packed), vp, i64, vp, vp, sz, ctypes.c_int32, vp],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -313,6 +321,40 @@ def linear_forward_noalloc(layer: Layer, dev: dict, x, y, stream=None):
     _check(lib().svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), _ptr(x), x.shape[0],
                                              _ptr(y), _stream(stream)),
            "svdq_linear_forward_noalloc")
+    return y
+
+
+def mlp_workspace_bytes(up: Layer, down: Layer, M: int):
+    """(total bytes, offset of the down layer's part) of svdq_mlp_forward's workspace."""
+    out, off = ctypes.c_size_t(), ctypes.c_size_t()
+    du, dd = up.desc, down.desc
+    _check(lib().svdq_mlp_workspace_bytes(ctypes.byref(du), ctypes.byref(dd), int(M), ctypes.byref(out),
+                                          ctypes.byref(off)), "svdq_mlp_workspace_bytes")
+    return out.value, off.value
+
+
+def mlp_fused(up: Layer, down: Layer, M: int) -> bool:
+    """Whether svdq_mlp_forward in MLP_AUTO mode takes the fused path for M tokens."""
+    f = ctypes.c_int32()
+    du, dd = up.desc, down.desc
+    _check(lib().svdq_mlp_fused(ctypes.byref(du), ctypes.byref(dd), int(M), ctypes.byref(f)), "svdq_mlp_fused")
+    return bool(f.value)
+
+
+def mlp_forward(up: Layer, dev_up: dict, down: Layer, dev_down: dict, x, y=None, workspace=None,
+                mode: int = MLP_AUTO, stream=None):
+    """y[M][down N] = down(GELU(up(x))) via svdq_mlp_forward (bf16 tensors)."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape[-1] == up.K
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, down.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(mlp_workspace_bytes(up, down, M)[0], 1), dtype=torch.uint8, device=x.device)
+    pu, pd = _packed_struct(up, dev_up), _packed_struct(down, dev_down)
+    du, dd = up.desc, down.desc
+    _check(lib().svdq_mlp_forward(ctypes.byref(du), ctypes.byref(pu), ctypes.byref(dd), ctypes.byref(pd), _ptr(x), M, _ptr(y), _ptr(workspace), workspace.numel(),
+                                  int(mode), _stream(stream)), "svdq_mlp_forward")
     return y
 
 

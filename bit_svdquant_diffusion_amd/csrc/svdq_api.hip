@@ -68,16 +68,23 @@ svdq_status check_packed_dev(const svdq_layer_desc* d, const svdq_packed* p) {
   return SVDQ_OK;
 }
 
+// M against the layer: the token limit, and the offsets the kernels address
+// with 32 bits (MXFP4 activation scale bytes by stage, the tiled INT4 GEMM's
+// activation codes by byte)
+svdq_status check_m(const svdq_layer_desc* d, int64_t M) {
+  if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
+  if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)kpad(d) + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
+    return SVDQ_ERR_SHAPE;
+  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * kpad(d) >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+
 svdq_status common_checks(const svdq_layer_desc* d, const svdq_packed* dev, const void* x,
                           int64_t M, const void* ws, size_t ws_bytes) {
   svdq_status st = check_desc(d);
   if (st != SVDQ_OK) return st;
-  if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
-  // MXFP4 activation scale bytes are addressed with 32-bit stage offsets,
-  // the tiled INT4 GEMM's activation codes with 32-bit byte offsets
-  if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)kpad(d) + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
-    return SVDQ_ERR_SHAPE;
-  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * kpad(d) >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
+  st = check_m(d, M);
+  if (st != SVDQ_OK) return st;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
@@ -135,6 +142,42 @@ GemmArgs gemm_args(const svdq_layer_desc* d, const svdq_packed* dev, int64_t M, 
   a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
   a.part = int4 || M <= kFewTokens ? (float*)(b + L.part) : nullptr;
   return a;
+}
+
+// The MLP pair's workspace: the up layer's, the down layer's, then the
+// hidden activation H = GELU(up(x)) as bf16 [M][up N] (composition) or the
+// fp32 partial X_hat L1 of the down layer per 256 hidden channels (fused)
+struct MlpLayout {
+  size_t down, mid, total;
+};
+MlpLayout mlp_layout(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M) {
+  MlpLayout L;
+  L.down = align256(ws_layout(up, M).total);
+  L.mid = L.down + align256(ws_layout(down, M).total);
+  const size_t hid = (size_t)M * up->N * 2;
+  const size_t zpart = (size_t)(up->N / 256) * M * rank32(down->rank) * 4;
+  L.total = L.mid + align256(hid > zpart ? hid : zpart);
+  return L;
+}
+
+svdq_status mlp_shape_checks(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M) {
+  if (!up || !down) return SVDQ_ERR_NULL;
+  svdq_status st = check_desc(up);
+  if (st != SVDQ_OK) return st;
+  st = check_desc(down);
+  if (st != SVDQ_OK) return st;
+  if (down->K != up->N) return SVDQ_ERR_SHAPE;
+  st = check_m(up, M);
+  if (st != SVDQ_OK) return st;
+  return check_m(down, M);
+}
+
+// The fused epilogue exists in the tiled INT4 GEMM: both layers INT4, the
+// hidden width in whole 256-channel tiles, and more tokens than the
+// weight-streaming kernel takes
+bool mlp_fusable(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M) {
+  return up->format == SVDQ_FMT_INT4_G64 && down->format == SVDQ_FMT_INT4_G64 && up->N % 256 == 0 &&
+         M > kFewTokens;
 }
 
 bool sync_debug() {
@@ -198,6 +241,78 @@ svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* d, const svdq_pac
     if (st != SVDQ_OK) return st;
   }
   return svdq_linear_forward(d, dev, x, M, y, ws, kNoAllocScratchBytes, stream);
+}
+
+svdq_status svdq_mlp_workspace_bytes(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M,
+                                     size_t* out, size_t* down_offset) {
+  svdq_status st = mlp_shape_checks(up, down, M);
+  if (st != SVDQ_OK) return st;
+  if (!out) return SVDQ_ERR_NULL;
+  const MlpLayout L = mlp_layout(up, down, M);
+  *out = L.total;
+  if (down_offset) *down_offset = L.down;
+  return SVDQ_OK;
+}
+
+svdq_status svdq_mlp_fused(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M, int32_t* fused) {
+  svdq_status st = mlp_shape_checks(up, down, M);
+  if (st != SVDQ_OK) return st;
+  if (!fused) return SVDQ_ERR_NULL;
+  *fused = mlp_fusable(up, down, M) ? 1 : 0;
+  return SVDQ_OK;
+}
+
+svdq_status svdq_mlp_forward(const svdq_layer_desc* up, const svdq_packed* dev_up, const svdq_layer_desc* down,
+                             const svdq_packed* dev_down, const uint16_t* x, int64_t M, uint16_t* y, void* ws,
+                             size_t ws_bytes, int32_t mode, void* stream) {
+  svdq_status st = mlp_shape_checks(up, down, M);
+  if (st != SVDQ_OK) return st;
+  if (mode != SVDQ_MLP_AUTO && mode != SVDQ_MLP_UNFUSED) return SVDQ_ERR_SHAPE;
+  st = check_packed_dev(up, dev_up);
+  if (st != SVDQ_OK) return st;
+  st = check_packed_dev(down, dev_down);
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  if (!x || !y || !ws) return SVDQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return SVDQ_ERR_SHAPE;
+  const MlpLayout L = mlp_layout(up, down, M);
+  if (ws_bytes < L.total) return SVDQ_ERR_WORKSPACE;
+  int cus = 0;
+  st = check_device(&cus);
+  if (st != SVDQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* b = (uint8_t*)ws;
+  uint8_t* wd = b + L.down;
+  st = after_launch(launch_stage1(stage1_args(up, dev_up, x, M, b), cus, s), s);
+  if (st != SVDQ_OK) return st;
+  if (mode == SVDQ_MLP_AUTO && mlp_fusable(up, down, M)) {
+    // the up GEMM's epilogue leaves the down layer's stage-1 output in its
+    // workspace (codes, scales, per-tile partial Z); one small kernel adds
+    // the partials into Z
+    const WsLayout D = ws_layout(down, M);
+    const int r32 = rank32(down->rank);
+    GemmArgs a = gemm_args(up, dev_up, M, b, nullptr);
+    a.nxt_qx = wd + D.qx;
+    a.nxt_sx = (float*)(wd + D.sx);
+    a.nxt_mu = dev_down->mu;
+    a.nxt_l1s = dev_down->l1;
+    a.nxt_zpart = (float*)(b + L.mid);
+    a.nxt_r32 = r32;
+    st = after_launch(launch_gemm_int4(a, cus, s), s);
+    if (st != SVDQ_OK) return st;
+    st = after_launch(launch_fused_zsum((const float*)(b + L.mid), up->N / 256, (int)M, r32, (uint16_t*)(wd + D.z),
+                                        (uint32_t*)(wd + D.flags), kSplitCounters, s),
+                      s);
+  } else {
+    uint16_t* hid = (uint16_t*)(b + L.mid);
+    st = after_launch(launch_gemm(gemm_args(up, dev_up, M, b, hid), cus, s), s);
+    if (st != SVDQ_OK) return st;
+    st = after_launch(launch_gelu_bf16(hid, (size_t)M * up->N, s), s);
+    if (st != SVDQ_OK) return st;
+    st = after_launch(launch_stage1(stage1_args(down, dev_down, hid, M, wd), cus, s), s);
+  }
+  if (st != SVDQ_OK) return st;
+  return after_launch(launch_gemm(gemm_args(down, dev_down, M, wd, y), cus, s), s);
 }
 
 svdq_status svdq_awq_forward(const svdq_awq_desc* d, const svdq_awq_packed* dev, const uint16_t* x, int64_t M,

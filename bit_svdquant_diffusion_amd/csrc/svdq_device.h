@@ -81,4 +81,99 @@ __device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint3
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// bf16 round to nearest even, as a float
+__device__ __forceinline__ float bf16_round(float v) { return __uint_as_float(f2bf(v) << 16); }
+
+// GELU(v) = v Phi(v), Phi the standard normal distribution function, with
+// Phi(-|v|) = erfc(|v| / sqrt 2) / 2 from the Chebyshev fit of Numerical
+// Recipes (Press et al., function erfcc: erfc(z) ~ t exp(-z^2 + P(t)),
+// t = 1 / (1 + z / 2), fractional error below 1.2e-7 for all z >= 0) and
+// Phi(|v|) = 1 - Phi(-|v|). Branch-free (one reciprocal, one exp2, ten
+// fused multiply-adds), and every step is written out (no contraction left
+// to the compiler), so the fused epilogue and the standalone kernel agree bit
+// for bit. Its error is far below the half ulp of the bf16 it is rounded to.
+__device__ __forceinline__ float gelu_f32(float v) {
+  const float z = __fmul_rn(__builtin_fabsf(v), 0.70710678118654752440f);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = __builtin_fmaf(p, t, -0.82215223f);
+  p = __builtin_fmaf(p, t, 1.48851587f);
+  p = __builtin_fmaf(p, t, -1.13520398f);
+  p = __builtin_fmaf(p, t, 0.27886807f);
+  p = __builtin_fmaf(p, t, -0.18628806f);
+  p = __builtin_fmaf(p, t, 0.09678418f);
+  p = __builtin_fmaf(p, t, 0.37409196f);
+  p = __builtin_fmaf(p, t, 1.00002368f);
+  p = __builtin_fmaf(p, t, -1.26551223f);
+  const float ex = __builtin_fmaf(-z, z, p);   // -z^2 + P(t), in natural-log units
+  const float lo = __fmul_rn(__fmul_rn(0.5f, t), __builtin_amdgcn_exp2f(__fmul_rn(ex, 1.44269504088896341f)));
+  return __fmul_rn(v, v >= 0.f ? __fsub_rn(1.0f, lo) : lo);
+}
+
+// The 16 INT4 codes of one lane's values xh (8 to c0, 8 to c1, low nibble
+// first) for a group scale sc = fl32(amax / 7): the round-half-to-even of
+// the exact quotient xh / sc, clamped to [-7, 7]; sc == 0 gives zeros. The
+// fast path and its exact redo are explained inline. Shared by stage 1 and
+// the GEMM epilogue that quantizes the next layer's activations, so both give
+// the same bits.
+__device__ __forceinline__ void int4_codes16(const float (&xh)[16], float sc, uint32_t& c0, uint32_t& c1) {
+  // t = x_hat * rcp(s) is within 2e-6 of the exact quotient (|q| <= 7,
+  // rcp within 1 ulp), so rint(t) is the answer unless t lies within
+  // 1e-5 of a half-integer. Adding 1.5 * 2^23 rounds t to an integer
+  // (nearest, ties to even) held in the low mantissa bits, whose low
+  // nibble is the two's complement code.
+  constexpr float kRound = 12582912.0f;
+  const float inv = __builtin_amdgcn_rcpf(sc);
+  float dmax = 0.f;   // largest |t - rint(t)| of the lane
+  c0 = 0;
+  c1 = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t0 = xh[e] * inv, t1 = xh[8 + e] * inv;
+    const float u0 = t0 + kRound, u1 = t1 + kRound;
+    dmax = __builtin_fmaxf(dmax, __builtin_fabsf(t0 - (u0 - kRound)));
+    dmax = __builtin_fmaxf(dmax, __builtin_fabsf(t1 - (u1 - kRound)));
+    c0 |= (__float_as_uint(u0) & 15u) << (4 * e);
+    c1 |= (__float_as_uint(u1) & 15u) << (4 * e);
+  }
+  if (!(sc >= 0x1p-100f)) {
+    // zero and tiny scales (rcp out of range): one comparison per level
+    c0 = 0;
+    c1 = 0;
+    if (sc > 0.f) {
+#pragma unroll 1
+      for (int e = 0; e < 8; ++e) {
+        c0 |= ((uint32_t)q_int4_slow(xh[e], sc) & 15u) << (4 * e);
+        c1 |= ((uint32_t)q_int4_slow(xh[8 + e], sc) & 15u) << (4 * e);
+      }
+    }
+  } else if (dmax > 0.49999f) {
+    // a value near a half-integer: redo the lane's values exactly.
+    // With k = floor(|t|) the answer is k or k + 1, and the sign of
+    // the fused |x_hat| - (k + 1/2) s, the sign of the exact
+    // difference, decides: above goes up, below stays, zero is an
+    // exact tie and goes to the even one. Where |t| and the exact
+    // quotient lie on two sides of an integer n the pair tested is
+    // (n - 1, n) or (n, n + 1), whose midpoint is still on the right
+    // side of the quotient. k + 1 never passes 7: |x_hat| <= amax <
+    // 7.5 s.
+    c0 = 0;
+    c1 = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float ax = __builtin_fabsf(xh[e]);
+      const float k = __builtin_floorf(ax * inv);
+      const float d = __builtin_fmaf(-(k + 0.5f), sc, ax);
+      const bool up = d > 0.f || (d == 0.f && (__float_as_uint(k + kRound) & 1u));
+      const float q = up ? k + 1.f : k;
+      const uint32_t code = __float_as_uint(__builtin_copysignf(q, xh[e]) + kRound) & 15u;
+      if (e < 8)
+        c0 |= code << (4 * e);
+      else
+        c1 |= code << (4 * (e - 8));
+    }
+  }
+}
+
+
 }  // namespace svdq

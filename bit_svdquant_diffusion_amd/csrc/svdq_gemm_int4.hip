@@ -43,6 +43,8 @@
 #include "svdq_internal.h"
 #include "svdq_layout.h"
 
+#include <algorithm>
+
 namespace svdq {
 
 namespace {
@@ -64,6 +66,11 @@ __host__ __device__ constexpr int kOpsOf(int w) { return kFragPerWave + (kScaleO
 constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 1024;
 constexpr int kScB = kScA + 2 * kBM * 4, kSlot = kScB + 2 * kBN * 4;
 constexpr size_t kLds = (size_t)kNStage * kSlot;
+// FUSE: after the ring, the cross-wave sum of the next layer's partial Z: the
+// partials of waves wn = 1..3 of both wave rows, one 32-token block and one
+// 32-rank block at a time
+constexpr size_t kZred = (size_t)2 * 3 * 16 * 64 * 4;
+static_assert(kLds + kZred <= 160 * 1024, "ring and Z reduction fit in LDS");
 static_assert(kTM == 2 && kTN == 2, "schedule below assumes 2 x 2 blocks per wave");
 static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
 static_assert(kNW * kFragPerWave == 2 * (kMB + kNBt), "fragment blocks partition");
@@ -130,7 +137,9 @@ static_assert(kSplitPieces == 2, "a run holds at most two pieces: its first and 
 // DEBUG_P: instead of dequantizing, write every group sum P (exact int32) of
 // the outputs inside the window [m0, m0 + mc) x [n0, n0 + nc) to p, over the
 // window's tiles only, with the same transfers, widening and MFMAs.
-template <bool DEBUG_P>
+// FUSE: the tile's output is the next layer's input (GELU between them): see
+// fused_tile below. Not combined with DEBUG_P.
+template <bool DEBUG_P, bool FUSE>
 __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, int grid) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -412,6 +421,111 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       }
     }
   };
+  // FUSE: instead of Y, this wave's 64 x 64 of GELU(bf16(acc + bias)) (a bf16
+  // value, as a separate GELU over bf16 Y would give) becomes the next
+  // layer's input: smoothed by its mu, one 64-channel group per token (the
+  // wave's channels), INT4 codes and scales by the stage-1 quantizer, stored
+  // in its fragment order (lane h keeps block j = h: the two lanes of a token
+  // trade the other block's 4-channel runs), and the partial X_hat L1 over
+  // these 64 channels on bf16 MFMAs, added over the tile's four wave columns
+  // in order through LDS and stored per 256-channel tile. Ends with every
+  // store landed (no Y stores for the ring waits to count).
+  auto fused_tile = [&](int m0t, int n0, int tn) {
+    // acc (+ bias, added by the caller) -> the next layer's smoothed input, in place
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(a.nxt_mu + n0 + 32 * j + 8 * q + 4 * h);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[j][i][4 * q + e] = bf16_round(gelu_f32(bf16_round(acc[j][i][4 * q + e]))) * m4[e];
+      }
+    const int grp = n0 / 64, nr = a.nxt_r32;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int t = m0t + wm * kWM + 32 * i + lr;   // the lane's token
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(acc[j][i][e]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));   // the token's other 32 channels
+      const float sc = amax / 7.0f;
+      uint32_t c[kTN][2];
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = acc[j][i][e];
+        int4_codes16(v, sc, c[j][0], c[j][1]);
+      }
+      const uint32_t o0 = __shfl_xor(h ? c[0][0] : c[1][0], 32), o1 = __shfl_xor(h ? c[0][1] : c[1][1], 32);
+      const uint32_t m0 = h ? c[1][0] : c[0][0], m1 = h ? c[1][1] : c[0][1];
+      // runs of channels 8k .. 8k + 3 are lane 0's, 8k + 4 .. 8k + 7 lane 1's
+      const uint32_t ev0 = h ? o0 : m0, od0 = h ? m0 : o0, ev1 = h ? o1 : m1, od1 = h ? m1 : o1;
+      const u32x4 out = u32x4{(ev0 & 0xFFFFu) | (od0 << 16), (ev0 >> 16) | (od0 & 0xFFFF0000u),
+                              (ev1 & 0xFFFFu) | (od1 << 16), (ev1 >> 16) | (od1 & 0xFFFF0000u)};
+      if (t < g.M) {   // (rows past M stay unwritten, as stage 1 leaves them)
+        *reinterpret_cast<u32x4*>(a.nxt_qx + (((size_t)(t / 32) * (g.N / 64) + grp) * 64 + 32 * h + t % 32) * 16) = out;
+        if (h == 0) a.nxt_sx[(size_t)grp * g.act_rows + t] = sc;
+      }
+    }
+    if (nr > 0) {
+      float* zred = reinterpret_cast<float*>(smem + kLds);
+      for (int rb = 0; rb < nr / 32; ++rb) {
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+          // A: the token's channels 32 j + 16 m + 4 h + (0..3, 8..11), that is
+          // acc[j][i][8 m .. 8 m + 7], as bf16; B: the same channels' L1 rows
+          // for rank 32 rb + lr, gathered from the stage-1 layout (8 bytes
+          // per 4 channels)
+          f32x16 zacc = f32x16{};
+#pragma unroll
+          for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              u32x2 bl[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int k = n0 + 32 * j + 16 * m + 8 * u + 4 * h, col = 32 * rb + lr;
+                const size_t li = (((((size_t)(k / 256) * 4 + (k % 256) / 64) * (nr / 16) + col / 16) * 2 + (k % 16) / 8) * 64 +
+                                   16 * ((k % 64) / 16) + col % 16) * 8 + k % 8;
+                bl[u] = *reinterpret_cast<const u32x2*>(a.nxt_l1s + li);
+              }
+              const f32x16& v = acc[j][i];
+              const u32x4 av = u32x4{cvt_bf16x2(v[8 * m + 0], v[8 * m + 1]), cvt_bf16x2(v[8 * m + 2], v[8 * m + 3]),
+                                     cvt_bf16x2(v[8 * m + 4], v[8 * m + 5]), cvt_bf16x2(v[8 * m + 6], v[8 * m + 7])};
+              zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             __builtin_bit_cast(bf16x8, u32x4{bl[0][0], bl[0][1], bl[1][0], bl[1][1]}),
+                                                             zacc, 0, 0, 0);
+            }
+          // the four wave columns' partials, added in column order
+          if (wn > 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) zred[(((wm * 3 + wn - 1) * 16 + e) * 64) + lane] = zacc[e];
+          }
+          __syncthreads();
+          if (wn == 0) {
+#pragma unroll
+            for (int w2 = 0; w2 < 3; ++w2)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) zacc[e] += zred[(((wm * 3 + w2) * 16 + e) * 64) + lane];
+            // 32 x 32 result: lane l, reg e -> token 8 (e / 4) + 4 h + e % 4, rank lr
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int tz = m0t + wm * kWM + 32 * i + 8 * (e / 4) + 4 * h + e % 4;
+              if (tz < g.M) a.nxt_zpart[((size_t)tn * g.M + tz) * nr + 32 * rb + lr] = zacc[e];
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // every store landed: the ring's later waits count no stores
+  };
   __shared__ int ticket_last;   // the workgroup took a tile's last ticket
 
   // prologue: the first kNStage - 1 ring steps in flight
@@ -439,7 +553,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       ++gs;
     }
     if constexpr (DEBUG_P) continue;
-    if (!sg.whole) {
+    if (!FUSE && !sg.whole) {   // (FUSE launches take whole tiles only)
       // a piece: publish the partial in this run's slot for it (its first
       // segment, else its last), then take the tile's ticket
       const int myslot = kSplitPieces * wg + (ck == ncl ? 0 : 1);
@@ -555,6 +669,16 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
         bv[j][4 * q + 2] = bf16lo(bw.y);
         bv[j][4 * q + 3] = bf16hi(bw.y);
       }
+    if constexpr (FUSE) {
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][i][e] += bv[j][e];
+      fused_tile(m0t, n0, tmc.tn);
+      continue;
+    }
     store_tile(m0t, n0, bv);
     stores_due = kNStage - 1;
   }
@@ -562,10 +686,13 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 }
 
 hipError_t prepare_gemm_int4() {
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_int4_kernel<false>,
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_int4_kernel<false, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemm_int4_kernel<true>,
+  e = hipFuncSetAttribute((const void*)gemm_int4_kernel<false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)(kLds + kZred));
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_int4_kernel<true, false>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
 }
 
@@ -595,7 +722,7 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
     g.rounds = 0;
     g.sk_base = ntiles;   // whole tiles only
     g.sk_tiles = 0;
-    hipLaunchKernelGGL(gemm_int4_kernel<true>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
+    hipLaunchKernelGGL((gemm_int4_kernel<true, false>), dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
     return hipGetLastError();
   }
   const int nlr = a.r32 > 0 ? a.r32 / 32 : 1;   // at least one: the bias rides in a low-rank stage
@@ -615,7 +742,55 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
     g.sk_base = ntiles;   // whole tiles only
     g.sk_tiles = 0;
   }
-  hipLaunchKernelGGL(gemm_int4_kernel<false>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
+  if (a.nxt_qx != nullptr) {
+    // whole tiles only: the epilogue's registers on top of the split's
+    // finisher would spill in the main loop
+    if (grid > ntiles) grid = ntiles;
+    g.rounds = (ntiles + grid - 1) / grid;
+    g.sk_base = ntiles;
+    g.sk_tiles = 0;
+    hipLaunchKernelGGL((gemm_int4_kernel<false, true>), dim3(grid), dim3(64 * kNW), kLds + kZred, st, a, g, grid);
+  } else
+    hipLaunchKernelGGL((gemm_int4_kernel<false, false>), dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
+  return hipGetLastError();
+}
+
+// Z = bf16 of the tile partials [tiles_n][M][r32] added in tile order, in
+// the stage-1 fragment order; the next layer's split counters cleared
+__global__ void fused_zsum_kernel(const float* __restrict__ zpart, int tiles_n, int M, int r32,
+                                  uint16_t* __restrict__ z, uint32_t* __restrict__ flags, int nflags) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < nflags) flags[idx] = 0u;
+  if (idx >= M * r32) return;
+  const int t = idx / r32, col = idx - t * r32;
+  float s = zpart[idx];
+  for (int c = 1; c < tiles_n; ++c) s += zpart[(size_t)c * M * r32 + idx];
+  z[(((size_t)(t / 32) * (r32 / 16) + col / 16) * 64 + 32 * ((col % 16) / 8) + t % 32) * 8 + col % 8] = (uint16_t)f2bf(s);
+}
+
+hipError_t launch_fused_zsum(const float* zpart, int tiles_n, int M, int r32, uint16_t* z, uint32_t* flags,
+                             int nflags, hipStream_t st) {
+  const int n = std::max(M * r32, nflags);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fused_zsum_kernel, dim3((n + 255) / 256), dim3(256), 0, st, zpart, tiles_n, M, r32, z, flags,
+                     nflags);
+  return hipGetLastError();
+}
+
+__global__ void gelu_bf16_kernel(uint16_t* __restrict__ y, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  u32x4 v = reinterpret_cast<u32x4*>(y)[i];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    v[d] = f2bf(gelu_f32(bf16lo(v[d]))) | (f2bf(gelu_f32(bf16hi(v[d]))) << 16);
+  reinterpret_cast<u32x4*>(y)[i] = v;
+}
+
+hipError_t launch_gelu_bf16(uint16_t* y, size_t n, hipStream_t st) {
+  const size_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, y, n8);
   return hipGetLastError();
 }
 

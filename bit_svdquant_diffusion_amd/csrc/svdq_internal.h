@@ -50,8 +50,26 @@ struct GemmArgs {
   // nullptr for the normal epilogue
   int32_t* p;
   int m0, mc, n0, nc;
+  // fused next layer (INT4 tiled kernel only; nxt_qx == nullptr otherwise):
+  // instead of Y, the epilogue writes the next layer's INT4 codes and scales
+  // of GELU(bf16(Y)) smoothed by nxt_mu (its stage-1 layout, K = this N) and
+  // the fp32 partial X_hat L1 of each 256-channel tile, [N/256][M][nxt_r32]
+  uint8_t* nxt_qx;
+  float* nxt_sx;
+  const float* nxt_mu;
+  const uint16_t* nxt_l1s;   // next layer's L1 in its stage-1 layout
+  float* nxt_zpart;
+  int nxt_r32;
 };
 hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st);
+// after a fused MLP-up GEMM: Z of the next layer = bf16 of the tile partials
+// added in tile order, in fragment order; also clears that layer's split
+// counters (its stage 1 does not run)
+hipError_t launch_fused_zsum(const float* zpart, int tiles_n, int M, int r32, uint16_t* z, uint32_t* flags,
+                             int nflags, hipStream_t st);
+// y = GELU(y) in place over n bf16 values (n % 8 == 0): the activation between
+// the MLP layers when they are not fused
+hipError_t launch_gelu_bf16(uint16_t* y, size_t n, hipStream_t st);
 // few tokens (INT4: at most 256, or 769 to 1024; MXFP4: at most 256; no
 // group-sum hook): the weight-streaming kernel of either format
 bool gemm_small_fits(const GemmArgs& a, int num_cus);

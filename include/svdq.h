@@ -257,6 +257,52 @@ SVDQ_API svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* desc, co
                                                  const uint16_t* x, int64_t M, uint16_t* y, void* hip_stream);
 
 /*
+ * The MLP of a transformer block on the 4-bit path: y = down(GELU(up(x))),
+ * GELU(v) = v Phi(v) (Phi the standard normal distribution function),
+ * applied to the bf16 output of `up` and rounded to bf16, as a separate
+ * activation between the two layers would be. The engine that runs SVDQuant
+ * fuses kernels that work on the same data, to cut memory traffic
+ * (aiflownews.com, "Nunchaku: the inference engine that makes SVDQuant
+ * practical"); here the up layer's GEMM epilogue applies the GELU and emits
+ * the down layer's kernel-(1) output directly: its smoothed INT4 codes and
+ * scales and, per 256 hidden channels, the partial X_hat L1, which one small
+ * kernel adds up. The hidden activation never goes to memory.
+ *   up: K0 -> N0, down: N0 -> N1 (down->K == up->N); x bf16 [M][K0],
+ *   y bf16 [M][N1] (device, 16-byte aligned); dev_up, dev_down: packed
+ *   layers on the device; workspace: >= svdq_mlp_workspace_bytes device
+ *   bytes; contents on entry ignored, on return the down layer's part (from
+ *   *down_offset) holds its codes, scales and X_hat L1 as svdq_stage1 lays
+ *   them out, for rows below M (the fused path leaves rows M .. round32(M)
+ *   as the composition leaves them: unwritten by this call).
+ *   mode SVDQ_MLP_AUTO: fused when svdq_mlp_fused says so, else the
+ *   composition; SVDQ_MLP_UNFUSED: always the composition (svdq_linear_forward
+ *   of up into the workspace, a GELU kernel in place, svdq_linear_forward of
+ *   down; the bf16 hidden activation [M][up N] is left in the workspace at
+ *   *down_offset plus the down layer's svdq_workspace_bytes rounded up to a
+ *   multiple of 256). The fused path's codes and scales equal the composition's bit for
+ *   bit (same GELU, same quantizer); its Z differs only in the fp32 summation
+ *   order of the partial X_hat L1.
+ * Fused when both layers are INT4, up->N % 256 == 0 and M > 256 (the tiled
+ * GEMM; fewer tokens take the weight-streaming kernel, with no fused
+ * epilogue). Errors: as svdq_linear_forward for either layer; SVDQ_ERR_SHAPE
+ * also for down->K != up->N or an unknown mode.
+ * svdq_mlp_workspace_bytes: the workspace bytes for M tokens and (if
+ * down_offset is not NULL) where the down layer's part starts in it.
+ * svdq_mlp_fused: *fused = 1 when SVDQ_MLP_AUTO takes the fused path for M.
+ * Both host only; errors SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_FORMAT.
+ */
+#define SVDQ_MLP_AUTO 0
+#define SVDQ_MLP_UNFUSED 1
+SVDQ_API svdq_status svdq_mlp_workspace_bytes(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M,
+                                              size_t* out, size_t* down_offset);
+SVDQ_API svdq_status svdq_mlp_fused(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M,
+                                    int32_t* fused);
+SVDQ_API svdq_status svdq_mlp_forward(const svdq_layer_desc* up, const svdq_packed* dev_up,
+                                      const svdq_layer_desc* down, const svdq_packed* dev_down, const uint16_t* x,
+                                      int64_t M, uint16_t* y, void* workspace, size_t workspace_bytes, int32_t mode,
+                                      void* hip_stream);
+
+/*
  * Test hook: only kernel (1) of svdq_linear_forward, filling the workspace.
  * Same arguments and errors as svdq_linear_forward minus y.
  */

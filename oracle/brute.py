@@ -176,3 +176,16 @@ def forward(p, x):
                 q += _val(xc[m][k], xs[m][k // g], fmt) * _val(p["codes"][n][k], p["scales"][n][k // g], fmt)
             Y[m][n] = lr + q + p["bias"][n]
     return Y, xc, xs, Z
+
+
+def gelu(v: float) -> float:
+    """v (1 + erf(v / sqrt 2)) / 2 for one number."""
+    return 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0)))
+
+
+def mlp_forward(p_up, p_down, x):
+    """The down layer on bf16(GELU(bf16(up(x)))), one number at a time."""
+    y_up = forward(p_up, x)[0]
+    h = [[bf16_round(gelu(bf16_round(v))) for v in row] for row in y_up]
+    return forward(p_down, h)[0]
+

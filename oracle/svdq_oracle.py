@@ -38,8 +38,16 @@ closed forms and invariants; none is "parity unpinned".
 A packed layer can also take a LoRA adapter without re-quantization
 (lora_extend): the adapter joins the 16-bit low-rank branch and the 4-bit
 residual is kept (same page, same section).
+
+Two layers in a row with a GELU between (a transformer block's MLP,
+mlp_forward): the engine fuses kernels that work on the same data ("Nunchaku:
+the inference engine that makes SVDQuant practical", aiflownews.com page).
+Fusion changes no value, so the oracle is the plain composition: the up
+layer's output as bf16, GELU, bf16, the down layer.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -375,3 +383,22 @@ def lora_extend(packed: dict, lora_a: np.ndarray, lora_b: np.ndarray, scale: flo
 def forward_rows(packed: dict, x_rows: np.ndarray) -> np.ndarray:
     """Forward for a subset of token rows (rows are independent in every step)."""
     return forward(packed, x_rows)
+
+
+# ----------------------------------------------------------------------------
+# Two layers with a GELU between (the MLP of a transformer block)
+# ----------------------------------------------------------------------------
+def gelu(v) -> np.ndarray:
+    """GELU(v) = v Phi(v), Phi the standard normal distribution function,
+    Phi(v) = erfc(-v / sqrt 2) / 2 (float64)."""
+    from scipy.special import erfc
+    v = np.asarray(v, dtype=np.float64)
+    return v * (0.5 * erfc(-v / math.sqrt(2.0)))
+
+
+def mlp_forward(up: dict, down: dict, x: np.ndarray) -> np.ndarray:
+    """Y [M][N_down] float64 = down(bf16(GELU(bf16(up(X))))): each layer's
+    output is rounded to bf16 as the layer writes it, and so is the GELU's."""
+    h = to_bf16(gelu(to_bf16(forward(up, x))))
+    return forward(down, h)
+

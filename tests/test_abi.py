@@ -174,3 +174,39 @@ def test_noalloc_host_checks():
                                              x.ctypes.data, None) == 0
         assert L.svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, -1,
                                              x.ctypes.data, None) == 2
+
+
+def test_mlp_host_logic():
+    """svdq_mlp_workspace_bytes / svdq_mlp_fused / svdq_mlp_forward host
+    checks: the layout holds both layers' workspaces and the larger of the
+    hidden activation and the fused partial Z; the fused path needs INT4
+    layers, whole 256-channel hidden tiles and more than 256 tokens."""
+    up = S.Layer(3072, 12288, 32, "int4")
+    down = S.Layer(12288, 3072, 32, "int4")
+    M = 4608
+    total, off = S.mlp_workspace_bytes(up, down, M)
+    wu, wd = S.workspace_bytes(up, M), S.workspace_bytes(down, M)
+    assert off >= wu and off % 256 == 0
+    assert total >= off + wd + M * 12288 * 2
+    assert S.mlp_fused(up, down, M) and S.mlp_fused(up, down, 257)
+    assert not S.mlp_fused(up, down, 256)
+    assert not S.mlp_fused(S.Layer(3072, 12288, 32, "mxfp4"), S.Layer(12288, 3072, 32, "mxfp4"), M)
+    assert not S.mlp_fused(S.Layer(3072, 12160, 32, "int4"), S.Layer(12160, 3072, 32, "int4"), M)
+    with pytest.raises(S.SvdqError) as e:   # down K != up N
+        S.mlp_workspace_bytes(up, S.Layer(3072, 3072, 32, "int4"), M)
+    assert e.value.status == 2
+    L = S.lib()
+    bufs = {n: np.zeros(64, np.uint8) for n in S.PACKED_FIELDS}
+    p = S.Packed(*[b.ctypes.data for b in bufs.values()])
+    du, dd = up.desc, down.desc
+    x = np.zeros(16, np.uint16)
+    ws = np.zeros(64, np.uint8)
+    # M == 0: no-op; unknown mode; short workspace (all before any HIP call)
+    assert L.svdq_mlp_forward(ctypes.byref(du), ctypes.byref(p), ctypes.byref(dd), ctypes.byref(p), None, 0,
+                              None, None, 0, 0, None) == 0
+    assert L.svdq_mlp_forward(ctypes.byref(du), ctypes.byref(p), ctypes.byref(dd), ctypes.byref(p),
+                              x.ctypes.data, 4, x.ctypes.data, ws.ctypes.data, ws.nbytes, 5, None) == 2
+    assert L.svdq_mlp_forward(ctypes.byref(du), ctypes.byref(p), ctypes.byref(dd), ctypes.byref(p),
+                              x.ctypes.data, 4, x.ctypes.data, ws.ctypes.data, ws.nbytes, 0, None) == 4
+    assert L.svdq_mlp_forward(None, ctypes.byref(p), ctypes.byref(dd), ctypes.byref(p),
+                              x.ctypes.data, 4, x.ctypes.data, ws.ctypes.data, ws.nbytes, 0, None) == 1

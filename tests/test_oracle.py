@@ -467,3 +467,53 @@ def test_calibrate_alpha_is_the_argmin():
     y = O.dequant_int4(qx, sx) @ w_eff[0] + xh @ w_eff[1] + lay.bias.astype(np.float64)
     ref = lay.x.astype(np.float64) @ lay.w_lin.T.astype(np.float64) + lay.bias
     np.testing.assert_allclose(np.sum((y - ref) ** 2), res["losses"].min(), rtol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# GELU and the two-layer MLP composition
+# --------------------------------------------------------------------------
+def test_gelu_closed_forms():
+    """GELU(v) = v Phi(v): Phi at 1, 2, -3 and -10 (tabulated normal
+    distribution values), the odd part v/2 (Phi(v) + Phi(-v) = 1), the even
+    part's curvature 1/sqrt(2 pi) at 0, and zero at zero."""
+    table = {1.0: 0.8413447460685429486, 2.0: 0.9772498680518207928, -3.0: 0.0013498980316300945267,
+             -10.0: 7.6198530241605260660e-24}
+    for v, phi in table.items():
+        got = float(O.gelu(np.array([v]))[0])
+        assert abs(got - v * phi) <= 1e-13 * abs(v * phi), (v, got)
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    rng = np.random.default_rng(8)
+    v = rng.standard_normal(1000) * 3
+    np.testing.assert_allclose(O.gelu(v) - O.gelu(-v), v, rtol=1e-14, atol=1e-15)
+    h = 1e-3
+    even = (O.gelu(np.array([h])) + O.gelu(np.array([-h])))[0] / 2
+    assert abs(even / (h * h) - 1.0 / math.sqrt(2.0 * math.pi)) < 1e-5
+
+
+def test_gelu_brute():
+    rng = np.random.default_rng(9)
+    v = np.concatenate([rng.standard_normal(500) * 2, [0.0, 1e-30, -1e-30, 5.0, -5.0]])
+    got = O.gelu(v)
+    ref = np.array([brute.gelu(float(t)) for t in v])
+    # the brute force's 1 + erf loses digits for negative v (about 1e-16 absolute)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_mlp_composition_brute(fmt):
+    """The MLP oracle against the scalar brute force: up (64 -> 128, rank 4),
+    bf16, GELU, bf16, down (128 -> 32, rank 8), three tokens."""
+    up = _tiny(3, 64, 128, seed=61, fmt=fmt)
+    down = _tiny(3, 128, 32, seed=62, fmt=fmt)
+    pu = O.pack(up.w_lin, up.bias, np.abs(up.x).max(axis=0), 4, fmt)
+    pd = O.pack(down.w_lin, down.bias, np.abs(down.x).max(axis=0), 8, fmt)
+    y = O.mlp_forward(pu, pd, up.x)
+    bu = brute.pack(up.w_lin.tolist(), up.bias.tolist(), np.abs(up.x).max(axis=0).tolist(),
+                    pu["l1"].tolist(), pu["l2"].tolist(), fmt)
+    bd = brute.pack(down.w_lin.tolist(), down.bias.tolist(), np.abs(down.x).max(axis=0).tolist(),
+                    pd["l1"].tolist(), pd["l2"].tolist(), fmt)
+    by = np.array(brute.mlp_forward(bu, bd, up.x.tolist()))
+    np.testing.assert_allclose(y, by, rtol=1e-12, atol=1e-12 * np.abs(by).max())
+    # the hidden activation really goes through the GELU: without it the output differs
+    y_lin = O.forward(pd, O.to_bf16(O.forward(pu, up.x)))
+    assert np.abs(y_lin - y).max() > 1e-2 * np.abs(y).max()
