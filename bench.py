@@ -368,6 +368,52 @@ def bench_c4(args, torch, S, synth):
             "block_effective_tops": round(bops / (bus * 1e-6) / 1e12, 2)}
 
 
+def bench_mlp(args, torch, S, synth):
+    """The image stream's MLP of a FLUX double-stream block (3072 -> 12288 ->
+    3072, rank 32, INT4) as one svdq_mlp_forward: fused (the up GEMM's
+    epilogue emits the down layer's codes, scales and partial Z; the hidden
+    activation never reaches HBM) against the composition (up, GELU kernel,
+    down), at batch 2 (8192 tokens) and at one image with its text (4608).
+    GPU time per call from graph replays over 2 buffer sets."""
+    import numpy as np
+    by = {s.name: s for s in synth.config_layers(4, small_m=False)}
+    su, sd = by["img_up"], by["img_down"]
+    lay_u, lay_d = synth.make_layer(su), synth.make_layer(sd)
+    t0 = time.time()
+    lu, ld = S.Layer(su.K, su.N, su.rank, su.fmt), S.Layer(sd.K, sd.N, sd.rank, sd.fmt)
+    hu = S.pack_weights(lu, lay_u.w_lin, lay_u.bias, np.abs(lay_u.x).max(axis=0))
+    hd = S.pack_weights(ld, lay_d.w_lin, lay_d.bias, np.abs(lay_d.x).max(axis=0))
+    log(f"  packed the MLP pair in {time.time() - t0:.1f}s")
+    rows = []
+    for M in (8192, 4608):
+        x = torch.from_numpy(lay_u.x_bits[:M].view(np.int16)).cuda().view(torch.bfloat16)
+        wsb = S.mlp_workspace_bytes(lu, ld, M)[0]
+        sets = [dict(du=S.to_device(lu, hu), dd=S.to_device(ld, hd), ws=torch.empty(wsb, dtype=torch.uint8, device="cuda"),
+                     y=torch.empty((M, sd.N), dtype=torch.bfloat16, device="cuda")) for _ in range(2)]
+        res = {}
+        for mode, name in ((S.MLP_AUTO, "fused"), (S.MLP_UNFUSED, "composition")):
+            calls = [lambda s=s, mode=mode: S.mlp_forward(lu, s["du"], ld, s["dd"], x, y=s["y"], workspace=s["ws"],
+                                                          mode=mode) for s in sets]
+            res[name] = time_graph(calls, max(10, args.steps // 5), torch)
+        fl = 2.0 * M * (su.K * su.N + sd.K * sd.N)
+        hid = M * su.N * 2
+        zpart = (su.N // 256) * M * 32 * 4
+        rows.append({"M": M, "fused": S.mlp_fused(lu, ld, M), "us_fused": round(res["fused"] * 1e3, 1),
+                     "us_composition": round(res["composition"] * 1e3, 1),
+                     "speedup": round(res["composition"] / res["fused"], 3),
+                     "effective_tops_fused": round(fl / (res["fused"] * 1e-3) / 1e12, 1),
+                     "composition_hidden_bytes": 4 * hid, "fused_partial_z_bytes": 2 * zpart})
+        log(f"mlp M={M}: fused {res['fused'] * 1e3:.1f} us, composition {res['composition'] * 1e3:.1f} us "
+            f"({res['composition'] / res['fused']:.3f}x)")
+        del sets
+        torch.cuda.empty_cache()
+    return {"workload": "FLUX double-stream image MLP 3072 -> 12288 -> 3072 (GELU), INT4 g64, r32",
+            "note": "the composition moves the bf16 hidden activation four times (the up GEMM writes it, "
+                    "the GELU kernel reads and rewrites it, the down layer's kernel 1 reads it); the fused "
+                    "path writes and reads fp32 partial Z per 256 hidden channels instead",
+            "runs": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +427,7 @@ def main():
     ap.add_argument("--no-c4", action="store_true", help="skip the FLUX block's linears (config 4)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and copy ceilings")
     ap.add_argument("--no-awq", action="store_true", help="skip the W4A16 (AWQ-style) layers")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the fused MLP pair")
     ap.add_argument("--no-settle", action="store_true",
                     help="skip the half second of untimed forwards before the warm-up (profiler runs)")
     ap.add_argument("--layer-markers", action="store_true",
@@ -479,6 +526,8 @@ def main():
         out["secondary"] = sec
     if not args.no_c4:
         out["c4"] = bench_c4(args, torch, S, synth)
+    if not args.no_mlp:
+        out["mlp"] = bench_mlp(args, torch, S, synth)
     if not args.no_awq:
         out["awq"] = bench_awq(args, torch, S, synth)
     if not args.no_cpu_baseline:

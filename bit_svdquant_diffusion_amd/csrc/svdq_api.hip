@@ -173,11 +173,11 @@ svdq_status mlp_shape_checks(const svdq_layer_desc* up, const svdq_layer_desc* d
 }
 
 // The fused epilogue exists in the tiled INT4 GEMM: both layers INT4, the
-// hidden width in whole 256-channel tiles, and more tokens than the
-// weight-streaming kernel takes
+// hidden width in whole 256-channel tiles, more tokens than the
+// weight-streaming kernel takes, and partial Z addressed with 32-bit offsets
 bool mlp_fusable(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M) {
   return up->format == SVDQ_FMT_INT4_G64 && down->format == SVDQ_FMT_INT4_G64 && up->N % 256 == 0 &&
-         M > kFewTokens;
+         M > kFewTokens && (uint64_t)(up->N / 256) * M * rank32(down->rank) * 4 < ((uint64_t)1 << 32);
 }
 
 bool sync_debug() {

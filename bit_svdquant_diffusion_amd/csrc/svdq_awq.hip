@@ -34,12 +34,6 @@ namespace {
 constexpr int kAwqWaves = 8;
 constexpr int kAwqRing = 6;     // groups of weights in flight per wave
 constexpr int kAwqPadK = 8;     // bf16 padding of an x_hat row in LDS
-
-typedef __bf16 awq_bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t awq_cvt_bf16x2(float lo, float hi) {
-  awq_bf16x2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
 }  // namespace
 
 // rows: x_hat rows staged at once (min(16, M))
@@ -99,10 +93,10 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.inv_s + k);
         const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.inv_s + k + 4);
         u32x4 o;
-        o[0] = awq_cvt_bf16x2(bf16lo(xv[0]) * s0[0], bf16hi(xv[0]) * s0[1]);
-        o[1] = awq_cvt_bf16x2(bf16lo(xv[1]) * s0[2], bf16hi(xv[1]) * s0[3]);
-        o[2] = awq_cvt_bf16x2(bf16lo(xv[2]) * s1[0], bf16hi(xv[2]) * s1[1]);
-        o[3] = awq_cvt_bf16x2(bf16lo(xv[3]) * s1[2], bf16hi(xv[3]) * s1[3]);
+        o[0] = cvt_bf16x2(bf16lo(xv[0]) * s0[0], bf16hi(xv[0]) * s0[1]);
+        o[1] = cvt_bf16x2(bf16lo(xv[1]) * s0[2], bf16hi(xv[1]) * s0[3]);
+        o[2] = cvt_bf16x2(bf16lo(xv[2]) * s1[0], bf16hi(xv[2]) * s1[1]);
+        o[3] = cvt_bf16x2(bf16lo(xv[3]) * s1[2], bf16hi(xv[3]) * s1[3]);
         *reinterpret_cast<u32x4*>(xs + (size_t)t * ldx + k) = o;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {

@@ -67,9 +67,9 @@ constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 10
 constexpr int kScB = kScA + 2 * kBM * 4, kSlot = kScB + 2 * kBN * 4;
 constexpr size_t kLds = (size_t)kNStage * kSlot;
 // FUSE: after the ring, the cross-wave sum of the next layer's partial Z: the
-// partials of waves wn = 1..3 of both wave rows, one 32-token block and one
-// 32-rank block at a time
-constexpr size_t kZred = (size_t)2 * 3 * 16 * 64 * 4;
+// partials of all eight waves for one 32-token block and 32-rank block
+constexpr size_t kZred = (size_t)kWGN * kWGM * 16 * 64 * 4;
+static_assert(kLds + kZred <= 160 * 1024, "LDS of the fused epilogue");
 static_assert(kLds + kZred <= 160 * 1024, "ring and Z reduction fit in LDS");
 static_assert(kTM == 2 && kTN == 2, "schedule below assumes 2 x 2 blocks per wave");
 static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
@@ -84,17 +84,17 @@ static_assert(2 * kBM * 4 == 1024 && 2 * kBN * 4 == 2048 && kBN * 2 <= 1024,
 #define SVDQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)   /* expcnt 7, lgkmcnt 0 */
 __device__ __forceinline__ void ring_barrier(int n) {
   __builtin_amdgcn_sched_barrier(0);
-  switch (n) {
-    case 3: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(4)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(6)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(8)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(11)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(12)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(14)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(16)); break;
+#define SVDQ_WAIT_CASE(k) \
+  case k: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(k)); break;
+  switch (n < 24 ? n : 24) {   // a larger n waits for 24: longer than needed, never shorter
+    SVDQ_WAIT_CASE(1) SVDQ_WAIT_CASE(2) SVDQ_WAIT_CASE(3) SVDQ_WAIT_CASE(4) SVDQ_WAIT_CASE(5) SVDQ_WAIT_CASE(6)
+    SVDQ_WAIT_CASE(7) SVDQ_WAIT_CASE(8) SVDQ_WAIT_CASE(9) SVDQ_WAIT_CASE(10) SVDQ_WAIT_CASE(11) SVDQ_WAIT_CASE(12)
+    SVDQ_WAIT_CASE(13) SVDQ_WAIT_CASE(14) SVDQ_WAIT_CASE(15) SVDQ_WAIT_CASE(16) SVDQ_WAIT_CASE(17)
+    SVDQ_WAIT_CASE(18) SVDQ_WAIT_CASE(19) SVDQ_WAIT_CASE(20) SVDQ_WAIT_CASE(21) SVDQ_WAIT_CASE(22)
+    SVDQ_WAIT_CASE(23) SVDQ_WAIT_CASE(24)
     default: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
   }
+#undef SVDQ_WAIT_CASE
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -102,11 +102,6 @@ __device__ __forceinline__ void ring_barrier(int n) {
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
-  return *reinterpret_cast<uint32_t*>(&v);
-}
 
 // int8 operands of one 32-channel half of a group: 16*q of the even channels
 // (lo) and of the odd channels (hi) of a 16-byte fragment
@@ -286,7 +281,10 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   // lane (or, DEBUG_P, the group-sum writes). Units are software-pipelined
   // within the wave: the MFMAs of unit u + 1 are issued before the vector
   // work of unit u, so the matrix pipe and the vector ALU run side by side.
-  int gs = 0, stores_due = 0;   // ring step being computed; ring steps still to absorb Y stores
+  // ring step being computed; ring steps still to absorb the last epilogue's
+  // stores, and how many stores that epilogue issued (the same in every wave)
+  int gs = 0, stores_due = 0;
+  const int nstores = FUSE ? kTM * (2 + (a.nxt_r32 > 0 ? a.nxt_r32 / 32 : 0)) : kStores;
   i32x4 alo[2][kTM], ahi[2][kTM], blo[2][kTN], bhi[2][kTN];
   float sxv[2][kTM], swv[2][kTN];
   i32x16 pp[2];
@@ -423,14 +421,17 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   };
   // FUSE: instead of Y, this wave's 64 x 64 of GELU(bf16(acc + bias)) (a bf16
   // value, as a separate GELU over bf16 Y would give) becomes the next
-  // layer's input: smoothed by its mu, one 64-channel group per token (the
-  // wave's channels), INT4 codes and scales by the stage-1 quantizer, stored
-  // in its fragment order (lane h keeps block j = h: the two lanes of a token
-  // trade the other block's 4-channel runs), and the partial X_hat L1 over
-  // these 64 channels on bf16 MFMAs, added over the tile's four wave columns
-  // in order through LDS and stored per 256-channel tile. Ends with every
-  // store landed (no Y stores for the ring waits to count).
+  // layer's input, smoothed by its mu: first the partial X_hat L1 over the
+  // tile's 256 channels on bf16 MFMAs (each wave its 64 channels; the four
+  // wave columns' partials added in column order through LDS by all eight
+  // waves, one 16-byte store per lane), then one 64-channel group per token
+  // quantized by the stage-1 quantizer, codes in the stage-1 fragment order
+  // (lane h keeps block j = h: the two lanes of a token trade the other
+  // block's 4-channel runs) and scales. Every store is issued by every wave
+  // (lanes past M or not holding a scale aim past the end of their buffer),
+  // kTM * (2 + r32 / 32) of them, which the next ring waits count.
   auto fused_tile = [&](int m0t, int n0, int tn) {
+    const int grp = n0 / 64, nr = a.nxt_r32;
     // acc (+ bias, added by the caller) -> the next layer's smoothed input, in place
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
@@ -440,10 +441,77 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[j][i][4 * q + e] = bf16_round(gelu_f32(bf16_round(acc[j][i][4 * q + e]))) * m4[e];
+          for (int e = 0; e < 4; e += 2) {
+            const uint32_t yb = cvt_bf16x2(acc[j][i][4 * q + e], acc[j][i][4 * q + e + 1]);   // Y as bf16
+            const uint32_t gb = cvt_bf16x2(gelu_f32(bf16lo(yb)), gelu_f32(bf16hi(yb)));
+            acc[j][i][4 * q + e] = bf16lo(gb) * m4[e];
+            acc[j][i][4 * q + e + 1] = bf16hi(gb) * m4[e + 1];
+          }
       }
-    const int grp = n0 / 64, nr = a.nxt_r32;
+    if (nr > 0) {
+      // zred [wave column][wave row][16][64]: one 32-token block's partials
+      float* zred = reinterpret_cast<float*>(smem + kLds);
+      const uint32_t zbytes = (uint32_t)((size_t)g.tiles_n * g.M * nr * 4);
+      const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(a.nxt_zpart, 0, zbytes, 0x00020000);
+      // the reduction's share of thread tid: wave row zr, token ztk of the
+      // block, ranks zc .. zc + 3; in the 32 x 32 accumulator layout that is
+      // register 4 (ztk / 8) + ztk % 4 of lanes zc + 32 ((ztk / 4) % 2) + (0..3)
+      const int zr = tid >> 8, ztk = (tid >> 3) & 31, zc = 4 * (tid & 7);
+      const int zoff = ((zr * 16 + 4 * (ztk / 8) + ztk % 4) * 64) + zc + 32 * ((ztk / 4) % 2);
+      for (int rb = 0; rb < nr / 32; ++rb) {
+        // B: L1 rows of channels n0 + 32 j + 16 m + 8 u + 4 h + (0..3) for
+        // rank 32 rb + lr, gathered from the stage-1 layout (8 bytes per 4 channels)
+        u32x4 bw[kTN][2];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            u32x2 bl[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int k = n0 + 32 * j + 16 * m + 8 * u + 4 * h, col = 32 * rb + lr;
+              const size_t li = (((((size_t)(k / 256) * 4 + (k % 256) / 64) * (nr / 16) + col / 16) * 2 + (k % 16) / 8) * 64 +
+                                 16 * ((k % 64) / 16) + col % 16) * 8 + k % 8;
+              bl[u] = *reinterpret_cast<const u32x2*>(a.nxt_l1s + li);
+            }
+            bw[j][m] = u32x4{bl[0][0], bl[0][1], bl[1][0], bl[1][1]};
+          }
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+          // A: the token's channels 32 j + 16 m + 4 h + (0..3, 8..11), that
+          // is acc[j][i][8 m .. 8 m + 7], as bf16
+          f32x16 zacc = f32x16{};
+#pragma unroll
+          for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const f32x16& v = acc[j][i];
+              const u32x4 av = u32x4{cvt_bf16x2(v[8 * m + 0], v[8 * m + 1]), cvt_bf16x2(v[8 * m + 2], v[8 * m + 3]),
+                                     cvt_bf16x2(v[8 * m + 4], v[8 * m + 5]), cvt_bf16x2(v[8 * m + 6], v[8 * m + 7])};
+              zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             __builtin_bit_cast(bf16x8, bw[j][m]), zacc, 0, 0, 0);
+            }
+          if (rb + i > 0) __syncthreads();   // the last block's reads are done
+#pragma unroll
+          for (int e = 0; e < 16; ++e) zred[(((wn * kWGM + wm) * 16 + e) * 64) + lane] = zacc[e];
+          __syncthreads();
+          f32x4 zs = *reinterpret_cast<const f32x4*>(zred + zoff);
+#pragma unroll
+          for (int c = 1; c < kWGN; ++c) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(zred + c * (kWGM * 16 * 64) + zoff);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zs[e] += v[e];
+          }
+          const int tz = m0t + zr * kWM + 32 * i + ztk;
+          const uint32_t zo = tz < g.M ? (uint32_t)((((size_t)tn * g.M + tz) * nr + 32 * rb + zc) * 4) : zbytes;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, zs), zrs, zo, 0, 0);
+        }
+      }
+    }
+    const uint32_t qbytes = (uint32_t)((size_t)(g.MB * 32) * (g.N / 2));
+    const uint32_t sbytes = (uint32_t)((size_t)(g.N / 64) * g.act_rows * 4);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(a.nxt_qx, 0, qbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(a.nxt_sx, 0, sbytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const int t = m0t + wm * kWM + 32 * i + lr;   // the lane's token
@@ -468,63 +536,13 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       const uint32_t ev0 = h ? o0 : m0, od0 = h ? m0 : o0, ev1 = h ? o1 : m1, od1 = h ? m1 : o1;
       const u32x4 out = u32x4{(ev0 & 0xFFFFu) | (od0 << 16), (ev0 >> 16) | (od0 & 0xFFFF0000u),
                               (ev1 & 0xFFFFu) | (od1 << 16), (ev1 >> 16) | (od1 & 0xFFFF0000u)};
-      if (t < g.M) {   // (rows past M stay unwritten, as stage 1 leaves them)
-        *reinterpret_cast<u32x4*>(a.nxt_qx + (((size_t)(t / 32) * (g.N / 64) + grp) * 64 + 32 * h + t % 32) * 16) = out;
-        if (h == 0) a.nxt_sx[(size_t)grp * g.act_rows + t] = sc;
-      }
+      // rows past M stay unwritten, as stage 1 leaves them
+      const bool live = t < g.M;
+      const uint32_t qo = live ? (uint32_t)((((size_t)(t / 32) * (g.N / 64) + grp) * 64 + 32 * h + t % 32) * 16) : qbytes;
+      const uint32_t so = live && h == 0 ? (uint32_t)(((size_t)grp * g.act_rows + t) * 4) : sbytes;
+      __builtin_amdgcn_raw_buffer_store_b128(out, qrs, qo, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srs, so, 0, 0);
     }
-    if (nr > 0) {
-      float* zred = reinterpret_cast<float*>(smem + kLds);
-      for (int rb = 0; rb < nr / 32; ++rb) {
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-          // A: the token's channels 32 j + 16 m + 4 h + (0..3, 8..11), that is
-          // acc[j][i][8 m .. 8 m + 7], as bf16; B: the same channels' L1 rows
-          // for rank 32 rb + lr, gathered from the stage-1 layout (8 bytes
-          // per 4 channels)
-          f32x16 zacc = f32x16{};
-#pragma unroll
-          for (int j = 0; j < kTN; ++j)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              u32x2 bl[2];
-#pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                const int k = n0 + 32 * j + 16 * m + 8 * u + 4 * h, col = 32 * rb + lr;
-                const size_t li = (((((size_t)(k / 256) * 4 + (k % 256) / 64) * (nr / 16) + col / 16) * 2 + (k % 16) / 8) * 64 +
-                                   16 * ((k % 64) / 16) + col % 16) * 8 + k % 8;
-                bl[u] = *reinterpret_cast<const u32x2*>(a.nxt_l1s + li);
-              }
-              const f32x16& v = acc[j][i];
-              const u32x4 av = u32x4{cvt_bf16x2(v[8 * m + 0], v[8 * m + 1]), cvt_bf16x2(v[8 * m + 2], v[8 * m + 3]),
-                                     cvt_bf16x2(v[8 * m + 4], v[8 * m + 5]), cvt_bf16x2(v[8 * m + 6], v[8 * m + 7])};
-              zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                             __builtin_bit_cast(bf16x8, u32x4{bl[0][0], bl[0][1], bl[1][0], bl[1][1]}),
-                                                             zacc, 0, 0, 0);
-            }
-          // the four wave columns' partials, added in column order
-          if (wn > 0) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) zred[(((wm * 3 + wn - 1) * 16 + e) * 64) + lane] = zacc[e];
-          }
-          __syncthreads();
-          if (wn == 0) {
-#pragma unroll
-            for (int w2 = 0; w2 < 3; ++w2)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) zacc[e] += zred[(((wm * 3 + w2) * 16 + e) * 64) + lane];
-            // 32 x 32 result: lane l, reg e -> token 8 (e / 4) + 4 h + e % 4, rank lr
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int tz = m0t + wm * kWM + 32 * i + 8 * (e / 4) + 4 * h + e % 4;
-              if (tz < g.M) a.nxt_zpart[((size_t)tn * g.M + tz) * nr + 32 * rb + lr] = zacc[e];
-            }
-          }
-          __syncthreads();
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // every store landed: the ring's later waits count no stores
   };
   __shared__ int ticket_last;   // the workgroup took a tile's last ticket
 
@@ -546,7 +564,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 #pragma unroll
       for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
     for (int st = sg.ka; st < sg.kb; ++st) {
-      ring_barrier(DEBUG_P ? 0 : nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
+      ring_barrier(DEBUG_P ? 0 : nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
       if (stores_due > 0) --stores_due;
       if (gs + kNStage - 1 < total) SVDQ_ISSUE(gs + kNStage - 1)
       stage_compute(smem + (gs % kNStage) * kSlot, st, m0t, n0t);
@@ -629,7 +647,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       continue;
     }
     for (int l = 0; l < nlr; ++l) {
-      ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? kStores : 0));
+      ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
       if (stores_due > 0) --stores_due;
       const bool more = gs + kNStage - 1 < total;
       if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)
@@ -677,9 +695,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[j][i][e] += bv[j][e];
       fused_tile(m0t, n0, tmc.tn);
-      continue;
+    } else {
+      store_tile(m0t, n0, bv);
     }
-    store_tile(m0t, n0, bv);
     stores_due = kNStage - 1;
   }
 #undef SVDQ_ISSUE
@@ -782,8 +800,7 @@ __global__ void gelu_bf16_kernel(uint16_t* __restrict__ y, size_t n8) {
   if (i >= n8) return;
   u32x4 v = reinterpret_cast<u32x4*>(y)[i];
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
-    v[d] = f2bf(gelu_f32(bf16lo(v[d]))) | (f2bf(gelu_f32(bf16hi(v[d]))) << 16);
+  for (int d = 0; d < 4; ++d) v[d] = cvt_bf16x2(gelu_f32(bf16lo(v[d])), gelu_f32(bf16hi(v[d])));
   reinterpret_cast<u32x4*>(y)[i] = v;
 }
 

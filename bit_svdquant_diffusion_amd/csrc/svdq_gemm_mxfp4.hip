@@ -106,11 +106,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
-  return *reinterpret_cast<uint32_t*>(&v);
-}
 
 struct Geo {
   int M, N, K, MB, NB, KS, nst, nlr, nstt, tiles_m, tiles_n;   // N, K padded

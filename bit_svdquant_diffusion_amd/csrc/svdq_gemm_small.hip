@@ -32,11 +32,6 @@ namespace {
 // groups loaded ahead of the one being multiplied (fewer with more token blocks: registers)
 __host__ __device__ constexpr int kPD(int mb) { return mb <= 2 ? 4 : (mb <= 4 ? 2 : 1); }
 
-typedef __bf16 sm_bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t sm_cvt_bf16x2(float lo, float hi) {
-  sm_bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // int8 operands of one 32-channel half of a group: 16*q of the even channels
 // (lo) and of the odd channels (hi) of a 16-byte fragment
@@ -57,7 +52,7 @@ __device__ __forceinline__ void sm_widen(const i32x4& w, i32x4& lo, i32x4& hi) {
 __device__ __forceinline__ void sm_store_block(const f32x16& v, uint16_t* y, int M, int ldy, int n0, int m, int h) {
   uint32_t o[8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) o[p] = sm_cvt_bf16x2(v[2 * p], v[2 * p + 1]);
+  for (int p = 0; p < 8; ++p) o[p] = cvt_bf16x2(v[2 * p], v[2 * p + 1]);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
 #pragma unroll

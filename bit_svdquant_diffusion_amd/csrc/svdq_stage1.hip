@@ -88,11 +88,6 @@ __device__ __forceinline__ float s1_max32(float a) {
   return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
-typedef __bf16 s1_bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t s1_cvt_bf16x2(float lo, float hi) {
-  s1_bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // E2M1 codes of 8 values scaled by 2^-e, element 2i in the low nibble of byte i
 __device__ __forceinline__ uint32_t s1_e2m1x8(const float* v, int e) {
@@ -299,8 +294,8 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
         if constexpr (NCB > 0) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const u32x4 av = u32x4{s1_cvt_bf16x2(xh[8 * t + 0], xh[8 * t + 1]), s1_cvt_bf16x2(xh[8 * t + 2], xh[8 * t + 3]),
-                                   s1_cvt_bf16x2(xh[8 * t + 4], xh[8 * t + 5]), s1_cvt_bf16x2(xh[8 * t + 6], xh[8 * t + 7])};
+            const u32x4 av = u32x4{cvt_bf16x2(xh[8 * t + 0], xh[8 * t + 1]), cvt_bf16x2(xh[8 * t + 2], xh[8 * t + 3]),
+                                   cvt_bf16x2(xh[8 * t + 4], xh[8 * t + 5]), cvt_bf16x2(xh[8 * t + 6], xh[8 * t + 7])};
 #pragma unroll
             for (int c = 0; c < NCB; ++c)
               zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),

@@ -282,9 +282,10 @@ SVDQ_API svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* desc, co
  *   multiple of 256). The fused path's codes and scales equal the composition's bit for
  *   bit (same GELU, same quantizer); its Z differs only in the fp32 summation
  *   order of the partial X_hat L1.
- * Fused when both layers are INT4, up->N % 256 == 0 and M > 256 (the tiled
+ * Fused when both layers are INT4, up->N % 256 == 0, M > 256 (the tiled
  * GEMM; fewer tokens take the weight-streaming kernel, with no fused
- * epilogue). Errors: as svdq_linear_forward for either layer; SVDQ_ERR_SHAPE
+ * epilogue) and the partial X_hat L1, (up->N / 256) M rank32(down->rank)
+ * fp32 values, stays below 4 GiB. Errors: as svdq_linear_forward for either layer; SVDQ_ERR_SHAPE
  * also for down->K != up->N or an unknown mode.
  * svdq_mlp_workspace_bytes: the workspace bytes for M tokens and (if
  * down_offset is not NULL) where the down layer's part starts in it.
