@@ -40,6 +40,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_MARKS = [0]
+
+
+def mark(args, torch, name):
+    """With --layer-markers: one byte-fill kernel before a workload, so that a
+    profiler trace attributes the dispatches after the k-th fill to the
+    workload logged as marker k."""
+    if not args.layer_markers:
+        return
+    _MARKS[0] += 1
+    torch.full((4096,), _MARKS[0] % 256, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[marker {_MARKS[0]}] {name}")
+
+
 def make_workload(spec, rotate, torch, S, synth, seed=0, packed=None):
     """Pack the layer with the library (randomized SVD) and replicate inputs,
     outputs, workspaces and packed weights `rotate` times in HBM. `packed`
@@ -295,6 +310,7 @@ def bench_awq(args, torch, S, synth):
     import numpy as np
     rows = []
     for sp in synth.awq_layers():
+        mark(args, torch, f"awq {sp.name}")
         lay = synth.make_layer(sp)
         t0 = time.time()
         host, alpha, _ = S.awq_pack(lay.w_lin, lay.bias, synth.calibration_rows(sp, 32))
@@ -326,11 +342,7 @@ def bench_c4(args, torch, S, synth):
     packs, rows = {}, []
     steps = max(10, args.steps // 5)
     for li, sp in enumerate(synth.config_layers(4)):
-        if args.layer_markers:
-            # a one-kernel fill of a byte buffer: in a rocprofv3 trace the
-            # dispatches of layer li follow the (li + 1)-th such fill
-            torch.full((4096,), li, dtype=torch.uint8, device="cuda")
-            torch.cuda.synchronize()
+        mark(args, torch, f"c4 {sp.name}")
         owner = sp.stream or sp.name
         rot = 16 if sp.M <= 256 else 2
         layer, host, _, sets = make_workload(sp, rot, torch, S, synth, packed=packs.get(owner))
@@ -386,6 +398,7 @@ def bench_mlp(args, torch, S, synth):
     log(f"  packed the MLP pair in {time.time() - t0:.1f}s")
     rows = []
     for M in (8192, 4608):
+        mark(args, torch, f"mlp M={M} (fused, then composition)")
         x = torch.from_numpy(lay_u.x_bits[:M].view(np.int16)).cuda().view(torch.bfloat16)
         wsb = S.mlp_workspace_bytes(lu, ld, M)[0]
         sets = [dict(du=S.to_device(lu, hu), dd=S.to_device(ld, hd), ws=torch.empty(wsb, dtype=torch.uint8, device="cuda"),
@@ -431,7 +444,7 @@ def main():
     ap.add_argument("--no-settle", action="store_true",
                     help="skip the half second of untimed forwards before the warm-up (profiler runs)")
     ap.add_argument("--layer-markers", action="store_true",
-                    help="launch one byte-fill kernel before each config-4 layer (layer boundaries in profiler traces)")
+                    help="launch one byte-fill kernel before each workload (boundaries in profiler traces)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -452,6 +465,7 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
 
     spec = synth.config_layers(2)[0]          # 4608 x 3072 -> 12288, r32, MXFP4
+    mark(args, torch, f"headline {spec.name}")
     layer, host, lay, sets = make_workload(spec, args.rotate, torch, S, synth)
     flops = 2.0 * spec.M * spec.N * spec.K
 
@@ -511,6 +525,7 @@ def main():
         sec = []
         for idx in (3, 1):
             sp = synth.config_layers(idx)[0]
+            mark(args, torch, f"secondary {sp.name}")
             del sets
             torch.cuda.empty_cache()
             l2, _, _, sets = make_workload(sp, args.rotate, torch, S, synth)

@@ -25,8 +25,7 @@
 // stages on v_mfma_f32_32x32x16_bf16 into the same accumulators.
 //
 // Work split. Whole rounds of tiles go one per workgroup. The tiles left
-// after them (between one and two rounds' worth, or all of them when there
-// are fewer tiles than workgroups) are cut into their K stages and dealt out
+// after them (less than one round's worth) are cut into their K stages and dealt out
 // as equal contiguous runs of (tile, stage) pairs, so every workgroup ends at
 // the same time. Each XCD deals its own share of those tiles (the ones the
 // tile map gives it) over its own workgroups, which keeps their operand
@@ -751,8 +750,10 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   if (grid > kSplitSlots) grid = kSplitSlots;
   if (grid >= 8) {
     grid &= ~7;   // every XCD holds the same number of workgroups
-    // whole rounds while at least one more round's worth of tiles remains
-    g.rounds = ntiles / grid > 1 ? ntiles / grid - 1 : 0;
+    // every whole round; the remainder is split. (Splitting the last whole
+    // round as well measured no faster and read more: runs that start
+    // mid-tile fall out of K step with their XCD's other workgroups.)
+    g.rounds = ntiles / grid;
     g.sk_base = g.rounds * grid;
     g.sk_tiles = ntiles - g.sk_base;
   } else {
