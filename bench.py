@@ -411,7 +411,7 @@ def bench_mlp(args, torch, S, synth):
         fl = 2.0 * M * (su.K * su.N + sd.K * sd.N)
         hid = M * su.N * 2
         zpart = (su.N // 256) * M * 32 * 4
-        rows.append({"M": M, "fused": S.mlp_fused(lu, ld, M), "us_fused": round(res["fused"] * 1e3, 1),
+        rows.append({"M": M, "format": "int4", "fused": S.mlp_fused(lu, ld, M), "us_fused": round(res["fused"] * 1e3, 1),
                      "us_composition": round(res["composition"] * 1e3, 1),
                      "speedup": round(res["composition"] / res["fused"], 3),
                      "effective_tops_fused": round(fl / (res["fused"] * 1e-3) / 1e12, 1),
@@ -420,7 +420,37 @@ def bench_mlp(args, torch, S, synth):
             f"({res['composition'] / res['fused']:.3f}x)")
         del sets
         torch.cuda.empty_cache()
-    return {"workload": "FLUX double-stream image MLP 3072 -> 12288 -> 3072 (GELU), INT4 g64, r32",
+    # the MXFP4 pair at 4608 tokens: the headline layer and its down layer
+    su2 = synth.config_layers(2)[0]
+    sd2 = synth.LayerSpec("mlp_down_fp4", su2.M, su2.N, su2.K, 32, "mxfp4", 3, x_kind="gelu",
+                          x_outlier_frac=0.005, x_outlier_scale=30.0, w_outlier_frac=0.0)
+    lu2, ld2 = S.Layer(su2.K, su2.N, 32, "mxfp4"), S.Layer(sd2.K, sd2.N, 32, "mxfp4")
+    lay_u2, lay_d2 = synth.make_layer(su2), synth.make_layer(sd2)
+    hu2 = S.pack_weights(lu2, lay_u2.w_lin, lay_u2.bias, np.abs(lay_u2.x).max(axis=0))
+    hd2 = S.pack_weights(ld2, lay_d2.w_lin, lay_d2.bias, np.abs(lay_d2.x).max(axis=0))
+    M = su2.M
+    mark(args, torch, f"mlp mxfp4 M={M} (fused, then composition)")
+    x = torch.from_numpy(lay_u2.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    wsb = S.mlp_workspace_bytes(lu2, ld2, M)[0]
+    sets = [dict(du=S.to_device(lu2, hu2), dd=S.to_device(ld2, hd2), ws=torch.empty(wsb, dtype=torch.uint8, device="cuda"),
+                 y=torch.empty((M, sd2.N), dtype=torch.bfloat16, device="cuda")) for _ in range(2)]
+    res = {}
+    for mode, name in ((S.MLP_AUTO, "fused"), (S.MLP_UNFUSED, "composition")):
+        calls = [lambda s=s, mode=mode: S.mlp_forward(lu2, s["du"], ld2, s["dd"], x, y=s["y"], workspace=s["ws"],
+                                                      mode=mode) for s in sets]
+        res[name] = time_graph(calls, max(10, args.steps // 5), torch)
+    fl = 2.0 * M * (su2.K * su2.N + sd2.K * sd2.N)
+    rows.append({"M": M, "format": "mxfp4", "fused": S.mlp_fused(lu2, ld2, M),
+                 "us_fused": round(res["fused"] * 1e3, 1), "us_composition": round(res["composition"] * 1e3, 1),
+                 "speedup": round(res["composition"] / res["fused"], 3),
+                 "effective_tops_fused": round(fl / (res["fused"] * 1e-3) / 1e12, 1),
+                 "composition_hidden_bytes": 4 * M * su2.N * 2, "fused_partial_z_bytes": 2 * (su2.N // 384) * M * 32 * 4})
+    log(f"mlp mxfp4 M={M}: fused {res['fused'] * 1e3:.1f} us, composition {res['composition'] * 1e3:.1f} us "
+        f"({res['composition'] / res['fused']:.3f}x)")
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": "FLUX MLP 3072 -> 12288 -> 3072 (GELU), r32: the double-stream image pair in INT4 g64 "
+                        "(8192 and 4608 tokens) and the headline MXFP4 layer with its down layer (4608 tokens)",
             "note": "the composition moves the bf16 hidden activation four times (the up GEMM writes it, "
                     "the GELU kernel reads and rewrites it, the down layer's kernel 1 reads it); the fused "
                     "path writes and reads fp32 partial Z per 256 hidden channels instead",

@@ -155,7 +155,7 @@ MlpLayout mlp_layout(const svdq_layer_desc* up, const svdq_layer_desc* down, int
   L.down = align256(ws_layout(up, M).total);
   L.mid = L.down + align256(ws_layout(down, M).total);
   const size_t hid = (size_t)M * up->N * 2;
-  const size_t zpart = (size_t)(up->N / 256) * M * rank32(down->rank) * 4;
+  const size_t zpart = (size_t)(up->N / 256) * M * rank32(down->rank) * 4;   // at most N / 256 tile columns
   L.total = L.mid + align256(hid > zpart ? hid : zpart);
   return L;
 }
@@ -172,12 +172,15 @@ svdq_status mlp_shape_checks(const svdq_layer_desc* up, const svdq_layer_desc* d
   return check_m(down, M);
 }
 
-// The fused epilogue exists in the tiled INT4 GEMM: both layers INT4, the
-// hidden width in whole 256-channel tiles, more tokens than the
-// weight-streaming kernel takes, and partial Z addressed with 32-bit offsets
+// The fused epilogue exists in the tiled GEMMs: both layers in one format,
+// the hidden width in whole tile columns (256 channels INT4, 384 MXFP4) and
+// whole stage-1 steps (256: the down layer's K needs no padding, which the
+// epilogue would not write), more tokens than the weight-streaming kernel
+// takes, and partial Z addressed with 32-bit offsets
+int mlp_tile_n(const svdq_layer_desc* up) { return up->format == SVDQ_FMT_INT4_G64 ? 256 : 384; }
 bool mlp_fusable(const svdq_layer_desc* up, const svdq_layer_desc* down, int64_t M) {
-  return up->format == SVDQ_FMT_INT4_G64 && down->format == SVDQ_FMT_INT4_G64 && up->N % 256 == 0 &&
-         M > kFewTokens && (uint64_t)(up->N / 256) * M * rank32(down->rank) * 4 < ((uint64_t)1 << 32);
+  return up->format == down->format && up->N % mlp_tile_n(up) == 0 && up->N % 256 == 0 && M > kFewTokens &&
+         (uint64_t)(up->N / mlp_tile_n(up)) * M * rank32(down->rank) * 4 < ((uint64_t)1 << 32);
 }
 
 bool sync_debug() {
@@ -287,21 +290,23 @@ svdq_status svdq_mlp_forward(const svdq_layer_desc* up, const svdq_packed* dev_u
   if (st != SVDQ_OK) return st;
   if (mode == SVDQ_MLP_AUTO && mlp_fusable(up, down, M)) {
     // the up GEMM's epilogue leaves the down layer's stage-1 output in its
-    // workspace (codes, scales, per-tile partial Z); one small kernel adds
-    // the partials into Z
+    // workspace (codes, scales, per-tile-column partial Z); one small kernel
+    // adds the partials into Z
     const WsLayout D = ws_layout(down, M);
     const int r32 = rank32(down->rank);
     GemmArgs a = gemm_args(up, dev_up, M, b, nullptr);
     a.nxt_qx = wd + D.qx;
-    a.nxt_sx = (float*)(wd + D.sx);
+    a.nxt_sx = wd + D.sx;
     a.nxt_mu = dev_down->mu;
     a.nxt_l1s = dev_down->l1;
     a.nxt_zpart = (float*)(b + L.mid);
     a.nxt_r32 = r32;
-    st = after_launch(launch_gemm_int4(a, cus, s), s);
+    const bool int4 = up->format == SVDQ_FMT_INT4_G64;
+    st = after_launch(int4 ? launch_gemm_int4(a, cus, s) : launch_gemm_mxfp4(a, cus, s), s);
     if (st != SVDQ_OK) return st;
-    st = after_launch(launch_fused_zsum((const float*)(b + L.mid), up->N / 256, (int)M, r32, (uint16_t*)(wd + D.z),
-                                        (uint32_t*)(wd + D.flags), kSplitCounters, s),
+    st = after_launch(launch_fused_zsum((const float*)(b + L.mid), up->N / mlp_tile_n(up), (int)M, r32,
+                                        (uint16_t*)(wd + D.z), int4 ? (uint32_t*)(wd + D.flags) : nullptr,
+                                        int4 ? kSplitCounters : 0, s),
                       s);
   } else {
     uint16_t* hid = (uint16_t*)(b + L.mid);

@@ -87,6 +87,26 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 // 2^-e as a float for e in [-127, 125].
 __device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
+// E2M1 codes of 8 values scaled by 2^-e, value k in nibble k (low nibble
+// first): v_cvt_scalef32_pk_fp4_f32 for a normal scale (it divides by 2^e
+// exactly, rounds to nearest even and saturates), else the exact
+// software encoder. Shared by stage 1 and the GEMM epilogue that quantizes
+// the next layer's activations, so both give the same bits.
+__device__ __forceinline__ uint32_t e2m1x8_codes(const float* v, int e) {
+  if (e >= -126) {
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
+  }
+  const float sinv = exp2_neg(e);
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_code(v[i] * sinv) << (4 * i);
+  return w;
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // GELU(v) = v Phi(v), Phi the standard normal distribution function, with

@@ -30,6 +30,7 @@
 // other instructions adds to the MFMA time rather than hiding under it.
 #include "svdq_gemm_common.h"
 #include "svdq_internal.h"
+#include "svdq_layout.h"
 
 namespace svdq {
 
@@ -90,14 +91,29 @@ static_assert(kMB * 128 <= 1024 && kNBt * 128 <= 2048 && kBN * 2 <= 1024, "scale
 // end of the work they repeat the last tile's), so two later steps are
 // always in flight: the wait is for all but 2 kOps of the wave's transfers,
 // plus the last tile's Y stores while they are still counted.
-__device__ __forceinline__ void ring_barrier(bool stores) {
+// FUSE: the fused epilogue's stores instead, nstores of them (up to 48);
+// a count past the cases waits for all outstanding operations.
+template <bool FUSE>
+__device__ __forceinline__ void ring_barrier(bool stores, int nstores) {
   __builtin_amdgcn_sched_barrier(0);
-  if (stores) __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps + kStores));
-  else __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps));
+  if (!stores) {
+    __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps));
+  } else if constexpr (!FUSE) {
+    __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps + kStores));
+  } else {
+#define SVDQ_FWAIT(k) \
+  case k: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(2 * kOps + k)); break;
+    switch (nstores) {
+      SVDQ_FWAIT(18) SVDQ_FWAIT(21) SVDQ_FWAIT(24) SVDQ_FWAIT(27) SVDQ_FWAIT(30)
+      SVDQ_FWAIT(33) SVDQ_FWAIT(36) SVDQ_FWAIT(39) SVDQ_FWAIT(42) SVDQ_FWAIT(45) SVDQ_FWAIT(48)
+      default: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(0)); break;
+    }
+#undef SVDQ_FWAIT
+  }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
-static_assert(2 * kOps + kStores < 64, "vmcnt range");
+static_assert(2 * kOps + kStores < 64 && 2 * kOps + 48 < 64, "vmcnt range");
 
 // Word 3 of the buffer resources: 32-bit data format, no swizzle, no added
 // thread id (untyped loads and stores ignore the rest).
@@ -123,6 +139,9 @@ struct Geo {
 // offset, so each tile sets the sources once.
 }  // namespace
 
+// FUSE: the tile's output is the next layer's input (GELU between them):
+// see fused_tile below.
+template <bool FUSE>
 __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g, int grid) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
   // tile's Y stores stay in flight.
 #define SVDQ_STEP(LOWRANK, LAST, DO_MFMA)                                                           \
   {                                                                                                 \
-    ring_barrier(stores_due > 0);                                                                   \
+    ring_barrier<FUSE>(stores_due > 0, nstores);                                                    \
     if (stores_due > 0) --stores_due;                                                               \
     if (wave < 4) SVDQ_ISSUE(gs + kNStage - 1)                                                      \
     const uint32_t slot = (gs & (kNStage - 1)) * kSlot;                                                   \
@@ -276,10 +295,147 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
 
   bool pending = false;   // deferred step-1 MFMAs of the previous ring step
   int gs = 0, stores_due = 0;
+  // stores of one tile's epilogue per wave (the same in every wave)
+  const int nstores = FUSE ? kTM * kTN * 2 + kTM * (a.nxt_r32 / 32) : kStores;
   const int nlr = g.nstt - g.nst;
   // this wave's LDS read offsets within a slot: fragment blocks and scale bytes
   const uint32_t rd_a = kCodeA + wm * kTM * 2048 + lane * 16, rd_b = kCodeB + wn * kTN * 2048 + lane * 16;
   const uint32_t rs_a = kScA + wm * kTM * 128 + lane * 2, rs_b = kScB + wn * kTN * 128 + lane * 2;
+  // FUSE: instead of Y, this wave's 96 x 96 of GELU(bf16(acc + bias)) (a bf16
+  // value, as a separate GELU over bf16 Y would give) becomes the next MXFP4
+  // layer's input, smoothed by its mu: first the partial X_hat L1 over the
+  // tile's 384 channels on bf16 MFMAs (each wave its 96 channels; the four
+  // wave columns' partials added in column order through LDS, in the ring
+  // slot the tile's last step used, by all eight waves, one 16-byte store per
+  // lane), then each token's three 32-channel blocks quantized by the stage-1
+  // quantizer: E8M0 scale byte and E2M1 codes in the stage-1 fragment order
+  // (the two lanes of a token trade 4-channel runs so that each stores 8
+  // contiguous bytes). Every store is issued by every wave (lanes past M, or
+  // not holding a scale, aim past the end of their buffer): kTM kTN 2 + kTM
+  // r32 / 32 of them, which the next ring waits count.
+  auto fused_tile = [&](int tm, int tn, const uint8_t* bslot, uint8_t* zslot) {
+    const int nr = a.nxt_r32, Kd = g.N, rows32 = g.MB * 32;
+    const int m0t = tm * kBM;
+    float* zred = reinterpret_cast<float*>(zslot);   // [wave column][wave row][16][64]
+    const uint32_t zbytes = (uint32_t)((size_t)g.tiles_n * g.M * nr * 4);
+    const uint32_t qbytes = (uint32_t)((size_t)rows32 * Kd / 2);
+    const uint32_t sbytes = (uint32_t)((size_t)(Kd / 128) * g.MB * 128);
+    // mu and L1 of the next layer through buffer resources: a lane offset
+    // plus wave-uniform offsets, so their addresses take few registers
+    const __amdgpu_buffer_rsrc_t rmu = __builtin_amdgcn_make_buffer_rsrc((void*)a.nxt_mu, 0, Kd * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rl1 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.nxt_l1s, 0, (uint32_t)Kd * (nr > 0 ? nr : 1) * 2, kRsrcWord3);
+    // the Z reduction's share of thread tid: wave row zr, token ztk of the
+    // block, ranks zc .. zc + 3; in the 32 x 32 accumulator layout that is
+    // register 4 (ztk / 8) + ztk % 4 of lanes zc + 32 ((ztk / 4) % 2) + (0..3)
+    const int zr = tid >> 8, ztk = (tid >> 3) & 31, zc = 4 * (tid & 7);
+    const int zoff = ((zr * 16 + 4 * (ztk / 8) + ztk % 4) * 64) + zc + 32 * ((ztk / 4) % 2);
+    // one 32-token block at a time (acc of the later blocks stays live)
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      // GELU(bf16(acc + bias)) as packed bf16 pairs: hb[j][p] holds
+      // accumulator values 2 p and 2 p + 1 of block (j, i)
+      uint32_t hb[kTN][8];
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 bw = *reinterpret_cast<const u32x2*>(bslot + (32 * j + 8 * q + 4 * h) * 2);
+          const uint32_t y0 = cvt_bf16x2(acc[j][i][4 * q + 0] + bf16lo(bw.x), acc[j][i][4 * q + 1] + bf16hi(bw.x));
+          const uint32_t y1 = cvt_bf16x2(acc[j][i][4 * q + 2] + bf16lo(bw.y), acc[j][i][4 * q + 3] + bf16hi(bw.y));
+          hb[j][2 * q] = cvt_bf16x2(gelu_f32(bf16lo(y0)), gelu_f32(bf16hi(y0)));
+          hb[j][2 * q + 1] = cvt_bf16x2(gelu_f32(bf16lo(y1)), gelu_f32(bf16hi(y1)));
+        }
+      // x_hat of values 8 m .. 8 m + 7 of block j (channels 32 cb + 16 m +
+      // 4 h + (0..3, 8..11)): the bf16 GELU times the next layer's mu
+      auto xhat8 = [&](int j, int m, int cb, float* o) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const f32x4 m4 = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rmu, 16 * h, (32 * cb + 16 * m + 8 * qq) * 4, 0));
+          const uint32_t p0 = hb[j][4 * m + 2 * qq], p1 = hb[j][4 * m + 2 * qq + 1];
+          o[4 * qq + 0] = bf16lo(p0) * m4[0];
+          o[4 * qq + 1] = bf16hi(p0) * m4[1];
+          o[4 * qq + 2] = bf16lo(p1) * m4[2];
+          o[4 * qq + 3] = bf16hi(p1) * m4[3];
+        }
+      };
+      for (int rb = 0; rb < nr / 32; ++rb) {
+        // A: the token's x_hat of channels 32 cb + 16 m + 4 h + (0..3, 8..11)
+        // as bf16; B: the same channels' L1 rows for rank 32 rb + lr, 8
+        // bytes per 4 channels of the stage-1 layout [K/256][4][r32/16][2]
+        // [64][8]: channel k = 32 cb + 16 m + 8 u + 4 h, column col sits at
+        // element (((k/256 4 + (k%256)/64) r32/16 + col/16) 2 + u) 512 +
+        // (16 ((k%64)/16) + col%16) 8 + 4 h
+        const uint32_t lane_off = ((lr / 16) * 1024 + (lr % 16) * 8 + 4 * h) * 2;
+        f32x16 zacc = f32x16{};
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+          const int cb = tn * kNBt + bperm(wn * kTN + j);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            u32x2 bl[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int sel = (((cb / 8) * 4 + (cb % 8) / 2) * (nr / 16) + 2 * rb) * 1024 + u * 512 +
+                              (32 * (cb % 2) + 16 * m) * 8;
+              bl[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rl1, lane_off, sel * 2, 0));
+            }
+            float x8[8];
+            xhat8(j, m, cb, x8);
+            const u32x4 av = u32x4{cvt_bf16x2(x8[0], x8[1]), cvt_bf16x2(x8[2], x8[3]), cvt_bf16x2(x8[4], x8[5]),
+                                   cvt_bf16x2(x8[6], x8[7])};
+            zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, u32x4{bl[0][0], bl[0][1], bl[1][0], bl[1][1]}),
+                                                           zacc, 0, 0, 0);
+          }
+        }
+        // the slot's fragments (first time) or the last block's partials are read
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) zred[(((wn * kWGM + wm) * 16 + e) * 64) + lane] = zacc[e];
+        __syncthreads();
+        f32x4 zs = *reinterpret_cast<const f32x4*>(zred + zoff);
+#pragma unroll
+        for (int c = 1; c < kWGN; ++c) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(zred + c * (kWGM * 16 * 64) + zoff);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zs[e] += v[e];
+        }
+        const int tz = m0t + zr * kWM + 32 * i + ztk;
+        const uint32_t zo = tz < g.M ? (uint32_t)((((size_t)tn * g.M + tz) * nr + 32 * rb + zc) * 4) : zbytes;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, zs),
+                                               __builtin_amdgcn_make_buffer_rsrc(a.nxt_zpart, 0, zbytes, kRsrcWord3),
+                                               zo, 0, 0);
+      }
+      // each token's three 32-channel blocks: E8M0 scale byte and E2M1 codes
+      const int t = m0t + wm * kWM + 32 * i + lr;   // the lane's token
+      const bool live = t < g.M;                    // rows past M stay unwritten, as stage 1 leaves them
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int cb = tn * kNBt + bperm(wn * kTN + j);
+        float v[16];
+        xhat8(j, 0, cb, v);
+        xhat8(j, 1, cb, v + 8);
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));   // the block's other 16 channels
+        const int ex = mx_exponent(amax);
+        // runs r = 2 q + h of 4 channels: A holds runs h and 2 + h, B runs
+        // 4 + h and 6 + h; after the swap lane h holds runs 4h .. 4h + 3
+        const uint32_t ca = e2m1x8_codes(v, ex), cbw = e2m1x8_codes(v + 8, ex);
+        const auto sw = __builtin_amdgcn_permlane32_swap(ca, cbw, false, false);
+        const uint32_t w0 = (sw[0] & 0xFFFFu) | (sw[1] << 16), w1 = (sw[0] >> 16) | (sw[1] & 0xFFFF0000u);
+        const uint32_t qo = live ? (uint32_t)f_code_byte(Kd, t, 32 * cb + 16 * h) : qbytes;
+        const uint32_t so = live && h == 0 ? (uint32_t)f_scale_index(rows32, t, cb) : sbytes;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, __builtin_amdgcn_make_buffer_rsrc(a.nxt_qx, 0, qbytes, kRsrcWord3),
+                                              qo, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(ex + 127),
+                                             __builtin_amdgcn_make_buffer_rsrc(a.nxt_sx, 0, sbytes, kRsrcWord3), so, 0, 0);
+      }
+    }
+  };
   // prologue: the first kNStage - 1 ring steps in flight
   for (int p = 0; p < kNStage - 1; ++p) SVDQ_ISSUE(p)
   for (int ct = 0; ct < my_tiles; ++ct) {
@@ -291,51 +447,58 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
       for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
     for (int s4 = 0; s4 < g.nst; ++s4) SVDQ_STEP(false, s4 == g.nst - 1, true)
     for (int l = 0; l < nlr; ++l) SVDQ_STEP(true, l == nlr - 1, a.r32 > 0)
+    // (every tile's last step runs its deferred MFMAs itself: saying so here
+    // leaves the deferred operands dead over the epilogue)
+    pending = false;
 
-    // + bias (from the last low-rank slot), bf16. The accumulator lane holds
-    // token m0 + 32 i + lr and channels 32 j + 8 q + 4 h + (0..3); swapping the
-    // packed pairs (q = 1, h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <->
-    // (q = 2, h = 1) between the lane halves leaves lane h with channels
-    // 32 j + 8 h + (0..7) and 32 j + 16 + 8 h + (0..7): two 16-byte stores,
-    // 32 contiguous bytes of one row per lane pair.
     const uint8_t* bslot = smem + ((gs - 1) & (kNStage - 1)) * kSlot + kScA + wn * kWN * 2;
-    // Y rows of this tile as a buffer resource: stores past its end are dropped
-    const int ynrec = min(g.M - tmc.tm * kBM, kBM) * g.ldy * 2;
-    const __amdgpu_buffer_rsrc_t yrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.ldy, 0, ynrec, kRsrcWord3);
+    if constexpr (FUSE) {
+      fused_tile(tmc.tm, tmc.tn, bslot, smem + ((gs - 1) & (kNStage - 1)) * kSlot);
+    } else {
+      // + bias (from the last low-rank slot), bf16. The accumulator lane holds
+      // token m0 + 32 i + lr and channels 32 j + 8 q + 4 h + (0..3); swapping the
+      // packed pairs (q = 1, h = 0) <-> (q = 0, h = 1) and (q = 3, h = 0) <->
+      // (q = 2, h = 1) between the lane halves leaves lane h with channels
+      // 32 j + 8 h + (0..7) and 32 j + 16 + 8 h + (0..7): two 16-byte stores,
+      // 32 contiguous bytes of one row per lane pair.
+      // Y rows of this tile as a buffer resource: stores past its end are dropped
+      const int ynrec = min(g.M - tmc.tm * kBM, kBM) * g.ldy * 2;
+      const __amdgpu_buffer_rsrc_t yrs =
+          __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)tmc.tm * kBM * g.ldy, 0, ynrec, kRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      float bv[16];
+      for (int j = 0; j < kTN; ++j) {
+        float bv[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 bw = *reinterpret_cast<const u32x2*>(bslot + (32 * j + 8 * q + 4 * h) * 2);
-        bv[4 * q + 0] = bf16lo(bw.x);
-        bv[4 * q + 1] = bf16hi(bw.x);
-        bv[4 * q + 2] = bf16lo(bw.y);
-        bv[4 * q + 3] = bf16hi(bw.y);
-      }
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        uint32_t o[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          o[p] = cvt_bf16x2(acc[j][i][2 * p] + bv[2 * p], acc[j][i][2 * p + 1] + bv[2 * p + 1]);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {   // (o[4p], o[4p+1]) is q = 2p, (o[4p+2], o[4p+3]) is q = 2p+1
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
-            o[4 * p + w] = r[0];
-            o[4 * p + 2 + w] = r[1];
-          }
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 bw = *reinterpret_cast<const u32x2*>(bslot + (32 * j + 8 * q + 4 * h) * 2);
+          bv[4 * q + 0] = bf16lo(bw.x);
+          bv[4 * q + 1] = bf16hi(bw.x);
+          bv[4 * q + 2] = bf16lo(bw.y);
+          bv[4 * q + 3] = bf16hi(bw.y);
         }
-        // always issued (the ring waits count them); the resource drops rows
-        // past M, and an 8-channel run past the layer's N is sent past the end
-        const int col = n0 + 32 * bperm(wn * kTN + j) + 8 * h;
-        const int off = ((wm * kWM + 32 * i + lr) * g.ldy + col) * 2;
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, col < g.ldy ? off : ynrec, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col + 16 < g.ldy ? off + 32 : ynrec,
-                                               0, 0);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+          uint32_t o[8];
+#pragma unroll
+          for (int p = 0; p < 8; ++p)
+            o[p] = cvt_bf16x2(acc[j][i][2 * p] + bv[2 * p], acc[j][i][2 * p + 1] + bv[2 * p + 1]);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {   // (o[4p], o[4p+1]) is q = 2p, (o[4p+2], o[4p+3]) is q = 2p+1
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto r = __builtin_amdgcn_permlane32_swap(o[4 * p + w], o[4 * p + 2 + w], false, false);
+              o[4 * p + w] = r[0];
+              o[4 * p + 2 + w] = r[1];
+            }
+          }
+          // always issued (the ring waits count them); the resource drops rows
+          // past M, and an 8-channel run past the layer's N is sent past the end
+          const int col = n0 + 32 * bperm(wn * kTN + j) + 8 * h;
+          const int off = ((wm * kWM + 32 * i + lr) * g.ldy + col) * 2;
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, yrs, col < g.ldy ? off : ynrec, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, yrs, col + 16 < g.ldy ? off + 32 : ynrec,
+                                                 0, 0);
+        }
       }
     }
     stores_due = kNStage - 1;
@@ -351,8 +514,11 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mxfp4_kernel(GemmArgs a, Geo g,
 }
 
 hipError_t prepare_gemm_mxfp4() {
-  return hipFuncSetAttribute((const void*)gemm_mxfp4_kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  const hipError_t e = hipFuncSetAttribute((const void*)gemm_mxfp4_kernel<false>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_mxfp4_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)kLds);
 }
 
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st) {
@@ -373,7 +539,10 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& a, int num_cus, hipStream_t st) {
   // persistent grid: one workgroup per CU, a multiple of 8 so each stays on its XCD's tiles
   int grid = num_cus > 0 ? num_cus : 256;
   if (grid > ntiles) grid = ntiles;
-  hipLaunchKernelGGL(gemm_mxfp4_kernel, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
+  if (a.nxt_qx != nullptr)
+    hipLaunchKernelGGL(gemm_mxfp4_kernel<true>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
+  else
+    hipLaunchKernelGGL(gemm_mxfp4_kernel<false>, dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
   return hipGetLastError();
 }
 

@@ -50,12 +50,13 @@ struct GemmArgs {
   // nullptr for the normal epilogue
   int32_t* p;
   int m0, mc, n0, nc;
-  // fused next layer (INT4 tiled kernel only; nxt_qx == nullptr otherwise):
-  // instead of Y, the epilogue writes the next layer's INT4 codes and scales
-  // of GELU(bf16(Y)) smoothed by nxt_mu (its stage-1 layout, K = this N) and
-  // the fp32 partial X_hat L1 of each 256-channel tile, [N/256][M][nxt_r32]
+  // fused next layer (tiled kernels only; nxt_qx == nullptr otherwise):
+  // instead of Y, the epilogue writes the next layer's codes and scales (its
+  // format, the same as this layer's) of GELU(bf16(Y)) smoothed by nxt_mu
+  // (its stage-1 layout, K = this N) and the fp32 partial X_hat L1 of each
+  // tile column (256 channels INT4, 384 MXFP4), [N/tile width][M][nxt_r32]
   uint8_t* nxt_qx;
-  float* nxt_sx;
+  void* nxt_sx;
   const float* nxt_mu;
   const uint16_t* nxt_l1s;   // next layer's L1 in its stage-1 layout
   float* nxt_zpart;

@@ -89,22 +89,6 @@ __device__ __forceinline__ float s1_max32(float a) {
 }
 
 
-// E2M1 codes of 8 values scaled by 2^-e, element 2i in the low nibble of byte i
-__device__ __forceinline__ uint32_t s1_e2m1x8(const float* v, int e) {
-  if (e >= -126) {   // normal scale: v_cvt_scalef32_pk_fp4_f32 divides by 2^e exactly, RNE, saturating
-    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], sc, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
-  }
-  const float sinv = exp2_neg(e);
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w |= e2m1_code(v[i] * sinv) << (4 * i);
-  return w;
-}
-
 template <int FMT, int NCB, int TH>
 __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mu, const uint16_t* __restrict__ l1s,
@@ -317,8 +301,8 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
           if (j == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsx, vsx, (cs * 4 + q) * Mp * 4, 0);
         } else {
           const int e = mx_exponent(amax);       // block b = j / 2 of the quarter
-          c0 = s1_e2m1x8(xh, e);
-          c1 = s1_e2m1x8(xh + 8, e);
+          c0 = e2m1x8_codes(xh, e);
+          c1 = e2m1x8_codes(xh + 8, e);
           if ((j & 1) == 0) {
             // fragment-order scale byte of 32-channel block kb = k0/32 + j/2:
             // stage kb/4, step (kb%4)/2, half kb%2

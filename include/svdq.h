@@ -264,9 +264,10 @@ SVDQ_API svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* desc, co
  * fuses kernels that work on the same data, to cut memory traffic
  * (aiflownews.com, "Nunchaku: the inference engine that makes SVDQuant
  * practical"); here the up layer's GEMM epilogue applies the GELU and emits
- * the down layer's kernel-(1) output directly: its smoothed INT4 codes and
- * scales and, per 256 hidden channels, the partial X_hat L1, which one small
- * kernel adds up. The hidden activation never goes to memory.
+ * the down layer's kernel-(1) output directly: its smoothed 4-bit codes and
+ * scales (INT4 or MXFP4, the pair's format) and, per tile column of hidden
+ * channels, the partial X_hat L1, which one small kernel adds up. The hidden
+ * activation never goes to memory.
  *   up: K0 -> N0, down: N0 -> N1 (down->K == up->N); x bf16 [M][K0],
  *   y bf16 [M][N1] (device, 16-byte aligned); dev_up, dev_down: packed
  *   layers on the device; workspace: >= svdq_mlp_workspace_bytes device
@@ -282,10 +283,12 @@ SVDQ_API svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* desc, co
  *   multiple of 256). The fused path's codes and scales equal the composition's bit for
  *   bit (same GELU, same quantizer); its Z differs only in the fp32 summation
  *   order of the partial X_hat L1.
- * Fused when both layers are INT4, up->N % 256 == 0, M > 256 (the tiled
- * GEMM; fewer tokens take the weight-streaming kernel, with no fused
- * epilogue) and the partial X_hat L1, (up->N / 256) M rank32(down->rank)
- * fp32 values, stays below 4 GiB. Errors: as svdq_linear_forward for either layer; SVDQ_ERR_SHAPE
+ * Fused when both layers have the same format, up->N is a whole number of
+ * the tiled GEMM's tile columns (256 channels INT4, 384 MXFP4) and of 256,
+ * M > 256 (the
+ * tiled GEMM; fewer tokens take the weight-streaming kernel, with no fused
+ * epilogue) and the partial X_hat L1, (up->N / tile width) M
+ * rank32(down->rank) fp32 values, stays below 4 GiB. Errors: as svdq_linear_forward for either layer; SVDQ_ERR_SHAPE
  * also for down->K != up->N or an unknown mode.
  * svdq_mlp_workspace_bytes: the workspace bytes for M tokens and (if
  * down_offset is not NULL) where the down layer's part starts in it.

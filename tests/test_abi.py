@@ -179,8 +179,9 @@ def test_noalloc_host_checks():
 def test_mlp_host_logic():
     """svdq_mlp_workspace_bytes / svdq_mlp_fused / svdq_mlp_forward host
     checks: the layout holds both layers' workspaces and the larger of the
-    hidden activation and the fused partial Z; the fused path needs INT4
-    layers, whole 256-channel hidden tiles and more than 256 tokens."""
+    hidden activation and the fused partial Z; the fused path needs one
+    format for both layers, whole tile columns of hidden channels and more
+    than 256 tokens."""
     up = S.Layer(3072, 12288, 32, "int4")
     down = S.Layer(12288, 3072, 32, "int4")
     M = 4608
@@ -190,8 +191,13 @@ def test_mlp_host_logic():
     assert total >= off + wd + M * 12288 * 2
     assert S.mlp_fused(up, down, M) and S.mlp_fused(up, down, 257)
     assert not S.mlp_fused(up, down, 256)
-    assert not S.mlp_fused(S.Layer(3072, 12288, 32, "mxfp4"), S.Layer(12288, 3072, 32, "mxfp4"), M)
+    assert S.mlp_fused(S.Layer(3072, 12288, 32, "mxfp4"), S.Layer(12288, 3072, 32, "mxfp4"), M)
+    # mixed formats, and hidden widths that are not whole tile columns (256 INT4, 384 MXFP4)
+    assert not S.mlp_fused(S.Layer(3072, 12288, 32, "mxfp4"), S.Layer(12288, 3072, 32, "int4"), M)
     assert not S.mlp_fused(S.Layer(3072, 12160, 32, "int4"), S.Layer(12160, 3072, 32, "int4"), M)
+    assert not S.mlp_fused(S.Layer(3072, 12544, 32, "mxfp4"), S.Layer(12544, 3072, 32, "mxfp4"), M)
+    assert not S.mlp_fused(S.Layer(3072, 1152, 32, "mxfp4"), S.Layer(1152, 3072, 32, "mxfp4"), M)
+    assert S.mlp_fused(S.Layer(3072, 1536, 32, "mxfp4"), S.Layer(1536, 3072, 32, "mxfp4"), M)
     with pytest.raises(S.SvdqError) as e:   # down K != up N
         S.mlp_workspace_bytes(up, S.Layer(3072, 3072, 32, "int4"), M)
     assert e.value.status == 2

@@ -66,6 +66,17 @@ PAIRS = [
     _pair("m1000_down_r0", 1000, 256, 768, 256, 16, 0, "int4", 72),
     # two 32-rank blocks in the fused Z, a padded up K and a padded down N
     _pair("m520_down_r64_padded", 520, 320, 512, 200, 32, 64, "int4", 74),
+    # one token past the few-token limit (the last row tile holds one live
+    # token: whole wave rows aim every store past the end), a single hidden
+    # tile column, three 32-rank blocks in the fused Z, the smallest up K
+    _pair("m257_h256_down_r96", 257, 64, 256, 128, 16, 96, "int4", 80),
+    # MXFP4 pairs (384-channel tile columns; the hidden width also whole
+    # 256-channel steps): two row tiles (the last one ragged) by two hidden
+    # tile columns; a rank-0 down layer over four columns and three row
+    # tiles; two 32-rank blocks with a padded up K and down N
+    _pair("m300_h768_fp4", 300, 512, 768, 256, 32, 32, "mxfp4", 82),
+    _pair("m500_h1536_down_r0_fp4", 500, 256, 1536, 128, 16, 0, "mxfp4", 84),
+    _pair("m260_h768_down_r64_fp4", 260, 384, 768, 200, 32, 64, "mxfp4", 86),
 ]
 
 
@@ -143,11 +154,14 @@ def test_mlp_fused_matches_composition_and_oracle(pair):
     _check_pair(up, down)
 
 
-def test_mlp_few_tokens_and_mxfp4_take_the_composition():
-    """With 256 tokens or fewer (weight-streaming GEMM) and for MXFP4 layers
-    the automatic mode runs the composition: the same bits as mode UNFUSED."""
+def test_mlp_few_tokens_and_partial_columns_take_the_composition():
+    """With 256 tokens or fewer (weight-streaming GEMM), and with a hidden
+    width that is not whole tile columns (384 channels for MXFP4) or whole
+    256-channel steps (1152), the automatic mode runs the composition: the
+    same bits as mode UNFUSED."""
     for name, up, down in (_pair("m256", 256, 512, 512, 256, 32, 32, "int4", 76),
-                           _pair("m300_fp4", 300, 512, 512, 256, 32, 32, "mxfp4", 78)):
+                           _pair("m300_h512_fp4", 300, 512, 512, 256, 32, 32, "mxfp4", 78),
+                           _pair("m300_h1152_fp4", 300, 256, 1152, 128, 16, 16, "mxfp4", 79)):
         _say(f"[mlp composition] {name}")
         lu, _ = C.library_host(up)
         ld, _ = C.library_host(down)
@@ -191,3 +205,16 @@ FULL_DOWN = next(s for s in synth.config_layers(4, small_m=False) if s.name == "
 def test_mlp_full_size_sampled():
     _say(f"[mlp full] {FULL_UP} -> {FULL_DOWN}")
     _check_pair(FULL_UP, FULL_DOWN, rows=C.sample_rows(FULL_UP.M))
+
+
+# the MXFP4 pair of the same block at one image with its text (4608 tokens):
+# the headline layer (MLP up, 3072 -> 12288) followed by its down layer
+FP4_UP = synth.config_layers(2)[0]
+FP4_DOWN = synth.LayerSpec("mlp_down_fp4", 4608, 12288, 3072, 32, "mxfp4", 3, x_kind="gelu",
+                           x_outlier_frac=0.005, x_outlier_scale=30.0, w_outlier_frac=0.0)
+
+
+@pytest.mark.slow
+def test_mlp_full_size_mxfp4_sampled():
+    _say(f"[mlp full fp4] {FP4_UP} -> {FP4_DOWN}")
+    _check_pair(FP4_UP, FP4_DOWN, rows=C.sample_rows(FP4_UP.M))
