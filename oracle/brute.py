@@ -87,7 +87,8 @@ def mx_block(vals):
 
 
 def bf16_round(v: float) -> float:
-    """Nearest bf16 value of a real, ties to even (8 significant bits)."""
+    """Nearest bf16 value of a real, ties to even (8 significant bits from
+    2^-126 up; below it the subnormals, spaced 2^-133)."""
     if v == 0.0:
         return 0.0
     e = math.floor(math.log2(abs(v)))
@@ -95,7 +96,7 @@ def bf16_round(v: float) -> float:
         e -= 1
     while 2.0 ** (e + 1) <= abs(v):
         e += 1
-    ulp = 2.0 ** (e - 7)
+    ulp = 2.0 ** (max(e, -126) - 7)
     q = _rne_half_even(v / ulp)
     return q * ulp
 

@@ -61,12 +61,17 @@ E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # index == code 
 # bf16 keeps the top 16 bits of the IEEE binary32 pattern.
 # ----------------------------------------------------------------------------
 def to_bf16(a) -> np.ndarray:
-    """Round real values (float64 or float32) to the nearest bf16 (8 significant
-    bits), ties to even, in one rounding; returns float32 holding the bf16 value.
-    v = f * 2^E with f in [0.5, 1): bf16(v) = rint(f * 2^8) * 2^(E-8), exact in float64."""
+    """Round real values (float64 or float32) to the nearest bf16, ties to even,
+    in one rounding; returns float32 holding the bf16 value. bf16 has float32's
+    exponent range with 7 fraction bits: 8 significant bits down to 2^-126, then
+    gradual underflow with a fixed spacing of 2^-133 (the subnormals).
+    v = f * 2^E with f in [0.5, 1): the spacing is 2^q with q = max(E - 8, -133),
+    and bf16(v) = rint(v / 2^q) * 2^q, exact in float64 (values past the largest
+    bf16 by half a spacing become inf in the float32 cast)."""
     v = np.asarray(a, dtype=np.float64)
-    f, E = np.frexp(v)
-    return (np.rint(f * 256.0) * np.exp2(E.astype(np.float64) - 8.0)).astype(np.float32)
+    _, E = np.frexp(v)
+    q = np.maximum(E.astype(np.float64) - 8.0, -133.0)
+    return (np.rint(v * np.exp2(-q)) * np.exp2(q)).astype(np.float32)
 
 
 def bf16_from_bits(bits) -> np.ndarray:

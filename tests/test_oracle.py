@@ -62,6 +62,31 @@ def test_brute_bf16_round_matches():
     assert O.to_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
 
 
+def test_bf16_round_bits_every_exponent():
+    """to_bf16 of float32 values equals round-to-nearest-even of the float32 bit
+    pattern to its top 16 bits (integer arithmetic on the bits, a separate
+    formulation that holds for subnormals and at the overflow edge): over every
+    bf16 value, the midpoints between neighbours and random patterns, including
+    the subnormals below 2^-126, whose spacing is 2^-133."""
+    rng = np.random.default_rng(4)
+    hi = np.arange(0, 0x7F80, dtype=np.uint32)                # every finite positive bf16
+    pats = np.concatenate([hi << 16, (hi << 16) | 0x8000, (hi << 16) | 0x7FFF, (hi << 16) | 0x8001,
+                           rng.integers(0, 0x7F800000, 200000, dtype=np.uint32)])
+    pats = np.concatenate([pats, pats | 0x80000000])
+    u = pats.astype(np.uint64)
+    want = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+    got = O.to_bf16(pats.view(np.float32))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # the smallest subnormal, its half (a tie: to zero) and the largest subnormal
+    assert O.to_bf16(np.array([2.0 ** -133]))[0] == np.float32(2.0 ** -133)
+    assert O.to_bf16(np.array([2.0 ** -134]))[0] == 0.0
+    assert O.to_bf16(np.array([3 * 2.0 ** -135]))[0] == np.float32(2.0 ** -133)
+    assert O.to_bf16(np.array([127 * 2.0 ** -133]))[0] == np.float32(127 * 2.0 ** -133)
+    v = rng.standard_normal(2000) * np.exp2(rng.integers(-140, -120, 2000))
+    ref = np.array([brute.bf16_round(float(t)) for t in v], dtype=np.float64)
+    assert np.array_equal(O.to_bf16(v).astype(np.float64), ref)
+
+
 # --------------------------------------------------------------------------
 # quantizer definitions: ties, ranges, error bounds, scale invariance
 # --------------------------------------------------------------------------
@@ -99,6 +124,53 @@ def test_int4_exact_quotient_not_float_division():
         if found >= 3:
             break
     assert found >= 1
+
+
+def subnormal_tie_pairs(limit: int = 64):
+    """bf16 pairs (amax, v) whose INT4 scale s = fl32(amax / 7) is subnormal and
+    for which v - (k + 1/2) s is exactly +-2^-150 (k = floor(v / s)): the
+    quotient lies as close to a half-integer as these scales allow. Found by
+    walking the bf16 values below 2^-120 with exact rational arithmetic."""
+    from fractions import Fraction
+    bits = np.arange(1, 0x0780, dtype=np.uint32) << 16           # positive bf16 below 2^-120
+    vals = bits.view(np.float32)
+    pairs = []
+    for amax in vals:
+        s = np.float32(amax / np.float32(7.0))
+        if s == 0 or s >= np.float32(2.0 ** -125):
+            continue
+        S = Fraction(float(s))
+        for k in range(7):
+            mid = (k + Fraction(1, 2)) * S
+            b = int(np.array([O.to_bf16(np.array([float(mid)], np.float32))[0]], np.float32).view(np.uint32)[0]) >> 16
+            for cb in (max(b - 1, 0), b, b + 1):         # the bf16 values around (k + 1/2) s
+                c = np.array([cb << 16], np.uint32).view(np.float32)[0]
+                if 0 < c <= amax and abs(Fraction(float(c)) - mid) == Fraction(1, 2 ** 150):
+                    pairs.append((np.float32(amax), np.float32(c)))
+        if len(pairs) >= limit:
+            break
+    return sorted(set(pairs))
+
+
+def test_int4_subnormal_scales_exact():
+    # subnormal scales: RNE of the exact quotient, checked with rationals, at
+    # the pairs whose quotient is closest to a half-integer
+    from fractions import Fraction
+    pairs = subnormal_tie_pairs()
+    assert len(pairs) >= 16
+    ups = downs = 0
+    for amax, v in pairs:
+        g = np.zeros(64, np.float32)
+        g[0], g[1], g[2] = amax, v, -v
+        q, s = O.quant_int4_rows(g[None, :])
+        assert s[0, 0] == np.float32(amax / np.float32(7.0)) and s[0, 0] < 2.0 ** -126
+        e = Fraction(float(v)) / Fraction(float(s[0, 0]))
+        k = int(e)
+        want = k + 1 if e - k > Fraction(1, 2) else k
+        assert q[0, 1] == want and q[0, 2] == -want, (amax, v)
+        ups += want == k + 1
+        downs += want == k
+    assert ups > 0 and downs > 0
 
 
 def test_int4_ranges_and_error_bound():
