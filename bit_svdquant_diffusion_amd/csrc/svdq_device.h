@@ -44,9 +44,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Exact INT4 code of x_hat for a group with scale s = fl32(amax/7) > 0: round
 // half to even of the exact quotient x_hat/s, clamped to [-7, 7]. The code is
-// counted from the signs of |x_hat| - (k + 1/2) s, each an exactly-signed
-// fused multiply-add (the product (k + 1/2) s is exact inside it). Used when a
-// rounded quotient lies too close to a half-integer to be trusted.
+// counted from the signs of |x_hat| - (k + 1/2) s, each a fused multiply-add
+// (the product (k + 1/2) s is exact inside it) whose sign is exact as long as
+// a nonzero difference cannot round to zero: the caller brings tiny operands
+// into the normal range first.
 __device__ __forceinline__ int q_int4_slow(float xh, float s) {
   float a = fabsf(xh);
   int q = 0;
@@ -165,14 +166,19 @@ __device__ __forceinline__ void int4_codes16(const float (&xh)[16], float sc, ui
     c1 |= (__float_as_uint(u1) & 15u) << (4 * e);
   }
   if (!(sc >= 0x1p-100f)) {
-    // zero and tiny scales (rcp out of range): one comparison per level
+    // zero and tiny scales (rcp out of range): one comparison per level, on
+    // the values and the scale times 2^100 (exact: |x_hat| < 7.5 s). Below
+    // about 2^-125 the unscaled |x_hat| - (k + 1/2) s can be 2^-150, which
+    // rounds to zero and would read as a tie; scaled, every nonzero
+    // difference stays far above the smallest float.
     c0 = 0;
     c1 = 0;
     if (sc > 0.f) {
+      const float su = sc * 0x1p100f;
 #pragma unroll 1
       for (int e = 0; e < 8; ++e) {
-        c0 |= ((uint32_t)q_int4_slow(xh[e], sc) & 15u) << (4 * e);
-        c1 |= ((uint32_t)q_int4_slow(xh[8 + e], sc) & 15u) << (4 * e);
+        c0 |= ((uint32_t)q_int4_slow(xh[e] * 0x1p100f, su) & 15u) << (4 * e);
+        c1 |= ((uint32_t)q_int4_slow(xh[8 + e] * 0x1p100f, su) & 15u) << (4 * e);
       }
     }
   } else if (dmax > 0.49999f) {
