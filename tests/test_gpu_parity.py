@@ -429,14 +429,16 @@ def test_stage1_quantizer_tie_points(fmt):
     assert np.array_equal(got["scales"], sx), "activation scales at tie points"
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
-def test_stage1_tiny_blocks(fmt):
-    """Codes and scales bit-exact with the oracle for groups (blocks) whose
-    maximum lies between the smallest bf16 subnormal and 2^-90: INT4 scales
-    below 2^-100 take the per-level comparison (subnormal scales included),
-    MXFP4 blocks whose shared exponent clamps at -127 take the software E2M1
-    encoder, and those at -126 the converter with the smallest normal scale."""
-    _say(f"[stage1 tiny] {fmt}")
+@pytest.mark.parametrize("fmt,regime", [("int4", "tiny"), ("mxfp4", "tiny"), ("int4", "huge"), ("mxfp4", "huge")])
+def test_stage1_extreme_blocks(fmt, regime):
+    """Codes and scales bit-exact with the oracle for groups (blocks) at the
+    ends of the bf16 range. tiny: maxima between the smallest bf16 subnormal
+    and 2^-90; INT4 scales below 2^-100 take the per-level comparison
+    (subnormal scales included), MXFP4 blocks whose shared exponent clamps at
+    -127 take the software E2M1 encoder, and those at -126 the converter with
+    the smallest normal scale. huge: maxima up to about 2^121 (INT4 scales
+    up to about 2^118, MXFP4 exponents up to 118)."""
+    _say(f"[stage1 extreme] {fmt} {regime}")
     K, N, r, M = 512, 64, 16, 48
     layer = S.Layer(K, N, r, fmt)
     rng = np.random.default_rng(11)
@@ -446,17 +448,24 @@ def test_stage1_tiny_blocks(fmt):
     host = S.quantize_residual(layer, w, None, np.ones(K, np.float32), l1, l2)
     dev = S.to_device(layer, host, "cuda")
     base = _tie_rows(fmt, K, M).astype(np.float64)   # ties, neighbours, saturation, zeros
-    shift = -(100 + 3 * (np.arange(M) % 12))          # rows at 2^-90 down to below 2^-133
+    if regime == "tiny":
+        shift = -(100 + 3 * (np.arange(M) % 12))      # rows at 2^-90 down to below 2^-133
+    else:
+        shift = 100 + (np.arange(M) % 12)             # block maxima up to about 2^121
     xr = O.to_bf16((base * np.exp2(shift)[:, None]).astype(np.float32))
-    if fmt == "int4":
+    assert np.all(np.isfinite(xr))
+    if regime == "tiny" and fmt == "int4":
         # groups whose quotient lies 2^-150 / s from a half-integer
         from tests.test_oracle import subnormal_tie_pairs
         for i, (amax, v) in enumerate(subnormal_tie_pairs()):
-            r, g = i % M, 3 + i // M
-            xr[r, 64 * g:64 * (g + 1)] = 0.0
-            xr[r, 64 * g:64 * g + 4] = [amax, v, -v, -amax]
+            rr, g = i % M, 3 + i // M
+            xr[rr, 64 * g:64 * (g + 1)] = 0.0
+            xr[rr, 64 * g:64 * g + 4] = [amax, v, -v, -amax]
     qx, sx = O.quantize_activations(xr.astype(np.float32), fmt)
-    if fmt == "int4":
+    if regime == "huge":
+        big = sx.astype(np.float64).max() if fmt == "int4" else int(sx.max()) - 127
+        assert big > (2.0 ** 110 if fmt == "int4" else 110)
+    elif fmt == "int4":
         tiny = (sx > 0) & (sx < 2.0 ** -100)
         assert tiny.sum() > 100 and ((sx > 0) & (sx < 2.0 ** -126)).sum() > 20, "subnormal scales covered"
     else:
@@ -466,8 +475,8 @@ def test_stage1_tiny_blocks(fmt):
     S.stage1(layer, dev, x, ws)
     torch.cuda.synchronize()
     got = S.unpack_workspace(layer, M, ws.cpu().numpy())
-    assert np.array_equal(got["codes"], qx.astype(np.int8)), "activation codes of tiny groups"
-    assert np.array_equal(got["scales"], sx), "activation scales of tiny groups"
+    assert np.array_equal(got["codes"], qx.astype(np.int8)), f"activation codes of {regime} groups"
+    assert np.array_equal(got["scales"], sx), f"activation scales of {regime} groups"
 
 
 # ----------------------------------------------------------------------------
