@@ -481,7 +481,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); the layer shards over tokens with no exchange, see the "
               f"design notes. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
