@@ -29,9 +29,6 @@
 namespace svdq {
 
 namespace {
-// groups loaded ahead of the one being multiplied (fewer with more token blocks: registers)
-__host__ __device__ constexpr int kPD(int mb) { return mb <= 2 ? 4 : (mb <= 4 ? 2 : 1); }
-
 
 // int8 operands of one 32-channel half of a group: 16*q of the even channels
 // (lo) and of the odd channels (hi) of a 16-byte fragment
