@@ -41,9 +41,13 @@ size_t awq_lds_bytes(int K, int rows) {
   return (size_t)rows * (K + kAwqPadK) * 2 + (size_t)(K / 128) * 16 * 4 + (size_t)kAwqWaves * 4 * 64 * 4;
 }
 
+// NB >= 4 runs when the staged rows hold one workgroup per CU: two waves per
+// SIMD, so it takes their registers and stages six items per thread at a
+// time; the others keep four waves per SIMD and stage one at a time.
 template <int NB>
-__global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(4))) void awq_kernel(AwqArgs a) {
+__global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 2 : 4))) void awq_kernel(AwqArgs a) {
   constexpr int KP = kAwqWaves / NB;   // waves (K parts) per n-block
+  constexpr int kAwqStage = NB >= 4 ? 6 : 1;   // staging items per thread with their loads in flight together
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K, G = K / 128, ldx = K + kAwqPadK;
   const int rows = min(16, a.M);   // rows of x_hat staged at once
@@ -82,16 +86,14 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
     }
     // x_hat of the live rows, eight channels a thread; the sixteen threads of
     // a 128-channel group (consecutive lanes) then add their partial sums of
-    // the bf16 values in a fixed butterfly order into S
-    for (int i0 = 0; i0 < rc * (K / 8); i0 += 64 * kAwqWaves) {
-      const int i = i0 + tid;
-      const bool in = i < rc * (K / 8);
+    // the bf16 values in a fixed butterfly order into S. With many rows
+    // (NB >= 4) a thread's items go in batches of kAwqStage whose loads are
+    // all issued before any is used, so a batch costs one memory round trip.
+    const int items = rc * (K / 8);
+    auto stage_item = [&](int i, bool in, const u32x4& xv, const f32x4& s0, const f32x4& s1) {
       const int t = in ? i / (K / 8) : 0, k = in ? (i - t * (K / 8)) * 8 : 0;
       float part = 0.f;
       if (in) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + t) * K + k);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.inv_s + k);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.inv_s + k + 4);
         u32x4 o;
         o[0] = cvt_bf16x2(bf16lo(xv[0]) * s0[0], bf16hi(xv[0]) * s0[1]);
         o[1] = cvt_bf16x2(bf16lo(xv[1]) * s0[2], bf16hi(xv[1]) * s0[3]);
@@ -104,13 +106,64 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
           part += bf16hi(o[d]);
         }
       }
-      // i0 and the group's first thread are multiples of 16: a group's
+      // i and the group's first thread are multiples of 16 apart: a group's
       // sixteen threads are lanes 16 j .. 16 j + 15 of one wave
       part += __shfl_xor(part, 8, 16);
       part += __shfl_xor(part, 4, 16);
       part += __shfl_xor(part, 2, 16);
       part += __shfl_xor(part, 1, 16);
       if (in && (i & 15) == 0) sxg[(k / 128) * 16 + t] = part;
+    };
+    auto item_src = [&](int i, int& t, int& k) {
+      t = i < items ? i / (K / 8) : 0;
+      k = i < items ? (i - t * (K / 8)) * 8 : 0;
+    };
+    if constexpr (kAwqStage == 1) {
+      for (int i0 = 0; i0 < items; i0 += 64 * kAwqWaves) {
+        const int i = i0 + tid;
+        const bool in = i < items;
+        const int t = in ? i / (K / 8) : 0, k = in ? (i - t * (K / 8)) * 8 : 0;
+        float part = 0.f;
+        if (in) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + t) * K + k);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.inv_s + k);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.inv_s + k + 4);
+          u32x4 o;
+          o[0] = cvt_bf16x2(bf16lo(xv[0]) * s0[0], bf16hi(xv[0]) * s0[1]);
+          o[1] = cvt_bf16x2(bf16lo(xv[1]) * s0[2], bf16hi(xv[1]) * s0[3]);
+          o[2] = cvt_bf16x2(bf16lo(xv[2]) * s1[0], bf16hi(xv[2]) * s1[1]);
+          o[3] = cvt_bf16x2(bf16lo(xv[3]) * s1[2], bf16hi(xv[3]) * s1[3]);
+          *reinterpret_cast<u32x4*>(xs + (size_t)t * ldx + k) = o;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            part += bf16lo(o[d]);
+            part += bf16hi(o[d]);
+          }
+        }
+        part += __shfl_xor(part, 8, 16);
+        part += __shfl_xor(part, 4, 16);
+        part += __shfl_xor(part, 2, 16);
+        part += __shfl_xor(part, 1, 16);
+        if (in && (i & 15) == 0) sxg[(k / 128) * 16 + t] = part;
+      }
+    } else {
+      for (int i0 = 0; i0 < items; i0 += 64 * kAwqWaves * kAwqStage) {
+        u32x4 xv[kAwqStage];
+        f32x4 s0[kAwqStage], s1[kAwqStage];
+#pragma unroll
+        for (int b = 0; b < kAwqStage; ++b) {   // out-of-range items load row 0 (in bounds, unused)
+          int t, k;
+          item_src(i0 + b * 64 * kAwqWaves + tid, t, k);
+          xv[b] = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + t) * K + k);
+          s0[b] = *reinterpret_cast<const f32x4*>(a.inv_s + k);
+          s1[b] = *reinterpret_cast<const f32x4*>(a.inv_s + k + 4);
+        }
+#pragma unroll
+        for (int b = 0; b < kAwqStage; ++b) {
+          const int i = i0 + b * 64 * kAwqWaves + tid;
+          stage_item(i, i < items, xv[b], s0[b], s1[b]);
+        }
+      }
     }
     __syncthreads();
 
@@ -165,7 +218,9 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
 
 hipError_t prepare_awq() {
   const int most = (int)awq_lds_bytes(4096, 16);
-  hipError_t e = hipFuncSetAttribute((const void*)awq_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
+  hipError_t e = hipFuncSetAttribute((const void*)awq_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)awq_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)awq_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, most);
   if (e != hipSuccess) return e;
@@ -177,7 +232,8 @@ hipError_t prepare_awq() {
 // n-block up to two per CU, two above. Measured on the FLUX shapes (graph
 // replays): 576 n-blocks 9.7 us with one, 8.9 with two; 1152 n-blocks 15.7,
 // 13.8 and 15.2 with one, two and four; 384 n-blocks the same with any.
-// When the LDS holds one workgroup per CU (16-row chunks), four n-blocks.
+// When the LDS holds one workgroup per CU (16-row chunks), four n-blocks, or
+// eight where four would leave workgroups for a second round on the CUs.
 hipError_t launch_awq(const AwqArgs& a, int num_cus, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int cus = num_cus > 0 ? num_cus : 256, nblk = a.N / 16;
@@ -187,8 +243,10 @@ hipError_t launch_awq(const AwqArgs& a, int num_cus, hipStream_t st) {
     hipLaunchKernelGGL(awq_kernel<1>, dim3(nblk), dim3(64 * kAwqWaves), lds, st, a);
   } else if (two_per_cu) {
     hipLaunchKernelGGL(awq_kernel<2>, dim3((nblk + 1) / 2), dim3(64 * kAwqWaves), lds, st, a);
-  } else {
+  } else if (nblk <= 4 * cus) {
     hipLaunchKernelGGL(awq_kernel<4>, dim3((nblk + 3) / 4), dim3(64 * kAwqWaves), lds, st, a);
+  } else {
+    hipLaunchKernelGGL(awq_kernel<8>, dim3((nblk + 7) / 8), dim3(64 * kAwqWaves), lds, st, a);
   }
   return hipGetLastError();
 }

@@ -29,6 +29,7 @@ CASES = synth.awq_layers() + [
     _spec("awq_m17_k4096_n48", 17, 4096, 48, 41),      # two token chunks, the largest K
     _spec("awq_m33_k1024_n2064", 33, 1024, 2064, 42),  # three chunks, 129 n-blocks
     _spec("awq_m5_k3072_n8208", 5, 3072, 8208, 43),    # two n-blocks a workgroup, a partial last one
+    _spec("awq_m16_k3072_n16464", 16, 3072, 16464, 44),  # eight n-blocks a workgroup, a partial last one
 ]
 
 
