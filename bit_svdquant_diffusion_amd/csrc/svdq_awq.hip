@@ -47,6 +47,7 @@ size_t awq_lds_bytes(int K, int rows) {
 template <int NB>
 __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 2 : 4))) void awq_kernel(AwqArgs a) {
   constexpr int KP = kAwqWaves / NB;   // waves (K parts) per n-block
+  static_assert(KP == 1 || KP == 2 || KP == 4 || KP == 8, "eight parts split evenly over the K parts");
   constexpr int kAwqStage = NB >= 4 ? 6 : 1;   // staging items per thread with their loads in flight together
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K, G = K / 128, ldx = K + kAwqPadK;
@@ -167,7 +168,49 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
 
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The groups fall into eight fixed parts (part q: groups [G q / 8,
+    // G (q + 1) / 8)), each summed from zero, and the parts are added as a
+    // balanced binary tree: a wave owns 8 / KP whole parts and builds their
+    // subtree, the K-part reduction below adds the waves' subtrees as the
+    // upper levels. So the sums associate the same way for any KP, and a
+    // row's output does not depend on how many rows the launch had. The
+    // pending left siblings sit in s0, s1, s2 (four or eight parts, the
+    // instances with 256 registers), or, with two parts, the first one in
+    // the wave's own slot of the reduction area (registers are short there).
+    constexpr int kParts = 8 / KP;   // parts of this wave
+    const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = z4, s0 = z4, s1 = z4, s2 = z4;
+    float* myred = red + wave * 4 * 64 + lane;   // [e * 64]
+    int q = 0;   // parts of this wave finished
+    auto part_end = [&](int qq) { return G * (kParts * kp + qq + 1) / 8; };
+    const int pe0 = part_end(0);
+    auto finish_parts = [&](int gn) {   // close every part that ends at or before group gn
+      if constexpr (kParts == 1) {
+        return;   // one part: acc is the wave's sum
+      } else if constexpr (kParts == 2) {
+        if (gn == pe0) {   // the first part ends here: called at g0, then after each group (gn > g0), so once
+#pragma unroll
+          for (int e = 0; e < 4; ++e) myred[e * 64] = acc[e];
+          acc = z4;
+        }
+        return;
+      }
+      while (q < kParts && part_end(q) <= gn) {
+        switch (q) {
+          case 0: s0 = acc; break;
+          case 1: s1 = s0 + acc; break;
+          case 2: s0 = acc; break;
+          case 3: s1 = s1 + (s0 + acc); break;
+          case 4: s0 = acc; break;
+          case 5: s2 = s0 + acc; break;
+          case 6: s0 = acc; break;
+          default: s1 = s1 + (s2 + (s0 + acc)); break;
+        }
+        acc = z4;
+        ++q;
+      }
+    };
+    finish_parts(g0);
     const bool arow = r < rc;   // this lane's MFMA row is a live token
     for (int gb = g0; gb < g1; gb += kAwqRing) {
 #pragma unroll
@@ -194,21 +237,33 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
           if (g + kAwqRing < g1) load(u, g + kAwqRing);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(scu, __builtin_fmaf(-zf, s4[e], p[e]), acc[e]);
+          finish_parts(g + 1);
         }
       }
     }
-    // the K parts' sums in K-part order, + bias, bf16 out
+    if constexpr (kParts == 2) {
+      // the second part ends at g1: its sum is acc
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[(wave * 4 + e) * 64 + lane] = acc[e];
+      for (int e = 0; e < 4; ++e) s1[e] = myred[e * 64] + acc[e];
+    } else {
+      finish_parts(g1);   // the last parts, empty ones included
+    }
+    const f32x4 mine = kParts == 1 ? acc : s1;   // this wave's subtree
+    // the waves' subtrees as the tree's upper levels, + bias, bf16 out
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(wave * 4 + e) * 64 + lane] = mine[e];
     __syncthreads();
     if (kp == 0 && live) {
       const int n = nb * 16 + r;
       const float bv = __uint_as_float((uint32_t)a.bias[n] << 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < KP; ++k2) s += red[((nbl + NB * k2) * 4 + e) * 64 + lane];
+        auto rk = [&](int k2) { return red[((nbl + NB * k2) * 4 + e) * 64 + lane]; };
+        float s;
+        if constexpr (KP == 1) s = rk(0);
+        else if constexpr (KP == 2) s = rk(0) + rk(1);
+        else if constexpr (KP == 4) s = (rk(0) + rk(1)) + (rk(2) + rk(3));
+        else s = ((rk(0) + rk(1)) + (rk(2) + rk(3))) + ((rk(4) + rk(5)) + (rk(6) + rk(7)));
         const int m = t0 + 4 * c + e;
         if (m < a.M) a.y[(size_t)m * a.N + n] = (uint16_t)f2bf(s + bv);
       }
