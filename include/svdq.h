@@ -458,9 +458,11 @@ SVDQ_API svdq_status svdq_awq_unpack(const svdq_awq_desc* desc, const svdq_awq_p
 /*
  * Runtime forward on the GPU: y bf16 [M][N] = layer(x bf16 [M][K]), one
  * kernel on hip_stream. x_hat = fl32(x inv_s) is rounded to bf16 for the
- * bf16 MFMA; sums in fp32. Built for a few rows (it streams the weights once
- * per 16 rows). No workspace, nothing allocated. Device pointers 16-byte
- * aligned. Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_DEVICE.
+ * bf16 MFMA; sums in fp32, in an order fixed by K alone, so a row's output
+ * is the same bits whatever M and the other rows are. Built for a few rows
+ * (it streams the weights once per 16 rows). No workspace, nothing
+ * allocated. Device pointers 16-byte aligned. Errors: SVDQ_ERR_NULL,
+ * SVDQ_ERR_SHAPE, SVDQ_ERR_DEVICE.
  */
 SVDQ_API svdq_status svdq_awq_forward(const svdq_awq_desc* desc, const svdq_awq_packed* dev, const uint16_t* x,
                                       int64_t M, uint16_t* y, void* hip_stream);
