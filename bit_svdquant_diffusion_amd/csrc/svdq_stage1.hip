@@ -5,8 +5,8 @@
 //   - per-token 4-bit quantization of x_hat (INT4 per 64 channels, or MXFP4
 //     per 32 channels);
 //   - the low-rank down-projection Z = x_hat L1 on bf16 MFMA, with x_hat
-//     rounded to bf16 ("the low rank branch held at higher precision such as
-//     16 bit"; the branches "share inputs", same page).
+//     rounded to bf16 (same page: the low-rank branch stays in a 16-bit
+//     format, and both branches read the same smoothed input).
 //
 // Work split: a workgroup owns 16 TH tokens (TH = 1 or 2 halves of 16) and
 // walks K in steps of 256 channels; wave w = 4 th + q takes the 64-channel
