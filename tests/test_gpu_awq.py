@@ -55,8 +55,14 @@ def test_awq_forward_matches_oracle(spec):
     C.check_y(C.bf16_tensor_to_f32(y), A.forward(ref, lay.x), f"awq {spec.name} alpha={al}")
 
 
-def test_awq_deterministic_and_m0():
-    spec = CASES[-1]
+@pytest.mark.parametrize("name", ["awq_m16_k3072_n16464", "awq_m17_k4096_n48"])
+def test_awq_deterministic_and_m0(name):
+    """Repeat calls give the same bits, M = 0 is a no-op, and a row's output
+    does not depend on the rows launched with it: one row alone (a one- or
+    two-block launch, K in eight or four parts per wave set) against the same
+    rows inside 16-row chunks (eight and four blocks a workgroup), bit for
+    bit, including the 17th row that forms a chunk of its own."""
+    spec = next(s for s in CASES if s.name == name)
     lay, host, ref, _ = _packed(spec, alpha=0.5)
     dev = S.awq_to_device(host)
     x = torch.from_numpy(lay.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
@@ -65,7 +71,7 @@ def test_awq_deterministic_and_m0():
     y0 = S.awq_forward(spec.K, spec.N, dev, x[:0])
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and y0.shape == (0, spec.N)
-    # a row's output does not depend on the other rows of its chunk
-    y3 = S.awq_forward(spec.K, spec.N, dev, x[2:3].contiguous())
-    torch.cuda.synchronize()
-    assert torch.equal(y3.view(torch.int16), y1[2:3].view(torch.int16))
+    for row in (2, spec.M - 1):
+        y3 = S.awq_forward(spec.K, spec.N, dev, x[row:row + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(y3.view(torch.int16), y1[row:row + 1].view(torch.int16)), row
