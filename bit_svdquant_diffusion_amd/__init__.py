@@ -21,7 +21,7 @@ __all__ = [
     "SVDQLinear", "EXPORTED_SYMBOLS", "Layer", "measure_mfma_peak", "measure_copy",
     "awq_packed_bytes", "awq_pack", "awq_unpack", "awq_to_device", "awq_forward",
     "pack_weights_gpu", "calibrate_alpha", "to_host", "mlp_workspace_bytes", "mlp_fused", "mlp_forward",
-    "MLP_AUTO", "MLP_UNFUSED",
+    "MLP_AUTO", "MLP_UNFUSED", "stage1_outputs",
 ]
 
 FMT_INT4 = 0
@@ -34,7 +34,7 @@ _LIB_NAME = "libsvdq.so"
 EXPORTED_SYMBOLS = [
     "svdq_status_string", "svdq_version", "svdq_packed_bytes", "svdq_pack_weights",
     "svdq_quantize_residual", "svdq_unpack_weights", "svdq_workspace_bytes",
-    "svdq_linear_forward", "svdq_stage1", "svdq_unpack_workspace",
+    "svdq_linear_forward", "svdq_stage1", "svdq_stage1_outputs", "svdq_unpack_workspace",
     "svdq_debug_int4_group_sums", "svdq_gemm", "svdq_linear_forward_noalloc", "svdq_lora_extend",
     "svdq_measure_mfma_peak", "svdq_measure_copy",
     "svdq_awq_packed_bytes", "svdq_awq_pack", "svdq_awq_unpack", "svdq_awq_forward",
@@ -130,6 +130,7 @@ def lib() -> ctypes.CDLL:
         "svdq_linear_forward": [D, P(Packed), vp, i64, vp, vp, sz, vp],
         "svdq_linear_forward_noalloc": [D, P(Packed), vp, i64, vp, vp],
         "svdq_stage1": [D, P(Packed), vp, i64, vp, sz, vp],
+        "svdq_stage1_outputs": [D, P(Packed), vp, i64, vp, vp, vp, vp, sz, vp],
         "svdq_gemm": [D, P(Packed), vp, sz, i64, vp, vp],
         "svdq_unpack_workspace": [D, i64, vp, sz, vp, vp, vp],
         "svdq_debug_int4_group_sums": [D, P(Packed), vp, sz, i64, i64, i64, i64, i64, vp, vp],
@@ -368,6 +369,35 @@ def stage1(layer: Layer, dev: dict, x, workspace=None, stream=None):
     _check(lib().svdq_stage1(ctypes.byref(d), ctypes.byref(p), _ptr(x), M, _ptr(workspace),
                              workspace.numel(), _stream(stream)), "svdq_stage1")
     return workspace
+
+
+def stage1_outputs(layer: Layer, dev: dict, x, workspace=None, codes=None, scales=None, z=None,
+                   stream=None) -> dict:
+    """Kernel (1) with its outputs in logical layouts as device tensors:
+    codes int8 [M][K], scales float32 [M][K/64] (INT4) or uint8 [M][K/32]
+    (MXFP4), z float32 [M][rank]; allocated here unless given."""
+    import torch
+    M = x.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(layer, M), 1), dtype=torch.uint8, device=x.device)
+    g = 64 if layer.fmt == "int4" else 32
+    if codes is None:
+        codes = torch.empty((M, layer.K), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, layer.K // g), dtype=torch.float32 if layer.fmt == "int4" else torch.uint8,
+                             device=x.device)
+    if z is None:
+        z = torch.empty((M, layer.rank), dtype=torch.float32, device=x.device)
+    assert codes.shape == (M, layer.K) and codes.dtype == torch.int8 and codes.is_contiguous()
+    assert scales.shape == (M, layer.K // g) and scales.is_contiguous()
+    assert scales.dtype == (torch.float32 if layer.fmt == "int4" else torch.uint8)
+    assert z.shape == (M, layer.rank) and z.dtype == torch.float32 and z.is_contiguous()
+    p = _packed_struct(layer, dev)
+    d = layer.desc
+    _check(lib().svdq_stage1_outputs(ctypes.byref(d), ctypes.byref(p), _ptr(x), M, _ptr(codes), _ptr(scales),
+                                     _ptr(z) if layer.rank else None, _ptr(workspace), workspace.numel(),
+                                     _stream(stream)), "svdq_stage1_outputs")
+    return {"codes": codes, "scales": scales, "z": z, "workspace": workspace}
 
 
 def gemm(layer: Layer, dev: dict, workspace, M: int, y, stream=None):

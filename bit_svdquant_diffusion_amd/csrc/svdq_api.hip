@@ -1,6 +1,7 @@
 // C-ABI entry points of libsvdq that touch the GPU: argument validation,
 // workspace carving and kernel launches on the caller's stream. No
 // allocation, no synchronization, nothing printed.
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -197,12 +198,69 @@ svdq_status after_launch(hipError_t e, hipStream_t s) {
   return SVDQ_OK;
 }
 
+// Logical views of a stage-1 workspace, the layouts of svdq_unpack_workspace:
+// codes int8 [M][K] (INT4 values, or E2M1 code bits), scales fp32 [M][K/64]
+// (INT4) or E8M0 bytes [M][K/32] (MXFP4), Z fp32 [M][rank] (its bf16 values).
+// One thread per output element over the three outputs in turn; an absent
+// output has no elements. mp = the INT4 scales' row stride, rows32 = the
+// MXFP4 scales' row blocks times 32.
+__global__ __launch_bounds__(256) void stage1_views_kernel(const uint8_t* __restrict__ qx, const void* __restrict__ sx,
+                                                           const uint16_t* __restrict__ zb, int64_t M, int K, int Kp,
+                                                           int int4, int r, int r32, int64_t mp, int64_t rows32,
+                                                           int8_t* codes, void* scales, float* z, int64_t n_codes,
+                                                           int64_t n_scales, int64_t n_z) {
+  const int64_t total = n_codes + n_scales + n_z;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < n_codes) {
+      const int64_t m = i / K;
+      const int k = (int)(i - m * K);
+      const uint8_t b = qx[f_code_byte(Kp, m, k)];
+      const int nib = (k & 1) ? (b >> 4) : (b & 15);
+      codes[i] = int4 ? (int8_t)(nib >= 8 ? nib - 16 : nib) : (int8_t)nib;
+    } else if (i < n_codes + n_scales) {
+      const int64_t j = i - n_codes;
+      const int G = int4 ? K / 64 : K / 32;
+      const int64_t m = j / G;
+      const int g = (int)(j - m * G);
+      if (int4)
+        static_cast<float*>(scales)[j] = static_cast<const float*>(sx)[(int64_t)g * mp + m];
+      else
+        static_cast<uint8_t*>(scales)[j] = static_cast<const uint8_t*>(sx)[f_scale_index(rows32, m, g)];
+    } else {
+      const int64_t j = i - n_codes - n_scales;
+      const int64_t m = j / r;
+      const int c = (int)(j - m * r);
+      z[j] = __uint_as_float((uint32_t)zb[frag16_index(r32, m, c)] << 16);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace svdq
 
 using namespace svdq;
 
 extern "C" {
+
+svdq_status svdq_stage1_outputs(const svdq_layer_desc* d, const svdq_packed* dev, const uint16_t* x, int64_t M,
+                                int8_t* codes, void* scales, float* z, void* ws, size_t ws_bytes, void* stream) {
+  svdq_status st = svdq_stage1(d, dev, x, M, ws, ws_bytes, stream);
+  if (st != SVDQ_OK || M == 0 || (!codes && !scales && !z)) return st;
+  const WsLayout L = ws_layout(d, M);
+  const bool int4 = d->format == SVDQ_FMT_INT4_G64;
+  const int64_t n_codes = codes ? M * d->K : 0;
+  const int64_t n_scales = scales ? M * (d->K / (int4 ? 64 : 32)) : 0;
+  const int64_t n_z = z ? M * d->rank : 0;
+  const int64_t total = n_codes + n_scales + n_z;
+  if (total == 0) return SVDQ_OK;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* b = (const uint8_t*)ws;
+  hipLaunchKernelGGL(stage1_views_kernel, dim3(grid), dim3(256), 0, s, b + L.qx, (const void*)(b + L.sx),
+                     (const uint16_t*)(b + L.z), M, d->K, kpad(d), int4 ? 1 : 0, d->rank, rank32(d->rank),
+                     act_rows(M), round32(M), codes, scales, z, n_codes, n_scales, n_z);
+  return after_launch(hipGetLastError(), s);
+}
 
 svdq_status svdq_stage1(const svdq_layer_desc* d, const svdq_packed* dev, const uint16_t* x,
                         int64_t M, void* ws, size_t ws_bytes, void* stream) {

@@ -314,6 +314,22 @@ SVDQ_API svdq_status svdq_stage1(const svdq_layer_desc* desc, const svdq_packed*
                         int64_t M, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Kernel (1) with its outputs in logical layouts on the device: the smoothed
+ * activations' 4-bit codes and scales and the low-rank product X_hat L1
+ * (aiflownews.com, "What SVDQuant actually does": smoothing, the 16-bit
+ * low-rank branch, 4-bit activations). Runs svdq_stage1 on the workspace
+ * (which it leaves filled), then one small kernel on the same stream writes
+ *   codes  int8 [M][K]: INT4 values in [-7,7], or E2M1 code bits 0..15
+ *   scales INT4: fp32 [M][K/64]; MXFP4: u8 [M][K/32] (E8M0 bytes)
+ *   z      fp32 [M][rank]: X_hat L1 as the GEMM uses it (bf16 values)
+ * Device pointers, each may be NULL to skip it; nothing is allocated.
+ * Errors: as svdq_stage1.
+ */
+SVDQ_API svdq_status svdq_stage1_outputs(const svdq_layer_desc* desc, const svdq_packed* dev, const uint16_t* x,
+                                         int64_t M, int8_t* codes, void* scales, float* z, void* workspace,
+                                         size_t workspace_bytes, void* hip_stream);
+
+/*
  * Kernel (2) of svdq_linear_forward alone: the 4-bit GEMM with its epilogue,
  * reading the activation codes, scales and X_hat L1 that svdq_stage1 left in
  * `workspace` for the same M. svdq_stage1 followed by svdq_gemm on one stream

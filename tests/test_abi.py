@@ -73,6 +73,7 @@ def test_null_pointers():
     # forward/stage1 validate before touching the device: null packed buffers -> NULL
     assert L.svdq_linear_forward(ctypes.byref(d), ctypes.byref(p), None, 4, None, None, 0, None) == 1
     assert L.svdq_stage1(ctypes.byref(d), None, None, 4, None, 0, None) == 1
+    assert L.svdq_stage1_outputs(ctypes.byref(d), None, None, 4, None, None, None, None, 0, None) == 1
 
 
 def test_forward_validation_before_device():

@@ -126,6 +126,48 @@ def test_stage1_codes_scales_z(spec):
         assert np.abs(d).max() <= 2e-2 * np.abs(zr).max()
 
 
+LOGICAL = [s for s in SMALL if s.name in ("c0", "c0_fp4", "ragged_m300", "ragged_m300_fp4", "m17_r0", "m17_r0_fp4",
+                                          "r128_fp4", "wide_k", "two_halves_m2100_r48_fp4", "small_m70_shares")]
+
+
+@pytest.mark.parametrize("spec", LOGICAL, ids=lambda s: s.name)
+def test_stage1_outputs_logical(spec):
+    """svdq_stage1_outputs: the device-side logical views equal the host
+    unpack of the same workspace bit for bit, and the codes and scales equal
+    the oracle's (Z within the layer's bar, being bf16 on the device). The
+    views start filled with 0x7f codes, NaN or 0xff scales and NaN Z, none of
+    which a correct view holds, so every element must have been written."""
+    _say(f"[stage1 outputs] {spec}")
+    layer, dev = C.device_layer(spec)
+    x = C.x_device(spec)
+    ws = torch.full((S.workspace_bytes(layer, spec.M),), 0xFF, dtype=torch.uint8, device="cuda")
+    g = 64 if spec.fmt == "int4" else 32
+    out = S.stage1_outputs(
+        layer, dev, x, workspace=ws,
+        codes=torch.full((spec.M, spec.K), 0x7F, dtype=torch.int8, device="cuda"),
+        scales=(torch.full((spec.M, spec.K // g), float("nan"), device="cuda") if spec.fmt == "int4"
+                else torch.full((spec.M, spec.K // g), 0xFF, dtype=torch.uint8, device="cuda")),
+        z=torch.full((spec.M, spec.rank), float("nan"), device="cuda"))
+    torch.cuda.synchronize()
+    host = S.unpack_workspace(layer, spec.M, ws.cpu().numpy())
+    codes = out["codes"].cpu().numpy()
+    scales = out["scales"].cpu().numpy()
+    assert np.array_equal(codes, host["codes"]), "codes: device view != host unpack"
+    assert np.array_equal(scales.view(np.uint8), host["scales"].view(np.uint8)), "scales: device view != host unpack"
+    ref = C.oracle_pack(spec)
+    lay = C.layer_data(spec)
+    _, parts = O.forward(ref, lay.x, return_parts=True)
+    assert np.array_equal(codes, parts["qx"].astype(np.int8)), "activation codes"
+    assert np.array_equal(scales, parts["sx"]), "activation scales"
+    if spec.rank:
+        z = out["z"].cpu().numpy()
+        assert np.array_equal(z.view(np.uint32), host["z"].astype(np.float32).view(np.uint32)), "z: view != unpack"
+        zr = parts["z"]
+        d = z - zr
+        assert np.linalg.norm(d) <= 1e-2 * np.linalg.norm(zr)
+        assert np.abs(d).max() <= 2e-2 * np.abs(zr).max()
+
+
 @pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
 def test_forward_matches_oracle(spec):
     _say(f"[forward] {spec}")
