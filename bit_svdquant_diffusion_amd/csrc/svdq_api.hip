@@ -244,6 +244,9 @@ extern "C" {
 
 svdq_status svdq_stage1_outputs(const svdq_layer_desc* d, const svdq_packed* dev, const uint16_t* x, int64_t M,
                                 int8_t* codes, void* scales, float* z, void* ws, size_t ws_bytes, void* stream) {
+  // fp32 outputs (Z, INT4 scales) need 4-byte alignment; checked before any work
+  if (d && (((uintptr_t)z & 3) || (d->format == SVDQ_FMT_INT4_G64 && ((uintptr_t)scales & 3))))
+    return SVDQ_ERR_SHAPE;
   svdq_status st = svdq_stage1(d, dev, x, M, ws, ws_bytes, stream);
   if (st != SVDQ_OK || M == 0 || (!codes && !scales && !z)) return st;
   const WsLayout L = ws_layout(d, M);

@@ -322,8 +322,9 @@ SVDQ_API svdq_status svdq_stage1(const svdq_layer_desc* desc, const svdq_packed*
  *   codes  int8 [M][K]: INT4 values in [-7,7], or E2M1 code bits 0..15
  *   scales INT4: fp32 [M][K/64]; MXFP4: u8 [M][K/32] (E8M0 bytes)
  *   z      fp32 [M][rank]: X_hat L1 as the GEMM uses it (bf16 values)
- * Device pointers, each may be NULL to skip it; nothing is allocated.
- * Errors: as svdq_stage1.
+ * Device pointers, each may be NULL to skip it; z and INT4 scales 4-byte
+ * aligned. Nothing is allocated.
+ * Errors: as svdq_stage1; SVDQ_ERR_SHAPE for a misaligned fp32 output.
  */
 SVDQ_API svdq_status svdq_stage1_outputs(const svdq_layer_desc* desc, const svdq_packed* dev, const uint16_t* x,
                                          int64_t M, int8_t* codes, void* scales, float* z, void* workspace,

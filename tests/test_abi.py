@@ -74,6 +74,9 @@ def test_null_pointers():
     assert L.svdq_linear_forward(ctypes.byref(d), ctypes.byref(p), None, 4, None, None, 0, None) == 1
     assert L.svdq_stage1(ctypes.byref(d), None, None, 4, None, 0, None) == 1
     assert L.svdq_stage1_outputs(ctypes.byref(d), None, None, 4, None, None, None, None, 0, None) == 1
+    # a misaligned fp32 output is refused before anything else
+    assert L.svdq_stage1_outputs(ctypes.byref(d), ctypes.byref(p), None, 4, None, None, ctypes.c_void_p(2), None,
+                                 0, None) == 2
 
 
 def test_forward_validation_before_device():
