@@ -220,3 +220,14 @@ def test_mlp_host_logic():
                               x.ctypes.data, 4, x.ctypes.data, ws.ctypes.data, ws.nbytes, 0, None) == 4
     assert L.svdq_mlp_forward(None, ctypes.byref(p), ctypes.byref(dd), ctypes.byref(p),
                               x.ctypes.data, 4, x.ctypes.data, ws.ctypes.data, ws.nbytes, 0, None) == 1
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without libsvdq.so the binding raises: there is no CPU fallback."""
+    monkeypatch.setattr(S, "_lib", None)
+    monkeypatch.setattr(S, "lib_path", lambda: "/nonexistent/libsvdq.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        S.lib()
+    layer = S.Layer(512, 512, 16, "int4")
+    with pytest.raises(RuntimeError, match="missing"):
+        S.workspace_bytes(layer, 64)
