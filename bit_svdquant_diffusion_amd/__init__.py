@@ -47,7 +47,7 @@ MLP_AUTO = 0
 MLP_UNFUSED = 1
 
 # bytes of the library-owned device workspace of svdq_linear_forward_noalloc
-NOALLOC_SCRATCH_BYTES = 128 << 20
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class SvdqError(RuntimeError):

@@ -70,13 +70,13 @@ svdq_status check_packed_dev(const svdq_layer_desc* d, const svdq_packed* p) {
 }
 
 // M against the layer: the token limit, and the offsets the kernels address
-// with 32 bits (MXFP4 activation scale bytes by stage, the tiled INT4 GEMM's
+// with 32 bits (MXFP4 activation scale bytes by stage, the tiled INT4 GEMM's FP6
 // activation codes by byte)
 svdq_status check_m(const svdq_layer_desc* d, int64_t M) {
   if (M < 0 || M > (1 << 24)) return SVDQ_ERR_SHAPE;
   if (d->format == SVDQ_FMT_MXFP4_G32 && ((int64_t)kpad(d) + 128) * (round32(M) / 32) >= ((int64_t)1 << 31))
     return SVDQ_ERR_SHAPE;
-  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * kpad(d) >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
+  if (d->format == SVDQ_FMT_INT4_G64 && round32(M) * kpad(d) / 4 * 3 >= ((int64_t)1 << 32)) return SVDQ_ERR_SHAPE;
   return SVDQ_OK;
 }
 
@@ -142,6 +142,8 @@ GemmArgs gemm_args(const svdq_layer_desc* d, const svdq_packed* dev, int64_t M, 
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
   a.flags = int4 ? (uint32_t*)(b + L.flags) : nullptr;
   a.part = int4 || M <= kFewTokens ? (float*)(b + L.part) : nullptr;
+  a.qx6 = int4_tiled_ws(d, M) ? (uint8_t*)(b + L.x6) : nullptr;
+  a.qw6 = int4_tiled_ws(d, M) ? (uint8_t*)(b + L.w6) : nullptr;
   return a;
 }
 
@@ -452,7 +454,7 @@ svdq_status svdq_debug_int4_group_sums(const svdq_layer_desc* d, const svdq_pack
   svdq_status st = check_desc(d);
   if (st != SVDQ_OK) return st;
   if (d->format != SVDQ_FMT_INT4_G64) return SVDQ_ERR_FORMAT;
-  if (M <= 0 || M > (1 << 24) || round32(M) * kpad(d) >= ((int64_t)1 << 33)) return SVDQ_ERR_SHAPE;
+  if (M <= 0 || check_m(d, M) != SVDQ_OK) return SVDQ_ERR_SHAPE;
   st = check_packed_dev(d, dev);
   if (st != SVDQ_OK) return st;
   if (!ws || !p) return SVDQ_ERR_NULL;

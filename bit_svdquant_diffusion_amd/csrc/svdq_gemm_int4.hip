@@ -50,29 +50,36 @@ namespace {
 constexpr int kBM = 128, kBN = 256, kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
 constexpr int kWM = kBM / kWGM, kWN = kBN / kWGN, kTM = kWM / 32, kTN = kWN / 32;
 constexpr int kMB = kBM / 32, kNBt = kBN / 32;     // 32-row blocks per tile: 4 (A), 8 (B)
-constexpr int kNStage = 4;
 constexpr int kGroupM = 8;
 constexpr int kStores = 2 * kTN * kTM;             // 16-byte Y stores per wave per tile
-// Transfers per stage: 24 fragment blocks of 1 KiB (3 per wave, from 3 w)
-// and 3 scale transfers of 1 KiB (A, then two of B) on waves 1, 2 and 3, or,
-// in low-rank stages, copies of the bias transfer. Each SIMD (waves w and
-// w + 4) issues 6 or 7 transfers per stage.
-constexpr int kFragPerWave = 3;
-__host__ __device__ constexpr int kScaleOp(int w) { return (w >= 1 && w <= 3) ? w - 1 : -1; }
-__host__ __device__ constexpr int kOpsOf(int w) { return kFragPerWave + (kScaleOp(w) >= 0 ? 1 : 0); }
-// one ring slot: A codes (4 blocks x 2 groups x 1 KiB), B codes (8 x 2 x 1 KiB),
-// A scales fp32 [2 groups][128], B scales fp32 [2 groups][256]
-constexpr int kCodeA = 0, kCodeB = kMB * 2 * 1024, kScA = kCodeB + kNBt * 2 * 1024;
+// Transfers per stage, five per wave: op o = 5 w + k (k = 0..4).
+// - 4-bit stage: ops 0..35 move the 36 FP6 fragment parts of 1 KiB (12 row
+//   blocks x [group 0 heads, group 1 heads, both groups' tails]), op 36 the A
+//   scales, ops 37 and 38 the two halves of the B scales, op 39 repeats op 38.
+// - low-rank stage: ops 0..23 move the 24 bf16 fragments of Z and L2^T
+//   (1 KiB each), the others copies of the bias transfer.
+// Every wave thus issues the same count in every stage, so the ring waits
+// have one form.
+constexpr int kOps = 5;
+constexpr int kParts4 = 3 * (kMB + kNBt);    // 4-bit fragment parts per stage
+constexpr int kPartsLr = 2 * (kMB + kNBt);   // low-rank fragments per stage
+// one ring slot: A codes (4 blocks x 3 KiB), B codes (8 x 3 KiB), A scales
+// fp32 [2 groups][128], B scales fp32 [2 groups][256]; a low-rank stage puts
+// its Z fragments at kCodeA and its L2^T fragments at kCodeB, 2 KiB per
+// block, and the bias at kScA
+constexpr int kCodeA = 0, kCodeB = kMB * 3 * 1024, kScA = kCodeB + kNBt * 3 * 1024;
 constexpr int kScB = kScA + 2 * kBM * 4, kSlot = kScB + 2 * kBN * 4;
-constexpr size_t kLds = (size_t)kNStage * kSlot;
-// FUSE: after the ring, the cross-wave sum of the next layer's partial Z: the
-// partials of all eight waves for one 32-token block and 32-rank block
+// ring slots: four, or three in the fused epilogue's launch, whose LDS also
+// holds the cross-wave sum of the next layer's partial Z (the partials of all
+// eight waves for one 32-token block and 32-rank block)
+__host__ __device__ constexpr int ring_slots(bool fuse) { return fuse ? 3 : 4; }
 constexpr size_t kZred = (size_t)kWGN * kWGM * 16 * 64 * 4;
-static_assert(kLds + kZred <= 160 * 1024, "LDS of the fused epilogue");
-static_assert(kLds + kZred <= 160 * 1024, "ring and Z reduction fit in LDS");
+constexpr size_t kLds = (size_t)ring_slots(false) * kSlot;
+constexpr size_t kLdsFuse = (size_t)ring_slots(true) * kSlot + kZred;
+static_assert(kLds <= 160 * 1024 - 256 && kLdsFuse <= 160 * 1024 - 256, "ring (and Z reduction) fit in LDS");
 static_assert(kTM == 2 && kTN == 2, "schedule below assumes 2 x 2 blocks per wave");
-static_assert(kLds <= 160 * 1024, "ring must fit in LDS");
-static_assert(kNW * kFragPerWave == 2 * (kMB + kNBt), "fragment blocks partition");
+static_assert(kNW * kOps == kParts4 + 4 && kPartsLr <= kParts4, "ops per stage partition");
+static_assert(kParts4 == (kNW - 1) * kOps + 1, "the scale ops are ops 1..4 of the last wave");
 static_assert(2 * kBM * 4 == 1024 && 2 * kBN * 4 == 2048 && kBN * 2 <= 1024,
               "one A and two B scale transfers of 64 lanes; the bias fits the A scale area");
 
@@ -110,6 +117,17 @@ __device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
     lo[d] = (int)(((uint32_t)w[d] << 4) & 0xF0F0F0F0u);
     hi[d] = (int)((uint32_t)w[d] & 0xF0F0F0F0u);
   }
+}
+
+// FP6 E2M3 field (sign, two exponent bits with bias 1, three mantissa bits)
+// of a two's-complement INT4 code nibble. The integers 1..7 are 1.0 x 2^0,
+// 1.0 x 2^1, 1.5 x 2^1, 1.0 x 2^2, 1.25 x 2^2, 1.5 x 2^2 and 1.75 x 2^2, so
+// every code is exact. The nibble 8 (-8) is never a code (codes lie in
+// [-7, 7]); it maps to -0.
+__device__ __forceinline__ uint32_t e2m3_field(uint32_t nib) {
+  constexpr uint64_t kPos = 0x1E1C1A1814100800ull;   // nibbles 0..7, one byte each, low byte first
+  constexpr uint64_t kNeg = 0x283034383A3C3E20ull;   // nibbles 8..15: -0, -7, -6, ..., -1
+  return (uint32_t)(((nib < 8 ? kPos : kNeg) >> (8 * (nib & 7))) & 0x3Fu);
 }
 
 struct Geo {
@@ -184,26 +202,27 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     }
   }
 
-  // issue side: next ring step to load (step is_s of segment is_k)
-  // and this wave's per-tile transfer sources as byte offsets from uniform
-  // bases: fragment item 3 w + k from src[k] (4-bit) and src[3 + k]
-  // (low-rank); the scale transfer from ssrc plus the stage times sstride;
-  // the bias from bsrc
-  const int frag0 = kFragPerWave * wave, sop = kScaleOp(wave);
-  const int nops = kOpsOf(wave);
+  // issue side: next ring step to load (step is_s of segment is_k), and this
+  // wave's per-tile transfer sources as byte offsets from uniform bases: op
+  // 5 w + k from src[k] in a 4-bit stage (a fragment part, or for the last
+  // wave's ops 1..4 its lane's scale entries) and from src[kOps + k] in a
+  // low-rank stage; the bias from bsrc
+  constexpr int NS = ring_slots(FUSE);
+  const int nops = kOps;
   int is_k = 0, is_s = 0, is_ka = 0, is_nk = 0, is_len = 0;   // segment, step in it, its stages
   long long is_u = u0;
-  uint32_t src[2 * kFragPerWave], ssrc = 0, bsrc = 0, sstride = 0;
+  uint32_t src[2 * kOps], bsrc = 0;
   const int per_l = a.r32 / 16;
+  const uint32_t sstr_a = 2u * g.act_rows * 4, sstr_b = 2u * g.N * 4;   // scale bytes per stage
   // every source as a buffer resource over the whole operand: a transfer is
   // one buffer load into LDS with the lane's 32-bit offset and the stage as
-  // a scalar offset (the API keeps the codes below 4 GiB)
+  // a scalar offset (the API keeps the FP6 activation codes below 4 GiB)
   auto rsrc = [](const void* p, uint64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)(uint32_t)min(bytes, (uint64_t)0xFFFFFFFFu),
                                              0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t rqx = rsrc(a.qx, (uint64_t)g.MB * g.KS * 1024);
-  const __amdgpu_buffer_rsrc_t rqw = rsrc(a.qw, (uint64_t)g.NB * g.KS * 1024);
+  const __amdgpu_buffer_rsrc_t rqx = rsrc(a.qx6, (uint64_t)g.MB * g.KS * 1536);
+  const __amdgpu_buffer_rsrc_t rqw = rsrc(a.qw6, (uint64_t)g.NB * g.KS * 1536);
   const __amdgpu_buffer_rsrc_t rz = rsrc(a.z, (uint64_t)g.MB * per_l * 1024);
   const __amdgpu_buffer_rsrc_t rl2 = rsrc(a.l2t, (uint64_t)g.NB * per_l * 1024);
   const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, (uint64_t)g.KS * g.act_rows * 4);
@@ -218,51 +237,59 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       is_len = seg_len(sg_);                                                                        \
       const TileMap tmi = tile_of(sg_.idx);                                                         \
       const int mb0 = tmi.tm * kMB, nb0 = tmi.tn * kNBt;                                            \
-      _Pragma("unroll") for (int k = 0; k < kFragPerWave; ++k) {                                    \
-        const int it = frag0 + k;                          /* fragment item 0..23 */               \
-        const bool isA = it < 2 * kMB;                                                              \
-        const int blk = isA ? (it >> 1) : ((it - 2 * kMB) >> 1);                                     \
-        const uint32_t b = (uint32_t)min((isA ? mb0 : nb0) + blk, (isA ? g.MB : g.NB) - 1);         \
-        src[k] = (b * g.KS + (it & 1)) * 1024 + lane * 16;                                          \
-        src[kFragPerWave + k] = (b * per_l + (it & 1)) * 1024 + lane * 16;                          \
-      }                                                                                             \
-      if (sop >= 0) {                                                                               \
-        /* entry e = 4 lane (+ 256 for the second B transfer) of [2 groups][T] */                  \
-        const bool isA = sop == 0;                                                                  \
-        const int T = isA ? kBM : kBN;                                                              \
-        const int e = (sop == 2 ? 256 : 0) + 4 * lane;                                              \
-        const int gg = e >= T ? 1 : 0, idx = e - gg * T;                                            \
-        const int lim = isA ? g.act_rows : g.N;                                                     \
-        const int row = min((isA ? mb0 : nb0) * 32 + idx, lim - 4);                                 \
-        ssrc = (uint32_t)(gg * lim + row) * 4;                                                      \
-        sstride = (uint32_t)(2 * lim * 4);                                                          \
+      _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                            \
+        const int o = kOps * wave + k;                                                              \
+        if (o < kParts4) {                                                                          \
+          /* part o % 3 of row block o / 3 (A), or of (o - 12) / 3 (B) */                          \
+          const bool isA = o < 3 * kMB;                                                             \
+          const int q = isA ? o : o - 3 * kMB;                                                      \
+          const uint32_t b = (uint32_t)min((isA ? mb0 : nb0) + q / 3, (isA ? g.MB : g.NB) - 1);     \
+          src[k] = (b * (uint32_t)g.nst * 3 + q % 3) * 1024 + lane * 16;                            \
+        } else {                                                                                    \
+          /* scales: entry e = 4 lane (+ 256 for the second B half) of [2 groups][T] */            \
+          const int sop = min(o - kParts4, 2);                                                      \
+          const bool isA = sop == 0;                                                                \
+          const int T = isA ? kBM : kBN;                                                            \
+          const int e = (sop == 2 ? 256 : 0) + 4 * lane;                                            \
+          const int gg = e >= T ? 1 : 0, idx = e - gg * T;                                          \
+          const int lim = isA ? g.act_rows : g.N;                                                   \
+          const int row = min((isA ? mb0 : nb0) * 32 + idx, lim - 4);                               \
+          src[k] = (uint32_t)(gg * lim + row) * 4;                                                  \
+        }                                                                                           \
+        if (o < kPartsLr) {                                                                         \
+          /* 16-column step o % 2 of row block o / 2 (Z), or of (o - 8) / 2 (L2^T) */              \
+          const bool isA = o < 2 * kMB;                                                             \
+          const int q = isA ? o : o - 2 * kMB;                                                      \
+          const uint32_t b = (uint32_t)min((isA ? mb0 : nb0) + (q >> 1), (isA ? g.MB : g.NB) - 1);  \
+          src[kOps + k] = (b * per_l + (q & 1)) * 1024 + lane * 16;                                 \
+        }                                                                                           \
       }                                                                                             \
       bsrc = (uint32_t)min(nb0 * 32 + 8 * lane, g.N - 8) * 2;                                       \
     }                                                                                               \
-    uint8_t* slot_w = smem + ((GS) % kNStage) * kSlot;                                              \
+    uint8_t* slot_w = smem + ((GS) % NS) * kSlot;                                                   \
     const bool lrs = is_s >= is_nk;                                                                 \
     const int sl = lrs ? is_s - is_nk : is_ka + is_s;                                               \
-    if (lrs && a.r32 == 0) {                                                                        \
-      /* no low-rank fragments: every transfer of the stage moves the bias */                      \
-      _Pragma("unroll") for (int k = 0; k < kFragPerWave + 1; ++k)                                  \
-        if (k < nops && lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
-    } else {                                                                                        \
-      _Pragma("unroll") for (int k = 0; k < kFragPerWave; ++k) {                                    \
-        const int it = frag0 + k;                                                                   \
-        const bool isA = it < 2 * kMB;                                                              \
-        const int dst = isA ? kCodeA + it * 1024 : kCodeB + (it - 2 * kMB) * 1024;                  \
-        const __amdgpu_buffer_rsrc_t rs = lrs ? (isA ? rz : rl2) : (isA ? rqx : rqw);                \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(slot_w + dst), 16, src[(lrs ? kFragPerWave : 0) + k], \
-                                                 sl * 2048, 0, 0);                                  \
-      }                                                                                             \
-      if (sop >= 0) {                                                                               \
-        if (lrs) {                                                                                  \
-          if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
-        } else {                                                                                    \
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(sop == 0 ? rsx : rsw,                            \
-                                                   lds_ptr(slot_w + (sop == 0 ? kScA : kScB + 1024 * (sop - 1))), 16, \
-                                                   ssrc, sl * sstride, 0, 0);                       \
+    _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                              \
+      const int o = kOps * wave + k;                                                                \
+      if (lrs) {                                                                                    \
+        if (a.r32 > 0 && o < kPartsLr) {                                                            \
+          const bool isA = o < 2 * kMB;                                                             \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rz : rl2,                                  \
+                                                   lds_ptr(slot_w + (isA ? kCodeA + o * 1024 : kCodeB + (o - 2 * kMB) * 1024)), \
+                                                   16, src[kOps + k], sl * 2048, 0, 0);             \
+        } else if (lane < 32) {                                                                     \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
         }                                                                                           \
+      } else if (o < kParts4) {                                                                     \
+        const bool isA = o < 3 * kMB;                                                               \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rqx : rqw,                                   \
+                                                 lds_ptr(slot_w + (isA ? kCodeA + o * 1024 : kCodeB + (o - 3 * kMB) * 1024)), \
+                                                 16, src[k], sl * 3072, 0, 0);                      \
+      } else {                                                                                      \
+        const int sop = min(o - kParts4, 2);                                                        \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sop == 0 ? rsx : rsw,                              \
+                                                 lds_ptr(slot_w + (sop == 0 ? kScA : kScB + 1024 * (sop - 1))), 16, \
+                                                 src[k], sl * (sop == 0 ? sstr_a : sstr_b), 0, 0);  \
       }                                                                                             \
     }                                                                                               \
     if (++is_s == is_len) {                                                                         \
@@ -275,23 +302,24 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   f32x16 acc[kTN][kTM];
 
   // The two groups of a stage are eight units u = (group u / 4, block
-  // j = (u / 2) % 2, i = u % 2). A unit is two i8 MFMAs for 256 P, one fp32
-  // MFMA for the scale outer product, and the dequant of its 16 outputs per
-  // lane (or, DEBUG_P, the group-sum writes). Units are software-pipelined
-  // within the wave: the MFMAs of unit u + 1 are issued before the vector
-  // work of unit u, so the matrix pipe and the vector ALU run side by side.
+  // j = (u / 2) % 2, i = u % 2). A unit is one block-scaled MFMA on the FP6
+  // codes with unit E8M0 scales, which gives the group's P exactly in fp32
+  // (integer products, |P| <= 49 * 64), every other unit one fp32 MFMA for
+  // the scale outer product of two blocks, and the dequant acc += P s of
+  // its 16 outputs per lane (or, DEBUG_P, the group-sum writes). Units are
+  // software-pipelined within the wave: the MFMAs of unit u + 1 are issued
+  // before the vector work of unit u.
   // ring step being computed; ring steps still to absorb the last epilogue's
   // stores, and how many stores that epilogue issued (the same in every wave)
   int gs = 0, stores_due = 0;
   const int nstores = FUSE ? kTM * (2 + (a.nxt_r32 > 0 ? a.nxt_r32 / 32 : 0)) : kStores;
-  i32x4 alo[2][kTM], ahi[2][kTM], blo[2][kTN], bhi[2][kTN];
+  i32x8 xo[2][kTM], wo[2][kTN];   // FP6 operands: six dwords of 32 fields, two unused
   float sxv[2][kTM], swv[2][kTN];
-  i32x16 pp[2];
+  f32x16 pf[2];
   f32x16 sc[2][2];   // [block pair (u / 2) % 2][i]
   auto mfma_unit = [&](int u) {
     const int gg = u >> 2, j = (u >> 1) & 1, i = u & 1;
-    i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(blo[gg][j], alo[gg][i], i32x16{}, 0, 0, 0);
-    pp[u & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bhi[gg][j], ahi[gg][i], p, 0, 0, 0);
+    pf[u & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo[gg][j], xo[gg][i], f32x16{}, 2, 2, 0, 127, 0, 127);
     if (!DEBUG_P && i == 0) {
       // scales of blocks (j, 0) and (j, 1) in one two-block outer product:
       // block b = lane / 32 takes the 32 channel scales of block row j and
@@ -307,7 +335,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   };
   auto valu_unit = [&](int u, int st, int m0t, int n0t) {
     const int gg = u >> 2, j = (u >> 1) & 1, i = u & 1;
-    const i32x16& p = pp[u & 1];
+    const f32x16& p = pf[u & 1];
     if constexpr (DEBUG_P) {
       const int tok = m0t + wm * kWM + 32 * i + lr;
 #pragma unroll
@@ -315,68 +343,48 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
         const int ch = n0t + wn * kWN + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
         if (tok >= a.m0 && tok < a.m0 + a.mc && ch >= a.n0 && ch < a.n0 + a.nc)
           if (2 * st + gg < a.ldk / 64)   // the layer's groups (not the padding)
-            a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (a.ldk / 64) + 2 * st + gg] = p[e] / 256;
+            a.p[((size_t)(tok - a.m0) * a.nc + (ch - a.n0)) * (a.ldk / 64) + 2 * st + gg] = (int)p[e];
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][i][e] = __builtin_fmaf((float)p[e], sc[(u >> 1) & 1][i][e], acc[j][i][e]);
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = __builtin_fmaf(p[e], sc[(u >> 1) & 1][i][e], acc[j][i][e]);
     }
   };
-  // One stage: raw fragments and scales of both groups are read from LDS up
-  // front; then eight pipeline steps, each its own scheduling region: the 3
-  // MFMAs of unit u + 1 spread over the ~32 vector instructions of unit u
-  // (step 2 also widens group 1, which unit 4 needs).
+  // One stage: the FP6 operands and scales of both groups are read from LDS
+  // up front (a lane's 24 bytes: its 16-byte head and its 8-byte tail);
+  // then eight pipeline steps, each its own scheduling region: the MFMAs of
+  // unit u + 1 spread over the 16 vector instructions of unit u.
   auto stage_compute = [&](const uint8_t* slot, int st, int m0t, int n0t) {
-    i32x4 ra[2][kTM], rb[2][kTN];
-    float rsx[2][kTM], rsw[2][kTN];
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
 #pragma unroll
       for (int t = 0; t < kTM; ++t) {
-        ra[gg][t] = *reinterpret_cast<const i32x4*>(slot + kCodeA + ((wm * kTM + t) * 2 + gg) * 1024 + lane * 16);
-        rsx[gg][t] = *reinterpret_cast<const float*>(slot + kScA + gg * (kBM * 4) + (wm * kWM + 32 * t + lr) * 4);
+        const int ba = wm * kTM + t;
+        const i32x4 hd = *reinterpret_cast<const i32x4*>(slot + kCodeA + (ba * 3 + gg) * 1024 + lane * 16);
+        const u32x2 tl = *reinterpret_cast<const u32x2*>(slot + kCodeA + (ba * 3 + 2) * 1024 + gg * 512 + lane * 8);
+        xo[gg][t] = i32x8{hd[0], hd[1], hd[2], hd[3], (int)tl[0], (int)tl[1], 0, 0};
+        sxv[gg][t] = *reinterpret_cast<const float*>(slot + kScA + gg * (kBM * 4) + (wm * kWM + 32 * t + lr) * 4);
       }
 #pragma unroll
       for (int t = 0; t < kTN; ++t) {
-        rb[gg][t] = *reinterpret_cast<const i32x4*>(slot + kCodeB + ((wn * kTN + t) * 2 + gg) * 1024 + lane * 16);
-        rsw[gg][t] = *reinterpret_cast<const float*>(slot + kScB + gg * (kBN * 4) + (wn * kWN + 32 * t + lr) * 4);
+        const int bb = wn * kTN + t;
+        const i32x4 hd = *reinterpret_cast<const i32x4*>(slot + kCodeB + (bb * 3 + gg) * 1024 + lane * 16);
+        const u32x2 tl = *reinterpret_cast<const u32x2*>(slot + kCodeB + (bb * 3 + 2) * 1024 + gg * 512 + lane * 8);
+        wo[gg][t] = i32x8{hd[0], hd[1], hd[2], hd[3], (int)tl[0], (int)tl[1], 0, 0};
+        swv[gg][t] = *reinterpret_cast<const float*>(slot + kScB + gg * (kBN * 4) + (wn * kWN + 32 * t + lr) * 4);
       }
     }
-    // int8 operands; the token scale carries the 1/256 of the widened codes
-    auto widen_group = [&](int gg) {
-#pragma unroll
-      for (int t = 0; t < kTM; ++t) {
-        widen(ra[gg][t], alo[gg][t], ahi[gg][t]);
-        sxv[gg][t] = rsx[gg][t] * (1.0f / 256.0f);
-      }
-#pragma unroll
-      for (int t = 0; t < kTN; ++t) {
-        widen(rb[gg][t], blo[gg][t], bhi[gg][t]);
-        swv[gg][t] = rsw[gg][t];
-      }
-    };
-    widen_group(0);
     mfma_unit(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (u == 2) widen_group(1);
       if (u + 1 < 8) mfma_unit(u + 1);
       valu_unit(u, st, m0t, n0t);
-      if (u == 2) {
+      if (u + 1 < 8) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
-      } else if (u + 1 < 8) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       }
     if (nr > 0) {
       // zred [wave column][wave row][16][64]: one 32-token block's partials
-      float* zred = reinterpret_cast<float*>(smem + kLds);
+      float* zred = reinterpret_cast<float*>(smem + (size_t)NS * kSlot);
       const uint32_t zbytes = (uint32_t)((size_t)g.tiles_n * g.M * nr * 4);
       const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(a.nxt_zpart, 0, zbytes, 0x00020000);
       // the reduction's share of thread tid: wave row zr, token ztk of the
@@ -545,8 +553,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
   };
   __shared__ int ticket_last;   // the workgroup took a tile's last ticket
 
-  // prologue: the first kNStage - 1 ring steps in flight
-  for (int p = 0; p < kNStage - 1 && p < total; ++p) SVDQ_ISSUE(p)
+  // prologue: the first NS - 1 ring steps in flight
+  for (int p = 0; p < NS - 1 && p < total; ++p) SVDQ_ISSUE(p)
   // this lane's 16 float4 of a partial tile in a workspace slot
   auto part_at = [&](int slot_wg, int f) -> float* {
     return a.part + (size_t)slot_wg * kPartFloats + ((size_t)(wave * 16 + f) * 64 + lane) * 4;
@@ -563,10 +571,10 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 #pragma unroll
       for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
     for (int st = sg.ka; st < sg.kb; ++st) {
-      ring_barrier(DEBUG_P ? 0 : nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
+      ring_barrier(DEBUG_P ? 0 : nops * min(NS - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
       if (stores_due > 0) --stores_due;
-      if (gs + kNStage - 1 < total) SVDQ_ISSUE(gs + kNStage - 1)
-      stage_compute(smem + (gs % kNStage) * kSlot, st, m0t, n0t);
+      if (gs + NS - 1 < total) SVDQ_ISSUE(gs + NS - 1)
+      stage_compute(smem + (gs % NS) * kSlot, st, m0t, n0t);
       ++gs;
     }
     if constexpr (DEBUG_P) continue;
@@ -642,15 +650,15 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
         }
       __builtin_amdgcn_s_waitcnt(0);   // no transfer is in flight: the next ring waits stay exact
       store_tile(m0t, n0, bv);
-      stores_due = kNStage - 1;
+      stores_due = NS - 1;
       continue;
     }
     for (int l = 0; l < nlr; ++l) {
-      ring_barrier(nops * min(kNStage - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
+      ring_barrier(nops * min(NS - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
       if (stores_due > 0) --stores_due;
-      const bool more = gs + kNStage - 1 < total;
-      if (more && wave < 4) SVDQ_ISSUE(gs + kNStage - 1)
-      const uint8_t* slot = smem + (gs % kNStage) * kSlot;
+      const bool more = gs + NS - 1 < total;
+      if (more && wave < 4) SVDQ_ISSUE(gs + NS - 1)
+      const uint8_t* slot = smem + (gs % NS) * kSlot;
       if (a.r32 > 0) {
 #pragma unroll
         for (int step = 0; step < 2; ++step) {
@@ -669,12 +677,12 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
                                                                   __builtin_bit_cast(bf16x8, fa[i]), acc[j][i], 0, 0, 0);
         }
       }
-      if (more && wave >= 4) SVDQ_ISSUE(gs + kNStage - 1)
+      if (more && wave >= 4) SVDQ_ISSUE(gs + NS - 1)
       ++gs;
     }
 
     // + bias (from the last low-rank slot), bf16 write
-    const uint8_t* bslot = smem + ((gs - 1) % kNStage) * kSlot + kScA + wn * kWN * 2;
+    const uint8_t* bslot = smem + ((gs - 1) % NS) * kSlot + kScA + wn * kWN * 2;
     float bv[kTN][16];
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
@@ -697,9 +705,41 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     } else {
       store_tile(m0t, n0, bv);
     }
-    stores_due = kNStage - 1;
+    stores_due = NS - 1;
   }
 #undef SVDQ_ISSUE
+}
+
+// The tiled GEMM's FP6 copy of 4-bit codes. Nibble fragment (row block b,
+// group f): 1 KiB, lane l's 16 bytes holding channels 32 h + [0, 32) with the
+// even channel in the low nibble. Its FP6 form is lane l's 24 bytes of 32
+// six-bit fields (field i at bit 6 i: channel 32 h + i), the first 16 bytes
+// in part f % 2 and the last 8 in part 2 at (f % 2) 512 + 8 l, of the 3 KiB
+// of (b, stage f / 2). One thread per lane and fragment, X's fragments
+// first, then W's.
+__global__ void expand_fp6_kernel(const uint8_t* __restrict__ qx, uint8_t* __restrict__ x6, int64_t nfx,
+                                  const uint8_t* __restrict__ qw, uint8_t* __restrict__ w6, int64_t nfw, int KS) {
+  const int64_t total = (nfx + nfw) * 64;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t fr = t >> 6;
+    const int lane = (int)(t & 63);
+    const bool isx = fr < nfx;
+    const int64_t q = isx ? fr : fr - nfx;
+    const u32x4 in = *reinterpret_cast<const u32x4*>((isx ? qx : qw) + q * 1024 + lane * 16);
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t f = e2m3_field((in[i >> 3] >> (4 * (i & 7))) & 15u);
+      const int bit = 6 * i;
+      w[bit >> 5] |= f << (bit & 31);
+      if ((bit & 31) > 26) w[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+    }
+    const int64_t b = q / KS;
+    const int f = (int)(q - b * KS);
+    uint8_t* dst = (isx ? x6 : w6) + (b * (KS / 2) + (f >> 1)) * 3072;
+    *reinterpret_cast<u32x4*>(dst + (f & 1) * 1024 + lane * 16) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x2*>(dst + 2048 + (f & 1) * 512 + lane * 8) = u32x2{w[4], w[5]};
+  }
 }
 
 hipError_t prepare_gemm_int4() {
@@ -707,7 +747,7 @@ hipError_t prepare_gemm_int4() {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)gemm_int4_kernel<false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)(kLds + kZred));
+                          (int)kLdsFuse);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute((const void*)gemm_int4_kernel<true, false>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
@@ -727,6 +767,14 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   g.ldy = a.ldy;
   g.tm_off = g.tn_off = 0;
   int grid = num_cus > 0 ? num_cus : 256;
+  // the FP6 copies of both operands' codes, then the GEMM on them
+  if (a.qx6 == nullptr || a.qw6 == nullptr) return hipErrorInvalidValue;
+  {
+    const int64_t nfx = (int64_t)g.MB * g.KS, nfw = (int64_t)g.NB * g.KS;
+    const int64_t blocks = ((nfx + nfw) * 64 + 255) / 256;
+    hipLaunchKernelGGL(expand_fp6_kernel, dim3((unsigned)std::min<int64_t>(blocks, 16384)), dim3(256), 0, st, a.qx,
+                       a.qx6, nfx, a.qw, a.qw6, nfw, g.KS);
+  }
   if (a.p) {
     // group-sum hook: only the tiles that hold the window, no low-rank stages
     g.nstt = g.nst;
@@ -768,7 +816,7 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
     g.rounds = (ntiles + grid - 1) / grid;
     g.sk_base = ntiles;
     g.sk_tiles = 0;
-    hipLaunchKernelGGL((gemm_int4_kernel<false, true>), dim3(grid), dim3(64 * kNW), kLds + kZred, st, a, g, grid);
+    hipLaunchKernelGGL((gemm_int4_kernel<false, true>), dim3(grid), dim3(64 * kNW), kLdsFuse, st, a, g, grid);
   } else
     hipLaunchKernelGGL((gemm_int4_kernel<false, false>), dim3(grid), dim3(64 * kNW), kLds, st, a, g, grid);
   return hipGetLastError();

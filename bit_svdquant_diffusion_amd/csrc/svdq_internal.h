@@ -42,6 +42,10 @@ struct GemmArgs {
   const uint16_t* l2t;
   const uint16_t* bias;  // bf16 [N]
   uint16_t* y;           // bf16 [M][ldy]
+  // tiled INT4 GEMM: the workspace areas that receive the FP6 copies of qx
+  // and qw (the launch fills them before the GEMM; layout in ws_layout)
+  uint8_t* qx6;
+  uint8_t* qw6;
   // INT4 split of the last tiles: per-tile ticket counters (cleared by
   // stage 1) and fp32 partial tiles, in the workspace
   uint32_t* flags;

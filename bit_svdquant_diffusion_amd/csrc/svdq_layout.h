@@ -101,9 +101,20 @@ constexpr size_t kPartAreaBytes = (size_t)kSplitPieces * kSplitSlots * kSplitPar
 // low-rank branch, stage 1's partial Z: fp32, per token group and piece the
 // raw MFMA accumulators of its waves, min(round32(M), kS1SplitRows) x
 // s1_pieces(K) x 4 x rank32.
+//
+// INT4 with more than kFewTokens tokens (the tiled GEMM) ends with the codes
+// of X and of W once more, as FP6 E2M3 fields (every INT4 code, being in
+// [-7, 7], is exact in E2M3), which the GEMM's launch fills from the 4-bit
+// codes before every GEMM: per 32-row block and 128-channel stage 3 KiB,
+// [group 0 heads][group 1 heads][tails], a lane's head the first 16 of its
+// 24 bytes (32 six-bit fields, field i at bit 6 i: channel 32 h + i), its
+// tail the last 8 (group 0 at 8 lane, group 1 at 512 + 8 lane).
 struct WsLayout {
-  size_t qx, sx, z, flags, part, zp, total;
+  size_t qx, sx, z, flags, part, zp, x6, w6, total;
 };
+inline bool int4_tiled_ws(const svdq_layer_desc* d, int64_t M) {
+  return d->format == SVDQ_FMT_INT4_G64 && M > kFewTokens;
+}
 inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   WsLayout w;
   const bool int4 = d->format == SVDQ_FMT_INT4_G64;
@@ -114,7 +125,10 @@ inline WsLayout ws_layout(const svdq_layer_desc* d, int64_t M) {
   w.flags = w.z + align256((size_t)rows * rank32(d->rank) * 2);
   w.part = w.flags + (int4 ? align256((size_t)kSplitCounters * 4) : 0);
   w.zp = w.part + (int4 || M <= kFewTokens ? kPartAreaBytes : 0);
-  w.total = w.zp + (size_t)s1_pieces(kpad(d)) * (rows < kS1SplitRows ? rows : kS1SplitRows) * 4 * rank32(d->rank) * 4;
+  w.x6 = align256(w.zp + (size_t)s1_pieces(kpad(d)) * (rows < kS1SplitRows ? rows : kS1SplitRows) * 4 * rank32(d->rank) * 4);
+  const bool fp6 = int4_tiled_ws(d, M);
+  w.w6 = w.x6 + (fp6 ? align256((size_t)rows * kpad(d) / 4 * 3) : 0);
+  w.total = w.w6 + (fp6 ? align256((size_t)npad(d) * kpad(d) / 4 * 3) : 0);
   return w;
 }
 

@@ -43,7 +43,8 @@
  *     layer and the workspace hold K padded to Kp = 256 ceil(K / 256) and N
  *     padded to Np = 32 ceil(N / 32) (the padding is zero and adds nothing);
  *     MXFP4 also (Kp + 128) * ceil(M / 32) < 2^31, INT4 also
- *     32 * ceil(M / 32) * Kp < 2^33 (activation codes below 4 GiB).
+ *     32 * ceil(M / 32) * Kp * 3 / 4 < 2^32 (the tiled GEMM's FP6 copy of the
+ *     activation codes below 4 GiB).
  *   - Device pointers (x, y, workspace and every packed buffer) must be
  *     16-byte aligned; a misaligned pointer returns SVDQ_ERR_SHAPE.
  *   - All functions are thread-safe; the only global state is a per-device
@@ -210,13 +211,16 @@ SVDQ_API svdq_status svdq_unpack_weights(const svdq_layer_desc* desc, const svdq
 /*
  * Bytes of device workspace svdq_linear_forward needs for M tokens:
  * the 4-bit activation codes, their scales and the rank-32-padded
- * X_hat L1 product; INT4 layers add 32 MiB of GEMM scratch (fp32 partial
+ * X_hat L1 product; INT4 layers add 64 MiB of GEMM scratch (fp32 partial
  * tiles and flags for the workgroups that share a tile's K stages, cleared
  * by svdq_stage1), and so do MXFP4 layers with M <= 256: with few tokens
- * the weight-streaming GEMM keeps its fp32 K-share partials there. With a low-rank branch, a last area holds kernel (1)'s
- * fp32 partial X_hat L1 per K piece (about twelve pieces) for up to 4096
- * rows, used when few token groups have their K pieces dealt over the CUs.
- * Host only.
+ * the weight-streaming GEMM keeps its fp32 K-share partials there. With a
+ * low-rank branch, an area holds kernel (1)'s fp32 partial X_hat L1 per K
+ * piece (about twelve pieces) for up to 4096 rows, used when few token
+ * groups have their K pieces dealt over the CUs. INT4 layers with M > 256
+ * end with the tiled GEMM's FP6 copies of the activation and weight codes
+ * (3/4 byte per code: 32 ceil(M / 32) Kp and Np Kp codes), which every
+ * GEMM refills from the 4-bit codes. Host only.
  */
 SVDQ_API svdq_status svdq_workspace_bytes(const svdq_layer_desc* desc, int64_t M, size_t* out);
 
@@ -241,18 +245,19 @@ SVDQ_API svdq_status svdq_linear_forward(const svdq_layer_desc* desc, const svdq
  * svdq_linear_forward for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc). Same kernels and result as svdq_linear_forward; the workspace is
- * a device array the library owns, SVDQ_NOALLOC_SCRATCH_BYTES (128 MiB) per
+ * a device array the library owns, SVDQ_NOALLOC_SCRATCH_BYTES (256 MiB) per
  * GPU, set aside when the library first runs on that GPU and held until the
  * process ends. Nothing is allocated here, and M is limited to the M for which
- * svdq_workspace_bytes(desc, M) <= SVDQ_NOALLOC_SCRATCH_BYTES (every layer of
- * up to 4608 tokens with K <= 12288). Every call on one GPU uses the same
+ * svdq_workspace_bytes(desc, M) <= SVDQ_NOALLOC_SCRATCH_BYTES (every linear of
+ * a FLUX transformer block at up to 4608 tokens; the largest, K = 15360 and
+ * N = 3072, needs 211 MiB). Every call on one GPU uses the same
  * array and leaves this call's codes, scales and X_hat L1 in it: calls that
  * overlap on one GPU (two streams, or two host threads without ordering)
  * race and give wrong results, so order them.
  * Errors: as svdq_linear_forward; SVDQ_ERR_WORKSPACE when the workspace for M
  * exceeds the array.
  */
-#define SVDQ_NOALLOC_SCRATCH_BYTES (128u << 20)
+#define SVDQ_NOALLOC_SCRATCH_BYTES (256u << 20)
 SVDQ_API svdq_status svdq_linear_forward_noalloc(const svdq_layer_desc* desc, const svdq_packed* dev,
                                                  const uint16_t* x, int64_t M, uint16_t* y, void* hip_stream);
 

@@ -105,10 +105,11 @@ def test_forward_validation_before_device():
         st = L.svdq_linear_forward(ctypes.byref(big), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
                                    ws.ctypes.data, ws.nbytes, None)
         assert st == want, (M, st)
-    # INT4 activation codes use 32-bit byte offsets: round32(M) * K < 2^33
-    # (codes below 4 GiB; exactly 4 GiB is refused)
+    # the tiled INT4 GEMM's FP6 activation codes use 32-bit byte offsets:
+    # round32(M) * K * 3 / 4 < 2^32 (below 4 GiB; 87360 * 65536 * 3 / 4 is
+    # the largest multiple of 32 rows under it)
     big4 = S.LayerDesc(65536, 512, 16, 0)
-    for M, want in (((1 << 17) - 32, 4), ((1 << 17) - 31, 2), (1 << 17, 2), (1 << 20, 2)):
+    for M, want in ((87360, 4), (87361, 2), (1 << 17, 2), (1 << 20, 2)):
         st = L.svdq_linear_forward(ctypes.byref(big4), ctypes.byref(p), x.ctypes.data, M, y.ctypes.data,
                                    ws.ctypes.data, ws.nbytes, None)
         assert st == want, (M, st)
@@ -163,7 +164,7 @@ def test_noalloc_host_checks():
     device, an M whose workspace exceeds the library's array, and treats
     M == 0 as a no-op."""
     L = S.lib()
-    assert S.NOALLOC_SCRATCH_BYTES == 128 << 20
+    assert S.NOALLOC_SCRATCH_BYTES == 256 << 20
     buf = np.zeros(1 << 16, np.uint8)
     p = S.Packed(*([buf.ctypes.data] * 6))
     x = np.zeros(16, np.uint16)
