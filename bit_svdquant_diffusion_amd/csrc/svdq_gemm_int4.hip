@@ -4,22 +4,24 @@
 // actually does": the two-branch computation; "Nunchaku: the inference
 // engine...": the branches share the output write).
 //
-// Integer part. Codes are stored in the same fragment order as the MXFP4
-// path: one 1 KiB block per 32 rows and 64-channel group, lane 32h + r holding
-// the 32 channels 32h + [0, 32) of row r. Widened in registers to int8 as
-// 16*q ((w << 4) & 0xF0F0F0F0 for the even channels, w & 0xF0F0F0F0 for the
-// odd ones), one group of a 32 x 32 block is two v_mfma_i32_32x32x32_i8 (even
-// channels, then odd channels into the same accumulator), giving 256 * P
-// exactly in int32.
+// Integer part. The stored codes are 4-bit (one 1 KiB fragment per 32 rows
+// and 64-channel group, lane 32h + r holding the 32 channels 32h + [0, 32)
+// of row r). Every INT4 code lies in [-7, 7], and each of those integers is
+// exact in FP6 E2M3, so before the GEMM a small kernel copies both operands'
+// codes into the workspace as FP6 fields, and one group of a 32 x 32 block
+// is one v_mfma_scale_f32_32x32x64_f8f6f4 on FP6 operands with unit E8M0
+// scales: the products are small integers and the group sum P (|P| <= 49 *
+// 64) comes out exactly, as an fp32 value.
 //
-// Dequantization. The per-output scale s_w[n] * s_x[m] / 256 of the group is
-// an outer product, so it comes from the matrix unit as well: one two-block
-// v_mfma_f32_32x32x1_2b_f32 gives it for two 32 x 32 blocks. That leaves two
-// vector instructions per output and group, acc += float(256 P) * s, in fp32.
+// Dequantization. The per-output scale s_w[n] * s_x[m] of the group is an
+// outer product, so it comes from the matrix unit as well: one two-block
+// v_mfma_f32_32x32x1_2b_f32 gives it for two 32 x 32 blocks. That leaves one
+// vector instruction per output and group, acc += P * s, in fp32.
 //
 // Data path and schedule follow the MXFP4 kernel: persistent workgroups (one
 // per CU) walk 128 x 256 tiles; direct buffer loads into LDS of 16 bytes per
-// lane fill a ring of LDS slots across tile boundaries; eight waves, 2 (M) x
+// lane (a lane's 24 FP6 bytes in two parts) fill a ring of LDS slots across
+// tile boundaries; eight waves, 2 (M) x
 // 4 (N), each own 64 x 64 (2 x 2 blocks of 32 x 32); one workgroup barrier
 // per 128-channel stage (two groups). The low-rank branch is r32/32 more
 // stages on v_mfma_f32_32x32x16_bf16 into the same accumulators.
@@ -109,27 +111,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(uint8_t* p) { return (lds_void*)p; }
 
 
-// int8 operands of one 32-channel half of a group: 16*q of the even channels
-// (lo) and of the odd channels (hi) of a 16-byte fragment
-__device__ __forceinline__ void widen(const i32x4& w, i32x4& lo, i32x4& hi) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    lo[d] = (int)(((uint32_t)w[d] << 4) & 0xF0F0F0F0u);
-    hi[d] = (int)((uint32_t)w[d] & 0xF0F0F0F0u);
-  }
-}
-
-// FP6 E2M3 field (sign, two exponent bits with bias 1, three mantissa bits)
-// of a two's-complement INT4 code nibble. The integers 1..7 are 1.0 x 2^0,
-// 1.0 x 2^1, 1.5 x 2^1, 1.0 x 2^2, 1.25 x 2^2, 1.5 x 2^2 and 1.75 x 2^2, so
-// every code is exact. The nibble 8 (-8) is never a code (codes lie in
-// [-7, 7]); it maps to -0.
-__device__ __forceinline__ uint32_t e2m3_field(uint32_t nib) {
-  constexpr uint64_t kPos = 0x1E1C1A1814100800ull;   // nibbles 0..7, one byte each, low byte first
-  constexpr uint64_t kNeg = 0x283034383A3C3E20ull;   // nibbles 8..15: -0, -7, -6, ..., -1
-  return (uint32_t)(((nib < 8 ? kPos : kNeg) >> (8 * (nib & 7))) & 0x3Fu);
-}
-
 struct Geo {
   int M, N, K, MB, NB, KS, nst, nstt, tiles_m, tiles_n, act_rows;   // N, K padded
   int r32;
@@ -148,7 +129,7 @@ static_assert(kSplitPieces == 2, "a run holds at most two pieces: its first and 
 
 // DEBUG_P: instead of dequantizing, write every group sum P (exact int32) of
 // the outputs inside the window [m0, m0 + mc) x [n0, n0 + nc) to p, over the
-// window's tiles only, with the same transfers, widening and MFMAs.
+// window's tiles only, with the same FP6 copies, transfers and MFMAs.
 // FUSE: the tile's output is the next layer's input (GELU between them): see
 // fused_tile below. Not combined with DEBUG_P.
 template <bool DEBUG_P, bool FUSE>
@@ -269,28 +250,39 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
     uint8_t* slot_w = smem + ((GS) % NS) * kSlot;                                                   \
     const bool lrs = is_s >= is_nk;                                                                 \
     const int sl = lrs ? is_s - is_nk : is_ka + is_s;                                               \
-    _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                              \
-      const int o = kOps * wave + k;                                                                \
-      if (lrs) {                                                                                    \
-        if (a.r32 > 0 && o < kPartsLr) {                                                            \
-          const bool isA = o < 2 * kMB;                                                             \
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rz : rl2,                                  \
-                                                   lds_ptr(slot_w + (isA ? kCodeA + o * 1024 : kCodeB + (o - 2 * kMB) * 1024)), \
-                                                   16, src[kOps + k], sl * 2048, 0, 0);             \
-        } else if (lane < 32) {                                                                     \
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
+    if (lrs) {                                                                                      \
+      if (a.r32 > 0 && wave * kOps < kPartsLr) {                                                    \
+        /* Z / L2^T fragments below op 24, copies of the bias from there */                        \
+        _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                          \
+          const int o = kOps * wave + k;                                                            \
+          if (o < kPartsLr) {                                                                       \
+            const bool isA = o < 2 * kMB;                                                           \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rz : rl2,                                \
+                                                     lds_ptr(slot_w + (isA ? kCodeA + o * 1024 : kCodeB + (o - 2 * kMB) * 1024)), \
+                                                     16, src[kOps + k], sl * 2048, 0, 0);           \
+          } else if (lane < 32) {                                                                   \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
+          }                                                                                         \
         }                                                                                           \
-      } else if (o < kParts4) {                                                                     \
-        const bool isA = o < 3 * kMB;                                                               \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rqx : rqw,                                   \
-                                                 lds_ptr(slot_w + (isA ? kCodeA + o * 1024 : kCodeB + (o - 3 * kMB) * 1024)), \
-                                                 16, src[k], sl * 3072, 0, 0);                      \
       } else {                                                                                      \
-        const int sop = min(o - kParts4, 2);                                                        \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sop == 0 ? rsx : rsw,                              \
-                                                 lds_ptr(slot_w + (sop == 0 ? kScA : kScB + 1024 * (sop - 1))), 16, \
-                                                 src[k], sl * (sop == 0 ? sstr_a : sstr_b), 0, 0);  \
+        _Pragma("unroll") for (int k = 0; k < kOps; ++k) if (lane < 32)                             \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds_ptr(slot_w + kScA), 16, bsrc, 0, 0, 0); \
       }                                                                                             \
+    } else if (wave < kNW - 1) {                                                                    \
+      /* five fragment parts; part o lands at o KiB (the B area follows the A area) */             \
+      _Pragma("unroll") for (int k = 0; k < kOps; ++k) {                                            \
+        const int o = kOps * wave + k;                                                              \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(o < 3 * kMB ? rqx : rqw, lds_ptr(slot_w + kCodeA + o * 1024), 16, \
+                                                 src[k], sl * 3072, 0, 0);                          \
+      }                                                                                             \
+    } else {                                                                                        \
+      /* the last fragment part, the A scales, both B scale halves, the second again */            \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rqw, lds_ptr(slot_w + kCodeA + (kParts4 - 1) * 1024), 16, src[0], \
+                                               sl * 3072, 0, 0);                                    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, lds_ptr(slot_w + kScA), 16, src[1], sl * sstr_a, 0, 0); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, lds_ptr(slot_w + kScB), 16, src[2], sl * sstr_b, 0, 0); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, lds_ptr(slot_w + kScB + 1024), 16, src[3], sl * sstr_b, 0, 0); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, lds_ptr(slot_w + kScB + 1024), 16, src[4], sl * sstr_b, 0, 0); \
     }                                                                                               \
     if (++is_s == is_len) {                                                                         \
       is_s = 0;                                                                                     \
@@ -382,9 +374,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       valu_unit(u, st, m0t, n0t);
       if (u + 1 < 8) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -713,33 +705,33 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 // The tiled GEMM's FP6 copy of 4-bit codes. Nibble fragment (row block b,
 // group f): 1 KiB, lane l's 16 bytes holding channels 32 h + [0, 32) with the
 // even channel in the low nibble. Its FP6 form is lane l's 24 bytes of 32
-// six-bit fields (field i at bit 6 i: channel 32 h + i), the first 16 bytes
-// in part f % 2 and the last 8 in part 2 at (f % 2) 512 + 8 l, of the 3 KiB
-// of (b, stage f / 2). One thread per lane and fragment, X's fragments
-// first, then W's.
-__global__ void expand_fp6_kernel(const uint8_t* __restrict__ qx, uint8_t* __restrict__ x6, int64_t nfx,
-                                  const uint8_t* __restrict__ qw, uint8_t* __restrict__ w6, int64_t nfw, int KS) {
-  const int64_t total = (nfx + nfw) * 64;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t fr = t >> 6;
-    const int lane = (int)(t & 63);
-    const bool isx = fr < nfx;
-    const int64_t q = isx ? fr : fr - nfx;
-    const u32x4 in = *reinterpret_cast<const u32x4*>((isx ? qx : qw) + q * 1024 + lane * 16);
-    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+// E2M3 fields (field i at bit 6 i: channel 32 h + i), the first 16 bytes in
+// part f % 2 and the last 8 in part 2 at (f % 2) 512 + 8 l, of the 3 KiB of
+// (b, stage f / 2). The codes, sign-extended and converted to fp32 (exact
+// small integers), go through v_cvt_scalef32_2xpk16_fp6_f32 with scale 1,
+// which is exact for them (every integer in [-7, 7] is an E2M3 value) and
+// puts element i of its first operand in field 2 i and of its second in
+// field 2 i + 1: the even and the odd channels. One thread per lane and
+// fragment: workgroup (x, y) takes row block x (X's row blocks first, then
+// W's) and its groups 4 y .. 4 y + 3, a wave per group.
+__global__ __launch_bounds__(256) void expand_fp6_kernel(const uint8_t* __restrict__ qx, uint8_t* __restrict__ x6,
+                                                         int mbx, const uint8_t* __restrict__ qw,
+                                                         uint8_t* __restrict__ w6, int KS) {
+  const int lane = threadIdx.x & 63;
+  const bool isx = (int)blockIdx.x < mbx;
+  const size_t b = isx ? blockIdx.x : blockIdx.x - mbx;
+  const int f = 4 * blockIdx.y + (threadIdx.x >> 6);
+  const u32x4 in = *reinterpret_cast<const u32x4*>((isx ? qx : qw) + ((b * KS + f) * 64 + lane) * 16);
+  f32x16 ev, od;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t f = e2m3_field((in[i >> 3] >> (4 * (i & 7))) & 15u);
-      const int bit = 6 * i;
-      w[bit >> 5] |= f << (bit & 31);
-      if ((bit & 31) > 26) w[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
-    }
-    const int64_t b = q / KS;
-    const int f = (int)(q - b * KS);
-    uint8_t* dst = (isx ? x6 : w6) + (b * (KS / 2) + (f >> 1)) * 3072;
-    *reinterpret_cast<u32x4*>(dst + (f & 1) * 1024 + lane * 16) = u32x4{w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x2*>(dst + 2048 + (f & 1) * 512 + lane * 8) = u32x2{w[4], w[5]};
+  for (int j = 0; j < 16; ++j) {
+    ev[j] = (float)(int)__builtin_amdgcn_sbfe((int)in[j >> 2], 8 * (j & 3), 4);
+    od[j] = (float)(int)__builtin_amdgcn_sbfe((int)in[j >> 2], 8 * (j & 3) + 4, 4);
   }
+  const auto w = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  uint8_t* dst = (isx ? x6 : w6) + (b * (KS / 2) + (f >> 1)) * 3072;
+  *reinterpret_cast<u32x4*>(dst + (f & 1) * 1024 + lane * 16) = u32x4{w[0], w[1], w[2], w[3]};
+  *reinterpret_cast<u32x2*>(dst + 2048 + (f & 1) * 512 + lane * 8) = u32x2{w[4], w[5]};
 }
 
 hipError_t prepare_gemm_int4() {
@@ -769,12 +761,8 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int num_cus, hipStream_t st) {
   int grid = num_cus > 0 ? num_cus : 256;
   // the FP6 copies of both operands' codes, then the GEMM on them
   if (a.qx6 == nullptr || a.qw6 == nullptr) return hipErrorInvalidValue;
-  {
-    const int64_t nfx = (int64_t)g.MB * g.KS, nfw = (int64_t)g.NB * g.KS;
-    const int64_t blocks = ((nfx + nfw) * 64 + 255) / 256;
-    hipLaunchKernelGGL(expand_fp6_kernel, dim3((unsigned)std::min<int64_t>(blocks, 16384)), dim3(256), 0, st, a.qx,
-                       a.qx6, nfx, a.qw, a.qw6, nfw, g.KS);
-  }
+  hipLaunchKernelGGL(expand_fp6_kernel, dim3(g.MB + g.NB, g.KS / 4), dim3(256), 0, st, a.qx, a.qx6, g.MB, a.qw,
+                     a.qw6, g.KS);
   if (a.p) {
     // group-sum hook: only the tiles that hold the window, no low-rank stages
     g.nstt = g.nst;

@@ -230,10 +230,12 @@ SVDQ_API svdq_status svdq_workspace_bytes(const svdq_layer_desc* desc, int64_t M
  *   device, workspace: >= svdq_workspace_bytes(desc, M) device bytes (contents
  *   on entry are ignored; on return they hold the activation codes, scales
  *   and X_hat L1 of this call).
- * Two kernels on hip_stream: (1) smoothing + per-token 4-bit quantization +
- * X_hat L1 on bf16 MFMA from one read of X; (2) the 4-bit GEMM (INT8 MFMA
- * with int32 group sums and per-group dequant for INT4; block-scaled FP4
- * MFMA for MXFP4) whose epilogue adds (X_hat L1) L2 + b and writes bf16 Y.
+ * Kernels on hip_stream: (1) smoothing + per-token 4-bit quantization +
+ * X_hat L1 on bf16 MFMA from one read of X; (2) the 4-bit GEMM (for INT4,
+ * exact per-group sums and per-group dequant: on FP6 copies of the codes
+ * that a small kernel writes into the workspace first with more than 256
+ * tokens, on INT8 MFMA with fewer; block-scaled FP4 MFMA for MXFP4) whose
+ * epilogue adds (X_hat L1) L2 + b and writes bf16 Y.
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_FORMAT, SVDQ_ERR_WORKSPACE,
  * SVDQ_ERR_DEVICE (not gfx950 / launch failure).
  */
@@ -361,8 +363,9 @@ SVDQ_API svdq_status svdq_unpack_workspace(const svdq_layer_desc* desc, int64_t 
  * for this M (the same dispatch): the tiled kernel, over the window's tiles
  * as whole tiles, or with few tokens the weight-streaming kernel in the
  * forward's own launch shape (K shares, K parts, token parts). Both use the
- * forward's loads, nibble widening and i8 MFMAs and store each group's sum
- * instead of dequantizing it. Only entries inside the window are written.
+ * forward's operands and MFMAs (the tiled kernel's FP6 copies of the codes
+ * and block-scaled MFMAs, the few-token kernel's widened nibbles and i8
+ * MFMAs) and store each group's sum instead of dequantizing it. Only entries inside the window are written.
  * The workspace must hold svdq_stage1 output for M tokens.
  * p: int32 device [mc][nc][K/64]. Errors: as svdq_linear_forward.
  */
