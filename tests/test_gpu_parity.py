@@ -168,6 +168,58 @@ def test_stage1_outputs_logical(spec):
         assert np.abs(d).max() <= 2e-2 * np.abs(zr).max()
 
 
+def _e2m3(f: np.ndarray) -> np.ndarray:
+    """Values of 6-bit FP6 E2M3 fields: sign bit 5, exponent bits 4..3 (bias
+    1, zero = subnormal), mantissa bits 2..0."""
+    f = f.astype(np.int64)
+    e, m = (f >> 3) & 3, f & 7
+    v = np.where(e == 0, m / 8.0, (1.0 + m / 8.0) * np.exp2(e - 1.0))
+    return np.where(f & 32, -v, v)
+
+
+def _fp6_copy_values(buf: np.ndarray, rows32: int, kp: int) -> np.ndarray:
+    """[rows32][kp] values of an FP6 copy of 4-bit codes, as the tiled INT4
+    GEMM's operand layout states it: per 32-row block and 128-channel stage
+    3 KiB, the 64 lanes' 16-byte heads of group 0, then of group 1, then the
+    8-byte tails of group 0 and of group 1; lane 32h + r's 24 bytes are 32
+    six-bit fields, field i at bit 6i holding channel 32h + i of row r."""
+    nb, nst = rows32 // 32, kp // 128
+    a = buf[: nb * nst * 3072].reshape(nb, nst, 3, 1024)
+    heads = a[:, :, :2, :].reshape(nb, nst, 2, 64, 16)
+    tails = a[:, :, 2, :].reshape(nb, nst, 2, 64, 8)
+    lane = np.concatenate([heads, tails], axis=-1)
+    bits = np.unpackbits(lane, axis=-1, bitorder="little").reshape(nb, nst, 2, 64, 32, 6)
+    f = (bits.astype(np.int64) << np.arange(6)).sum(-1)
+    v = _e2m3(f).reshape(nb, nst, 2, 2, 32, 32)   # [block][stage][group][h][r][i]
+    return v.transpose(0, 4, 1, 2, 3, 5).reshape(nb * 32, nst * 128)
+
+
+@pytest.mark.parametrize("name", ["ragged_m300", "k1088_n4104_split", "k320_n40", "two_halves_m8194"])
+def test_int4_fp6_copies_hold_the_codes(name):
+    """The tiled INT4 GEMM's FP6 copies (the last two workspace areas after a
+    GEMM): decoded on the host they equal the oracle's activation codes and
+    weight codes exactly, with zeros in the padded channels and rows."""
+    spec = next(s for s in SMALL if s.name == name)
+    _say(f"[fp6 copies] {spec}")
+    layer, dev, x, ws = _run_stage1(spec)
+    y = torch.empty((spec.M, spec.N), dtype=torch.bfloat16, device="cuda")
+    S.gemm(layer, dev, ws, spec.M, y)
+    torch.cuda.synchronize()
+    kp, rows, np_ = (spec.K + 255) // 256 * 256, (spec.M + 31) // 32 * 32, (spec.N + 31) // 32 * 32
+    a256 = lambda v: (v + 255) // 256 * 256
+    buf = ws.cpu().numpy()
+    w6 = buf.size - a256(np_ * kp * 3 // 4)
+    x6 = w6 - a256(rows * kp * 3 // 4)
+    ref = C.oracle_pack(spec)
+    _, parts = O.forward(ref, C.layer_data(spec).x, return_parts=True)
+    xv = _fp6_copy_values(buf[x6:w6], rows, kp)
+    wv = _fp6_copy_values(buf[w6:], np_, kp)
+    assert np.array_equal(xv[:spec.M, :spec.K], parts["qx"].astype(np.float64)), "activation codes"
+    assert not np.any(xv[:spec.M, spec.K:]), "activation padding"
+    assert np.array_equal(wv[:spec.N, :spec.K], ref["qw"].astype(np.float64)), "weight codes"
+    assert not np.any(wv[:, spec.K:]) and not np.any(wv[spec.N:, :]), "weight padding"
+
+
 @pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
 def test_forward_matches_oracle(spec):
     _say(f"[forward] {spec}")
