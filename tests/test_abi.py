@@ -172,7 +172,8 @@ def test_noalloc_host_checks():
         d = S.LayerDesc(K, N, 32, fmt)
         # 4608 tokens fit (the documented bound); far more do not
         assert S.workspace_bytes(S.Layer(K, N, 32, "int4" if fmt == 0 else "mxfp4"), 4608) <= S.NOALLOC_SCRATCH_BYTES
-        big = 1 << 16
+        big = 1 << 18   # its workspace exceeds the array in every format
+        assert S.workspace_bytes(S.Layer(K, N, 32, "int4" if fmt == 0 else "mxfp4"), big) > S.NOALLOC_SCRATCH_BYTES
         assert L.svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, big,
                                              x.ctypes.data, None) == 4
         assert L.svdq_linear_forward_noalloc(ctypes.byref(d), ctypes.byref(p), x.ctypes.data, 0,
