@@ -338,10 +338,12 @@ SVDQ_API svdq_status svdq_stage1_outputs(const svdq_layer_desc* desc, const svdq
                                          size_t workspace_bytes, void* hip_stream);
 
 /*
- * Kernel (2) of svdq_linear_forward alone: the 4-bit GEMM with its epilogue,
- * reading the activation codes, scales and X_hat L1 that svdq_stage1 left in
- * `workspace` for the same M. svdq_stage1 followed by svdq_gemm on one stream
- * equals svdq_linear_forward. Errors: as svdq_linear_forward.
+ * Kernel (2) of svdq_linear_forward alone: the 4-bit GEMM with its epilogue
+ * (for INT4 with more than 256 tokens, preceded by the kernel that writes the
+ * FP6 copies of the codes into the workspace), reading the activation codes,
+ * scales and X_hat L1 that svdq_stage1 left in `workspace` for the same M.
+ * svdq_stage1 followed by svdq_gemm on one stream equals svdq_linear_forward.
+ * Errors: as svdq_linear_forward.
  */
 SVDQ_API svdq_status svdq_gemm(const svdq_layer_desc* desc, const svdq_packed* dev,
                                const void* workspace, size_t workspace_bytes, int64_t M,
