@@ -110,7 +110,10 @@ typedef struct {
  * of a 64-lane fragment holds row 32b + r):
  *   qw   u8 [N/32][K/64][64][16]  lane 32h + r: 4-bit codes (INT4 two's
  *                                 complement or E2M1) of channels 64s + 32h +
- *                                 [0, 32), two per byte, low nibble first
+ *                                 [0, 32), two per byte, low nibble first;
+ *                                 INT4 codes lie in [-7, 7] (the nibble 8,
+ *                                 -8, is outside the format: the tiled GEMM's
+ *                                 FP6 copy cannot hold it)
  *   l2   bf16 [N/32][rank32/16][64][8]  L2 transposed, rank padded to a multiple
  *                                 of 32 (zeros); lane 32h + r of step c holds
  *                                 rank columns 16c + 8h + [0, 8)
