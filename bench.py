@@ -30,8 +30,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "SVDQuant W4A4 linear effective TOPS at 4608×3072×12288; % of MFMA peak"
-PEAK_TFLOPS = {"mxfp4": 10100.0, "int4": 10100.0}   # MI355X dense MFMA: FP4 and FP6 10.1 PF (the tiled INT4 GEMM
-# runs its group sums on FP6 E2M3 copies of the codes)
+PEAK_TFLOPS = {"mxfp4": 10100.0, "fp6": 10100.0, "i8": 5000.0}   # MI355X dense MFMA: FP4 and FP6
+# 10.1 PF, INT8 5.0 POPS
+
+
+def int4_gemm_mfma(M, N, cus):
+    """The MFMA an INT4 layer's GEMM runs on: the tiled kernel's FP6 copies of
+    the codes, or the few-token kernel's INT8 (the library's dispatch rule:
+    at most 256 tokens, or 769 to 1024 unless the 32-channel blocks overfill
+    one round of CUs by at most a quarter)."""
+    nb = (N + 31) // 32
+    small = M <= 256 or (768 < M <= 1024 and not (nb > cus and 4 * nb <= 5 * cus))
+    return "i8" if small else "fp6"
 PEAK_HBM_GBS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm_mxfp4_mlp_up_4608x3072x12288_counters.md")
 GEMM_SOURCE = os.path.join(ROOT, "bit_svdquant_diffusion_amd", "csrc", "svdq_gemm_mxfp4.hip")
@@ -363,11 +373,12 @@ def bench_c4(args, torch, S, synth):
         fl = 2.0 * sp.M * sp.N * sp.K
         hb = stage1_bytes(sp) + gemm_bytes(sp)
         t = fl / (ms * 1e-3) / 1e12
+        mf = int4_gemm_mfma(sp.M, sp.N, torch.cuda.get_device_properties(0).multi_processor_count)
         gbs = hb / (ms * 1e-3) / 1e9
         rows.append({"workload": sp.name, "M": sp.M, "K": sp.K, "N": sp.N, "rank": sp.rank, "format": sp.fmt,
                      "us": round(ms * 1e3, 2), "us_eager_launches": round(ms_eager * 1e3, 2),
-                     "effective_tops": round(t, 2),
-                     "pct_of_fp6_peak": round(100 * t / PEAK_TFLOPS["int4"], 2),
+                     "effective_tops": round(t, 2), "gemm_mfma": mf,
+                     "pct_of_mfma_peak": round(100 * t / PEAK_TFLOPS[mf], 2),
                      "hbm_algorithmic_bytes": hb, "hbm_gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                      "stage1_us": round(a1 * 1e3, 2), "gemm_us": round(a2 * 1e3, 2)})
@@ -566,7 +577,7 @@ def main():
             t = fl / (ms2 * 1e-3) / 1e12
             sec.append({"workload": sp.name, "M": sp.M, "K": sp.K, "N": sp.N, "rank": sp.rank,
                         "format": sp.fmt, "ms_per_step": round(ms2, 6), "effective_tops": round(t, 2),
-                        "pct_of_fp6_peak": round(100 * t / PEAK_TFLOPS["int4"], 2),
+                        "gemm_mfma": "fp6", "pct_of_mfma_peak": round(100 * t / PEAK_TFLOPS["fp6"], 2),
                         "stage1_us": round(a1 * 1e3, 2), "gemm_us": round(a2 * 1e3, 2)})
             log(f"{sp.name}: {ms2 * 1e3:.1f} us/step, {t:.1f} TOPS (stage1 {a1*1e3:.1f} us, gemm {a2*1e3:.1f} us)")
         out["secondary"] = sec
