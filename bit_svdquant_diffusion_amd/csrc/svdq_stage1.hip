@@ -32,6 +32,8 @@
 // swizzled by the token index, so the read-back is free of bank conflicts.
 // The four partial Z tiles are summed in LDS in wave order (deterministic)
 // and stored as bf16.
+#include <type_traits>
+
 #include "svdq_device.h"
 #include "svdq_internal.h"
 #include "svdq_layout.h"
@@ -228,15 +230,22 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) S1_ISSUE()
 
-  for (int i = 0; i < T; ++i) {
+  // One step of the walk. The first D steps wait for counts that depend on
+  // the step; every later step waits for the same count, so the walk runs
+  // them in a second copy of the body whose wait is a constant.
+  auto step = [&](const int i, auto steady) {
         // 1. step i's transfers have landed once only the operations issued
         //    after them are outstanding (a finished piece's partial-Z stores
         //    only add to those: the wait gets longer, never shorter)
         __builtin_amdgcn_sched_barrier(0);
-        switch (i < D ? i : D) {
-          S1_WAIT_CASE(0) S1_WAIT_CASE(1) S1_WAIT_CASE(2) S1_WAIT_CASE(3)
-          S1_WAIT_CASE(4) S1_WAIT_CASE(5) S1_WAIT_CASE(6) S1_WAIT_CASE(7)
-          default: __builtin_amdgcn_s_waitcnt(S1_VMCNT(0)); break;
+        if constexpr (decltype(steady)::value) {
+          __builtin_amdgcn_s_waitcnt(S1_VMCNT(Cfg::count(D)));
+        } else {
+          switch (i) {
+            S1_WAIT_CASE(0) S1_WAIT_CASE(1) S1_WAIT_CASE(2) S1_WAIT_CASE(3)
+            S1_WAIT_CASE(4) S1_WAIT_CASE(5) S1_WAIT_CASE(6) S1_WAIT_CASE(7)
+            default: __builtin_amdgcn_s_waitcnt(S1_VMCNT(0)); break;
+          }
         }
         // both halves' L1 transfers are in: the other half's become visible
         // at the barrier, which also means every wave is done reading the
@@ -261,17 +270,19 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
         __builtin_amdgcn_sched_barrier(0);
         const int k0 = cs * S1_STEP + q * 64;   // first channel of the quarter
         // a quarter past the layer's channels (padding up to whole steps) is zero
-        const bool live = k0 < XK;
+        // (an all-ones or all-zeros mask ANDed into the products: a select per
+        // value would be compiled into branches that copy the whole array)
+        const uint32_t live = k0 < XK ? 0xFFFFFFFFu : 0u;
         float xh[16];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const f32x4 mv = muv[t];
           const u32x4& xw = t < 2 ? xa : xb;
           const uint32_t w0 = xw[(t & 1) * 2], w1 = xw[(t & 1) * 2 + 1];
-          xh[4 * t + 0] = live ? bf16lo(w0) * mv.x : 0.f;
-          xh[4 * t + 1] = live ? bf16hi(w0) * mv.y : 0.f;
-          xh[4 * t + 2] = live ? bf16lo(w1) * mv.z : 0.f;
-          xh[4 * t + 3] = live ? bf16hi(w1) * mv.w : 0.f;
+          xh[4 * t + 0] = __uint_as_float(__float_as_uint(bf16lo(w0) * mv.x) & live);
+          xh[4 * t + 1] = __uint_as_float(__float_as_uint(bf16hi(w0) * mv.y) & live);
+          xh[4 * t + 2] = __uint_as_float(__float_as_uint(bf16lo(w1) * mv.z) & live);
+          xh[4 * t + 3] = __uint_as_float(__float_as_uint(bf16hi(w1) * mv.w) & live);
         }
 
         // 3. Z += bf16(x_hat) L1: MFMA t takes channels 16j + 8t .. +7 of each lane
@@ -332,7 +343,10 @@ __global__ __launch_bounds__(64 * S1_WAVES * TH) void stage1_kernel(
           ++cp;
           if (cp < pe) compute_next();
         }
-  }
+  };
+  const int T0 = T < D ? T : D;
+  for (int i = 0; i < T0; ++i) step(i, std::false_type{});
+  for (int i = T0; i < T; ++i) step(i, std::true_type{});
 #undef S1_ISSUE
 #undef S1_WAIT_CASE
   // the transfers issued past the last step still write the ring
