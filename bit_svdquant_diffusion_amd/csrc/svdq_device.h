@@ -93,18 +93,21 @@ __device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint3
 // exactly, rounds to nearest even and saturates), else the exact
 // software encoder. Shared by stage 1 and the GEMM epilogue that quantizes
 // the next layer's activations, so both give the same bits.
+// Every lane runs the converter (with the smallest normal scale where its
+// own would be denormal); only lanes with e = -127 then redo their values in
+// software, so the common case has no branch around the converter.
 __device__ __forceinline__ uint32_t e2m1x8_codes(const float* v, int e) {
-  if (e >= -126) {
-    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], sc, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
-  }
-  const float sinv = exp2_neg(e);
-  uint32_t w = 0;
+  const float sc = __uint_as_float((uint32_t)((e >= -126 ? e : -126) + 127) << 23);
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], sc, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
+  if (e < -126) {
+    const float sinv = exp2_neg(e);
+    w = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w |= e2m1_code(v[i] * sinv) << (4 * i);
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(v[i] * sinv) << (4 * i);
+  }
   return w;
 }
 

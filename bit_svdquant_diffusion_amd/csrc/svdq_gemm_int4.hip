@@ -90,11 +90,18 @@ static_assert(2 * kBM * 4 == 1024 && 2 * kBN * 4 == 2048 && kBN * 2 <= 1024,
 // rule as the MXFP4 kernel: operations retire in issue order, so n = the
 // number issued after the transfer being waited for).
 #define SVDQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)   /* expcnt 7, lgkmcnt 0 */
-__device__ __forceinline__ void ring_barrier(int n) {
+// `steady`: the step has two ring steps in flight after it and no stores
+// counted, so n = C. Tested first, on its own flag: a test of n itself is
+// folded by the compiler into the search through the cases, which every step
+// would then walk.
+template <int C>
+__device__ __forceinline__ void ring_barrier(bool steady, int n) {
   __builtin_amdgcn_sched_barrier(0);
 #define SVDQ_WAIT_CASE(k) \
   case k: __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(k)); break;
-  switch (n < 24 ? n : 24) {   // a larger n waits for 24: longer than needed, never shorter
+  if (steady) {
+    __builtin_amdgcn_s_waitcnt(SVDQ_VMCNT(C));
+  } else switch (n < 24 ? n : 24) {   // a larger n waits for 24: longer than needed, never shorter
     SVDQ_WAIT_CASE(1) SVDQ_WAIT_CASE(2) SVDQ_WAIT_CASE(3) SVDQ_WAIT_CASE(4) SVDQ_WAIT_CASE(5) SVDQ_WAIT_CASE(6)
     SVDQ_WAIT_CASE(7) SVDQ_WAIT_CASE(8) SVDQ_WAIT_CASE(9) SVDQ_WAIT_CASE(10) SVDQ_WAIT_CASE(11) SVDQ_WAIT_CASE(12)
     SVDQ_WAIT_CASE(13) SVDQ_WAIT_CASE(14) SVDQ_WAIT_CASE(15) SVDQ_WAIT_CASE(16) SVDQ_WAIT_CASE(17)
@@ -563,7 +570,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
 #pragma unroll
       for (int i = 0; i < kTM; ++i) acc[j][i] = f32x16{};
     for (int st = sg.ka; st < sg.kb; ++st) {
-      ring_barrier(DEBUG_P ? 0 : nops * min(NS - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
+      ring_barrier<kOps * (NS - 2)>(!DEBUG_P && stores_due == 0 && total - 1 - gs >= NS - 2,
+                                    DEBUG_P ? 0 : nops * min(NS - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
       if (stores_due > 0) --stores_due;
       if (gs + NS - 1 < total) SVDQ_ISSUE(gs + NS - 1)
       stage_compute(smem + (gs % NS) * kSlot, st, m0t, n0t);
@@ -646,7 +654,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_int4_kernel(GemmArgs a, Geo g, 
       continue;
     }
     for (int l = 0; l < nlr; ++l) {
-      ring_barrier(nops * min(NS - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
+      ring_barrier<kOps * (NS - 2)>(stores_due == 0 && total - 1 - gs >= NS - 2,
+                                    nops * min(NS - 2, total - 1 - gs) + (stores_due > 0 ? nstores : 0));
       if (stores_due > 0) --stores_due;
       const bool more = gs + NS - 1 < total;
       if (more && wave < 4) SVDQ_ISSUE(gs + NS - 1)
