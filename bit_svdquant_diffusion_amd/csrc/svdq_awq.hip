@@ -19,8 +19,9 @@
 // K-part order through LDS. Tokens go in chunks of up to 16 (the MFMA's
 // rows): the chunk's live rows of x_hat (bf16, rows padded by 8 channels
 // against LDS bank conflicts) and their S sit in LDS, so with a couple of
-// rows the LDS is small and several workgroups share a CU; rows past the
-// chunk enter the MFMA as zeros. Each wave keeps six groups of weights in
+// rows the LDS is small and several workgroups share a CU; MFMA rows past
+// the chunk repeat a staged row, and their outputs are never stored. Each
+// wave keeps six groups of weights in
 // flight (16-byte loads, 1 KiB per n-block and group), the first ones issued
 // before the staging.
 #include "svdq_device.h"
@@ -211,7 +212,14 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
       }
     };
     finish_parts(g0);
-    const bool arow = r < rc;   // this lane's MFMA row is a live token
+    // the group after which the next part closes: the per-group test is one
+    // comparison, and the part bookkeeping runs only where a part ends
+    int next_end = kParts > 1 && q < kParts ? part_end(q) : 0x7fffffff;
+    // A row r of the MFMA feeds only output row r (token r of the chunk):
+    // lanes of rows past the chunk read a staged row (the last one, so the
+    // read stays inside the staging area) and their outputs are not stored.
+    // An unconditional read lets the group's four reads issue together.
+    const int arow_off = min(r, rows - 1) * ldx;
     for (int gb = g0; gb < g1; gb += kAwqRing) {
 #pragma unroll
       for (int u = 0; u < kAwqRing; ++u) {
@@ -222,8 +230,7 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
           for (int t = 0; t < 4; ++t) {
             // A: token r, channels 128 g + 32 t + 8 c + (0..7); B: the same
             // channels of output 16 nb + r as bf16 128 + q
-            const u32x4 av = arow ? *reinterpret_cast<const u32x4*>(xs + (size_t)r * ldx + g * 128 + 32 * t + 8 * c)
-                                  : u32x4{0, 0, 0, 0};
+            const u32x4 av = *reinterpret_cast<const u32x4*>(xs + arow_off + g * 128 + 32 * t + 8 * c);
             const uint32_t w = (uint32_t)wq[u][t];
             const u32x4 bv = u32x4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
                                    ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
@@ -237,7 +244,10 @@ __global__ __launch_bounds__(64 * kAwqWaves) __attribute__((amdgpu_waves_per_eu(
           if (g + kAwqRing < g1) load(u, g + kAwqRing);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(scu, __builtin_fmaf(-zf, s4[e], p[e]), acc[e]);
-          finish_parts(g + 1);
+          if (g + 1 >= next_end) {
+            finish_parts(g + 1);
+            next_end = q < kParts ? part_end(q) : 0x7fffffff;
+          }
         }
       }
     }
